@@ -1,0 +1,356 @@
+/*
+ * bitnet_oracle.c -- plain, slow CPU oracle for the W1.58A8 BitLinear.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the CPU-baseline
+ * leg of the benchmark load this file's shared object; the product library
+ * never includes, links or calls it, and it shares no code with the HIP path.
+ *
+ * Pages cited (title, then section):
+ *   [BitVLA] "BitVLA -- 1.58-bit Vision-Language-Action on Core AI"
+ *            (Core AI model zoo).
+ *   [Guide]  "BitNet-Embeddings-0.6B/270M: I2_S Conversion and Inference
+ *            Optimization Guide" (microsoft/BitNet docs).
+ *   [BitMar] "BitMar: Low-Bit Multimodal Fusion with Episodic Memory for Edge
+ *            Devices" (AI summary page).
+ *
+ * What is computed (y = linear(ActQuant(x), WeightQuant(W)), no bias):
+ *   WeightQuant  [BitVLA s1; Guide s2 and s3.3 "I2_S Ternary Packing"]:
+ *                one scale per source tensor, s = 1/mean|W|, codes
+ *                t = clamp(round(W*s), -1, +1), dequantised value t/s.
+ *   ActQuant     [BitVLA s1; Guide s2]: per token, int8 codes
+ *                q = clamp(round(x*127/max|x|), -128, 127), dequantised by
+ *                dividing by 127/max|x|.
+ *   Encoding     [Guide s3.3; BitVLA s2]: stored code u = t + 1, i.e.
+ *                -1 -> 0, 0 -> 1, +1 -> 2.
+ *   Tails        [BitVLA s2]: K must be a multiple of 16; N is arbitrary.
+ *
+ * Readings taken where the pages leave a step open (each one is also listed
+ * with its reasons in the design notes of the repository):
+ *   R1  "round" is round-half-to-even, for weights and activations.
+ *   R2  mean|W| is an fp64 sum of |W| over k ascending within a row, then
+ *       over the tensor's rows ascending, one fp64 division by rows*K, then
+ *       rounding to fp32.
+ *   R3  s = 1/mean is an fp32 division; the code uses the fp32 product W*s.
+ *   R4  ActQuant uses one fp32 factor sa = 127/amax, then the fp32 product
+ *       x*sa; a_scale = amax/127 (fp32 division).
+ *   R5  A token with amax == 0 gets q = 0 and a_scale = 0.
+ *   R6  A fused weight (q|k|v, gate|up) keeps one scale per source tensor
+ *       ("segment"); w_scale[n] is the scale of row n's segment.
+ *   R7  Where W*s is NaN (only 0 * inf, i.e. a zero weight in a tensor whose
+ *       mean rounded to 0) the code is 0.
+ *   R8  Epilogue: f = a_scale[m] * w_scale[n] in fp32, then y = (float)acc * f
+ *       in fp32; a bf16 output is y rounded to nearest-even.
+ *   R9  Storage layout ("layout v1", this library's own, not I2_S):
+ *       Kp = K rounded up to a multiple of 128; row n occupies Kp/4 bytes;
+ *       element k of a row is in byte 4*(k/16) + (k%4), bits
+ *       2*((k%16)/4) .. +1; positions k >= K hold code 1 (weight 0).
+ *
+ * Everything here is a direct loop over the definition.  No blocking, no
+ * fusion, no intrinsics.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+/* ---------------------------------------------------------------- scalars */
+
+/* bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits. */
+float orc_bf16_to_f32(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN. */
+uint16_t orc_f32_to_bf16(float f)
+{
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    if (isnan(f))
+        return (uint16_t)((bits >> 16) | 0x0040u);
+    uint32_t upper = bits >> 16;        /* truncated candidate               */
+    uint32_t rest = bits & 0xFFFFu;     /* the part that is dropped          */
+    if (rest > 0x8000u)
+        upper += 1;                     /* more than half: round up          */
+    else if (rest == 0x8000u && (upper & 1u))
+        upper += 1;                     /* exactly half: round to even       */
+    return (uint16_t)upper;             /* carry into the exponent is right: */
+                                        /* it yields the next binade or inf  */
+}
+
+static float load_elem(const void* base, int dtype, int64_t idx)
+{
+    if (dtype == ORC_BF16)
+        return orc_bf16_to_f32(((const uint16_t*)base)[idx]);
+    return ((const float*)base)[idx];
+}
+
+/* round half to even in the current (default: nearest-even) mode, R1 */
+static float round_half_even(float v)
+{
+    return nearbyintf(v);
+}
+
+int64_t orc_padded_k(int64_t K)
+{
+    if (K <= 0 || K % 16 != 0)
+        return -1;
+    return (K + 127) / 128 * 128;
+}
+
+/* ------------------------------------------------------------ WeightQuant */
+
+/* Sum of |W[n, k]| for k = 0..K-1, ascending, in fp64 (R2). */
+double orc_row_abs_sum(const void* W, int dtype, int64_t n, int64_t K, int64_t ldw)
+{
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        s += fabs((double)load_elem(W, dtype, n * ldw + k));
+    return s;
+}
+
+/* mean|W| of rows [row0, row0 + rows): row sums added in row order (R2). */
+float orc_segment_mean(const void* W, int dtype, int64_t row0, int64_t rows,
+                       int64_t K, int64_t ldw)
+{
+    double total = 0.0;
+    for (int64_t n = row0; n < row0 + rows; ++n)
+        total += orc_row_abs_sum(W, dtype, n, K, ldw);
+    return (float)(total / (double)(rows * K));
+}
+
+/* Ternary code of one weight given the tensor's fp32 factor s (R1, R3, R7). */
+int8_t orc_ternary(float w, float s)
+{
+    float p = w * s;
+    if (isnan(p))
+        return 0;
+    float r = round_half_even(p);
+    if (r > 1.0f)
+        r = 1.0f;
+    if (r < -1.0f)
+        r = -1.0f;
+    return (int8_t)r;
+}
+
+/*
+ * WeightQuant of an [N, K] tensor made of n_segs source tensors stacked by
+ * rows (seg_rows[i] rows each; n_segs == 0 means one tensor of N rows).
+ * Outputs: t [N][K] codes in {-1,0,1}; w_scale [N]; seg_mean [n_segs or 1];
+ * zero_count [n_segs or 1] = number of zero codes among the real K columns.
+ * Returns 0, or -1 if the segment rows do not add up to N, or -2 if a weight
+ * is not finite.
+ */
+int orc_weight_quant(const void* W, int dtype, int64_t N, int64_t K, int64_t ldw,
+                     const int64_t* seg_rows, int32_t n_segs,
+                     int8_t* t, float* w_scale, float* seg_mean, int64_t* zero_count)
+{
+    int64_t one = N;
+    if (n_segs <= 0) {
+        seg_rows = &one;
+        n_segs = 1;
+    }
+    int64_t total = 0;
+    for (int32_t i = 0; i < n_segs; ++i)
+        total += seg_rows[i];
+    if (total != N)
+        return -1;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            if (!isfinite(load_elem(W, dtype, n * ldw + k)))
+                return -2;
+
+    int64_t row0 = 0;
+    for (int32_t i = 0; i < n_segs; ++i) {
+        float mean = orc_segment_mean(W, dtype, row0, seg_rows[i], K, ldw);
+        float s = 1.0f / mean;
+        int64_t zeros = 0;
+        for (int64_t n = row0; n < row0 + seg_rows[i]; ++n) {
+            w_scale[n] = mean;
+            for (int64_t k = 0; k < K; ++k) {
+                int8_t c = orc_ternary(load_elem(W, dtype, n * ldw + k), s);
+                t[n * K + k] = c;
+                zeros += (c == 0);
+            }
+        }
+        if (seg_mean)
+            seg_mean[i] = mean;
+        if (zero_count)
+            zero_count[i] = zeros;
+        row0 += seg_rows[i];
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------- layout v1 */
+
+/* Byte index and bit offset of element k inside a row (R9). */
+static int64_t v1_byte(int64_t k) { return 4 * (k / 16) + (k % 4); }
+static int v1_shift(int64_t k) { return (int)(2 * ((k % 16) / 4)); }
+
+/* Pack codes t [N][K] into packed [N][Kp/4]; stored code u = t + 1. */
+int orc_pack(const int8_t* t, int64_t N, int64_t K, uint8_t* packed)
+{
+    int64_t Kp = orc_padded_k(K);
+    if (Kp < 0)
+        return -1;
+    int64_t row_bytes = Kp / 4;
+    memset(packed, 0, (size_t)(N * row_bytes));
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < Kp; ++k) {
+            unsigned u = (k < K) ? (unsigned)(t[n * K + k] + 1) : 1u;
+            packed[n * row_bytes + v1_byte(k)] |= (uint8_t)(u << v1_shift(k));
+        }
+    }
+    return 0;
+}
+
+/* Inverse of orc_pack over the real columns.  Returns -1 on a bad K, or the
+ * number of 2-bit fields that hold the unused value 3 (0 for a valid buffer). */
+int64_t orc_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* t)
+{
+    int64_t Kp = orc_padded_k(K);
+    if (Kp < 0)
+        return -1;
+    int64_t row_bytes = Kp / 4, bad = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            unsigned u = (packed[n * row_bytes + v1_byte(k)] >> v1_shift(k)) & 3u;
+            bad += (u == 3u);
+            t[n * K + k] = (int8_t)((int)u - 1);
+        }
+    }
+    return bad;
+}
+
+/* -------------------------------------------------------------- ActQuant */
+
+/*
+ * Per-token ActQuant of x [M, K] (row stride ldx, fp32 or bf16).
+ * q [M][Kp]: int8 codes, columns K..Kp-1 set to 0.  a_scale [M] = amax/127.
+ * q_rowsum [M] = sum of q over the row.  (R1, R4, R5.)
+ */
+int orc_act_quant(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                  int8_t* q, float* a_scale, int32_t* q_rowsum)
+{
+    int64_t Kp = orc_padded_k(K);
+    if (Kp < 0)
+        return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(load_elem(x, dtype, m * ldx + k));
+            if (a > amax)
+                amax = a;
+        }
+        int64_t sum = 0;
+        if (amax == 0.0f) {
+            for (int64_t k = 0; k < Kp; ++k)
+                q[m * Kp + k] = 0;
+            a_scale[m] = 0.0f;
+        } else {
+            float sa = 127.0f / amax;
+            for (int64_t k = 0; k < K; ++k) {
+                float r = round_half_even(load_elem(x, dtype, m * ldx + k) * sa);
+                if (r > 127.0f)
+                    r = 127.0f;
+                if (r < -128.0f)
+                    r = -128.0f;
+                q[m * Kp + k] = (int8_t)r;
+                sum += (int8_t)r;
+            }
+            for (int64_t k = K; k < Kp; ++k)
+                q[m * Kp + k] = 0;
+            a_scale[m] = amax / 127.0f;
+        }
+        q_rowsum[m] = (int32_t)sum;
+    }
+    return 0;
+}
+
+/* ----------------------------------------------------------- integer dot */
+
+/*
+ * acc[m][n] = sum_{k<K} q[m][k] * t[n][k], summed in int64 and stored as
+ * int32.  q has row stride Kp, t has row stride K.  Rows n are split over
+ * nthreads threads (results do not depend on it).  Returns -1 if a sum does
+ * not fit in int32.
+ */
+int orc_int_dot(const int8_t* q, int64_t M, int64_t K, const int8_t* t, int64_t N,
+                int32_t* acc, int nthreads)
+{
+    int64_t Kp = orc_padded_k(K);
+    if (Kp < 0)
+        return -1;
+    int overflow = 0;
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static) reduction(| : overflow)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int64_t)q[m * Kp + k] * (int64_t)t[n * K + k];
+            if (s > INT32_MAX || s < INT32_MIN)
+                overflow = 1;
+            acc[m * N + n] = (int32_t)s;
+        }
+    }
+    return overflow ? -1 : 0;
+}
+
+/* The same sum for a list of (m, n) pairs only. */
+int orc_int_dot_pairs(const int8_t* q, int64_t K, const int8_t* t,
+                      int64_t n_pairs, const int64_t* m_idx, const int64_t* n_idx,
+                      int32_t* acc)
+{
+    int64_t Kp = orc_padded_k(K);
+    if (Kp < 0)
+        return -1;
+    for (int64_t i = 0; i < n_pairs; ++i) {
+        int64_t s = 0;
+        for (int64_t k = 0; k < K; ++k)
+            s += (int64_t)q[m_idx[i] * Kp + k] * (int64_t)t[n_idx[i] * K + k];
+        acc[i] = (int32_t)s;
+    }
+    return 0;
+}
+
+/* -------------------------------------------------------------- epilogue */
+
+/* y[m][n] = (float)acc[m][n] * (a_scale[m] * w_scale[n]), all fp32 (R8). */
+float orc_dequant_one(int32_t acc, float a_scale, float w_scale)
+{
+    float f = a_scale * w_scale;
+    return (float)acc * f;
+}
+
+void orc_epilogue(const int32_t* acc, int64_t M, int64_t N, const float* a_scale,
+                  const float* w_scale, int out_dtype, void* y, int64_t ldy)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float v = orc_dequant_one(acc[m * N + n], a_scale[m], w_scale[n]);
+            if (out_dtype == ORC_BF16)
+                ((uint16_t*)y)[m * ldy + n] = orc_f32_to_bf16(v);
+            else
+                ((float*)y)[m * ldy + n] = v;
+        }
+    }
+}
+
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

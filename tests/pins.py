@@ -1,0 +1,339 @@
+"""Pins: checks that tie the CPU oracle to things other than itself.
+
+Each ``pin_*`` function takes an ``Oracle`` handle and raises AssertionError if
+the oracle disagrees with a hand-worked example from the pages' formulas
+(``tests/golden``), a closed form, an invariant, a library routine on a special
+case, or a brute force on tiny inputs.  The same functions run against the
+committed oracle (all must pass) and against deliberately broken copies of it
+(at least one must fail), which shows that the set is sharp enough to catch a
+dropped term, a wrong sign or index, or a transposed operand.
+
+Run as a script (``python tests/pins.py <liboracle.so>``) it prints a JSON list
+of the pins that failed; the mutation test uses that to isolate each broken
+copy in a process of its own.
+"""
+from __future__ import annotations
+
+import json
+import math
+import sys
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parents[1]
+GOLDEN = Path(__file__).resolve().parent / "golden"
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+import brute  # noqa: E402  (tests/brute.py: independent fp64 brute force)
+
+
+# ----------------------------------------------------------------- helpers
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Exactly representable fp32 values -> bf16 bit patterns (truncation is exact here)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    bits = a.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0), "fixture value is not exactly representable in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32)
+
+
+def read_golden(name: str) -> dict:
+    out: dict = {}
+    for line in (GOLDEN / name).read_text().splitlines():
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *vals = line.split()
+        out.setdefault(key, []).append(vals)
+    return out
+
+
+def rng_bf16(rng: np.random.Generator, shape, scale=1.0, dist="normal") -> np.ndarray:
+    if dist == "normal":
+        v = rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)
+    else:
+        v = rng.laplace(0.0, scale / math.sqrt(2.0), size=shape).astype(np.float32)
+    # round-to-nearest-even to bf16 done in integer arithmetic (input prep only)
+    bits = v.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return bits.astype(np.uint16)
+
+
+# -------------------------------------------------------------------- pins
+
+def pin_bf16_conversions(orc):
+    """bf16<->fp32 conversions against the IEEE definition / torch's rounding."""
+    import torch
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    widened = np.array([orc.lib.orc_bf16_to_f32(int(b)) for b in allbits[::257]], dtype=np.float32)
+    ref = bf16_bits_to_f32(allbits[::257])
+    assert np.array_equal(widened.view(np.uint32), ref.view(np.uint32))
+    rng = np.random.default_rng(7)
+    vals = np.concatenate([
+        rng.standard_normal(3000).astype(np.float32) * np.float32(1e3),
+        # exact ties: low 16 bits 0x8000, both parities of the kept lsb
+        (np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x7F7F8000, 0x00018000, 0x7F7FFFFF],
+                  dtype=np.uint32)).view(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 1e-40, -3e-39], dtype=np.float32),
+    ])
+    mine = orc.bf16_from_f32(vals)
+    theirs = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, theirs)
+    nan = orc.bf16_from_f32(np.array([np.nan], dtype=np.float32))[0]
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F) != 0
+
+
+def pin_weight_ties_golden(orc):
+    g = read_golden("weight_ties.txt")
+    N, K = int(g["N"][0][0]), int(g["K"][0][0])
+    W = f32_to_bf16_bits(np.array(g["W"], dtype=np.float32).reshape(N, K))
+    T = np.array(g["T"], dtype=np.int8).reshape(N, K)
+    t, w_scale, seg_mean, zeros = orc.weight_quant(W)
+    assert seg_mean[0] == np.float32(g["mean"][0][0])
+    assert np.all(w_scale == seg_mean[0])
+    assert np.array_equal(t, T)
+    assert zeros[0] == np.count_nonzero(T == 0)
+
+
+def pin_act_ties_golden(orc):
+    g = read_golden("act_ties.txt")
+    K = int(g["K"][0][0])
+    x = f32_to_bf16_bits(np.array(g["X"][0], dtype=np.float32).reshape(1, K))
+    q, a_scale, rowsum = orc.act_quant(x)
+    expect = np.array(g["Q"][0], dtype=np.int8)
+    assert q.shape == (1, orc.padded_k(K))
+    assert np.array_equal(q[0, :K], expect)
+    assert not q[0, K:].any()
+    assert a_scale[0] == np.float32(g["a_scale"][0][0])
+    assert rowsum[0] == int(g["q_rowsum"][0][0])
+
+
+def pin_pack_golden(orc):
+    g = read_golden("pack_v1.txt")
+    K = int(g["K"][0][0])
+    t = np.array(g["T"][0], dtype=np.int8).reshape(1, K)
+    expect = np.array([int(b, 16) for b in g["BYTES"][0]], dtype=np.uint8)
+    packed = orc.pack(t)
+    assert packed.shape == (1, expect.size)
+    assert np.array_equal(packed[0], expect)
+    back, bad = orc.unpack(packed, K)
+    assert bad == 0 and np.array_equal(back, t)
+
+
+def pin_pack_roundtrip_and_padding(orc):
+    rng = np.random.default_rng(11)
+    for K in (16, 48, 128, 144, 1152, 4304):
+        t = rng.integers(-1, 2, size=(5, K), dtype=np.int8)
+        packed = orc.pack(t)
+        Kp = -(-K // 128) * 128
+        assert packed.shape == (5, Kp // 4)
+        back, bad = orc.unpack(packed, K)
+        assert bad == 0 and np.array_equal(back, t)
+        # every 2-bit field at k >= K holds 1, and no field anywhere holds 3
+        fields = np.stack([(packed >> s) & 3 for s in (0, 2, 4, 6)], -1)
+        assert not np.any(fields == 3)
+        # the number of fields equal to u in the whole row = count(t+1 == u) + padding
+        for u in (0, 1, 2):
+            want = np.count_nonzero(t + 1 == u, axis=1) + (Kp - K) * (u == 1)
+            assert np.array_equal(np.count_nonzero(fields == u, axis=(1, 2)), want)
+
+
+def pin_codes_invariant_and_zero_fraction(orc):
+    """Codes lie in {-1,0,1}; zero fraction matches the closed forms."""
+    rng = np.random.default_rng(3)
+    N, K = 512, 2048
+    for dist, p0 in (("normal", math.erf(0.5 * math.sqrt(2 / math.pi) / math.sqrt(2))),
+                     ("laplace", 1 - math.exp(-0.5))):
+        W = rng_bf16(rng, (N, K), 0.02, dist)
+        t, _, _, zeros = orc.weight_quant(W)
+        assert set(np.unique(t).tolist()) <= {-1, 0, 1}
+        frac = zeros[0] / (N * K)
+        sigma = math.sqrt(p0 * (1 - p0) / (N * K))
+        assert abs(frac - p0) < 5 * sigma, (dist, frac, p0)
+        assert zeros[0] == np.count_nonzero(t == 0)
+
+
+def pin_max_maps_to_127(orc):
+    """Every token's max-|x| element maps to +-127 with its sign; |q| <= 127."""
+    rng = np.random.default_rng(5)
+    M, K = 256, 512
+    mag = np.exp(rng.uniform(-30, 30, size=(M, 1))).astype(np.float32)
+    x = rng_bf16_from(rng.standard_normal((M, K)).astype(np.float32) * mag)
+    q, a_scale, _ = orc.act_quant(x)
+    xv = bf16_bits_to_f32(x)
+    idx = np.argmax(np.abs(xv), axis=1)
+    top = q[np.arange(M), idx]
+    assert np.array_equal(top, np.where(xv[np.arange(M), idx] > 0, 127, -127).astype(np.int8))
+    assert np.abs(q.astype(np.int32)).max() <= 127
+
+
+def rng_bf16_from(v: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return bits.astype(np.uint16)
+
+
+def pin_permutation_weights(orc):
+    """W = a permutation matrix P (non-symmetric): codes = P, acc[m, n] = q[m, pi(n)],
+    y = acc * (amax/127) * (1/K) -- a closed form, every step exact for K a power of 2."""
+    rng = np.random.default_rng(9)
+    K = 64
+    perm = rng.permutation(K)
+    Wf = np.zeros((K, K), dtype=np.float32)
+    Wf[np.arange(K), perm] = 1.0
+    W = f32_to_bf16_bits(Wf)
+    t, w_scale, seg_mean, _ = orc.weight_quant(W)
+    assert seg_mean[0] == np.float32(1.0 / K)
+    assert np.array_equal(t, Wf.astype(np.int8))
+    x = rng_bf16(rng, (3, K))
+    q, a_scale, _ = orc.act_quant(x)
+    acc = orc.int_dot(q, t)
+    assert np.array_equal(acc, q[:, perm].astype(np.int32))
+    y = orc.epilogue(acc, a_scale, w_scale)
+    amax = np.abs(bf16_bits_to_f32(x)).max(axis=1)
+    want = acc.astype(np.float64) * (amax.astype(np.float32) / np.float32(127)).astype(np.float64)[:, None] / K
+    assert np.array_equal(y, want.astype(np.float32))
+
+
+def pin_constant_weights(orc):
+    """W = +c everywhere: codes all +1 and acc = q_rowsum; W = -c gives -q_rowsum."""
+    rng = np.random.default_rng(13)
+    K, N = 96, 5
+    x = rng_bf16(rng, (4, K))
+    q, _, rowsum = orc.act_quant(x)
+    for sign in (1.0, -1.0):
+        W = f32_to_bf16_bits(np.full((N, K), sign * 0.375, dtype=np.float32))
+        t, w_scale, _, _ = orc.weight_quant(W)
+        assert np.all(t == int(sign)) and np.all(w_scale == np.float32(0.375))
+        acc = orc.int_dot(q, t)
+        assert np.array_equal(acc, np.repeat((sign * rowsum).astype(np.int32)[:, None], N, 1))
+    assert np.array_equal(rowsum, q.astype(np.int64).sum(1).astype(np.int32))
+
+
+def pin_symmetry_and_pow2_scaling(orc):
+    rng = np.random.default_rng(17)
+    x = rng_bf16(rng, (8, 160))
+    W = rng_bf16(rng, (24, 160), 0.02)
+    q, a, r = orc.act_quant(x)
+    qn, an, rn = orc.act_quant(x ^ np.uint16(0x8000))          # -x
+    assert np.array_equal(qn, -q) and np.array_equal(an, a) and np.array_equal(rn, -r)
+    t, ws, _, _ = orc.weight_quant(W)
+    tn, wsn, _, _ = orc.weight_quant(W ^ np.uint16(0x8000))      # -W
+    assert np.array_equal(tn, -t) and np.array_equal(wsn, ws)
+    for j in (-3, 4):                                            # x * 2^j, W * 2^j
+        xs = f32_to_bf16_bits(bf16_bits_to_f32(x) * np.float32(2.0 ** j))
+        qs, as_, _ = orc.act_quant(xs)
+        assert np.array_equal(qs, q) and np.array_equal(as_, a * np.float32(2.0 ** j))
+        Ws = f32_to_bf16_bits(bf16_bits_to_f32(W) * np.float32(2.0 ** j))
+        ts, wss, _, _ = orc.weight_quant(Ws)
+        assert np.array_equal(ts, t) and np.array_equal(wss, ws * np.float32(2.0 ** j))
+
+
+def pin_zero_token_and_zero_tensor(orc):
+    K = 32
+    x = np.zeros((2, K), dtype=np.uint16)
+    x[1, 5] = f32_to_bf16_bits(np.array([3.0], dtype=np.float32))[0]
+    q, a, r = orc.act_quant(x)
+    assert not q[0].any() and a[0] == 0 and r[0] == 0
+    assert q[1, 5] == 127 and np.count_nonzero(q[1]) == 1 and a[1] == np.float32(3.0) / np.float32(127)
+    W = np.zeros((3, K), dtype=np.uint16)
+    t, ws, mean, zeros = orc.weight_quant(W)
+    assert not t.any() and not ws.any() and mean[0] == 0 and zeros[0] == 3 * K
+    y = orc.epilogue(orc.int_dot(q, t), a, ws)
+    assert np.array_equal(y, np.zeros((2, 3), dtype=np.float32))  # +0 and -0 both compare equal
+
+
+def pin_int_dot_bruteforce(orc):
+    """Integer dot equals numpy int64 matmul (a library primitive) on several shapes."""
+    rng = np.random.default_rng(19)
+    for M, N, K in ((1, 1, 16), (3, 7, 48), (9, 33, 144), (2, 65, 1152)):
+        Kp = -(-K // 128) * 128
+        q = np.zeros((M, Kp), dtype=np.int8)
+        q[:, :K] = rng.integers(-127, 128, size=(M, K))
+        t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        acc = orc.int_dot(q, t)
+        want = q[:, :K].astype(np.int64) @ t.astype(np.int64).T
+        assert np.array_equal(acc, want.astype(np.int32))
+        mi = rng.integers(0, M, 20)
+        ni = rng.integers(0, N, 20)
+        assert np.array_equal(orc.int_dot_pairs(q, t, mi, ni), want[mi, ni].astype(np.int32))
+    q = np.full((1, 6912), 127, dtype=np.int8)                 # largest K of the workloads:
+    t = np.ones((1, 6912), dtype=np.int8)                     # 127 * K fits in int32
+    assert orc.int_dot(q, t)[0, 0] == 127 * 6912
+
+
+def pin_segments(orc):
+    """A fused tensor keeps one scale per source tensor, on the right rows."""
+    rng = np.random.default_rng(23)
+    K = 256
+    A = rng_bf16(rng, (40, K), 0.02)
+    B = rng_bf16(rng, (24, K), 0.2)
+    C = rng_bf16(rng, (8, K), 0.002)
+    fused = np.concatenate([A, B, C], 0)
+    t, ws, means, zeros = orc.weight_quant(fused, [40, 24, 8])
+    for part, rows, sl, sigma in ((A, 40, slice(0, 40), 0.02), (B, 24, slice(40, 64), 0.2),
+                                  (C, 8, slice(64, 72), 0.002)):
+        tp, wsp, mp, zp = orc.weight_quant(part)
+        assert np.array_equal(t[sl], tp) and np.all(ws[sl] == mp[0])
+        assert abs(mp[0] / (sigma * math.sqrt(2 / math.pi)) - 1) < 0.1
+    assert np.array_equal(means, [ws[0], ws[40], ws[64]])
+    t1, ws1, _, _ = orc.weight_quant(fused)                      # one scale for all: differs
+    assert not np.array_equal(t1, t)
+
+
+def pin_float_linear_tiny(orc):
+    """y against an independent fp64 brute force of linear(ActQuant(x), WeightQuant(W))."""
+    rng = np.random.default_rng(29)
+    for M, N, K in ((1, 1, 16), (2, 3, 32), (3, 5, 48), (8, 16, 128), (3, 33, 144)):
+        x = rng_bf16(rng, (M, K))
+        W = rng_bf16(rng, (N, K), 0.02)
+        res = orc.linear(x, W)
+        yref, bound, q_b, t_b = brute.linear(bf16_bits_to_f32(x), bf16_bits_to_f32(W))
+        assert np.array_equal(res["q"][:, :K], q_b)
+        assert np.array_equal(res["t"], t_b)
+        err = np.abs(res["y"].astype(np.float64) - yref)
+        assert np.all(err <= bound), (M, N, K, float(err.max()))
+        bf = orc.epilogue(res["acc"], res["a_scale"], res["w_scale"], "bf16")
+        assert np.array_equal(bf, orc.bf16_from_f32(res["y"]))
+
+
+def pin_act_quant_exact_rational(orc):
+    """q against the exact value of the fp32 formula: sa = fl(127/amax) by numpy's
+    correctly rounded fp32 division; x*sa is exact in fp64, rounded once to fp32."""
+    rng = np.random.default_rng(31)
+    x = rng_bf16(rng, (64, 256))
+    xv = bf16_bits_to_f32(x)
+    q, a, r = orc.act_quant(x)
+    amax = np.abs(xv).max(1)
+    sa = np.float32(127) / amax
+    prod = (xv.astype(np.float64) * sa.astype(np.float64)[:, None]).astype(np.float32)
+    want = np.clip(np.rint(prod), -128, 127).astype(np.int8)
+    assert np.array_equal(q[:, :256], want)
+    assert np.array_equal(a, amax / np.float32(127))
+    assert np.array_equal(r, want.astype(np.int64).sum(1).astype(np.int32))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+def failing_pins(orc) -> list:
+    bad = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except Exception:  # an assertion, or a mutant that breaks a precondition
+            bad.append(pin.__name__)
+    return bad
+
+
+if __name__ == "__main__":
+    sys.path.insert(0, str(ROOT))
+    from oracle.oracle import Oracle
+
+    print(json.dumps(failing_pins(Oracle(sys.argv[1]))))

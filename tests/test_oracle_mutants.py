@@ -1,0 +1,91 @@
+"""Plant one plausible mistake at a time in a copy of the oracle (on the CPU)
+and check that the pins catch every one of them.
+
+Each mutant is compiled from the committed C source with one textual change and
+its pins run in a process of their own, so a mutant that misbehaves cannot take
+the test runner down.  Every mutation keeps all memory accesses in bounds.
+"""
+import json
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+from pathlib import Path
+
+from oracle import oracle as orc_mod
+
+HERE = Path(__file__).resolve().parent
+
+MUTANTS = [
+    ("weight rounding half away from zero",
+     "float r = round_half_even(p);", "float r = roundf(p);"),
+    ("activation rounding half away from zero",
+     "float r = round_half_even(load_elem(x, dtype, m * ldx + k) * sa);",
+     "float r = roundf(load_elem(x, dtype, m * ldx + k) * sa);"),
+    ("activation factor applied as (x*127)/amax",
+     "float r = round_half_even(load_elem(x, dtype, m * ldx + k) * sa);",
+     "float r = round_half_even(load_elem(x, dtype, m * ldx + k) * 127.0f / amax);"),
+    ("stored code sign flipped",
+     "(unsigned)(t[n * K + k] + 1)", "(unsigned)(1 - t[n * K + k])"),
+    ("padding code 0 instead of 1",
+     "(unsigned)(t[n * K + k] + 1) : 1u;", "(unsigned)(t[n * K + k] + 1) : 0u;"),
+    ("byte and bit roles of the layout transposed",
+     "static int64_t v1_byte(int64_t k) { return 4 * (k / 16) + (k % 4); }\n"
+     "static int v1_shift(int64_t k) { return (int)(2 * ((k % 16) / 4)); }",
+     "static int64_t v1_byte(int64_t k) { return 4 * (k / 16) + (k % 16) / 4; }\n"
+     "static int v1_shift(int64_t k) { return (int)(2 * (k % 4)); }"),
+    ("mean divides by K instead of rows*K",
+     "return (float)(total / (double)(rows * K));", "return (float)(total / (double)(K));"),
+    ("segments ignored (one scale for the fused tensor)",
+     "float mean = orc_segment_mean(W, dtype, row0, seg_rows[i], K, ldw);",
+     "float mean = orc_segment_mean(W, dtype, 0, N, K, ldw);"),
+    ("absolute value dropped in amax",
+     "float a = fabsf(load_elem(x, dtype, m * ldx + k));",
+     "float a = load_elem(x, dtype, m * ldx + k);"),
+    ("absolute value dropped in mean|W|",
+     "s += fabs((double)load_elem(W, dtype, n * ldw + k));",
+     "s += (double)load_elem(W, dtype, n * ldw + k);"),
+    ("q_rowsum drops the last element",
+     "sum += (int8_t)r;", "sum += (k + 1 < K) ? (int8_t)r : 0;"),
+    ("integer dot reads the codes transposed",
+     "s += (int64_t)q[m * Kp + k] * (int64_t)t[n * K + k];",
+     "s += (int64_t)q[m * Kp + k] * (int64_t)t[k * N + n];"),
+    ("integer dot drops the last k",
+     "for (int64_t k = 0; k < K; ++k)\n                s += (int64_t)q[m * Kp + k]",
+     "for (int64_t k = 0; k < K - 1; ++k)\n                s += (int64_t)q[m * Kp + k]"),
+    ("epilogue drops w_scale", "float f = a_scale * w_scale;", "float f = a_scale;"),
+    ("epilogue uses a_scale twice", "float f = a_scale * w_scale;", "float f = a_scale * a_scale;"),
+    ("a_scale stored as 127/amax", "a_scale[m] = amax / 127.0f;", "a_scale[m] = 127.0f / amax;"),
+    ("bf16 output truncates", "if (rest > 0x8000u)", "if (rest > 0xFFFFu)"),
+    ("bf16 ties away from zero",
+     "else if (rest == 0x8000u && (upper & 1u))", "else if (rest == 0x8000u)"),
+    ("q tail left non-zero",
+     "for (int64_t k = K; k < Kp; ++k)\n                q[m * Kp + k] = 0;",
+     "for (int64_t k = K; k < Kp; ++k)\n                q[m * Kp + k] = 1;"),
+    ("weight clamp at +-2",
+     "if (r > 1.0f)\n        r = 1.0f;\n    if (r < -1.0f)\n        r = -1.0f;",
+     "if (r > 2.0f)\n        r = 2.0f;\n    if (r < -2.0f)\n        r = -2.0f;"),
+    ("zero count counts non-zeros", "zeros += (c == 0);", "zeros += (c != 0);"),
+    ("unpack offset wrong", "t[n * K + k] = (int8_t)((int)u - 1);", "t[n * K + k] = (int8_t)((int)u - 2);"),
+]
+
+
+def _run_mutant(args):
+    idx, (name, old, new), src, tmp = args
+    assert src.count(old) == 1, f"mutation '{name}' does not match the source exactly once"
+    c_file = tmp / f"mutant{idx}.c"
+    c_file.write_text(src.replace(old, new))
+    so = tmp / f"mutant{idx}.so"
+    orc_mod.build(source=c_file, out=so)
+    out = subprocess.run([sys.executable, str(HERE / "pins.py"), str(so)],
+                         capture_output=True, text=True, timeout=300)
+    caught = json.loads(out.stdout.strip().splitlines()[-1]) if out.returncode == 0 else ["<crashed>"]
+    return name, caught
+
+
+def test_every_planted_mistake_is_caught(tmp_path):
+    src = orc_mod.SOURCE.read_text()
+    jobs = [(i, m, src, tmp_path) for i, m in enumerate(MUTANTS)]
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        results = list(pool.map(_run_mutant, jobs))
+    missed = [name for name, caught in results if not caught]
+    assert not missed, f"pins missed: {missed}"
