@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of the W1.58A8 BitLinear on one MI355X; prints one JSON line.
+
+Headline (``value``): decode GEMV packed-weight GB/s at M = 1 on the
+BitNet-b1.58-2B-shaped 30-layer stream (210 projections, 521 MB of packed
+ternary weights, one token per projection).  A step is one pass over all 210
+projections: per-token ActQuant, the ternary product and the dequant epilogue,
+run as one grouped launch.
+
+``gemm``: prefill int8 TOPS at M = 4096 on the BitNet-b1.58-2B-shaped prefill
+(fused gate|up 2560->13824, down 6912->2560, q|k|v 2560->3840).  A step is,
+for each projection, ActQuant followed by the int8-MFMA GEMM.
+
+Each part carries a ``roofline`` object for its dominant kernel (algorithmic
+bytes or int ops per launch over the launch's average duration, timed with HIP
+events on the stream the kernel runs on) and a ``cpu_baseline`` object: the
+plain CPU oracle, untuned, timed on a bounded sample of the same workload on
+this host's cores.  Inputs are seeded synthetic tensors of the workloads'
+shapes; weights are packed before timing (packing is offline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "BitLinear GEMV packed-weight GB/s (M=1) and GEMM int8 TOPS (M=4096), % of peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, published (5.0 POPS)
+PROFILES = ROOT / "profiles"
+
+
+def kernel_source_hash(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        h.update((ROOT / "ternary_weight_bitlinear_amd" / "csrc" / n).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(name: str, src_hash: str):
+    """HBM bytes per launch from a committed counter summary, if it matches the current kernel source."""
+    f = PROFILES / f"{name}_traffic.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text())
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------- decode
+
+def setup_decode(tw, wl, torch, layers: int):
+    w = wl.WORKLOADS["c2"]
+    items, nbytes = [], 0
+    for layer in range(layers):
+        for i, p in enumerate(w.projections):
+            W = wl.weight_for(w, i, layer=layer, device="cuda")
+            pw = tw.pack(W)
+            del W
+            x = wl.activation_for(w, i, layer=layer, device="cuda")
+            y = torch.empty((1, p.N), dtype=torch.float32, device="cuda")
+            items.append((x, pw, y))
+            nbytes += p.N * p.K // 4
+    return items, nbytes
+
+
+def time_region(torch, fn, steps: int, warmup: int):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps      # ms per step
+
+
+def bench_decode(tw, wl, torch, steps, warmup, per_call: bool):
+    items, nbytes = setup_decode(tw, wl, torch, 30)
+    group = tw.GroupedBitLinear(items)
+    ms = time_region(torch, group, steps, warmup)     # one launch per step
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    src = kernel_source_hash("gemv.hip", "gemv.h", "device_common.h")
+    out = dict(value=gbps, ms_per_step=ms, bytes=nbytes, launches_per_step=1,
+               roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s",
+                             frac=gbps / HBM_PEAK_GBPS,
+                             traffic=traffic_from_profile("gemv_grouped_bitnet2b_decode_30_layers", src)))
+    if per_call:
+        # the same 210 projections as 210 single-problem calls (one fused launch each),
+        # replayed from a HIP graph: what a decoder that cannot group its calls pays
+        ws = [(torch.empty((1, tw.padded_k(pw.K)), dtype=torch.int8, device="cuda"),
+               torch.empty(1, dtype=torch.float32, device="cuda"),
+               torch.empty(1, dtype=torch.int32, device="cuda")) for _, pw, _ in items]
+
+        def calls():
+            for (x, pw, y), w_ in zip(items, ws):
+                tw.bitlinear(x, pw, out=y, workspace=w_)
+        calls()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls()
+        ms_pc = time_region(torch, g.replay, max(steps // 2, 3), 2)
+        out["per_call"] = dict(value=nbytes / (ms_pc * 1e-3) / 1e9, unit="GB/s", ms_per_step=ms_pc,
+                               launches_per_step=len(items), note="one fused launch per projection, HIP graph")
+    del group, items
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline_decode(wl, torch, budget_s: float):
+    from oracle.oracle import Oracle
+    orc = Oracle()
+    w = wl.WORKLOADS["c2"]
+    threads = orc.max_threads()
+    done_bytes, spent, layers = 0, 0.0, 0
+    while spent < budget_s and layers < w.layers:
+        for i, p in enumerate(w.projections):
+            W = wl.weight_for(w, i, layer=layers, device="cuda").cpu()
+            x = wl.activation_for(w, i, layer=layers, device="cuda").cpu()
+            Wb = W.view(torch.int16).numpy().view("uint16")
+            xb = x.view(torch.int16).numpy().view("uint16")
+            t, ws, _, _ = orc.weight_quant(Wb)            # packing: not timed
+            t0 = time.perf_counter()
+            q, a, _ = orc.act_quant(xb)
+            acc = orc.int_dot(q, t, nthreads=threads)
+            orc.epilogue(acc, a, ws)
+            spent += time.perf_counter() - t0
+            done_bytes += p.N * p.K // 4
+        layers += 1
+    return dict(value=done_bytes / spent / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"first {layers} of 30 decode layers ({layers * 7} projections, "
+                       f"{done_bytes / 1e6:.1f} MB packed), ActQuant + int dot + epilogue, "
+                       f"{spent:.1f} s")
+
+
+# ------------------------------------------------------------------- prefill
+
+def bench_prefill(tw, wl, torch, steps, warmup, out_dtype):
+    w = wl.WORKLOADS["c5"]
+    projs = []
+    for i, p in enumerate(w.projections):
+        pw = tw.pack(wl.weight_for(w, i, device="cuda"), p.segments or None)
+        x = wl.activation_for(w, i, device="cuda")
+        q = torch.empty((w.M, tw.padded_k(p.K)), dtype=torch.int8, device="cuda")
+        a = torch.empty(w.M, dtype=torch.float32, device="cuda")
+        r = torch.empty(w.M, dtype=torch.int32, device="cuda")
+        y = torch.empty((w.M, p.N), dtype=out_dtype, device="cuda")
+        projs.append((p, pw, x, q, a, r, y))
+    ops = sum(2 * w.M * p.N * p.K for p, *_ in projs)
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [[(Ev(), Ev()) for _ in projs] for _ in range(steps)]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(events):
+        for j, (p, pw, x, q, a, r, y) in enumerate(projs):
+            tw._lib.check(tw._lib.lib().bitnet_act_quant(stream, x.data_ptr(), tw._dtype(x), w.M, p.K, p.K,
+                                                         q.data_ptr(), a.data_ptr(), r.data_ptr()))
+            if events:
+                events[j][0].record()
+            tw.linear(q, a, r, pw, out=y)
+            if events:
+                events[j][1].record()
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    start, end = Ev(), Ev()
+    start.record()
+    for s_ in range(steps):
+        step(evs[s_])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    per_launch = [e0.elapsed_time(e1) for row in evs for e0, e1 in row]
+    gemm_ms = sum(per_launch) / len(per_launch)
+    ops_per_launch = ops / len(projs)
+    achieved = ops_per_launch / (gemm_ms * 1e-3) / 1e12
+    tops = ops / (ms * 1e-3) / 1e12
+    src = kernel_source_hash("gemm.hip", "device_common.h")
+    return dict(metric="GEMM int8 TOPS (M=4096)", value=tops, unit="TOPS", ms_per_step=ms,
+                config=dict(workload=w.name, M=w.M, projections=[f"{p.name} {p.K}->{p.N}" for p, *_ in projs],
+                            out_dtype=str(out_dtype).replace("torch.", ""),
+                            step="ActQuant + GEMM per projection"),
+                roofline=dict(bound="mfma", achieved=achieved, peak=INT8_PEAK_TOPS, unit="TOPS",
+                              frac=achieved / INT8_PEAK_TOPS,
+                              traffic=traffic_from_profile("gemm_bitnet2b_prefill_m4096", src)),
+                gemm_ms_per_launch=gemm_ms, launches_per_step=2 * len(projs))
+
+
+def cpu_baseline_prefill(wl, torch, budget_s: float):
+    from oracle.oracle import Oracle
+    orc = Oracle()
+    w = wl.WORKLOADS["c5"]
+    threads = orc.max_threads()
+    ops, spent, tokens = 0, 0.0, 0
+    rows = 16
+    while spent < budget_s and tokens < 256:
+        for i, p in enumerate(w.projections):
+            W = wl.weight_for(w, i, device="cuda").cpu()
+            x = wl.activation_for(w, i, device="cuda")[tokens:tokens + rows].cpu()
+            t, ws, _, _ = orc.weight_quant(W.view(torch.int16).numpy().view("uint16"), p.segments or None)
+            t0 = time.perf_counter()
+            q, a, _ = orc.act_quant(x.view(torch.int16).numpy().view("uint16"))
+            acc = orc.int_dot(q, t, nthreads=threads)
+            orc.epilogue(acc, a, ws)
+            spent += time.perf_counter() - t0
+            ops += 2 * rows * p.N * p.K
+        tokens += rows
+    return dict(value=ops / spent / 1e12, unit="TOPS", cores=threads, kind="oracle",
+                sample=f"{tokens} of 4096 tokens through all 3 prefill projections "
+                       f"({ops / 1e9:.1f} G int ops), ActQuant + int dot + epilogue, {spent:.1f} s")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget per CPU-baseline leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-call", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this BitLinear path runs on a single MI355X "
+              "(multi-GPU sharding is a design note, not built). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import ternary_weight_bitlinear_amd as tw
+    from ternary_weight_bitlinear_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    tw._lib.lib()   # fail loudly now if the HIP library is not built
+
+    line = dict(metric=METRIC, value=None, unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                ms_per_step=None, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="int8",
+                data="synthetic",
+                config=dict(workload=wl.WORKLOADS["c2"].name, M=1, layers=30, projections=210,
+                            launch="grouped: all 210 projections in one launch, ActQuant fused",
+                            weights="bf16 latent N(0, 0.02), per-tensor absmean ternary",
+                            activations="bf16 N(0, 1), one token per projection", out_dtype="float32"))
+    if args.only in (None, "decode"):
+        d = bench_decode(tw, wl, torch, args.steps, args.warmup, not args.no_per_call)
+        line.update(value=d["value"], ms_per_step=d["ms_per_step"], roofline=d["roofline"])
+        line["config"]["packed_bytes"] = d["bytes"]
+        if "per_call" in d:
+            line["per_call"] = d["per_call"]
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_decode(wl, torch, args.cpu_seconds)
+    if args.only in (None, "prefill"):
+        g = bench_prefill(tw, wl, torch, args.steps, args.warmup, torch.bfloat16)
+        if not args.no_cpu_baseline:
+            g["cpu_baseline"] = cpu_baseline_prefill(wl, torch, args.cpu_seconds)
+        line["gemm"] = g
+        if args.only == "prefill":
+            line.update(value=g["value"], unit="TOPS", ms_per_step=g["ms_per_step"], roofline=g["roofline"],
+                        config=g["config"])
+            line["config"]["workload"] = wl.WORKLOADS["c5"].name
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

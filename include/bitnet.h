@@ -1,0 +1,237 @@
+/*
+ * bitnet.h -- C ABI of libbitnet_hip.so, a W1.58A8 BitLinear for MI355X (gfx950).
+ *
+ *   y = linear(ActQuant(x), WeightQuant(W)),  no bias.
+ *
+ * Pages cited (title, then section):
+ *   [BitVLA] "BitVLA -- 1.58-bit Vision-Language-Action on Core AI"
+ *            (Core AI model zoo).
+ *   [Guide]  "BitNet-Embeddings-0.6B/270M: I2_S Conversion and Inference
+ *            Optimization Guide" (microsoft/BitNet docs).
+ *
+ * Method.  WeightQuant is per-tensor absmean: s = 1/mean|W|, ternary codes
+ * t = clamp(round(W*s), -1, 1), dequantised as t/s [BitVLA s1; Guide s2,
+ * s3.3 "I2_S Ternary Packing"].  ActQuant is per-token absmax int8:
+ * q = clamp(round(x*127/max|x|), -128, 127), dequantised by 127/max|x|
+ * [BitVLA s1; Guide s2].  The product is an exact int32 sum of q*t, rescaled by
+ * (max|x|/127) * mean|W|.  ActQuant runs before the ternary product and the
+ * codes are built from the bf16 latent weights [BitVLA s2].
+ *
+ * Numerics fixed by this library where the pages leave them open:
+ *   - "round" is round-half-to-even (weights and activations);
+ *   - mean|W| = fp64 sum over k ascending per row, rows ascending, one fp64
+ *     division by rows*K, rounded to fp32; s = 1.0f/mean (fp32 division);
+ *     t = clamp(rne(fp32(W*s)), -1, 1), and t = 0 where W*s is NaN;
+ *   - sa = 127.0f/amax (fp32), q = clamp(rne(fp32(x*sa)), -128, 127),
+ *     a_scale = amax/127.0f; a token with amax == 0 gets q = 0, a_scale = 0;
+ *   - y = (float)acc * (a_scale[m] * w_scale[n]) in fp32; bf16 output is that
+ *     value rounded to nearest-even.
+ * Every integer result (codes, packed bytes, q, q_rowsum, acc) is exact and
+ * independent of launch configuration.
+ *
+ * Packed weight layout v1 (this library's own; not I2_S).  Stored code
+ * u = t + 1, so -1 -> 0, 0 -> 1, +1 -> 2 [Guide s3.3; BitVLA s2].  Rows are
+ * padded to Kp = bitnet_padded_k(K) elements.  Row n occupies Kp/4 bytes at
+ * offset n*Kp/4.  Element k of a row lives in byte 4*(k/16) + k%4 at bits
+ * 2*((k%16)/4)..+1; equivalently, little-endian 32-bit word j holds elements
+ * 16j..16j+15 and (word >> 2p) & 0x03030303 gives elements 16j+4p+0..3 in its
+ * four bytes.  Elements K..Kp-1 hold code 1 (weight 0).  There are no padding
+ * rows: N is arbitrary [BitVLA s2 asks for arbitrary N and K % 16 == 0].
+ * w_scale[n] (fp32) is mean|W| of the source tensor that row n belongs to, one
+ * value per output row, a 1-D array of N floats [BitVLA s2: per-tensor scale
+ * stored per row].
+ *
+ * Conventions for every entry point:
+ *   - Sizes are element counts; M, N, K > 0; K % 16 == 0; K <= 1048576;
+ *     M, N <= 2^31 - 1.  Leading dimensions (ld*) are in elements.
+ *   - The caller owns and allocates every buffer.  Device pointers are HIP
+ *     device memory on the current device; the library allocates no memory
+ *     that outlives a call (bitnet_pack_weights with BITNET_MEM_DEVICE uses
+ *     stream-ordered temporaries of O(N) bytes that it frees before
+ *     returning).
+ *   - Device work is enqueued on `stream` (0 = the null stream) and is
+ *     asynchronous unless stated otherwise.
+ *   - Every argument check runs before any launch; a failed check launches
+ *     nothing and returns BITNET_ERR_INVALID_ARG (detail in
+ *     bitnet_last_error()).  A failed launch returns BITNET_ERR_HIP.
+ *   - Pointers named "16-byte aligned" must be; strides keep rows aligned
+ *     because Kp is a multiple of 128.
+ *   - No exceptions and no printing cross this boundary; all functions are
+ *     reentrant.  Calls that overlap on one stream are ordered by the stream.
+ */
+#ifndef BITNET_H
+#define BITNET_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITNET_ABI_VERSION 1
+
+typedef enum {
+    BITNET_OK = 0,
+    BITNET_ERR_INVALID_ARG = 1,  /* bad size, stride, pointer, alignment or dtype */
+    BITNET_ERR_UNSUPPORTED = 2,  /* valid request this build does not handle      */
+    BITNET_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed     */
+    BITNET_ERR_NONFINITE = 4     /* a weight given to the packer is inf or NaN     */
+} bitnet_status_t;
+
+typedef enum { BITNET_F32 = 0, BITNET_BF16 = 1 } bitnet_dtype_t;
+
+typedef enum { BITNET_MEM_HOST = 0, BITNET_MEM_DEVICE = 1 } bitnet_mem_t;
+
+/* ABI version of the loaded library (BITNET_ABI_VERSION). */
+int32_t bitnet_abi_version(void);
+
+/* Padded row length Kp = K rounded up to a multiple of 128; -1 if K <= 0,
+ * K % 16 != 0 or K is above the limit. */
+int64_t bitnet_padded_k(int64_t K);
+
+/* Bytes of a packed [N, K] weight: N * Kp / 4; -1 on a bad N or K. */
+int64_t bitnet_packed_bytes(int64_t N, int64_t K);
+
+/*
+ * WeightQuant + pack [BitVLA s1, s2; Guide s3.3 "I2_S Ternary Packing"].
+ *
+ * W        [N, K] latent weights, row stride ldw >= K, dtype w_dtype
+ *          (BITNET_BF16 or BITNET_F32).  Host memory if where == HOST,
+ *          device memory if where == DEVICE.
+ * seg_rows host array of n_segs row counts summing to N: the fused weight is
+ *          n_segs source tensors stacked by rows (e.g. q|k|v), each with its
+ *          own mean|W|.  seg_rows == NULL or n_segs == 0 means one tensor.
+ * packed   out, [N][Kp/4] bytes in layout v1, same memory kind as W,
+ *          16-byte aligned.
+ * w_scale  out, [N] fp32, same memory kind as W.
+ * seg_mean out, optional host array [max(n_segs,1)]: mean|W| per segment.
+ * zero_count out, optional host array [max(n_segs,1)]: zero codes per
+ *          segment over the real K columns (the zero-weight fraction).
+ * stream   used for DEVICE only.  A DEVICE call is synchronous: it waits for
+ *          its own work on `stream` before returning (it must read back the
+ *          non-finite flag), and it needs O(N) bytes of temporary device
+ *          memory, taken and returned on `stream`.
+ * Errors:  INVALID_ARG for bad sizes/pointers/segments; NONFINITE if any
+ *          weight is inf or NaN (outputs are then unspecified); HIP.
+ */
+bitnet_status_t bitnet_pack_weights(bitnet_mem_t where, hipStream_t stream,
+                                    const void* W, bitnet_dtype_t w_dtype,
+                                    int64_t N, int64_t K, int64_t ldw,
+                                    const int64_t* seg_rows, int32_t n_segs,
+                                    uint8_t* packed, float* w_scale,
+                                    float* seg_mean, int64_t* zero_count);
+
+/*
+ * ActQuant, per token [BitVLA s1; Guide s2].  Device memory throughout.
+ *
+ * x        [M, K] activations, row stride ldx >= K, dtype x_dtype (BF16 or
+ *          F32).  Non-finite activations give unspecified results.
+ * q        out, [M][Kp] int8, 16-byte aligned; columns K..Kp-1 are written 0.
+ * a_scale  out, [M] fp32 = amax/127 (0 for an all-zero token).
+ * q_rowsum out, [M] int32 = sum over k of q[m][k].
+ */
+bitnet_status_t bitnet_act_quant(hipStream_t stream, const void* x, bitnet_dtype_t x_dtype,
+                                 int64_t M, int64_t K, int64_t ldx,
+                                 int8_t* q, float* a_scale, int32_t* q_rowsum);
+
+/*
+ * Ternary linear on quantised operands + dequant epilogue [BitVLA s1, s2;
+ * Guide s2 (no bias)].  Device memory throughout.
+ *
+ * q, a_scale, q_rowsum  as produced by bitnet_act_quant for [M, K].
+ * packed, w_scale       as produced by bitnet_pack_weights for [N, K].
+ * y        out, [M, N] with row stride ldy >= N, dtype y_dtype (F32 or BF16):
+ *          y[m][n] = (float)acc[m][n] * (a_scale[m] * w_scale[n]),
+ *          acc[m][n] = sum_{k<K} q[m][k] * t[n][k] (exact int32).
+ * acc_debug optional out, [M][N] int32 (row stride N): the exact acc.
+ * M <= 16 runs the streaming decode kernel (one pass over the packed weight);
+ * larger M runs the int8-MFMA GEMM.  Both give identical bits.
+ */
+bitnet_status_t bitnet_linear_forward(hipStream_t stream,
+                                      const int8_t* q, const float* a_scale,
+                                      const int32_t* q_rowsum, int64_t M, int64_t K,
+                                      const uint8_t* packed, const float* w_scale, int64_t N,
+                                      void* y, bitnet_dtype_t y_dtype, int64_t ldy,
+                                      int32_t* acc_debug);
+
+/*
+ * Whole BitLinear from activations: bitnet_act_quant then
+ * bitnet_linear_forward, enqueued back to back on `stream` [BitVLA s2: the
+ * wrapper applies ActQuant before the ternary kernel].  q, a_scale and
+ * q_rowsum are caller-provided buffers that receive the quantised activations
+ * (same shapes as in bitnet_act_quant).  For M * Kp <= 32768 bytes with
+ * 16-byte-aligned x rows this is a single launch: the decode kernel quantises
+ * the tokens itself and its first workgroup also stores q, a_scale and
+ * q_rowsum; otherwise it is two launches.
+ */
+bitnet_status_t bitnet_bitlinear_forward(hipStream_t stream,
+                                         const void* x, bitnet_dtype_t x_dtype,
+                                         int64_t M, int64_t K, int64_t ldx,
+                                         const uint8_t* packed, const float* w_scale, int64_t N,
+                                         void* y, bitnet_dtype_t y_dtype, int64_t ldy,
+                                         int8_t* q, float* a_scale, int32_t* q_rowsum);
+
+/*
+ * Many independent decode-size BitLinears in one launch.  A decoder streams
+ * the weights of many projections per token (one position at a time, M = 1:
+ * [BitVLA s3]); each matrix alone moves only a few MB, far too little to
+ * amortise a kernel launch, so a caller that holds several independent
+ * problems can run them as one grouped launch.  Each item is
+ * y_i = linear(ActQuant(x_i), WeightQuant(W_i)) with its own activations,
+ * packed weight, scales and output; items may differ in N and K.
+ */
+typedef struct {
+    const void* x;           /* [M, K] activations (device), row stride ldx    */
+    int64_t ldx;             /* elements; x and ldx*size keep rows 16-B aligned */
+    const uint8_t* packed;   /* [N][Kp/4] layout v1 (device), 16-byte aligned   */
+    const float* w_scale;    /* [N] (device)                                    */
+    void* y;                 /* [M, N] output (device), row stride ldy          */
+    int64_t ldy;
+    int64_t N;
+    int64_t K;
+} bitnet_group_item_t;
+
+/* Host-side handle of a prepared group (contents private to the library). */
+typedef struct {
+    int64_t opaque[8];
+} bitnet_group_plan_t;
+
+/* Device bytes bitnet_group_plan needs for `count` items (-1 if count <= 0). */
+int64_t bitnet_group_table_bytes(int32_t count);
+
+/*
+ * Validate `count` items (host array) that share M (1..16), the activation
+ * dtype and the output dtype, and write their launch table into table_dev
+ * (caller-owned device memory of at least bitnet_group_table_bytes(count)
+ * bytes, 16-byte aligned).  Fills *plan.  Synchronous (uploads the table on
+ * `stream` and waits).  The plan stays valid while table_dev and every buffer
+ * the items name stay allocated; their contents may change between launches.
+ * Errors: INVALID_ARG for any bad item (its index is in bitnet_last_error());
+ * UNSUPPORTED if M * Kp exceeds 65536 bytes for some item; HIP.
+ */
+bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t* items, int32_t count,
+                                  int64_t M, bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype,
+                                  void* table_dev, int64_t table_bytes, bitnet_group_plan_t* plan);
+
+/*
+ * Run every item of a plan in one kernel launch on `stream`: each workgroup
+ * quantises its item's tokens (ActQuant, same numerics as bitnet_act_quant)
+ * and streams its share of that item's packed weight once.  Results are
+ * bit-identical to bitnet_bitlinear_forward on each item.  Makes no
+ * allocation and no host-device copy, so it can be captured in a HIP graph.
+ */
+bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_plan_t* plan);
+
+/* Static text for a status code. */
+const char* bitnet_status_string(bitnet_status_t s);
+
+/* Detail of the calling thread's last failure ("" if none); valid until that
+ * thread's next call into the library. */
+const char* bitnet_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_H */

@@ -1,1 +1,187 @@
-"""W1.58A8 BitLinear on MI355X (gfx950): Python binding of the C-ABI library."""
+"""W1.58A8 BitLinear on MI355X (gfx950): Python binding of libbitnet_hip.so.
+
+    y = linear(ActQuant(x), WeightQuant(W))
+
+("BitVLA -- 1.58-bit Vision-Language-Action on Core AI", s1 and s2;
+"BitNet-Embeddings-0.6B/270M: I2_S Conversion and Inference Optimization
+Guide", s2 and s3.3.)  Every function here only marshals arguments: torch
+supplies device memory and the current HIP stream, the C ABI in
+``include/bitnet.h`` does all of the work in HIP kernels.  Non-OK statuses
+raise ``BitnetError``.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import BitnetError
+
+__all__ = ["BitnetError", "PackedWeight", "padded_k", "packed_bytes", "pack", "act_quant",
+           "linear", "bitlinear", "GroupedBitLinear", "library_path"]
+
+_DT = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+
+
+def library_path() -> str:
+    return str(_lib.LIBRARY)
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def padded_k(K: int) -> int:
+    """Kp = K rounded up to a multiple of 128 (-1 if K is not a positive multiple of 16)."""
+    return int(_lib.lib().bitnet_padded_k(K))
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(_lib.lib().bitnet_packed_bytes(N, K))
+
+
+@dataclass
+class PackedWeight:
+    packed: torch.Tensor      # uint8 [N, Kp/4], layout v1
+    w_scale: torch.Tensor     # float32 [N]
+    N: int
+    K: int
+    seg_mean: torch.Tensor    # float32 [segments] (host)
+    zero_count: torch.Tensor  # int64 [segments] (host)
+
+
+def pack(W: torch.Tensor, segments=None) -> PackedWeight:
+    """WeightQuant + pack of W [N, K] (bf16 or fp32).  A CUDA tensor is packed by the
+    device kernels, a CPU tensor by the library's host packer (chosen by where W lives)."""
+    ldw = _rows(W, "W")
+    N, K = W.shape
+    Kp = padded_k(K)
+    if Kp < 0:
+        raise ValueError(f"K={K} must be a positive multiple of 16")
+    segs = list(segments) if segments else [N]
+    seg_arr = (torch.tensor(segs, dtype=torch.int64))
+    packed = torch.empty((N, Kp // 4), dtype=torch.uint8, device=W.device)
+    w_scale = torch.empty(N, dtype=torch.float32, device=W.device)
+    seg_mean = torch.empty(len(segs), dtype=torch.float32)
+    zeros = torch.empty(len(segs), dtype=torch.int64)
+    on_gpu = W.is_cuda
+    with torch.cuda.device(W.device) if on_gpu else _nullctx():
+        st = _lib.lib().bitnet_pack_weights(
+            _lib.MEM_DEVICE if on_gpu else _lib.MEM_HOST, _stream(W) if on_gpu else None,
+            W.data_ptr(), _dtype(W), N, K, ldw, seg_arr.data_ptr(), len(segs),
+            packed.data_ptr(), w_scale.data_ptr(), seg_mean.data_ptr(), zeros.data_ptr())
+    _lib.check(st)
+    return PackedWeight(packed, w_scale, N, K, seg_mean, zeros)
+
+
+class _nullctx:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False
+
+
+def act_quant(x: torch.Tensor):
+    """Per-token ActQuant of x [M, K] (CUDA, bf16 or fp32) -> (q [M, Kp] int8, a_scale [M], q_rowsum [M])."""
+    ldx = _rows(x, "x")
+    M, K = x.shape
+    Kp = padded_k(K)
+    if Kp < 0:
+        raise ValueError(f"K={K} must be a positive multiple of 16")
+    q = torch.empty((M, Kp), dtype=torch.int8, device=x.device)
+    a_scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    rowsum = torch.empty(M, dtype=torch.int32, device=x.device)
+    with torch.cuda.device(x.device):
+        _lib.check(_lib.lib().bitnet_act_quant(_stream(x), x.data_ptr(), _dtype(x), M, K, ldx,
+                                               q.data_ptr(), a_scale.data_ptr(), rowsum.data_ptr()))
+    return q, a_scale, rowsum
+
+
+def linear(q: torch.Tensor, a_scale: torch.Tensor, q_rowsum: torch.Tensor, w: PackedWeight,
+           out_dtype=torch.float32, out: torch.Tensor | None = None, acc_debug: bool = False):
+    """y [M, N] = (acc) * (a_scale[m] * w_scale[n]) with acc the exact int32 sum of q*t.
+    Returns y, or (y, acc) when acc_debug is set."""
+    M = q.shape[0]
+    if q.shape[1] != padded_k(w.K):
+        raise ValueError("q must be [M, Kp] for the packed weight's K")
+    y = out if out is not None else torch.empty((M, w.N), dtype=out_dtype, device=q.device)
+    ldy = _rows(y, "y")
+    acc = torch.empty((M, w.N), dtype=torch.int32, device=q.device) if acc_debug else None
+    with torch.cuda.device(q.device):
+        _lib.check(_lib.lib().bitnet_linear_forward(
+            _stream(q), q.data_ptr(), a_scale.data_ptr(), q_rowsum.data_ptr(), M, w.K,
+            w.packed.data_ptr(), w.w_scale.data_ptr(), w.N, y.data_ptr(), _dtype(y), ldy,
+            acc.data_ptr() if acc is not None else None))
+    return (y, acc) if acc_debug else y
+
+
+def bitlinear(x: torch.Tensor, w: PackedWeight, out_dtype=torch.float32, out: torch.Tensor | None = None,
+              workspace=None):
+    """y = linear(ActQuant(x), WeightQuant(W)) from activations x [M, K].
+    ``workspace`` may pass preallocated (q, a_scale, q_rowsum) buffers."""
+    ldx = _rows(x, "x")
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError("x and the packed weight disagree on K")
+    if workspace is None:
+        workspace = (torch.empty((M, padded_k(K)), dtype=torch.int8, device=x.device),
+                     torch.empty(M, dtype=torch.float32, device=x.device),
+                     torch.empty(M, dtype=torch.int32, device=x.device))
+    q, a_scale, rowsum = workspace
+    y = out if out is not None else torch.empty((M, w.N), dtype=out_dtype, device=x.device)
+    ldy = _rows(y, "y")
+    with torch.cuda.device(x.device):
+        _lib.check(_lib.lib().bitnet_bitlinear_forward(
+            _stream(x), x.data_ptr(), _dtype(x), M, K, ldx, w.packed.data_ptr(), w.w_scale.data_ptr(),
+            w.N, y.data_ptr(), _dtype(y), ldy, q.data_ptr(), a_scale.data_ptr(), rowsum.data_ptr()))
+    return y
+
+
+class GroupedBitLinear:
+    """Many independent decode-size BitLinears (shared M <= 16) run as one launch.
+
+    ``items`` is a list of (x [M, K], PackedWeight, y [M, N]) device tensors; the
+    plan keeps pointers to them, so they must stay alive and in place.  Calling
+    the object writes y_i = linear(ActQuant(x_i), WeightQuant(W_i)) for all i."""
+
+    def __init__(self, items):
+        if not items:
+            raise ValueError("need at least one item")
+        x0 = items[0][0]
+        M = x0.shape[0]
+        self._keep = list(items)
+        arr = (_lib.GroupItem * len(items))()
+        for i, (x, w, y) in enumerate(items):
+            if x.shape != (M, w.K) or y.shape != (M, w.N):
+                raise ValueError(f"item {i}: shapes do not match")
+            arr[i] = _lib.GroupItem(x.data_ptr(), _rows(x, "x"), w.packed.data_ptr(), w.w_scale.data_ptr(),
+                                    y.data_ptr(), _rows(y, "y"), w.N, w.K)
+        nbytes = int(_lib.lib().bitnet_group_table_bytes(len(items)))
+        self.table = torch.empty(nbytes, dtype=torch.uint8, device=x0.device)
+        self.plan = _lib.GroupPlan()
+        self.device = x0.device
+        with torch.cuda.device(x0.device):
+            _lib.check(_lib.lib().bitnet_group_plan(
+                _stream(x0), ctypes.cast(arr, ctypes.c_void_p), len(items), M, _dtype(x0),
+                _dtype(items[0][2]), self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
+        self.bytes = sum(w.N * w.K // 4 for _, w, _ in items)
+
+    def __call__(self):
+        with torch.cuda.device(self.device):
+            _lib.check(_lib.lib().bitnet_bitlinear_grouped(torch.cuda.current_stream(self.device).cuda_stream,
+                                                           ctypes.byref(self.plan)))

@@ -1,0 +1,205 @@
+// act_quant.hip -- per-token absmax int8 activation quantisation on gfx950.
+//
+// Method: "BitVLA -- 1.58-bit Vision-Language-Action on Core AI", s1 (ActQuant
+// is per-token int8: round(x*127/max|x|) clamped to [-128, 127]) and
+// "BitNet-Embeddings-0.6B/270M: I2_S Conversion and Inference Optimization
+// Guide", s2 (8-bit absmax activations, per token).  Fixed here: one fp32
+// factor sa = 127/amax, q = rne(x*sa), a_scale = amax/127, q = 0 and
+// a_scale = 0 for an all-zero token.
+//
+// One 256-thread workgroup per token.  Each thread holds up to VPT vectors of
+// 8 elements in registers, so the token is read from HBM once: absmax is a
+// wave butterfly (v_max over __shfl_xor) plus a 4-entry LDS step, and the
+// quantised row, its int32 sum and the scale are written in the same pass.
+// The kernel is HBM-bound: 2 B read + 1 B written per element (bf16 input).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace bitnet {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+// 8 consecutive elements as fp32, from bf16 or fp32 storage.
+template <typename T>
+struct Vec8;
+
+template <>
+struct Vec8<uint16_t> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&v)[8]) {
+        uint4 w = *reinterpret_cast<const uint4*>(p);
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+    }
+    static __device__ __forceinline__ void load_scalar(const uint16_t* p, float (&v)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(p[i]);
+    }
+};
+
+template <>
+struct Vec8<float> {
+    static __device__ __forceinline__ void load(const float* p, float (&v)[8]) {
+        float4 a = *reinterpret_cast<const float4*>(p);
+        float4 b = *reinterpret_cast<const float4*>(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    static __device__ __forceinline__ void load_scalar(const float* p, float (&v)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = p[i];
+    }
+};
+
+template <typename T, bool kAligned>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
+    if constexpr (kAligned) Vec8<T>::load(p, v);
+    else Vec8<T>::load_scalar(p, v);
+}
+
+// Quantise 8 values with factor sa; returns their sum, writes 8 int8 codes.
+__device__ __forceinline__ int quant8(const float (&v)[8], float sa, uint2& out) {
+    int sum = 0;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float r = fminf(fmaxf(rne(v[i] * sa), -128.0f), 127.0f);
+        int c = static_cast<int>(r);
+        sum += c;
+        uint32_t byte = static_cast<uint32_t>(c) & 0xFFu;
+        if (i < 4) lo |= byte << (8 * i);
+        else hi |= byte << (8 * (i - 4));
+    }
+    out = make_uint2(lo, hi);
+    return sum;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r = fmaxf(r, red[i]);
+    return r;
+}
+
+__device__ __forceinline__ int block_sum(int v, int* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) == 0) red[w] = v;
+    __syncthreads();
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) r += red[i];
+    return r;
+}
+
+// VPT > 0: the token stays in registers (K <= 8 * 256 * VPT).
+// VPT == 0: any K; the row is read twice (the second read hits L2).
+template <typename T, int VPT, bool kAligned>
+__global__ __launch_bounds__(kThreads) void act_quant_kernel(
+    const T* __restrict__ x, int64_t ldx, int K, int Kp,
+    int8_t* __restrict__ q, float* __restrict__ a_scale, int32_t* __restrict__ q_rowsum) {
+    __shared__ float red_f[kWaves];
+    __shared__ int red_i[kWaves];
+    const int64_t m = blockIdx.x;
+    const T* xr = x + m * ldx;
+    int8_t* qr = q + m * static_cast<int64_t>(Kp);
+    const int nvec = K / 8;
+    const int tid = threadIdx.x;
+
+    float amax_local = 0.0f;
+    float v[VPT > 0 ? VPT : 1][8];
+    if constexpr (VPT > 0) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int vi = tid + i * kThreads;
+            if (vi < nvec) {
+                load8<T, kAligned>(xr + vi * 8, v[i]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) amax_local = fmaxf(amax_local, fabsf(v[i][e]));
+            }
+        }
+    } else {
+        for (int vi = tid; vi < nvec; vi += kThreads) {
+            load8<T, kAligned>(xr + vi * 8, v[0]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax_local = fmaxf(amax_local, fabsf(v[0][e]));
+        }
+    }
+    const float amax = block_max(amax_local, red_f);
+    // amax == 0: every x is +-0 and sa = 0 gives q = 0 exactly.
+    const float sa = (amax == 0.0f) ? 0.0f : 127.0f / amax;
+
+    int sum_local = 0;
+    if constexpr (VPT > 0) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int vi = tid + i * kThreads;
+            if (vi < nvec) {
+                uint2 out;
+                sum_local += quant8(v[i], sa, out);
+                *reinterpret_cast<uint2*>(qr + vi * 8) = out;
+            }
+        }
+    } else {
+        for (int vi = tid; vi < nvec; vi += kThreads) {
+            load8<T, kAligned>(xr + vi * 8, v[0]);
+            uint2 out;
+            sum_local += quant8(v[0], sa, out);
+            *reinterpret_cast<uint2*>(qr + vi * 8) = out;
+        }
+    }
+    // zero tail K..Kp-1 (at most 112 bytes, 8-byte stores)
+    for (int vi = nvec + tid; vi < Kp / 8; vi += kThreads)
+        *reinterpret_cast<uint2*>(qr + vi * 8) = make_uint2(0u, 0u);
+
+    const int total = block_sum(sum_local, red_i);
+    if (tid == 0) {
+        q_rowsum[m] = total;
+        a_scale[m] = (amax == 0.0f) ? 0.0f : amax / 127.0f;
+    }
+}
+
+template <typename T, bool kAligned>
+hipError_t launch_t(const T* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, float* a_scale,
+                    int32_t* q_rowsum, int Kp, hipStream_t stream) {
+    const int nvec = static_cast<int>(K / 8);
+    const dim3 grid(static_cast<unsigned>(M)), block(kThreads);
+    const int vpt = (nvec + kThreads - 1) / kThreads;
+    if (vpt <= 1)
+        act_quant_kernel<T, 1, kAligned><<<grid, block, 0, stream>>>(x, ldx, (int)K, Kp, q, a_scale, q_rowsum);
+    else if (vpt <= 2)
+        act_quant_kernel<T, 2, kAligned><<<grid, block, 0, stream>>>(x, ldx, (int)K, Kp, q, a_scale, q_rowsum);
+    else if (vpt <= 4)
+        act_quant_kernel<T, 4, kAligned><<<grid, block, 0, stream>>>(x, ldx, (int)K, Kp, q, a_scale, q_rowsum);
+    else if (vpt <= 8)
+        act_quant_kernel<T, 8, kAligned><<<grid, block, 0, stream>>>(x, ldx, (int)K, Kp, q, a_scale, q_rowsum);
+    else
+        act_quant_kernel<T, 0, kAligned><<<grid, block, 0, stream>>>(x, ldx, (int)K, Kp, q, a_scale, q_rowsum);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx,
+                            int8_t* q, float* a_scale, int32_t* q_rowsum, int64_t Kp,
+                            hipStream_t stream) {
+    const size_t esize = x_bf16 ? 2 : 4;
+    const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && ((ldx * esize) % 16 == 0);
+    if (x_bf16) {
+        auto* p = static_cast<const uint16_t*>(x);
+        return aligned ? launch_t<uint16_t, true>(p, M, K, ldx, q, a_scale, q_rowsum, (int)Kp, stream)
+                       : launch_t<uint16_t, false>(p, M, K, ldx, q, a_scale, q_rowsum, (int)Kp, stream);
+    }
+    auto* p = static_cast<const float*>(x);
+    return aligned ? launch_t<float, true>(p, M, K, ldx, q, a_scale, q_rowsum, (int)Kp, stream)
+                   : launch_t<float, false>(p, M, K, ldx, q, a_scale, q_rowsum, (int)Kp, stream);
+}
+
+}  // namespace bitnet

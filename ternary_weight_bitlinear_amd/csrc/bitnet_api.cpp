@@ -1,0 +1,425 @@
+// bitnet_api.cpp -- the C ABI declared in include/bitnet.h.
+//
+// Every entry point validates its arguments on the host before any launch and
+// reports failures through a status code plus a thread-local message.  The
+// device work itself lives in the .hip files behind kernels.h.
+//
+// The host packer (BITNET_MEM_HOST) is the same WeightQuant + layout-v1 pack
+// as the device packer ("BitVLA -- 1.58-bit Vision-Language-Action on Core
+// AI", s1 and s2; "BitNet-Embeddings-0.6B/270M: I2_S Conversion and Inference
+// Optimization Guide", s3.3 "I2_S Ternary Packing"), for converting weights
+// offline without a GPU.  It is chosen explicitly by the caller through
+// `where`; nothing in the library falls back to it.
+#include "../../include/bitnet.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "gemv.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxK = 1 << 20;
+constexpr int64_t kMaxMN = 0x7FFFFFFF;
+constexpr int64_t kGemvMaxM = 16;
+constexpr int64_t kFusedLdsBytes = 32768;     // single call: M * Kp bytes of q in LDS
+constexpr int64_t kGroupLdsBytes = 65536;     // grouped launch: M * max Kp
+constexpr int64_t kPlanMagic = 0x62746E6770ll;   // "btngp"
+
+thread_local std::string g_last_error;
+
+bitnet_status_t fail(bitnet_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+bitnet_status_t fail(bitnet_status_t s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+bitnet_status_t ok() {
+    g_last_error.clear();
+    return BITNET_OK;
+}
+
+bitnet_status_t hip_fail(hipError_t e, const char* what) {
+    return fail(BITNET_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t padded_k(int64_t K) {
+    if (K <= 0 || K % 16 != 0 || K > kMaxK) return -1;
+    return (K + 127) / 128 * 128;
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+bitnet_status_t check_dims(const char* fn, int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || M > kMaxMN) return fail(BITNET_ERR_INVALID_ARG, "%s: M=%lld out of range", fn, (long long)M);
+    if (N <= 0 || N > kMaxMN) return fail(BITNET_ERR_INVALID_ARG, "%s: N=%lld out of range", fn, (long long)N);
+    if (padded_k(K) < 0)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: K=%lld must be a positive multiple of 16 and <= %lld", fn,
+                    (long long)K, (long long)kMaxK);
+    return BITNET_OK;
+}
+
+bool valid_dtype(bitnet_dtype_t d) { return d == BITNET_F32 || d == BITNET_BF16; }
+
+// ---------------------------------------------------------------- host packer
+
+float host_load(const void* W, bitnet_dtype_t dt, int64_t idx) {
+    if (dt == BITNET_BF16) {
+        uint32_t bits = static_cast<uint32_t>(static_cast<const uint16_t*>(W)[idx]) << 16;
+        float f;
+        std::memcpy(&f, &bits, sizeof f);
+        return f;
+    }
+    return static_cast<const float*>(W)[idx];
+}
+
+bitnet_status_t host_pack(const void* W, bitnet_dtype_t dt, int64_t N, int64_t K, int64_t ldw,
+                          const std::vector<int64_t>& seg_start, uint8_t* packed, float* w_scale,
+                          float* seg_mean, int64_t* zero_count) {
+    const int64_t Kp = padded_k(K);
+    const int n_segs = static_cast<int>(seg_start.size()) - 1;
+    std::vector<double> row_sum(static_cast<size_t>(N));
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = host_load(W, dt, n * ldw + k);
+            if (!std::isfinite(v))
+                return fail(BITNET_ERR_NONFINITE, "bitnet_pack_weights: W[%lld][%lld] is not finite",
+                            (long long)n, (long long)k);
+            acc += std::fabs(static_cast<double>(v));
+        }
+        row_sum[static_cast<size_t>(n)] = acc;
+    }
+    const int64_t words_per_row = Kp / 16;
+    for (int s = 0; s < n_segs; ++s) {
+        double total = 0.0;
+        for (int64_t n = seg_start[s]; n < seg_start[s + 1]; ++n) total += row_sum[static_cast<size_t>(n)];
+        const int64_t rows = seg_start[s + 1] - seg_start[s];
+        const float mean = static_cast<float>(total / static_cast<double>(rows * K));
+        const float scale = 1.0f / mean;
+        int64_t zeros = 0;
+        for (int64_t n = seg_start[s]; n < seg_start[s + 1]; ++n) {
+            w_scale[n] = mean;
+            for (int64_t j = 0; j < words_per_row; ++j) {
+                uint32_t word = 0;
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t k = 16 * j + e;
+                    uint32_t u = 1u;
+                    if (k < K) {
+                        const float p = host_load(W, dt, n * ldw + k) * scale;
+                        const int t = (p > 0.5f) - (p < -0.5f);
+                        u = static_cast<uint32_t>(t + 1);
+                        zeros += (t == 0);
+                    }
+                    word |= u << (8 * (e % 4) + 2 * (e / 4));
+                }
+                uint8_t* dst = packed + n * (Kp / 4) + 4 * j;
+                for (int b = 0; b < 4; ++b) dst[b] = static_cast<uint8_t>(word >> (8 * b));
+            }
+        }
+        if (seg_mean) seg_mean[s] = mean;
+        if (zero_count) zero_count[s] = zeros;
+    }
+    return ok();
+}
+
+// -------------------------------------------------------------- device packer
+
+struct DeviceTemps {
+    hipStream_t stream = nullptr;
+    void* p = nullptr;
+    ~DeviceTemps() {
+        if (p) {
+            hipFreeAsync(p, stream);
+            hipStreamSynchronize(stream);
+        }
+    }
+};
+
+bitnet_status_t device_pack(hipStream_t stream, const void* W, bitnet_dtype_t dt, int64_t N, int64_t K,
+                            int64_t ldw, const std::vector<int64_t>& seg_start, uint8_t* packed,
+                            float* w_scale, float* seg_mean, int64_t* zero_count) {
+    const int64_t Kp = padded_k(K);
+    const int n_segs = static_cast<int>(seg_start.size()) - 1;
+    // one block of temporaries: row_sum | seg_start | seg_mean | seg_zero | status
+    const size_t off_start = static_cast<size_t>(N) * sizeof(double);
+    const size_t off_mean = off_start + (n_segs + 1) * sizeof(int64_t);
+    const size_t off_zero = (off_mean + n_segs * sizeof(float) + 7) / 8 * 8;
+    const size_t off_status = off_zero + n_segs * sizeof(unsigned long long);
+    const size_t bytes = off_status + sizeof(unsigned int);
+    DeviceTemps temps;
+    temps.stream = stream;
+    hipError_t e = hipMallocAsync(&temps.p, bytes, stream);
+    if (e != hipSuccess) {
+        temps.p = nullptr;
+        return hip_fail(e, "bitnet_pack_weights: temporary allocation");
+    }
+    char* base = static_cast<char*>(temps.p);
+    auto* d_row_sum = reinterpret_cast<double*>(base);
+    auto* d_start = reinterpret_cast<int64_t*>(base + off_start);
+    auto* d_mean = reinterpret_cast<float*>(base + off_mean);
+    auto* d_zero = reinterpret_cast<unsigned long long*>(base + off_zero);
+    auto* d_status = reinterpret_cast<unsigned int*>(base + off_status);
+    if ((e = hipMemcpyAsync(d_start, seg_start.data(), (n_segs + 1) * sizeof(int64_t), hipMemcpyHostToDevice,
+                            stream)) != hipSuccess)
+        return hip_fail(e, "bitnet_pack_weights: segment table upload");
+    if ((e = hipMemsetAsync(d_status, 0, sizeof(unsigned int), stream)) != hipSuccess)
+        return hip_fail(e, "bitnet_pack_weights: status clear");
+    e = bitnet::launch_pack(W, dt == BITNET_BF16, N, K, ldw, Kp, d_start, n_segs, d_row_sum, d_mean, d_zero,
+                            d_status, packed, w_scale, stream);
+    if (e != hipSuccess) return hip_fail(e, "bitnet_pack_weights: launch");
+    unsigned int status = 0;
+    std::vector<float> means(static_cast<size_t>(n_segs));
+    std::vector<unsigned long long> zeros(static_cast<size_t>(n_segs));
+    if ((e = hipMemcpyAsync(&status, d_status, sizeof status, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+        (e = hipMemcpyAsync(means.data(), d_mean, n_segs * sizeof(float), hipMemcpyDeviceToHost, stream)) !=
+            hipSuccess ||
+        (e = hipMemcpyAsync(zeros.data(), d_zero, n_segs * sizeof(unsigned long long), hipMemcpyDeviceToHost,
+                            stream)) != hipSuccess)
+        return hip_fail(e, "bitnet_pack_weights: read-back");
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "bitnet_pack_weights: sync");
+    if (status & 1u) return fail(BITNET_ERR_NONFINITE, "bitnet_pack_weights: a weight is not finite");
+    for (int s = 0; s < n_segs; ++s) {
+        if (seg_mean) seg_mean[s] = means[static_cast<size_t>(s)];
+        if (zero_count) zero_count[s] = static_cast<int64_t>(zeros[static_cast<size_t>(s)]);
+    }
+    return ok();
+}
+
+bitnet_status_t check_linear(const int8_t* q, const float* a_scale, const int32_t* q_rowsum, int64_t M,
+                             int64_t K, const uint8_t* packed, const float* w_scale, int64_t N, void* y,
+                             bitnet_dtype_t y_dtype, int64_t ldy, const char* fn) {
+    bitnet_status_t s = check_dims(fn, M, N, K);
+    if (s != BITNET_OK) return s;
+    if (!q || !a_scale || !q_rowsum || !packed || !w_scale || !y)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (!valid_dtype(y_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad y dtype %d", fn, (int)y_dtype);
+    if (ldy < N) return fail(BITNET_ERR_INVALID_ARG, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+    if (!aligned(q, 16) || !aligned(packed, 16))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: q and packed must be 16-byte aligned", fn);
+    if (!aligned(y, y_dtype == BITNET_F32 ? 4 : 2) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
+        !aligned(q_rowsum, 4))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned y or scale pointer", fn);
+    return BITNET_OK;
+}
+
+bitnet_status_t check_act_quant(const void* x, bitnet_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                const int8_t* q, const float* a_scale, const int32_t* q_rowsum, const char* fn) {
+    bitnet_status_t s = check_dims(fn, M, 1, K);
+    if (s != BITNET_OK) return s;
+    if (!x || !q || !a_scale || !q_rowsum) return fail(BITNET_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (!valid_dtype(x_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad x dtype %d", fn, (int)x_dtype);
+    if (ldx < K) return fail(BITNET_ERR_INVALID_ARG, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+    if (!aligned(x, x_dtype == BITNET_F32 ? 4 : 2) || !aligned(q, 16) || !aligned(a_scale, 4) ||
+        !aligned(q_rowsum, 4))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned pointer (q must be 16-byte aligned)", fn);
+    return BITNET_OK;
+}
+
+bitnet_status_t run_linear(hipStream_t stream, const int8_t* q, const float* a_scale, const int32_t* q_rowsum,
+                           int64_t M, int64_t K, const uint8_t* packed, const float* w_scale, int64_t N, void* y,
+                           bitnet_dtype_t y_dtype, int64_t ldy, int32_t* acc_debug, const char* fn) {
+    const int64_t Kp = padded_k(K);
+    const bool bf16 = y_dtype == BITNET_BF16;
+    hipError_t e = (M <= kGemvMaxM)
+                       ? bitnet::launch_gemv(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, bf16, ldy,
+                                             acc_debug, stream)
+                       : bitnet::launch_gemm(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, bf16, ldy,
+                                             acc_debug, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bitnet_abi_version(void) { return BITNET_ABI_VERSION; }
+
+int64_t bitnet_padded_k(int64_t K) { return padded_k(K); }
+
+int64_t bitnet_packed_bytes(int64_t N, int64_t K) {
+    const int64_t Kp = padded_k(K);
+    if (Kp < 0 || N <= 0 || N > kMaxMN) return -1;
+    return N * (Kp / 4);
+}
+
+bitnet_status_t bitnet_pack_weights(bitnet_mem_t where, hipStream_t stream, const void* W, bitnet_dtype_t w_dtype,
+                                    int64_t N, int64_t K, int64_t ldw, const int64_t* seg_rows, int32_t n_segs,
+                                    uint8_t* packed, float* w_scale, float* seg_mean, int64_t* zero_count) {
+    const char* fn = "bitnet_pack_weights";
+    bitnet_status_t s = check_dims(fn, 1, N, K);
+    if (s != BITNET_OK) return s;
+    if (where != BITNET_MEM_HOST && where != BITNET_MEM_DEVICE)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: bad memory kind %d", fn, (int)where);
+    if (!W || !packed || !w_scale) return fail(BITNET_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (!valid_dtype(w_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad W dtype %d", fn, (int)w_dtype);
+    if (ldw < K) return fail(BITNET_ERR_INVALID_ARG, "%s: ldw=%lld < K=%lld", fn, (long long)ldw, (long long)K);
+    if (!aligned(packed, 16) || !aligned(w_scale, 4) || !aligned(W, w_dtype == BITNET_F32 ? 4 : 2))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned pointer (packed must be 16-byte aligned)", fn);
+    if (n_segs < 0 || (n_segs > 0 && !seg_rows))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: bad segment table", fn);
+    std::vector<int64_t> seg_start{0};
+    if (n_segs == 0 || !seg_rows) {
+        seg_start.push_back(N);
+    } else {
+        for (int32_t i = 0; i < n_segs; ++i) {
+            if (seg_rows[i] <= 0)
+                return fail(BITNET_ERR_INVALID_ARG, "%s: segment %d has %lld rows", fn, i, (long long)seg_rows[i]);
+            seg_start.push_back(seg_start.back() + seg_rows[i]);
+            if (seg_start.back() > N) break;
+        }
+        if (seg_start.back() != N || static_cast<int32_t>(seg_start.size()) != n_segs + 1)
+            return fail(BITNET_ERR_INVALID_ARG, "%s: segment rows do not add up to N=%lld", fn, (long long)N);
+    }
+    if (where == BITNET_MEM_HOST) return host_pack(W, w_dtype, N, K, ldw, seg_start, packed, w_scale, seg_mean, zero_count);
+    return device_pack(stream, W, w_dtype, N, K, ldw, seg_start, packed, w_scale, seg_mean, zero_count);
+}
+
+bitnet_status_t bitnet_act_quant(hipStream_t stream, const void* x, bitnet_dtype_t x_dtype, int64_t M, int64_t K,
+                                 int64_t ldx, int8_t* q, float* a_scale, int32_t* q_rowsum) {
+    const char* fn = "bitnet_act_quant";
+    bitnet_status_t s = check_act_quant(x, x_dtype, M, K, ldx, q, a_scale, q_rowsum, fn);
+    if (s != BITNET_OK) return s;
+    hipError_t e = bitnet::launch_act_quant(x, x_dtype == BITNET_BF16, M, K, ldx, q, a_scale, q_rowsum,
+                                            padded_k(K), stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+bitnet_status_t bitnet_linear_forward(hipStream_t stream, const int8_t* q, const float* a_scale,
+                                      const int32_t* q_rowsum, int64_t M, int64_t K, const uint8_t* packed,
+                                      const float* w_scale, int64_t N, void* y, bitnet_dtype_t y_dtype, int64_t ldy,
+                                      int32_t* acc_debug) {
+    const char* fn = "bitnet_linear_forward";
+    bitnet_status_t s = check_linear(q, a_scale, q_rowsum, M, K, packed, w_scale, N, y, y_dtype, ldy, fn);
+    if (s != BITNET_OK) return s;
+    if (acc_debug && !aligned(acc_debug, 4)) return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned acc_debug", fn);
+    return run_linear(stream, q, a_scale, q_rowsum, M, K, packed, w_scale, N, y, y_dtype, ldy, acc_debug, fn);
+}
+
+bitnet_status_t bitnet_bitlinear_forward(hipStream_t stream, const void* x, bitnet_dtype_t x_dtype, int64_t M,
+                                         int64_t K, int64_t ldx, const uint8_t* packed, const float* w_scale,
+                                         int64_t N, void* y, bitnet_dtype_t y_dtype, int64_t ldy, int8_t* q,
+                                         float* a_scale, int32_t* q_rowsum) {
+    const char* fn = "bitnet_bitlinear_forward";
+    bitnet_status_t s = check_act_quant(x, x_dtype, M, K, ldx, q, a_scale, q_rowsum, fn);
+    if (s != BITNET_OK) return s;
+    s = check_linear(q, a_scale, q_rowsum, M, K, packed, w_scale, N, y, y_dtype, ldy, fn);
+    if (s != BITNET_OK) return s;
+    const int64_t Kp = padded_k(K);
+    const int64_t esize = x_dtype == BITNET_BF16 ? 2 : 4;
+    const bool fuse = M <= kGemvMaxM && M * Kp <= kFusedLdsBytes && aligned(x, 16) && (ldx * esize) % 16 == 0;
+    hipError_t e;
+    if (fuse) {
+        bitnet::GemvProblem p{};
+        p.x = x; p.ldx = ldx;
+        p.q_out = q; p.a_scale_out = a_scale; p.rowsum_out = q_rowsum;
+        p.packed = packed; p.w_scale = w_scale; p.y = y; p.ldy = ldy;
+        p.M = (int)M; p.N = (int)N; p.K = (int)K; p.Kp = (int)Kp;
+        e = bitnet::launch_gemv_fused(p, x_dtype == BITNET_BF16, y_dtype == BITNET_BF16, stream);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return ok();
+    }
+    e = bitnet::launch_act_quant(x, x_dtype == BITNET_BF16, M, K, ldx, q, a_scale, q_rowsum, Kp, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return run_linear(stream, q, a_scale, q_rowsum, M, K, packed, w_scale, N, y, y_dtype, ldy, nullptr, fn);
+}
+
+int64_t bitnet_group_table_bytes(int32_t count) {
+    if (count <= 0) return -1;
+    return static_cast<int64_t>(count) * static_cast<int64_t>(sizeof(bitnet::GemvProblem));
+}
+
+bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t* items, int32_t count, int64_t M,
+                                  bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype, void* table_dev,
+                                  int64_t table_bytes, bitnet_group_plan_t* plan) {
+    const char* fn = "bitnet_group_plan";
+    if (count <= 0 || !items || !plan || !table_dev)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: need count > 0, items, table_dev and plan", fn);
+    if (!aligned(table_dev, 16) || table_bytes < bitnet_group_table_bytes(count))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: table_dev must be 16-byte aligned and hold %lld bytes", fn,
+                    (long long)bitnet_group_table_bytes(count));
+    if (M <= 0 || M > kGemvMaxM) return fail(BITNET_ERR_INVALID_ARG, "%s: M=%lld must be in 1..16", fn, (long long)M);
+    if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad dtype", fn);
+    const int64_t esize = x_dtype == BITNET_BF16 ? 2 : 4;
+    std::vector<bitnet::GemvProblem> table(static_cast<size_t>(count));
+    int64_t tiles = 0, max_kp = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const bitnet_group_item_t& it = items[i];
+        char where[64];
+        snprintf(where, sizeof where, "%s: item %d", fn, i);
+        bitnet_status_t s = check_dims(where, M, it.N, it.K);
+        if (s != BITNET_OK) return s;
+        if (!it.x || !it.packed || !it.w_scale || !it.y)
+            return fail(BITNET_ERR_INVALID_ARG, "%s: a required pointer is NULL", where);
+        if (it.ldx < it.K || it.ldy < it.N) return fail(BITNET_ERR_INVALID_ARG, "%s: ldx < K or ldy < N", where);
+        if (!aligned(it.x, 16) || (it.ldx * esize) % 16 != 0 || !aligned(it.packed, 16) ||
+            !aligned(it.w_scale, 4) || !aligned(it.y, y_dtype == BITNET_F32 ? 4 : 2))
+            return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned pointer or x row stride", where);
+        const int64_t Kp = padded_k(it.K);
+        if (M * Kp > kGroupLdsBytes)
+            return fail(BITNET_ERR_UNSUPPORTED, "%s: M*Kp=%lld exceeds %lld bytes", where, (long long)(M * Kp),
+                        (long long)kGroupLdsBytes);
+        bitnet::GemvProblem& p = table[static_cast<size_t>(i)];
+        p = bitnet::GemvProblem{};
+        p.x = it.x; p.ldx = it.ldx; p.packed = it.packed; p.w_scale = it.w_scale;
+        p.y = it.y; p.ldy = it.ldy;
+        p.M = (int)M; p.N = (int)it.N; p.K = (int)it.K; p.Kp = (int)Kp;
+        p.tile0 = (int)tiles;
+        tiles += bitnet::gemv_tiles(it.N);
+        if (tiles > kMaxMN) return fail(BITNET_ERR_INVALID_ARG, "%s: too many workgroups in the group", fn);
+        if (Kp > max_kp) max_kp = Kp;
+    }
+    hipError_t e = hipMemcpyAsync(table_dev, table.data(), table.size() * sizeof(bitnet::GemvProblem),
+                                  hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "bitnet_group_plan: table upload");
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "bitnet_group_plan: sync");
+    plan->opaque[0] = kPlanMagic;
+    plan->opaque[1] = static_cast<int64_t>(reinterpret_cast<uintptr_t>(table_dev));
+    plan->opaque[2] = count;
+    plan->opaque[3] = M;
+    plan->opaque[4] = tiles;
+    plan->opaque[5] = M * max_kp;
+    plan->opaque[6] = x_dtype;
+    plan->opaque[7] = y_dtype;
+    return ok();
+}
+
+bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_plan_t* plan) {
+    const char* fn = "bitnet_bitlinear_grouped";
+    if (!plan || plan->opaque[0] != kPlanMagic)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: plan was not made by bitnet_group_plan", fn);
+    const auto* table = reinterpret_cast<const bitnet::GemvProblem*>(static_cast<uintptr_t>(plan->opaque[1]));
+    hipError_t e = bitnet::launch_gemv_grouped(table, static_cast<int>(plan->opaque[2]), plan->opaque[4],
+                                               static_cast<size_t>(plan->opaque[5]), true,
+                                               plan->opaque[6] == BITNET_BF16, plan->opaque[7] == BITNET_BF16,
+                                               stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+const char* bitnet_status_string(bitnet_status_t s) {
+    switch (s) {
+        case BITNET_OK: return "ok";
+        case BITNET_ERR_INVALID_ARG: return "invalid argument";
+        case BITNET_ERR_UNSUPPORTED: return "unsupported";
+        case BITNET_ERR_HIP: return "HIP error";
+        case BITNET_ERR_NONFINITE: return "non-finite weight";
+    }
+    return "unknown status";
+}
+
+const char* bitnet_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

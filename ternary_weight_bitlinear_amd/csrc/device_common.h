@@ -1,0 +1,75 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels.
+//
+// Numerics: every kernel is compiled with -ffp-contract=off and correctly
+// rounded fp32 division, so x*sa, 127/amax, a_scale*w_scale and (float)acc*f
+// are single IEEE operations with round-to-nearest-even, the same operations
+// in the same order as the definition in bitnet.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern -> fp32 (exact widening).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN -> quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Two packed bf16 (low half = element 0) -> fp32 pair.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round half to even (v_rndne_f32).
+__device__ __forceinline__ float rne(float v) { return __builtin_rintf(v); }
+
+// Four stored codes of one 32-bit packed word, lane p = 0..3: the bytes hold
+// elements 16j+4p+0..3 as unsigned values u in {0,1,2}.
+__device__ __forceinline__ uint32_t codes_of(uint32_t word, int p) {
+    return (word >> (2 * p)) & 0x03030303u;
+}
+
+// Expand one packed word (16 elements) into a 16-byte int8 MFMA operand whose
+// byte 4p+b is element 16j+4p+b.
+__device__ __forceinline__ v4i expand_word(uint32_t w) {
+    v4i r;
+    r[0] = static_cast<int>(w & 0x03030303u);
+    r[1] = static_cast<int>((w >> 2) & 0x03030303u);
+    r[2] = static_cast<int>((w >> 4) & 0x03030303u);
+    r[3] = static_cast<int>((w >> 6) & 0x03030303u);
+    return r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// 16x16x64 int8 MFMA (gfx950): C[i][j] += sum_k A[i][k] B[k][j]; lane l holds
+// row i = l%16 of A and column j = l%16 of B for one group of 16 k values
+// (the same group for A and B), and C[4*(l/16)+r][l%16] in register r.
+__device__ __forceinline__ v4i mfma16(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+}  // namespace bitnet

@@ -1,0 +1,37 @@
+// kernels.h -- internal launchers behind the C ABI (not part of the public API).
+// Each launcher enqueues on `stream` and returns the launch status.  Shapes and
+// pointers are validated by the caller (bitnet_api.cpp) before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+// Per-token ActQuant of x [M, K] (row stride ldx) into q [M][Kp].
+hipError_t launch_act_quant(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx,
+                            int8_t* q, float* a_scale, int32_t* q_rowsum, int64_t Kp,
+                            hipStream_t stream);
+
+// Linear on quantised operands, M <= 16: one streaming pass over packed.
+hipError_t launch_gemv(const int8_t* q, const float* a_scale, const int32_t* q_rowsum,
+                       int64_t M, int64_t Kp, const uint8_t* packed, const float* w_scale,
+                       int64_t N, void* y, bool y_bf16, int64_t ldy, int32_t* acc_debug,
+                       hipStream_t stream);
+
+// Linear on quantised operands, any M: int8-MFMA GEMM.
+hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_rowsum,
+                       int64_t M, int64_t Kp, const uint8_t* packed, const float* w_scale,
+                       int64_t N, void* y, bool y_bf16, int64_t ldy, int32_t* acc_debug,
+                       hipStream_t stream);
+
+// Device WeightQuant + pack.  seg_start_dev [n_segs + 1] holds the first row of
+// every segment and N at the end.  Temporaries: row_sum [N] doubles,
+// seg_mean_dev / seg_zero_dev [n_segs], status_dev (bit 0: non-finite weight).
+hipError_t launch_pack(const void* W, bool w_bf16, int64_t N, int64_t K, int64_t ldw,
+                       int64_t Kp, const int64_t* seg_start_dev, int32_t n_segs,
+                       double* row_sum, float* seg_mean_dev, unsigned long long* seg_zero_dev,
+                       unsigned int* status_dev, uint8_t* packed, float* w_scale,
+                       hipStream_t stream);
+
+}  // namespace bitnet

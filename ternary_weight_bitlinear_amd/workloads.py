@@ -116,9 +116,10 @@ def draw_weight(shape, seed: int, dist: str = "normal", sigma: float = WEIGHT_SI
     if dist == "normal":
         w = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * sigma
     elif dist == "laplace":
+        # Laplace(0, b) = b * (E1 - E2) with E1, E2 ~ Exp(1): finite for every draw
         b = sigma / math.sqrt(2.0)
-        u = torch.rand(shape, generator=g, device=device, dtype=torch.float32) - 0.5
-        w = -b * torch.sign(u) * torch.log1p(-2.0 * u.abs())
+        e = torch.empty((2, *shape), device=device, dtype=torch.float32).exponential_(generator=g)
+        w = b * (e[0] - e[1])
     else:
         raise ValueError(dist)
     return w.to(torch.bfloat16)

@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects bad arguments before launching anything, and its host
+packer (BITNET_MEM_HOST) produces the oracle's bytes, scales and counts."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+import torch
+
+import ternary_weight_bitlinear_amd as tw
+from ternary_weight_bitlinear_amd import _lib
+from ternary_weight_bitlinear_amd import workloads as wl
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "bitnet.h"
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(bitnet_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_main_calls():
+    names = declared_functions()
+    for fn in ("bitnet_pack_weights", "bitnet_act_quant", "bitnet_linear_forward"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    handle = ctypes.CDLL(tw.library_path())
+    for name in declared_functions():
+        assert hasattr(handle, name), name
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_sizes_and_strings():
+    L = _lib.lib()
+    assert L.bitnet_abi_version() == 1
+    assert [L.bitnet_padded_k(k) for k in (16, 128, 144, 1152, 4304, 6912)] == [128, 128, 256, 1152, 4352, 6912]
+    assert [L.bitnet_padded_k(k) for k in (0, -16, 8, 100, (1 << 20) + 16)] == [-1] * 5
+    assert L.bitnet_packed_bytes(3, 4304) == 3 * 4352 // 4
+    assert L.bitnet_packed_bytes(0, 16) == -1
+    for s in range(5):
+        assert L.bitnet_status_string(s)
+
+
+def _status_and_error(fn, *args):
+    st = fn(*args)
+    return st, _lib.lib().bitnet_last_error().decode()
+
+
+def test_argument_errors_launch_nothing():
+    """Every call here fails validation on the host, so no HIP call is made."""
+    L = _lib.lib()
+    buf = (ctypes.c_uint8 * 4096)()
+    p = ctypes.addressof(buf)
+    p16 = (p + 15) // 16 * 16
+    cases = [
+        (L.bitnet_act_quant, (None, p16, _lib.BF16, 1, 15, 16, p16, p16, p16), "K=15"),
+        (L.bitnet_act_quant, (None, p16, _lib.BF16, 0, 16, 16, p16, p16, p16), "M=0"),
+        (L.bitnet_act_quant, (None, p16, _lib.BF16, 1, 16, 8, p16, p16, p16), "ldx"),
+        (L.bitnet_act_quant, (None, None, _lib.BF16, 1, 16, 16, p16, p16, p16), "NULL"),
+        (L.bitnet_act_quant, (None, p16, 7, 1, 16, 16, p16, p16, p16), "dtype"),
+        (L.bitnet_act_quant, (None, p16, _lib.BF16, 1, 16, 16, p16 + 4, p16, p16), "aligned"),
+        (L.bitnet_linear_forward, (None, p16, p16, p16, 1, 16, p16, p16, 4, p16, _lib.F32, 3, None), "ldy"),
+        (L.bitnet_linear_forward, (None, p16, p16, p16, 1, 16, p16 + 8, p16, 4, p16, _lib.F32, 4, None), "aligned"),
+        (L.bitnet_linear_forward, (None, p16, p16, p16, 1, 16, p16, p16, 0, p16, _lib.F32, 4, None), "N=0"),
+        (L.bitnet_linear_forward, (None, p16, p16, None, 1, 16, p16, p16, 4, p16, _lib.F32, 4, None), "NULL"),
+        (L.bitnet_linear_forward, (None, p16, p16, p16, 1, 16, p16, p16, 4, p16, 5, 4, None), "dtype"),
+        (L.bitnet_bitlinear_forward, (None, p16, _lib.BF16, 2, 32, 32, p16, p16, 4, p16, _lib.F32, 2,
+                                      p16, p16, p16), "ldy"),
+        (L.bitnet_pack_weights, (_lib.MEM_HOST, None, p16, _lib.BF16, 4, 16, 16,
+                                 (ctypes.c_int64 * 2)(2, 1), 2, p16, p16, None, None), "segment"),
+        (L.bitnet_pack_weights, (_lib.MEM_HOST, None, p16, _lib.BF16, 4, 16, 16,
+                                 (ctypes.c_int64 * 2)(4, 0), 2, p16, p16, None, None), "segment 1"),
+        (L.bitnet_pack_weights, (9, None, p16, _lib.BF16, 4, 16, 16, None, 0, p16, p16, None, None), "memory"),
+        (L.bitnet_pack_weights, (_lib.MEM_DEVICE, None, p16, _lib.BF16, 4, 24, 24, None, 0, p16, p16, None,
+                                 None), "K=24"),
+    ]
+    for fn, args, needle in cases:
+        st, msg = _status_and_error(fn, *args)
+        assert st == _lib.ERR_INVALID_ARG, (fn.__name__, needle, st, msg)
+        assert needle in msg, (needle, msg)
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("N,K,segments,dtype,ldw_extra", [
+    (1, 16, None, torch.bfloat16, 0),
+    (33, 144, None, torch.bfloat16, 16),
+    (64, 1152, (32, 16, 16), torch.bfloat16, 0),
+    (17, 4304, None, torch.bfloat16, 0),
+    (40, 256, (8, 32), torch.float32, 32),
+])
+def test_host_packer_matches_oracle(orc, N, K, segments, dtype, ldw_extra):
+    base = wl.draw_weight((N, K + ldw_extra), seed=N * 1000 + K, dist="normal")
+    if segments:  # very different scales per segment
+        scales = torch.cat([torch.full((r, 1), 10.0 ** i) for i, r in enumerate(segments)])
+        base = (base.float() * scales).to(torch.bfloat16)
+    W = base.to(dtype)[:, :K]          # a strided view when ldw_extra > 0
+    pw = tw.pack(W, segments)
+    Wn = _bits(W.contiguous()) if dtype == torch.bfloat16 else W.contiguous().numpy()
+    t, w_scale, seg_mean, zeros = orc.weight_quant(Wn, segments)
+    assert np.array_equal(pw.packed.numpy(), orc.pack(t))
+    assert np.array_equal(pw.w_scale.numpy().view(np.uint32), w_scale.view(np.uint32))
+    assert np.array_equal(pw.seg_mean.numpy().view(np.uint32), seg_mean.view(np.uint32))
+    assert np.array_equal(pw.zero_count.numpy(), zeros)
+
+
+def test_host_packer_rejects_non_finite():
+    W = wl.draw_weight((4, 32), seed=5)
+    W[2, 7] = float("inf")
+    with pytest.raises(tw.BitnetError) as e:
+        tw.pack(W)
+    assert e.value.status == _lib.ERR_NONFINITE
+    W[2, 7] = float("nan")
+    with pytest.raises(tw.BitnetError):
+        tw.pack(W)
+
+
+def test_host_packer_degenerate_tensors(orc):
+    W = torch.zeros((3, 48), dtype=torch.bfloat16)
+    pw = tw.pack(W)
+    assert torch.all(pw.packed == 0x55) and torch.all(pw.w_scale == 0) and pw.zero_count[0] == 3 * 48
+    W = torch.full((2, 16), -0.25, dtype=torch.bfloat16)
+    pw = tw.pack(W)
+    t, _ = orc.unpack(pw.packed.numpy(), 16)
+    assert np.all(t == -1)

@@ -1,0 +1,254 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: packed bytes, codes, w_scale, q, a_scale, q_rowsum and the int32 acc are
+bit-exact; fp32 y is within 1e-5 relative of the oracle (the operation order is
+the same, so it is expected and checked to be bit-exact as well); bf16 y is
+bit-exact.  Inputs come from the seeded generators in
+ternary_weight_bitlinear_amd.workloads; the oracle sees the same bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import ternary_weight_bitlinear_amd as tw
+from ternary_weight_bitlinear_amd import _lib
+from ternary_weight_bitlinear_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def f32bits(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def check_y(y_dev: torch.Tensor, y_orc: np.ndarray):
+    if y_dev.dtype == torch.bfloat16:
+        assert np.array_equal(bits(y_dev), y_orc)
+        return
+    y = y_dev.cpu().numpy()
+    rel = np.abs(y.astype(np.float64) - y_orc) / np.maximum(np.abs(y_orc.astype(np.float64)), 1e-30)
+    assert np.all((rel <= 1e-5) | (y == y_orc)), float(rel.max())
+    assert np.array_equal(f32bits(y), f32bits(y_orc))     # same op order: bit-exact
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[case] {request.node.nodeid}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ ActQuant
+
+@pytest.mark.parametrize("M,K,dist", [
+    (1, 16, "normal"), (1, 2560, "normal_outliers"), (3, 144, "normal"), (17, 1152, "normal"),
+    (64, 4304, "student_t_channels"), (5, 6912, "normal"), (2, 20480, "normal"), (300, 1024, "normal"),
+])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_act_quant(orc, M, K, dist, dtype):
+    x = wl.draw_activation((M, K), seed=M * 7 + K, dist=dist)
+    xd = x.to(DEV).to(dtype)
+    q, a, r = tw.act_quant(xd)
+    xo = bits(x) if dtype == torch.bfloat16 else x.float().numpy()
+    qo, ao, ro = orc.act_quant(xo)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(f32bits(a.cpu().numpy()), f32bits(ao))
+    assert np.array_equal(r.cpu().numpy(), ro)
+
+
+def test_act_quant_strided_zero_and_extreme_tokens(orc):
+    K = 272
+    base = wl.draw_activation((6, K + 40), seed=99).to(DEV)
+    base[1].zero_()                                  # all-zero token
+    base[2] *= 2.0 ** 100                            # huge values
+    base[3] *= 2.0 ** -100                           # tiny values
+    base[4, 3] = 254.0                               # exact ties (amax = 254)
+    base[4, :3] = torch.tensor([1.0, 3.0, 5.0])
+    base[4, 4:] = 0
+    x = base[:, :K]                                  # ldx = K + 40, rows not 16-byte aligned
+    q, a, r = tw.act_quant(x)
+    qo, ao, ro = orc.act_quant(bits(x))
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(f32bits(a.cpu().numpy()), f32bits(ao))
+    assert np.array_equal(r.cpu().numpy(), ro)
+    assert a[1].item() == 0 and not q[1].any()
+
+
+# -------------------------------------------------------------------- packer
+
+@pytest.mark.parametrize("N,K,segments,dist", [
+    (1, 16, None, "normal"), (5, 144, None, "normal"), (33, 1152, (11, 11, 11), "normal"),
+    (640, 2560, None, "normal"), (4304, 1152, None, "normal"), (1152, 4304, None, "laplace"),
+    (3840, 2560, (2560, 640, 640), "normal"), (70, 6912, (35, 35), "laplace"),
+])
+def test_device_pack(orc, N, K, segments, dist):
+    W = wl.draw_weight((N, K), seed=N + K, dist=dist)
+    if segments:
+        scales = torch.cat([torch.full((rr, 1), 3.0 ** i) for i, rr in enumerate(segments)])
+        W = (W.float() * scales).to(torch.bfloat16)
+    pw = tw.pack(W.to(DEV), segments)
+    t, ws, sm, zc = orc.weight_quant(bits(W), segments)
+    assert np.array_equal(pw.packed.cpu().numpy(), orc.pack(t))
+    assert np.array_equal(f32bits(pw.w_scale.cpu().numpy()), f32bits(ws))
+    assert np.array_equal(f32bits(pw.seg_mean.numpy()), f32bits(sm))
+    assert np.array_equal(pw.zero_count.numpy(), zc)
+    # the host packer of the library gives the same bytes
+    ph = tw.pack(W, segments)
+    assert torch.equal(ph.packed, pw.packed.cpu())
+
+
+def test_device_pack_fp32_strided_and_degenerate(orc):
+    W = wl.draw_weight((48, 320), seed=3).float().to(DEV)[:, :304]
+    pw = tw.pack(W)
+    t, ws, _, _ = orc.weight_quant(W.cpu().contiguous().numpy())
+    assert np.array_equal(pw.packed.cpu().numpy(), orc.pack(t))
+    assert np.array_equal(f32bits(pw.w_scale.cpu().numpy()), f32bits(ws))
+    Z = torch.zeros((20, 64), dtype=torch.bfloat16, device=DEV)
+    pz = tw.pack(Z)
+    assert torch.all(pz.packed == 0x55) and torch.all(pz.w_scale == 0)
+
+
+def test_device_pack_rejects_non_finite():
+    W = wl.draw_weight((9, 64), seed=4).to(DEV)
+    W[5, 60] = float("nan")
+    with pytest.raises(tw.BitnetError) as e:
+        tw.pack(W)
+    assert e.value.status == _lib.ERR_NONFINITE
+
+
+# -------------------------------------------------------------------- linear
+
+LINEAR_CASES = [
+    # decode kernel (M <= 16)
+    (1, 1, 16), (1, 16, 128), (1, 33, 144), (1, 640, 2560), (2, 257, 1152), (5, 130, 4304),
+    (8, 64, 6912), (16, 100, 2048), (1, 4304, 1152),
+    # GEMM (M > 16)
+    (17, 16, 16), (33, 130, 144), (130, 257, 1152), (300, 200, 4304), (257, 129, 6912), (512, 640, 2560),
+]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_CASES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_linear(orc, M, N, K, out):
+    x, W = wl.random_case(M * 131 + N * 7 + K, M, N, K, x_dist="normal_outliers")
+    ref = orc.linear(bits(x), bits(W), out=out)
+    pw = tw.pack(W.to(DEV))
+    q, a, r = tw.act_quant(x.to(DEV))
+    y, acc = tw.linear(q, a, r, pw, out_dtype=torch.float32 if out == "f32" else torch.bfloat16,
+                       acc_debug=True)
+    assert np.array_equal(pw.packed.cpu().numpy(), ref["packed"])
+    assert np.array_equal(q.cpu().numpy(), ref["q"])
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    check_y(y, ref["y"])
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 17, 64])
+def test_linear_segments_and_strided_output(orc, M):
+    K, segs = 2560, (256, 64, 64)
+    N = sum(segs)
+    x = wl.draw_activation((M, K), seed=M)
+    W = torch.cat([wl.draw_weight((rr, K), seed=10 + i, dist="laplace") * (4.0 ** i)
+                   for i, rr in enumerate(segs)]).to(torch.bfloat16)
+    ref = orc.linear(bits(x), bits(W), segments=segs)
+    pw = tw.pack(W.to(DEV), segs)
+    q, a, r = tw.act_quant(x.to(DEV))
+    ybuf = torch.full((M, N + 24), float("nan"), device=DEV)
+    y = tw.linear(q, a, r, pw, out=ybuf[:, :N])
+    check_y(y, ref["y"])
+    assert torch.isnan(ybuf[:, N:]).all()            # nothing written past N
+
+
+def test_batch_invariance(orc):
+    """A token's output bits do not depend on M or on the kernel (decode vs GEMM)."""
+    K, N = 1152, 300
+    x, W = wl.random_case(77, 200, N, K)
+    pw = tw.pack(W.to(DEV))
+    xd = x.to(DEV)
+    y_all = tw.bitlinear(xd, pw)
+    for lo, hi in ((0, 1), (5, 13), (100, 116), (150, 167), (0, 200)):
+        y_part = tw.bitlinear(xd[lo:hi].contiguous(), pw)
+        assert torch.equal(y_part, y_all[lo:hi])
+
+
+def test_bitlinear_equals_two_calls(orc):
+    for M in (1, 9, 40):
+        x, W = wl.random_case(M, M, 96, 512)
+        pw = tw.pack(W.to(DEV))
+        xd = x.to(DEV)
+        q, a, r = tw.act_quant(xd)
+        y2 = tw.linear(q, a, r, pw, out_dtype=torch.bfloat16)
+        y1 = tw.bitlinear(xd, pw, out_dtype=torch.bfloat16)
+        assert torch.equal(y1, y2)
+        assert np.array_equal(bits(y1), orc.linear(bits(x), bits(W), out="bf16")["y"])
+
+
+def test_closed_forms_on_device():
+    """Permutation weights give acc = q[:, perm]; constant weights give acc = q_rowsum."""
+    K = 256
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(1))
+    P = torch.zeros((K, K), dtype=torch.bfloat16)
+    P[torch.arange(K), perm] = 1.0
+    x = wl.draw_activation((20, K), seed=5).to(DEV)
+    q, a, r = tw.act_quant(x)
+    for M in (1, 20):
+        _, acc = tw.linear(q[:M], a[:M], r[:M], tw.pack(P.to(DEV)), acc_debug=True)
+        assert torch.equal(acc, q[:M, :K][:, perm.to(DEV)].int())
+        _, acc = tw.linear(q[:M], a[:M], r[:M], tw.pack(torch.full((7, K), 0.5, dtype=torch.bfloat16,
+                                                                    device=DEV)), acc_debug=True)
+        assert torch.equal(acc, r[:M, None].expand(M, 7))
+
+
+def test_linear_argument_errors_on_device():
+    x = torch.zeros((2, 32), dtype=torch.bfloat16, device=DEV)
+    q, a, r = tw.act_quant(x)
+    pw = tw.pack(torch.ones((4, 32), dtype=torch.bfloat16, device=DEV))
+    y = torch.empty((2, 3), device=DEV)
+    with pytest.raises(tw.BitnetError) as e:
+        _lib.check(_lib.lib().bitnet_linear_forward(None, q.data_ptr(), a.data_ptr(), r.data_ptr(), 2, 32,
+                                                    pw.packed.data_ptr(), pw.w_scale.data_ptr(), 4,
+                                                    y.data_ptr(), _lib.F32, 3, None))
+    assert e.value.status == _lib.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("M,dtype", [(1, torch.bfloat16), (3, torch.bfloat16), (2, torch.float32)])
+def test_grouped_matches_oracle_and_single_calls(orc, M, dtype):
+    shapes = [(2560, 2560), (640, 2560), (6912, 2560), (2560, 6912), (33, 144), (4304, 1152), (1, 16),
+              (1152, 4304), (17, 16384 if M == 1 else 4096)]
+    items, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        x, W = wl.random_case(500 + i, M, N, K, x_dist="normal_outliers")
+        pw = tw.pack(W.to(DEV))
+        xd = x.to(DEV).to(dtype)
+        y = torch.full((M, N), float("nan"), device=DEV)
+        items.append((xd, pw, y))
+        xo = bits(x) if dtype == torch.bfloat16 else x.float().numpy()
+        refs.append(orc.linear(xo, bits(W)))
+    group = tw.GroupedBitLinear(items)
+    for rep in range(2):                       # the plan is reusable
+        for _, _, y in items:
+            y.fill_(float("nan"))
+        group()
+        torch.cuda.synchronize()
+        for (xd, pw, y), ref in zip(items, refs):
+            check_y(y, ref["y"])
+            assert torch.equal(y, tw.bitlinear(xd, pw))
+
+
+def test_grouped_plan_rejects_bad_items():
+    x = torch.zeros((1, 64), dtype=torch.bfloat16, device=DEV)
+    pw = tw.pack(torch.ones((8, 64), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        tw.GroupedBitLinear([(x, pw, torch.empty((1, 9), device=DEV))])
+    x17 = torch.zeros((17, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(tw.BitnetError) as e:
+        tw.GroupedBitLinear([(x17, pw, torch.empty((17, 8), device=DEV))])
+    assert e.value.status == _lib.ERR_INVALID_ARG
