@@ -354,7 +354,7 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
     if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad dtype", fn);
     const int64_t esize = x_dtype == BITNET_BF16 ? 2 : 4;
     std::vector<bitnet::GemvProblem> table(static_cast<size_t>(count));
-    int64_t tiles = 0, max_kp = 0;
+    int64_t tiles = 0, steps = 0, max_kp = 0;
     for (int32_t i = 0; i < count; ++i) {
         const bitnet_group_item_t& it = items[i];
         char where[64];
@@ -368,17 +368,21 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
             !aligned(it.w_scale, 4) || !aligned(it.y, y_dtype == BITNET_F32 ? 4 : 2))
             return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned pointer or x row stride", where);
         const int64_t Kp = padded_k(it.K);
-        if (M * Kp > kGroupLdsBytes)
-            return fail(BITNET_ERR_UNSUPPORTED, "%s: M*Kp=%lld exceeds %lld bytes", where, (long long)(M * Kp),
-                        (long long)kGroupLdsBytes);
+        if (static_cast<int64_t>(bitnet::gemv_group_lds(M, Kp)) > kGroupLdsBytes)
+            return fail(BITNET_ERR_UNSUPPORTED, "%s: M tokens of K=%lld need more than %lld bytes of LDS", where,
+                        (long long)it.K, (long long)kGroupLdsBytes);
         bitnet::GemvProblem& p = table[static_cast<size_t>(i)];
         p = bitnet::GemvProblem{};
         p.x = it.x; p.ldx = it.ldx; p.packed = it.packed; p.w_scale = it.w_scale;
         p.y = it.y; p.ldy = it.ldy;
         p.M = (int)M; p.N = (int)it.N; p.K = (int)it.K; p.Kp = (int)Kp;
         p.tile0 = (int)tiles;
-        tiles += bitnet::gemv_tiles(it.N);
-        if (tiles > kMaxMN) return fail(BITNET_ERR_INVALID_ARG, "%s: too many workgroups in the group", fn);
+        p.ntiles = (int)bitnet::gemv_group_tiles(it.N);
+        p.steps = (int)bitnet::gemv_group_steps(Kp);
+        p.step0 = steps;
+        tiles += p.ntiles;
+        steps += static_cast<int64_t>(p.ntiles) * p.steps;
+        if (tiles > kMaxMN) return fail(BITNET_ERR_INVALID_ARG, "%s: too many tiles in the group", fn);
         if (Kp > max_kp) max_kp = Kp;
     }
     hipError_t e = hipMemcpyAsync(table_dev, table.data(), table.size() * sizeof(bitnet::GemvProblem),
@@ -390,9 +394,9 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
     plan->opaque[2] = count;
     plan->opaque[3] = M;
     plan->opaque[4] = tiles;
-    plan->opaque[5] = M * max_kp;
-    plan->opaque[6] = x_dtype;
-    plan->opaque[7] = y_dtype;
+    plan->opaque[5] = static_cast<int64_t>(bitnet::gemv_group_lds(M, max_kp));
+    plan->opaque[6] = static_cast<int64_t>(x_dtype) | (static_cast<int64_t>(y_dtype) << 8);
+    plan->opaque[7] = steps;
     return ok();
 }
 
@@ -402,9 +406,9 @@ bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_
         return fail(BITNET_ERR_INVALID_ARG, "%s: plan was not made by bitnet_group_plan", fn);
     const auto* table = reinterpret_cast<const bitnet::GemvProblem*>(static_cast<uintptr_t>(plan->opaque[1]));
     hipError_t e = bitnet::launch_gemv_grouped(table, static_cast<int>(plan->opaque[2]), plan->opaque[4],
-                                               static_cast<size_t>(plan->opaque[5]), true,
-                                               plan->opaque[6] == BITNET_BF16, plan->opaque[7] == BITNET_BF16,
-                                               stream);
+                                               plan->opaque[7], static_cast<size_t>(plan->opaque[5]),
+                                               (plan->opaque[6] & 0xFF) == BITNET_BF16,
+                                               ((plan->opaque[6] >> 8) & 0xFF) == BITNET_BF16, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }

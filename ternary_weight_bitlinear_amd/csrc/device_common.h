@@ -13,6 +13,24 @@ namespace bitnet {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Loads and stores through pointers that the compiler cannot prove global (for
+// example pointers read from a descriptor in memory) would otherwise become
+// flat accesses, which count against both wait counters and force a full
+// wait before every use; these casts make them global_load / global_store so
+// independent loads can stay in flight.
+#define BITNET_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ T gload(const void* p) {
+    return *(const BITNET_GLOBAL T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ void gstore(void* p, T v) {
+    *(BITNET_GLOBAL T*)(p) = v;
+}
 
 constexpr int kWave = 64;
 

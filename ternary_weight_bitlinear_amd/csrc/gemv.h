@@ -22,19 +22,27 @@ struct GemvProblem {
     int64_t ldy;
     int32_t* acc_debug;        // optional [M][N]
     int32_t M, N, K, Kp;
-    int32_t tile0;             // grouped: index of this problem's first workgroup
+    int32_t tile0;             // grouped: global index of this problem's first 64-row tile
+    int32_t ntiles;            // grouped: tiles of this problem
+    int32_t steps;             // grouped: 256-element k steps per tile (Kp / 256, rounded up)
     int32_t reserved;
+    int64_t step0;             // grouped: steps of all earlier problems (ntiles * steps each)
 };
 
-// Workgroups (tiles of output rows) a problem with N rows needs.
-int64_t gemv_tiles(int64_t N);
+// LDS bytes the grouped kernel needs for M tokens of the longest row.
+size_t gemv_group_lds(int64_t M, int64_t max_Kp);
+
+// Tiles (64 output rows) and k steps per tile of a grouped problem.
+int64_t gemv_group_tiles(int64_t N);
+int64_t gemv_group_steps(int64_t Kp);
 
 // Fused ActQuant + decode linear for one problem; LDS holds M*Kp bytes.
 hipError_t launch_gemv_fused(const GemvProblem& p, bool x_bf16, bool y_bf16, hipStream_t stream);
 
-// Many independent problems in one launch; table_dev is a device array of
-// `count` descriptors ordered by tile0, total_tiles = sum of gemv_tiles(N).
-hipError_t launch_gemv_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles, size_t lds,
-                               bool fused, bool x_bf16, bool y_bf16, hipStream_t stream);
+// Many independent problems in one launch (ActQuant fused); table_dev is a
+// device array of `count` descriptors with tile0 / ntiles / steps / step0 set.
+hipError_t launch_gemv_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,
+                               int64_t total_steps, size_t lds, bool x_bf16, bool y_bf16,
+                               hipStream_t stream);
 
 }  // namespace bitnet
