@@ -9,12 +9,21 @@
 // Design.
 //  * v_mfma_i32_32x32x32_i8: on gfx950 it runs at about twice the rate of the
 //    16x16x64 form (measured ~4.5 vs ~2.6 int8 POPS with registers only).
-//    Lane l holds row l%32 of A, column l%32 of B and 16 k values of group
-//    l/32; the accumulator's register r holds C[8(r/4) + 4(l/32) + r%4][l%32].
+//    Lane l supplies row l%32 of the first operand, column l%32 of the second
+//    and 16 k values of group l/32; register r of the result holds
+//    D[8(r/4) + 4(l/32) + r%4][l%32].  The codes are the first operand and
+//    the activations the second, so D is the transposed output tile and each
+//    lane ends with four consecutive outputs of one row: the epilogue writes
+//    them as one 8-byte (bf16) or 16-byte (fp32) store.
 //  * Workgroup tile BM x BN, k stage BK = 128, double-buffered in LDS; waves
 //    in a WGM x WGN grid, each owning (BM/WGM) x (BN/WGN) as 32x32 tiles held
-//    in accumulation registers.  Global loads of stage k+1 go to registers
-//    while stage k is computed, then to the other LDS buffer.
+//    in accumulation registers.
+//  * Global loads run PF stages ahead of the MFMAs through PF register sets,
+//    so a load has PF stages of matrix work to land in; a stage is written to
+//    the free LDS buffer one stage before it is used.  The loads are buffer
+//    loads: rows past M or N and stages past the end lie outside the buffer's
+//    range and read as zero, so every load is issued unconditionally and the
+//    compiler can keep exact wait counts.
 //  * Codes stay packed in LDS (a quarter of an int8 tile).  In one stage lane
 //    group g takes the contiguous k range [64g, 64g + 64) of the stage, so its
 //    B operand for the whole stage is one 16-byte LDS read (four packed words,
@@ -26,11 +35,12 @@
 //    (the padded tail has q = 0) to get the exact sum of q*t.
 //  * LDS rows are padded (A: 144 B, B: 48 B) so that the 16-byte reads of 16
 //    consecutive rows fall in distinct bank groups.
-//  * Tiles are ordered XCD-aware: consecutive workgroup ids go round-robin to
-//    the 8 XCDs, so the id is remapped to give each XCD a contiguous band of
-//    tiles that share activation rows in its own L2.
+//  * Tile order: workgroup b runs on XCD b % 8, so ids are remapped to give
+//    each XCD a contiguous range of the tile sequence, and the sequence walks
+//    bands of GM tile rows column by column, so the workgroups that run
+//    together on one XCD share both activation rows and code rows in its L2.
 //  * Kp is a multiple of 128 = BK, so there is no K tail; ragged M and N are
-//    handled by zero-filled loads and guarded stores.
+//    handled by the buffer range and guarded stores.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -41,9 +51,15 @@ constexpr int BK = 128;          // k elements per stage
 constexpr int kApad = 16;        // bytes of padding per LDS activation row
 constexpr int kBpad = 16;        // bytes of padding per LDS code row
 constexpr int kXcds = 8;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // offset past any buffer range used here
+constexpr int kRsrcWord3 = 0x00020000;          // raw 32-bit buffer access on gfx9-family parts
 
 __device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
 template <int BM, int BN>
@@ -51,36 +67,51 @@ constexpr size_t lds_bytes() {
     return 2 * (static_cast<size_t>(BM) * (BK + kApad) + static_cast<size_t>(BN) * (BK / 4 + kBpad));
 }
 
-template <int BM, int BN, int WGM, int WGN, bool kOutBf16>
+struct TileOrder {
+    int tiles_m, tiles_n, group_m;
+};
+
+// Workgroup id -> (tile row, tile column).
+__device__ __forceinline__ void tile_of(const TileOrder& o, int& tm, int& tn) {
+    const int tiles = o.tiles_m * o.tiles_n;
+    const int b = blockIdx.x;
+    // ids with b % 8 == x form XCD x's queue; give it tiles [start_x, start_x + count_x)
+    const int per = tiles / kXcds, rem = tiles % kXcds, x = b % kXcds;
+    const int seq = x * per + min(x, rem) + b / kXcds;
+    const int band = o.group_m * o.tiles_n;
+    const int first_m = (seq / band) * o.group_m;
+    const int rows = min(o.tiles_m - first_m, o.group_m);
+    const int in_band = seq % band;
+    tm = first_m + in_band % rows;
+    tn = in_band / rows;
+}
+
+template <int BM, int BN, int WGM, int WGN, int PF, bool kOutBf16>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ a_scale,
     const int32_t* __restrict__ q_rowsum, int M, int Kp,
     const uint8_t* __restrict__ packed, const float* __restrict__ w_scale, int N,
-    void* __restrict__ y, int64_t ldy, int32_t* __restrict__ acc_debug, int tiles_m, int tiles_n) {
+    void* __restrict__ y, int64_t ldy, int32_t* __restrict__ acc_debug, TileOrder order, int vec_store) {
     constexpr int kThreads = WGM * WGN * 64;
     constexpr int WM = BM / WGM, WN = BN / WGN;      // per-wave tile
     constexpr int TM = WM / 32, TN = WN / 32;        // 32x32 MFMA tiles per wave
     constexpr int A_ROW = BK + kApad;
     constexpr int B_ROW = BK / 4 + kBpad;
-    constexpr int A_LOADS = BM * BK / 16 / kThreads; // 16-byte global loads per thread
+    constexpr int A_LOADS = BM * BK / 16 / kThreads; // 16-byte loads per thread per stage
     constexpr int B_LOADS = BN * (BK / 4) / 16 / kThreads;
-    static_assert(A_LOADS >= 1 && B_LOADS >= 1 && TM >= 1 && TN >= 1, "tile shape");
+    static_assert(A_LOADS >= 1 && B_LOADS >= 1 && TM >= 1 && TN >= 1 && PF >= 1, "tile shape");
     static_assert(BM * BK / 16 % kThreads == 0 && BN * (BK / 4) / 16 % kThreads == 0, "tile shape");
 
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     __shared__ __attribute__((aligned(16))) float as_s[BM];      // a_scale of the tile's rows
     __shared__ __attribute__((aligned(16))) int32_t rs_s[BM];    // q_rowsum of the tile's rows
+    __shared__ __attribute__((aligned(16))) float ws_s[BN];      // w_scale of the tile's columns
     int8_t* a_lds = lds;                                           // [2][BM][A_ROW]
     uint8_t* b_lds = reinterpret_cast<uint8_t*>(lds + 2 * BM * A_ROW);   // [2][BN][B_ROW]
 
-    // XCD-aware tile order: workgroup b runs on XCD b % 8; give XCD x the
-    // contiguous tile range [x * T/8, (x+1) * T/8), walked n-fastest so the
-    // workgroups of one XCD share activation rows.
-    const int tiles = tiles_m * tiles_n;
-    int tile = blockIdx.x;
-    if (tiles % kXcds == 0) tile = (blockIdx.x % kXcds) * (tiles / kXcds) + blockIdx.x / kXcds;
-    const int m0 = (tile / tiles_n) * BM;
-    const int n0 = (tile % tiles_n) * BN;
+    int tm, tn;
+    tile_of(order, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid % 64;
@@ -88,65 +119,64 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(
     const int wm = wave / WGN, wn = wave % WGN;
     const int r32 = lane % 32;     // A row / B column inside a 32x32 tile
     const int g = lane / 32;       // k group: bytes [64g, 64g + 64) of a stage
-    const int64_t brow_bytes = Kp / 4;
-
-    u32x4 a_reg[A_LOADS];
-    u32x4 b_reg[B_LOADS];
-    auto load_stage = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
-            const int f = i * kThreads + tid;
-            const int r = f / (BK / 16), s = f % (BK / 16);
-            const int m = m0 + r;
-            a_reg[i] = u32x4{0u, 0u, 0u, 0u};
-            if (m < M) a_reg[i] = gload<u32x4>(q + static_cast<int64_t>(m) * Kp + k0 + 16 * s);
-        }
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) {
-            const int f = i * kThreads + tid;
-            const int r = f / (BK / 64), s = f % (BK / 64);
-            const int n = n0 + r;
-            b_reg[i] = u32x4{0u, 0u, 0u, 0u};          // code 0 rows contribute nothing
-            if (n < N) b_reg[i] = gload<u32x4>(packed + static_cast<int64_t>(n) * brow_bytes + k0 / 4 + 16 * s);
-        }
-    };
-    auto store_stage = [&](int st) {
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
-            const int f = i * kThreads + tid;
-            const int r = f / (BK / 16), s = f % (BK / 16);
-            *reinterpret_cast<u32x4*>(a_lds + st * BM * A_ROW + r * A_ROW + 16 * s) = a_reg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) {
-            const int f = i * kThreads + tid;
-            const int r = f / (BK / 64), s = f % (BK / 64);
-            *reinterpret_cast<u32x4*>(b_lds + st * BN * B_ROW + r * B_ROW + 16 * s) = b_reg[i];
-        }
-    };
-
-    v16i acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
-
-    for (int i = tid; i < BM; i += kThreads) {
-        const int m = m0 + i;
-        as_s[i] = m < M ? a_scale[m] : 0.0f;
-        rs_s[i] = m < M ? q_rowsum[m] : 0;
-    }
+    const int brow_bytes = Kp / 4;
     const int stages = Kp / BK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
 
-    for (int ks = 0; ks < stages; ++ks) {
-        const int st = ks & 1;
-        if (ks + 1 < stages) load_stage((ks + 1) * BK);
+    // Buffer ranges cover exactly the tile's valid rows.
+    const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(q + static_cast<int64_t>(m0) * Kp), 0, a_rows * Kp, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(packed + static_cast<int64_t>(n0) * brow_bytes), 0, b_rows * brow_bytes, kRsrcWord3);
 
+    // Per-thread offsets of its pieces inside stage 0.
+    uint32_t a_off[A_LOADS], b_off[B_LOADS];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+        const int f = i * kThreads + tid;
+        a_off[i] = static_cast<uint32_t>((f / (BK / 16)) * Kp + 16 * (f % (BK / 16)));
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+        const int f = i * kThreads + tid;
+        b_off[i] = static_cast<uint32_t>((f / (BK / 64)) * brow_bytes + 16 * (f % (BK / 64)));
+    }
+
+    u32x4 a_reg[PF][A_LOADS];
+    u32x4 b_reg[PF][B_LOADS];
+    auto load_stage = [&](u32x4 (&ar)[A_LOADS], u32x4 (&br)[B_LOADS], int ks) {
+        const bool in = ks < stages;
+        const uint32_t ka = in ? static_cast<uint32_t>(ks * BK) : kOutOfRange;
+        const uint32_t kb = in ? static_cast<uint32_t>(ks * (BK / 4)) : kOutOfRange;
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) ar[i] = bload(a_rsrc, a_off[i] + ka);
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i) br[i] = bload(b_rsrc, b_off[i] + kb);
+    };
+    auto store_stage = [&](const u32x4 (&ar)[A_LOADS], const u32x4 (&br)[B_LOADS], int st) {
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) {
+            const int f = i * kThreads + tid;
+            const int r = f / (BK / 16), s = f % (BK / 16);
+            *reinterpret_cast<u32x4*>(a_lds + st * BM * A_ROW + r * A_ROW + 16 * s) = ar[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i) {
+            const int f = i * kThreads + tid;
+            const int r = f / (BK / 64), s = f % (BK / 64);
+            *reinterpret_cast<u32x4*>(b_lds + st * BN * B_ROW + r * B_ROW + 16 * s) = br[i];
+        }
+    };
+
+    v16i acc[TN][TM];              // acc[j][i]: transposed 32x32 output tile (n of j, m of i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
+
+    auto compute_stage = [&](int st) {
         const int8_t* a_base = a_lds + st * BM * A_ROW + (wm * WM + r32) * A_ROW + 64 * g;
         const uint8_t* b_base = b_lds + st * BN * B_ROW + (wn * WN + r32) * B_ROW + 16 * g;
         u32x4 bw[TN];
@@ -163,73 +193,144 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < TN; ++j) acc[j][i] = mfma32(b[j], a[i], acc[j][i]);
         }
+    };
 
-        if (ks + 1 < stages) {
-            store_stage(st ^ 1);
+    for (int i = tid; i < BM; i += kThreads) {
+        const int m = m0 + i;
+        as_s[i] = m < M ? a_scale[m] : 0.0f;
+        rs_s[i] = m < M ? q_rowsum[m] : 0;
+    }
+    for (int i = tid; i < BN; i += kThreads) ws_s[i] = n0 + i < N ? w_scale[n0 + i] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < PF; ++u) load_stage(a_reg[u], b_reg[u], u);
+    store_stage(a_reg[0], b_reg[0], 0);
+    __syncthreads();
+
+    // Stage k's data sits in register set k % PF from stage k - PF on; at the
+    // end of stage k the set holding stage k + 1 goes to LDS buffer (k+1) % 2.
+    // The main loop covers the groups of PF stages that are all followed by
+    // another stage, so its stores and barriers are unconditional; the
+    // scheduling barrier keeps the next loads ahead of the stage's MFMAs.
+    int k = 0;
+    for (; k + PF < stages; k += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int kk = k + u;
+            load_stage(a_reg[u], b_reg[u], kk + PF);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_stage(kk & 1);
+            store_stage(a_reg[(u + 1) % PF], b_reg[(u + 1) % PF], (kk + 1) & 1);
             __syncthreads();
         }
     }
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+        const int kk = k + u;
+        if (kk < stages) {
+            compute_stage(kk & 1);
+            if (kk + 1 < stages) {
+                store_stage(a_reg[(u + 1) % PF], b_reg[(u + 1) % PF], (kk + 1) & 1);
+                __syncthreads();
+            }
+        }
+    }
 
-    // epilogue: register r of lane l holds C[8(r/4) + 4g + r%4][r32] of each
-    // 32x32 tile; the per-row scale and sum come from LDS, four rows per read
+    // epilogue: register 4rb + rr of lane l holds output row m = i*32 + l%32,
+    // column n = j*32 + 8rb + 4(l/32) + rr of the wave's tile
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 32 + r32;
-        if (n >= N) continue;
-        const float ws = w_scale[n];
+    for (int i = 0; i < TM; ++i) {
+        const int ml = wm * WM + i * 32 + r32;
+        const int m = m0 + ml;
+        const float as = as_s[ml];
+        const int32_t rs = rs_s[ml];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+        for (int j = 0; j < TN; ++j) {
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                const int row = wm * WM + i * 32 + 8 * rb + 4 * g;          // local row of r = 4rb
-                const f32x4 as4 = *reinterpret_cast<const f32x4*>(&as_s[row]);
-                const v4i rs4 = *reinterpret_cast<const v4i*>(&rs_s[row]);
+                const int nl = wn * WN + j * 32 + 8 * rb + 4 * g;
+                const int n = n0 + nl;
+                const f32x4 ws4 = *reinterpret_cast<const f32x4*>(&ws_s[nl]);
+                int32_t e[4];
+                f32x4 v;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int m = m0 + row + rr;
-                    if (m >= M) continue;
-                    const int32_t exact = acc[i][j][4 * rb + rr] - rs4[rr];
-                    const float v = static_cast<float>(exact) * (as4[rr] * ws);
-                    if constexpr (kOutBf16)
-                        static_cast<__bf16*>(y)[m * ldy + n] = static_cast<__bf16>(v);   // v_cvt_pk_bf16_f32: RNE
-                    else
-                        static_cast<float*>(y)[m * ldy + n] = v;
-                    if (acc_debug) acc_debug[static_cast<int64_t>(m) * N + n] = exact;
+                    e[rr] = acc[j][i][4 * rb + rr] - rs;
+                    v[rr] = static_cast<float>(e[rr]) * (as * ws4[rr]);
+                }
+                if (m >= M) continue;
+                const int64_t off = static_cast<int64_t>(m) * ldy + n;
+                if (vec_store && n + 3 < N) {
+                    if constexpr (kOutBf16) {
+                        bf16x4 h;
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) h[rr] = static_cast<__bf16>(v[rr]);   // v_cvt_pk_bf16_f32: RNE
+                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(y) + off) = h;
+                    } else {
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + off) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        if (n + rr >= N) break;
+                        if constexpr (kOutBf16)
+                            static_cast<__bf16*>(y)[off + rr] = static_cast<__bf16>(v[rr]);
+                        else
+                            static_cast<float*>(y)[off + rr] = v[rr];
+                    }
+                }
+                if (acc_debug) {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        if (n + rr < N) acc_debug[static_cast<int64_t>(m) * N + n + rr] = e[rr];
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int PF>
 hipError_t launch_tile(const int8_t* q, const float* a_scale, const int32_t* q_rowsum, int64_t M, int64_t Kp,
                        const uint8_t* packed, const float* w_scale, int64_t N, void* y, bool y_bf16,
-                       int64_t ldy, int32_t* acc_debug, hipStream_t stream) {
-    const int tiles_m = static_cast<int>((M + BM - 1) / BM);
-    const int tiles_n = static_cast<int>((N + BN - 1) / BN);
+                       int64_t ldy, int32_t* acc_debug, int group_m, hipStream_t stream) {
+    TileOrder order;
+    order.tiles_m = static_cast<int>((M + BM - 1) / BM);
+    order.tiles_n = static_cast<int>((N + BN - 1) / BN);
+    order.group_m = group_m > 0 ? group_m : order.tiles_m;
     constexpr size_t lds = lds_bytes<BM, BN>();
-    const dim3 grid(static_cast<unsigned>(tiles_m) * tiles_n), block(WGM * WGN * 64);
-    auto kern = y_bf16 ? gemm_kernel<BM, BN, WGM, WGN, true> : gemm_kernel<BM, BN, WGM, WGN, false>;
+    const dim3 grid(static_cast<unsigned>(order.tiles_m) * order.tiles_n), block(WGM * WGN * 64);
+    auto kern = y_bf16 ? gemm_kernel<BM, BN, WGM, WGN, PF, true> : gemm_kernel<BM, BN, WGM, WGN, PF, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
+    // vector stores need every row start aligned to 4 elements
+    const int vec_store = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
     kern<<<grid, block, lds, stream>>>(q, a_scale, q_rowsum, (int)M, (int)Kp, packed, w_scale, (int)N, y, ldy,
-                                       acc_debug, tiles_m, tiles_n);
+                                       acc_debug, order, vec_store);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Build-time knobs: register prefetch distance and tile rows per band.
+#ifndef BITNET_GEMM_PF
+#define BITNET_GEMM_PF 2
+#endif
+#ifndef BITNET_GEMM_GM
+#define BITNET_GEMM_GM 8
+#endif
+
 hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_rowsum,
                        int64_t M, int64_t Kp, const uint8_t* packed, const float* w_scale,
                        int64_t N, void* y, bool y_bf16, int64_t ldy, int32_t* acc_debug,
                        hipStream_t stream) {
-    // 128x128 tiles, 4 waves of 64x64: measured faster than 256x256 on every
-    // prefill shape here (more workgroups per CU hide the load latency).
-    return launch_tile<128, 128, 2, 2>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16, ldy, acc_debug,
-                                       stream);
+    // 128x128 tiles, 4 waves of 64x64 (3 workgroups per CU).  Measured against
+    // 128x256, 256x128 and 256x256 tiles, whose larger accumulator sets drop
+    // the occupancy to one workgroup per CU and run 30-35% slower.
+    return launch_tile<128, 128, 2, 2, BITNET_GEMM_PF>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16,
+                                                       ldy, acc_debug, BITNET_GEMM_GM, stream);
 }
 
 }  // namespace bitnet
