@@ -86,8 +86,8 @@ __device__ __forceinline__ void tile_of(const TileOrder& o, int& tm, int& tn) {
     tn = in_band / rows;
 }
 
-template <int BM, int BN, int WGM, int WGN, int PF, bool kOutBf16>
-__global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(
+template <int BM, int BN, int WGM, int WGN, int PF, int kWaves, bool kOutBf16>
+__global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(kWaves))) void gemm_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ a_scale,
     const int32_t* __restrict__ q_rowsum, int M, int Kp,
     const uint8_t* __restrict__ packed, const float* __restrict__ w_scale, int N,
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_kernel(
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int PF>
+template <int BM, int BN, int WGM, int WGN, int PF, int kWaves>
 hipError_t launch_tile(const int8_t* q, const float* a_scale, const int32_t* q_rowsum, int64_t M, int64_t Kp,
                        const uint8_t* packed, const float* w_scale, int64_t N, void* y, bool y_bf16,
                        int64_t ldy, int32_t* acc_debug, int group_m, hipStream_t stream) {
@@ -301,7 +301,8 @@ hipError_t launch_tile(const int8_t* q, const float* a_scale, const int32_t* q_r
     order.group_m = group_m > 0 ? group_m : order.tiles_m;
     constexpr size_t lds = lds_bytes<BM, BN>();
     const dim3 grid(static_cast<unsigned>(order.tiles_m) * order.tiles_n), block(WGM * WGN * 64);
-    auto kern = y_bf16 ? gemm_kernel<BM, BN, WGM, WGN, PF, true> : gemm_kernel<BM, BN, WGM, WGN, PF, false>;
+    auto kern = y_bf16 ? gemm_kernel<BM, BN, WGM, WGN, PF, kWaves, true>
+                       : gemm_kernel<BM, BN, WGM, WGN, PF, kWaves, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
@@ -322,15 +323,58 @@ hipError_t launch_tile(const int8_t* q, const float* a_scale, const int32_t* q_r
 #define BITNET_GEMM_GM 8
 #endif
 
+namespace {
+
+// Workgroups of one kernel that are resident on the current device at once
+// (CUs x blocks per CU), cached per device; 0 if the query fails.
+template <typename Kern>
+int resident_slots(Kern kern, int threads, size_t lds, int (&cache)[64]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), threads, lds) !=
+            hipSuccess)
+            return 0;
+        cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
+    }
+    return cache[dev];
+}
+
+// Share of the launched rounds' resident slots that hold a tile.
+double round_fill(int64_t tiles, int slots) {
+    if (slots <= 0) return 1.0;
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    return static_cast<double>(tiles) / static_cast<double>(rounds * slots);
+}
+
+int g_slots_small[64], g_slots_wide[64];
+
+}  // namespace
+
 hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_rowsum,
                        int64_t M, int64_t Kp, const uint8_t* packed, const float* w_scale,
                        int64_t N, void* y, bool y_bf16, int64_t ldy, int32_t* acc_debug,
                        hipStream_t stream) {
-    // 128x128 tiles, 4 waves of 64x64 (3 workgroups per CU).  Measured against
-    // 128x256, 256x128 and 256x256 tiles, whose larger accumulator sets drop
-    // the occupancy to one workgroup per CU and run 30-35% slower.
-    return launch_tile<128, 128, 2, 2, BITNET_GEMM_PF>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16,
-                                                       ldy, acc_debug, BITNET_GEMM_GM, stream);
+    // Two tiles: 128x128 with 2x2 waves of 64x64 (3 workgroups per CU), and
+    // 128x256 with 1x4 waves of 128x64 (2 per CU), which halves the code
+    // expansion and the global bytes per MFMA and runs each tile ~7% faster.
+    // The grid runs in rounds of resident workgroups, so the choice weighs
+    // that gain against the share of the last round left empty (e.g. N=3840:
+    // 960 small tiles fill 1.25 rounds of 768, 480 wide tiles 0.94 of 512).
+    const int slots_small = resident_slots(gemm_kernel<128, 128, 2, 2, BITNET_GEMM_PF, 3, true>, 256,
+                                           lds_bytes<128, 128>(), g_slots_small);
+    const int slots_wide = resident_slots(gemm_kernel<128, 256, 1, 4, BITNET_GEMM_PF, 2, true>, 256,
+                                          lds_bytes<128, 256>(), g_slots_wide);
+    const int64_t tiles_m = (M + 127) / 128;
+    const double small = round_fill(tiles_m * ((N + 127) / 128), slots_small);
+    const double wide = 1.07 * round_fill(tiles_m * ((N + 255) / 256), slots_wide);
+    if (wide > small)
+        return launch_tile<128, 256, 1, 4, BITNET_GEMM_PF, 2>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y,
+                                                              y_bf16, ldy, acc_debug, BITNET_GEMM_GM, stream);
+    return launch_tile<128, 128, 2, 2, BITNET_GEMM_PF, 3>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16,
+                                                          ldy, acc_debug, BITNET_GEMM_GM, stream);
 }
 
 }  // namespace bitnet
