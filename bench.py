@@ -45,14 +45,22 @@ def kernel_source_hash(*names: str) -> str:
 
 
 def traffic_from_profile(name: str, src_hash: str):
-    """HBM bytes per launch from a committed counter summary, if it matches the current kernel source."""
-    f = PROFILES / f"{name}_traffic.json"
+    """HBM bytes per launch from a committed counter summary (profiles/<name>_traffic.md,
+    lines "- key: value"), or None when it was taken on a different kernel source."""
+    f = PROFILES / f"{name}_traffic.md"
     if not f.exists():
         return None
-    d = json.loads(f.read_text())
-    if d.get("kernel_source_hash") != src_hash:
+    fields = {}
+    for ln in f.read_text().splitlines():
+        if ln.startswith("- ") and ": " in ln:
+            k, v = ln[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_hash") != src_hash:
         return None
-    return d.get("hbm_bytes_per_launch")
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 # ------------------------------------------------------------------- decode
@@ -231,6 +239,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-call", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first fill and copy a buffer of this many MiB three times: plain kernels of "
+                         "known HBM traffic, for scaling FETCH_SIZE/WRITE_SIZE counters in a profiled run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this BitLinear path runs on a single MI355X "
@@ -245,6 +256,16 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     tw._lib.lib()   # fail loudly now if the HIP library is not built
+
+    if args.calib_copy_mib > 0:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            src.fill_(1)          # writes n bytes
+            dst.copy_(src)        # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     line = dict(metric=METRIC, value=None, unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
                 ms_per_step=None, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="int8",

@@ -385,6 +385,12 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
         if (tiles > kMaxMN) return fail(BITNET_ERR_INVALID_ARG, "%s: too many tiles in the group", fn);
         if (Kp > max_kp) max_kp = Kp;
     }
+    int stream_grid = 0;
+    size_t lds = bitnet::gemv_group_lds(M, max_kp);
+    if (!bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &stream_grid, &lds)) {
+        stream_grid = 0;
+        lds = bitnet::gemv_group_lds(M, max_kp);
+    }
     hipError_t e = hipMemcpyAsync(table_dev, table.data(), table.size() * sizeof(bitnet::GemvProblem),
                                   hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return hip_fail(e, "bitnet_group_plan: table upload");
@@ -394,8 +400,9 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
     plan->opaque[2] = count;
     plan->opaque[3] = M;
     plan->opaque[4] = tiles;
-    plan->opaque[5] = static_cast<int64_t>(bitnet::gemv_group_lds(M, max_kp));
-    plan->opaque[6] = static_cast<int64_t>(x_dtype) | (static_cast<int64_t>(y_dtype) << 8);
+    plan->opaque[5] = static_cast<int64_t>(lds);
+    plan->opaque[6] = static_cast<int64_t>(x_dtype) | (static_cast<int64_t>(y_dtype) << 8) |
+                      (static_cast<int64_t>(stream_grid) << 32);
     plan->opaque[7] = steps;
     return ok();
 }
@@ -407,6 +414,7 @@ bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_
     const auto* table = reinterpret_cast<const bitnet::GemvProblem*>(static_cast<uintptr_t>(plan->opaque[1]));
     hipError_t e = bitnet::launch_gemv_grouped(table, static_cast<int>(plan->opaque[2]), plan->opaque[4],
                                                plan->opaque[7], static_cast<size_t>(plan->opaque[5]),
+                                               static_cast<int>(plan->opaque[6] >> 32),
                                                (plan->opaque[6] & 0xFF) == BITNET_BF16,
                                                ((plan->opaque[6] >> 8) & 0xFF) == BITNET_BF16, stream);
     if (e != hipSuccess) return hip_fail(e, fn);

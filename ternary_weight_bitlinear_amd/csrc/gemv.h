@@ -39,10 +39,19 @@ int64_t gemv_group_steps(int64_t Kp);
 // Fused ActQuant + decode linear for one problem; LDS holds M*Kp bytes.
 hipError_t launch_gemv_fused(const GemvProblem& p, bool x_bf16, bool y_bf16, hipStream_t stream);
 
+// Whether the streaming kernel (per-wave LDS ring of DMA weight loads) can
+// run this table of problems (host copy, tile0 / ntiles / steps / step0 set):
+// every workgroup's problems must fit its LDS share.  On success gives the
+// grid and the dynamic LDS bytes to launch with.
+bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_tiles, int64_t total_steps,
+                      int* grid, size_t* lds);
+
 // Many independent problems in one launch (ActQuant fused); table_dev is a
 // device array of `count` descriptors with tile0 / ntiles / steps / step0 set.
+// stream_grid > 0 runs the streaming kernel with that grid and `lds` from
+// gemv_stream_plan, otherwise the persistent kernel with `lds` for the longest row.
 hipError_t launch_gemv_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,
-                               int64_t total_steps, size_t lds, bool x_bf16, bool y_bf16,
+                               int64_t total_steps, size_t lds, int stream_grid, bool x_bf16, bool y_bf16,
                                hipStream_t stream);
 
 }  // namespace bitnet

@@ -37,6 +37,8 @@
 //
 // Every global access goes through gload / gstore (global address space), so
 // the ring's loads are counted by vmcnt alone and are waited for one at a time.
+#include <algorithm>
+
 #include "device_common.h"
 #include "gemv.h"
 #include "kernels.h"
@@ -418,14 +420,9 @@ __global__ __launch_bounds__(kThreads) void gemv_persistent_kernel(GemvProblem s
     int seg_begin = t_begin;
     while (true) {
         const int seg_end = min(t_end, P.tile0 + P.ntiles);
-        if constexpr (kFused)
-            quantise_tokens<kXBf16, 2, true>(P, q_lds, as_lds, rs_lds, red_f, red_i,
-                                             P.q_out != nullptr && seg_begin == P.tile0);
-        else
-            stage_tokens(P, q_lds, as_lds, rs_lds);
-        const int8_t* abase = q_lds + (m_ok ? col : 0) * padded_q_row(P.Kp) + 64 * grp;
         const int chunks = P.Kp / 64;
         const int row_bytes = P.Kp / 4;
+        const int8_t* abase = nullptr;                  // token rows in LDS, set once staged
 
         // producer: next (tile, batch) of this segment; past its end it keeps
         // re-reading the last tile (exactly U*TN loads per batch, never used)
@@ -525,10 +522,19 @@ __global__ __launch_bounds__(kThreads) void gemv_persistent_kernel(GemvProblem s
             return false;
         };
 
+        // The segment's first weight loads go out before its tokens are
+        // staged, so their latency overlaps the ActQuant prologue (whose own
+        // loads then wait behind them in the same queue).
         u32x4 bufA[U][TN], bufB[U][TN];
         load_batch(bufA);
         load_batch(bufB);
         prefetch_epilogue();
+        if constexpr (kFused)
+            quantise_tokens<kXBf16, 2, true>(P, q_lds, as_lds, rs_lds, red_f, red_i,
+                                             P.q_out != nullptr && seg_begin == P.tile0);
+        else
+            stage_tokens(P, q_lds, as_lds, rs_lds);
+        abase = q_lds + (m_ok ? col : 0) * padded_q_row(P.Kp) + 64 * grp;
         while (true) {
             consume(bufA);
             load_batch(bufA);
@@ -540,6 +546,300 @@ __global__ __launch_bounds__(kThreads) void gemv_persistent_kernel(GemvProblem s
         if (seg_end == t_end) break;
         seg_begin = seg_end;
         P = ps.get(++pc);
+    }
+}
+
+// ---------------------------------------------------------------- streaming kernel
+//
+// Same work split, tiles and MFMA arithmetic as the persistent kernel, with a
+// different memory pipeline.  Each wave streams its 16 rows x 64 bytes per k
+// step through a private ring of kDepth LDS slots filled by buffer_load ... lds
+// (the memory unit writes LDS directly, no registers involved), issued up to
+// kDepth - 1 steps ahead of the steps being computed and running straight
+// through tile and problem boundaries, so about kDepth KB per wave stay in
+// flight at all times.  Lane l's 16 bytes land at slot offset 16*l and are read
+// back by lane l alone, so waves never synchronise in the loop; a pass over
+// two steps waits for their loads with vmcnt(kDepth - 2).  Every problem the workgroup touches
+// is quantised into LDS once, before the loop (its token loads queue behind
+// the first ring loads), so a problem boundary only moves the A pointer.
+// Rows past N and k past Kp lie outside the buffer range and read as zero.
+#ifndef BITNET_STREAM_DEPTH
+#define BITNET_STREAM_DEPTH 8
+#endif
+#ifndef BITNET_STREAM_PER_CU
+#define BITNET_STREAM_PER_CU 2
+#endif
+constexpr int kDepth = BITNET_STREAM_DEPTH;
+constexpr int kStreamMaxProblems = 16;          // problems one workgroup may touch
+constexpr uint32_t kStreamOutOfRange = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;          // raw 32-bit buffer access on gfx9-family parts
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__shared__ __attribute__((aligned(1024))) int8_t g_stream_ring[kDepth * kThreads * 16];
+
+// Token rows of the workgroup's problems, then the w_scale of its rows: a
+// static array sized to the workgroup's LDS share.
+constexpr int kStreamStaticOther = 2 * 4 * kStreamMaxProblems * 16 + 2 * 4 * kWaves;
+constexpr int kStreamQBytes = (160 * 1024 / BITNET_STREAM_PER_CU - kDepth * kThreads * 16 - kStreamStaticOther - 256) / 256 * 256;
+static_assert(kStreamQBytes >= 8192, "streaming kernel: too little LDS left for token rows");
+static_assert(kThreads * 16 == 4096 && kDepth % 2 == 0, "ring slot stride and pairs of steps");
+static_assert(kBatch % 2 == 0, "token rows must be zero padded to whole pairs of k steps");
+__shared__ __attribute__((aligned(16))) int8_t g_stream_q[kStreamQBytes];
+
+template <int kVm>
+__device__ __forceinline__ void wait_vm() {     // s_waitcnt vmcnt(kVm), other counters untouched
+    static_assert(kVm >= 0 && kVm < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS reads of the streaming loop, each with its completion wait in the same
+// asm block.  The compiler does not see these reads, so it adds no wait for
+// the ring's DMA loads in flight (it would otherwise order every LDS read
+// after all of them); the loop's own vmcnt waits order the ring.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+__device__ __forceinline__ u32x4 lds_read16(const void* p) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p)) : "memory");
+    return v;
+}
+__device__ __forceinline__ float lds_read_f32(const void* p) {
+    float v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p)) : "memory");
+    return v;
+}
+__device__ __forceinline__ void lds_write_i32(void* p, int32_t v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+// Two consecutive ring slots of the lane (slot stride kThreads * 16 bytes).
+__device__ __forceinline__ void lds_read_ring2(const void* p, u32x4& w0, u32x4& w1) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:4096\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(w0), "=&v"(w1)
+                 : "v"(lds_addr(p))
+                 : "memory");
+}
+// A operands of two consecutive k steps (64 + 64 bytes, 256 bytes apart).
+__device__ __forceinline__ void lds_read_a2(const void* p, v4i (&a)[2][4]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\tds_read_b128 %2, %8 offset:32\n\t"
+        "ds_read_b128 %3, %8 offset:48\n\tds_read_b128 %4, %8 offset:256\n\tds_read_b128 %5, %8 offset:272\n\t"
+        "ds_read_b128 %6, %8 offset:288\n\tds_read_b128 %7, %8 offset:304\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]), "=&v"(a[1][0]), "=&v"(a[1][1]),
+          "=&v"(a[1][2]), "=&v"(a[1][3])
+        : "v"(lds_addr(p))
+        : "memory");
+}
+__device__ __forceinline__ void lds_read64(const void* p, v4i (&a)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\tds_read_b128 %2, %4 offset:32\n\t"
+        "ds_read_b128 %3, %4 offset:48\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(lds_addr(p))
+        : "memory");
+}
+
+// k steps of a tile, rounded up to whole pairs (the loop takes two per pass;
+// the token rows are zero padded that far, see padded_q_row).
+__device__ __forceinline__ int stream_steps(int Kp) { return ((Kp / 64 + 3) / 4 + 1) / 2 * 2; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t packed_rsrc(const GemvProblem& p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.packed), 0, p.N * (p.Kp / 4), kRsrcWord3);
+}
+
+template <bool kFused, bool kGrouped, bool kXBf16, bool kOutBf16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITNET_STREAM_PER_CU)))
+void gemv_stream_kernel(GemvProblem single,
+                                                               const GemvProblem* __restrict__ table,
+                                                               int count, int total_tiles, int64_t total_steps) {
+    int8_t* const q_lds = g_stream_q;                   // the workgroup's problems' token rows
+    __shared__ float red_f[kWaves];
+    __shared__ int red_i[kWaves];
+    __shared__ __attribute__((aligned(16))) float as_lds[kStreamMaxProblems * 16];
+    __shared__ __attribute__((aligned(16))) int rs_lds[kStreamMaxProblems * 16];
+
+    const Problems<kGrouped> ps{table, single, count};
+    const int64_t s_lo = total_steps * blockIdx.x / gridDim.x;
+    const int64_t s_hi = total_steps * (blockIdx.x + 1) / gridDim.x;
+    const int t_begin = first_tile_from_step(ps, s_lo, total_tiles);
+    const int t_end = first_tile_from_step(ps, s_hi, total_tiles);
+    if (t_begin >= t_end) return;                       // workgroup-uniform
+    const int p_first = find_problem(ps, t_begin);
+    const int p_last = find_problem(ps, t_end - 1);     // the host keeps the span within kStreamMaxProblems
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int col = lane % 16;
+    const int grp = lane / 16;
+    int8_t* const ring = g_stream_ring + wave * 1024;   // slot j of this wave: ring + j * kThreads * 16
+
+    // producer: the (tile, step) sequence of the workgroup, kDepth - 1 ahead
+    int pp = p_first;
+    GemvProblem PP = ps.get(pp);
+    __amdgpu_buffer_rsrc_t rsrc = packed_rsrc(PP);
+    int tp = t_begin, sp = 0, steps_p = stream_steps(PP.Kp), chunks_p = PP.Kp / 64, slot_p = 0;
+    uint32_t rowoff = static_cast<uint32_t>(((tp - PP.tile0) * 64 + wave * 16 + col) * (PP.Kp / 4) + 16 * grp);
+    auto produce = [&]() {
+        // chunks past the row (padding steps) read nothing
+        const uint32_t off = tp < t_end && 4 * sp + grp < chunks_p ? rowoff + 64u * static_cast<uint32_t>(sp)
+                                                                   : kStreamOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(ring + slot_p * kThreads * 16), 16, off, 0, 0, 0);
+        slot_p = slot_p + 1 == kDepth ? 0 : slot_p + 1;
+        if (tp < t_end && ++sp == steps_p) {
+            sp = 0;
+            ++tp;
+            rowoff += static_cast<uint32_t>(64 * (PP.Kp / 4));
+            if (tp < t_end && tp == PP.tile0 + PP.ntiles) {
+                PP = ps.get(++pp);
+                rsrc = packed_rsrc(PP);
+                steps_p = stream_steps(PP.Kp);
+                chunks_p = PP.Kp / 64;
+                rowoff = static_cast<uint32_t>((wave * 16 + col) * (PP.Kp / 4) + 16 * grp);
+            }
+        }
+    };
+    // The ring holds kDepth steps: before the pass over steps (k, k+1) the
+    // producer has issued up to step k + kDepth - 3, and the pass issues
+    // k + kDepth - 2 and k + kDepth - 1 into the slots of k - 2 and k - 1,
+    // which the previous pass has read.
+#pragma unroll
+    for (int i = 0; i < kDepth - 2; ++i) produce();
+
+    // Stage, into LDS, the w_scale of every row of the workgroup's tiles (one
+    // 64-float DMA per tile, after the token rows) and the tokens of every
+    // problem it touches.  The DMAs go out first; the token loads queue behind
+    // them and behind the ring's first loads, so one memory latency covers all.
+    {
+        int q_bytes = 0;
+        for (int pi = p_first; pi <= p_last; ++pi) {
+            const GemvProblem Pi = ps.get(pi);
+            q_bytes += Pi.M * padded_q_row(Pi.Kp);
+        }
+        int8_t* ws_lds = q_lds + q_bytes;
+        for (int pi = p_first; pi <= p_last; ++pi) {
+            const GemvProblem Pi = ps.get(pi);
+            const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(Pi.w_scale), 0, Pi.N * static_cast<int>(sizeof(float)), kRsrcWord3);
+            const int t0 = max(t_begin, Pi.tile0), t1 = min(t_end, Pi.tile0 + Pi.ntiles);
+            for (int t = t0 + wave; t < t1; t += kWaves)   // rows past N read as zero
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ws_rsrc, (lds_ptr_t)(ws_lds + (t - t_begin) * 64 * sizeof(float)), 4,
+                    static_cast<uint32_t>(((t - Pi.tile0) * 64 + lane) * sizeof(float)), 0, 0, 0);
+        }
+        int off = 0;
+        for (int pi = p_first; pi <= p_last; ++pi) {
+            const GemvProblem Pi = ps.get(pi);
+            const int j = pi - p_first;
+            if constexpr (kFused)
+                quantise_tokens<kXBf16, 2, true>(Pi, q_lds + off, as_lds + 16 * j, rs_lds + 16 * j, red_f, red_i,
+                                                 Pi.q_out != nullptr && t_begin <= Pi.tile0);
+            else
+                stage_tokens(Pi, q_lds + off, as_lds + 16 * j, rs_lds + 16 * j);
+            off += Pi.M * padded_q_row(Pi.Kp);
+        }
+        // Every wave's DMAs so far (ring and w_scale) have landed once its own
+        // vmcnt drains (long done where the wave had token loads, since loads
+        // complete in order); then the barrier makes them visible to all waves.
+        wait_vm<0>();
+        __syncthreads();
+    }
+
+    // consumer
+    int q_total = 0;
+    for (int pi = p_first; pi <= p_last; ++pi) {
+        const GemvProblem Pi = ps.get(pi);
+        q_total += Pi.M * padded_q_row(Pi.Kp);
+    }
+    const int wg_rows = (t_end - t_begin) * 64;
+    const float* ws_lds = reinterpret_cast<const float*>(q_lds + q_total);
+    int32_t* out_lds = reinterpret_cast<int32_t*>(q_lds + q_total) + wg_rows;   // [M][wg_rows] exact sums
+    int pc = p_first, pj = 0, tc = t_begin, sc = 0, slot_c = 0;
+    GemvProblem P = ps.get(pc);
+    int steps_c = stream_steps(P.Kp);
+    int qoff = 0;
+    const bool m_ok = col < P.M;                        // M is shared by the group
+    const int8_t* abase = q_lds + (m_ok ? col : 0) * padded_q_row(P.Kp) + 64 * grp;
+    // q_rowsum of tokens 4*grp .. 4*grp+3 of the current problem
+    u32x4 rs4 = lds_read16(rs_lds + 4 * grp);
+    v4i acc[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[f] = v4i{0, 0, 0, 0};
+    v4i a[2][4];                                        // zero where the lane has no token
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) a[i][f] = v4i{0, 0, 0, 0};
+
+    // two k steps per pass
+    while (true) {
+        produce();
+        produce();
+        wait_vm<kDepth - 2>();                          // both steps' ring loads have landed
+        u32x4 w[2];
+        lds_read_ring2(ring + slot_c * kThreads * 16 + 16 * lane, w[0], w[1]);
+        slot_c = slot_c + 2 == kDepth ? 0 : slot_c + 2;
+        if (m_ok) lds_read_a2(abase + 256 * sc, a);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 v = w[i];
+            const v4i b0 = {int(v.x & 0x03030303u), int(v.y & 0x03030303u), int(v.z & 0x03030303u),
+                            int(v.w & 0x03030303u)};
+            const v4i b1 = {int(v.x & 0x0C0C0C0Cu), int(v.y & 0x0C0C0C0Cu), int(v.z & 0x0C0C0C0Cu),
+                            int(v.w & 0x0C0C0C0Cu)};
+            const v4i b2 = {int(v.x & 0x30303030u), int(v.y & 0x30303030u), int(v.z & 0x30303030u),
+                            int(v.w & 0x30303030u)};
+            const v4i b3 = {int((v.x >> 1) & 0x60606060u), int((v.y >> 1) & 0x60606060u),
+                            int((v.z >> 1) & 0x60606060u), int((v.w >> 1) & 0x60606060u)};
+            acc[0] = mfma16(a[i][0], b0, acc[0]);
+            acc[1] = mfma16(a[i][1], b1, acc[1]);
+            acc[2] = mfma16(a[i][2], b2, acc[2]);
+            acc[3] = mfma16(a[i][3], b3, acc[3]);
+        }
+        sc += 2;
+        if (sc < steps_c) continue;
+        // tile epilogue: lane holds token m = 4*grp + r of row n; the exact sum
+        // goes to LDS (a global store here would sit in the ring's in-order
+        // queue); the scaled outputs are written after the loop
+        sc = 0;
+        {
+            const int row = (tc - t_begin) * 64 + wave * 16 + col;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * grp + r;
+                if (m < P.M) {
+                    const int32_t sum_qu = acc[0][r] + (acc[1][r] >> 2) + (acc[2][r] >> 4) + (acc[3][r] >> 5);
+                    lds_write_i32(out_lds + m * wg_rows + row, sum_qu - static_cast<int32_t>(rs4[r]));
+                }
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[f] = v4i{0, 0, 0, 0};
+        if (++tc == t_end) break;
+        if (tc == P.tile0 + P.ntiles) {
+            qoff += P.M * padded_q_row(P.Kp);
+            P = ps.get(++pc);
+            ++pj;
+            steps_c = stream_steps(P.Kp);
+            abase = q_lds + qoff + (m_ok ? col : 0) * padded_q_row(P.Kp) + 64 * grp;
+            rs4 = lds_read16(rs_lds + 16 * pj + 4 * grp);
+        }
+    }
+    wait_vm<0>();                                       // ring loads past the end land before the LDS is reused
+    __syncthreads();
+
+    // outputs of the workgroup's rows, problem by problem, consecutive threads
+    // on consecutive rows
+    for (int pi = p_first, j = 0; pi <= p_last; ++pi, ++j) {
+        const GemvProblem Pi = ps.get(pi);
+        const int t0 = max(t_begin, Pi.tile0), t1 = min(t_end, Pi.tile0 + Pi.ntiles);
+        const int rows = (t1 - t0) * 64;
+        for (int i = threadIdx.x; i < Pi.M * rows; i += kThreads) {
+            const int m = i / rows, rr = i % rows;
+            const int n = (t0 - Pi.tile0) * 64 + rr;
+            if (n >= Pi.N) continue;
+            const int lrow = (t0 - t_begin) * 64 + rr;
+            store_output<kOutBf16>(Pi, m, n, out_lds[m * wg_rows + lrow], as_lds[16 * j + m], ws_lds[lrow]);
+        }
     }
 }
 
@@ -594,6 +894,65 @@ hipError_t launch_persistent(const GemvProblem& single, const GemvProblem* table
                                                                stream);
 }
 
+// Workgroups of the streaming kernel resident at once on the current device.
+int stream_grid() {
+    static int cached[64] = {0};
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = cus * BITNET_STREAM_PER_CU;
+    }
+    return cached[dev];
+}
+
+// Host copy of the kernel's first_tile_from_step.
+int64_t host_first_tile(const GemvProblem* t, int count, int64_t s, int64_t total_tiles) {
+    int lo = 0, hi = count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (t[mid].step0 <= s) lo = mid;
+        else hi = mid - 1;
+    }
+    const int64_t k = (s - t[lo].step0 + t[lo].steps - 1) / t[lo].steps;
+    if (k >= t[lo].ntiles) return lo + 1 < count ? t[lo + 1].tile0 : total_tiles;
+    return t[lo].tile0 + k;
+}
+
+int host_find_problem(const GemvProblem* t, int count, int64_t tile) {
+    int lo = 0, hi = count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (t[mid].tile0 <= tile) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <bool kFused, bool kGrouped, bool XB, bool YB>
+hipError_t launch_stream_t(const GemvProblem& single, const GemvProblem* table, int count, int64_t total_tiles,
+                           int64_t total_steps, int grid, size_t lds, hipStream_t stream) {
+    auto kern = gemv_stream_kernel<kFused, kGrouped, XB, YB>;
+    kern<<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream>>>(single, table, count,
+                                                                           static_cast<int>(total_tiles), total_steps);
+    return hipGetLastError();
+}
+
+template <bool kFused, bool kGrouped>
+hipError_t launch_stream(const GemvProblem& single, const GemvProblem* table, int count, int64_t total_tiles,
+                         int64_t total_steps, int grid, size_t lds, bool x_bf16, bool y_bf16, hipStream_t stream) {
+    if (x_bf16) {
+        if (y_bf16) return launch_stream_t<kFused, kGrouped, true, true>(single, table, count, total_tiles,
+                                                                        total_steps, grid, lds, stream);
+        return launch_stream_t<kFused, kGrouped, true, false>(single, table, count, total_tiles, total_steps, grid,
+                                                              lds, stream);
+    }
+    if (y_bf16) return launch_stream_t<kFused, kGrouped, false, true>(single, table, count, total_tiles,
+                                                                     total_steps, grid, lds, stream);
+    return launch_stream_t<kFused, kGrouped, false, false>(single, table, count, total_tiles, total_steps, grid,
+                                                           lds, stream);
+}
+
 // A single problem laid out as a one-entry group.
 GemvProblem as_group_of_one(GemvProblem p, int64_t& tiles, int64_t& steps) {
     p.tile0 = 0;
@@ -615,6 +974,35 @@ int64_t gemv_group_steps(int64_t Kp) {          // batches of kBatch k steps per
     return (steps + kBatch - 1) / kBatch;
 }
 
+bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_tiles, int64_t total_steps,
+                      int* grid_out, size_t* lds_out) {
+    const int grid = static_cast<int>(std::min<int64_t>(stream_grid(), total_tiles));
+    if (grid <= 0 || count <= 0) return false;
+    // buffer offsets are 32-bit: every problem's padded rows must stay below 2 GiB
+    for (int i = 0; i < count; ++i)
+        if (static_cast<int64_t>(host_table[i].ntiles) * 64 * (host_table[i].Kp / 4) >= (int64_t(1) << 31))
+            return false;
+    // the token rows of each workgroup's problems must fit the static array
+    size_t need = 0;
+    for (int b = 0; b < grid; ++b) {
+        const int64_t lo = total_steps * b / grid, hi = total_steps * (b + 1) / grid;
+        const int64_t t0 = host_first_tile(host_table, count, lo, total_tiles);
+        const int64_t t1 = host_first_tile(host_table, count, hi, total_tiles);
+        if (t0 >= t1) continue;
+        const int p0 = host_find_problem(host_table, count, t0), p1 = host_find_problem(host_table, count, t1 - 1);
+        if (p1 - p0 + 1 > kStreamMaxProblems) return false;
+        // w_scale and the M exact sums of each row
+        size_t bytes = static_cast<size_t>(t1 - t0) * 64 * sizeof(float) * (1 + host_table[p0].M);
+        for (int i = p0; i <= p1; ++i)
+            bytes += static_cast<size_t>(host_table[i].M) * padded_q_row(host_table[i].Kp);
+        need = std::max(need, bytes);
+    }
+    if (need > static_cast<size_t>(kStreamQBytes)) return false;
+    *grid_out = grid;
+    *lds_out = 0;                                       // all of the kernel's LDS is static
+    return true;
+}
+
 hipError_t launch_gemv(const int8_t* q, const float* a_scale, const int32_t* q_rowsum,
                        int64_t M, int64_t Kp, const uint8_t* packed, const float* w_scale,
                        int64_t N, void* y, bool y_bf16, int64_t ldy, int32_t* acc_debug,
@@ -626,6 +1014,10 @@ hipError_t launch_gemv(const int8_t* q, const float* a_scale, const int32_t* q_r
     if (N * (Kp / 4) >= kPersistMinBytes) {
         int64_t tiles = 0, steps = 0;
         const GemvProblem g = as_group_of_one(p, tiles, steps);
+        int grid = 0;
+        size_t lds = 0;
+        if (gemv_stream_plan(&g, 1, tiles, steps, &grid, &lds))
+            return launch_stream<false, false>(g, nullptr, 1, tiles, steps, grid, lds, true, y_bf16, stream);
         return launch_persistent<false, false>(g, nullptr, 1, tiles, steps, gemv_group_lds(M, Kp), true, y_bf16,
                                                stream);
     }
@@ -636,6 +1028,10 @@ hipError_t launch_gemv_fused(const GemvProblem& p, bool x_bf16, bool y_bf16, hip
     if (static_cast<int64_t>(p.N) * (p.Kp / 4) >= kPersistMinBytes) {
         int64_t tiles = 0, steps = 0;
         const GemvProblem g = as_group_of_one(p, tiles, steps);
+        int grid = 0;
+        size_t lds = 0;
+        if (gemv_stream_plan(&g, 1, tiles, steps, &grid, &lds))
+            return launch_stream<true, false>(g, nullptr, 1, tiles, steps, grid, lds, x_bf16, y_bf16, stream);
         return launch_persistent<true, false>(g, nullptr, 1, tiles, steps, gemv_group_lds(p.M, p.Kp), x_bf16,
                                               y_bf16, stream);
     }
@@ -643,9 +1039,12 @@ hipError_t launch_gemv_fused(const GemvProblem& p, bool x_bf16, bool y_bf16, hip
 }
 
 hipError_t launch_gemv_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,
-                               int64_t total_steps, size_t lds, bool x_bf16, bool y_bf16,
+                               int64_t total_steps, size_t lds, int stream_grid_size, bool x_bf16, bool y_bf16,
                                hipStream_t stream) {
     GemvProblem none{};
+    if (stream_grid_size > 0)
+        return launch_stream<true, true>(none, table_dev, count, total_tiles, total_steps, stream_grid_size, lds,
+                                         x_bf16, y_bf16, stream);
     return launch_persistent<true, true>(none, table_dev, count, total_tiles, total_steps, lds, x_bf16, y_bf16,
                                          stream);
 }

@@ -131,6 +131,8 @@ LINEAR_CASES = [
     # decode kernel (M <= 16)
     (1, 1, 16), (1, 16, 128), (1, 33, 144), (1, 640, 2560), (2, 257, 1152), (5, 130, 4304),
     (8, 64, 6912), (16, 100, 2048), (1, 4304, 1152),
+    # single calls of 8 MB or more packed bytes: the streaming decode kernel
+    (1, 13824, 2560), (3, 8200, 4096),
     # GEMM (M > 16)
     (17, 16, 16), (33, 130, 144), (130, 257, 1152), (300, 200, 4304), (257, 129, 6912), (512, 640, 2560),
 ]
@@ -241,6 +243,25 @@ def test_grouped_matches_oracle_and_single_calls(orc, M, dtype):
         for (xd, pw, y), ref in zip(items, refs):
             check_y(y, ref["y"])
             assert torch.equal(y, tw.bitlinear(xd, pw))
+
+
+def test_grouped_large_tokens_use_persistent_kernel(orc):
+    """M=16 tokens of K=4096 exceed the streaming kernel's LDS share per workgroup,
+    so the plan falls back to the persistent kernel; results are the same."""
+    M = 16
+    shapes = [(640, 4096), (2560, 4096), (97, 4096), (1000, 2048)]
+    items, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        x, W = wl.random_case(900 + i, M, N, K)
+        pw = tw.pack(W.to(DEV))
+        y = torch.full((M, N), float("nan"), device=DEV)
+        items.append((x.to(DEV), pw, y))
+        refs.append(orc.linear(bits(x), bits(W)))
+    group = tw.GroupedBitLinear(items)
+    group()
+    torch.cuda.synchronize()
+    for (_, _, y), ref in zip(items, refs):
+        check_y(y, ref["y"])
 
 
 def test_grouped_plan_rejects_bad_items():
