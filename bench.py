@@ -102,7 +102,7 @@ def bench_decode(tw, wl, torch, steps, warmup, per_call: bool):
     out = dict(value=gbps, ms_per_step=ms, bytes=nbytes, launches_per_step=1,
                roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s",
                              frac=gbps / HBM_PEAK_GBPS,
-                             traffic=traffic_from_profile("gemv_grouped_bitnet2b_decode_30_layers", src)))
+                             traffic=traffic_from_profile("decode_gemv_bitnet2b_30_layers_m1", src)))
     if per_call:
         # the same 210 projections as 210 single-problem calls (one fused launch each),
         # replayed from a HIP graph: what a decoder that cannot group its calls pays
@@ -126,30 +126,34 @@ def bench_decode(tw, wl, torch, steps, warmup, per_call: bool):
     return out
 
 
-def cpu_baseline_decode(wl, torch, budget_s: float):
+def cpu_baseline_decode(wl, torch, budget_s: float, max_layers: int = 3):
+    """The oracle's ActQuant + int dot + epilogue over the first layers' projections
+    (weights quantised once, untimed), cycled until budget_s of timed work."""
     from oracle.oracle import Oracle
     orc = Oracle()
     w = wl.WORKLOADS["c2"]
     threads = orc.max_threads()
-    done_bytes, spent, layers = 0, 0.0, 0
-    while spent < budget_s and layers < w.layers:
+    prepared = []
+    for layer in range(max_layers):
         for i, p in enumerate(w.projections):
-            W = wl.weight_for(w, i, layer=layers, device="cuda").cpu()
-            x = wl.activation_for(w, i, layer=layers, device="cuda").cpu()
-            Wb = W.view(torch.int16).numpy().view("uint16")
-            xb = x.view(torch.int16).numpy().view("uint16")
-            t, ws, _, _ = orc.weight_quant(Wb)            # packing: not timed
+            W = wl.weight_for(w, i, layer=layer, device="cuda").cpu()
+            x = wl.activation_for(w, i, layer=layer, device="cuda").cpu()
+            t, ws, _, _ = orc.weight_quant(W.view(torch.int16).numpy().view("uint16"))
+            prepared.append((x.view(torch.int16).numpy().view("uint16"), t, ws, p.N * p.K // 4))
+    done_bytes, spent, passes = 0, 0.0, 0
+    while spent < budget_s:
+        for xb, t, ws, nb in prepared:
             t0 = time.perf_counter()
             q, a, _ = orc.act_quant(xb)
             acc = orc.int_dot(q, t, nthreads=threads)
             orc.epilogue(acc, a, ws)
             spent += time.perf_counter() - t0
-            done_bytes += p.N * p.K // 4
-        layers += 1
+            done_bytes += nb
+        passes += 1
     return dict(value=done_bytes / spent / 1e9, unit="GB/s", cores=threads, kind="oracle",
-                sample=f"first {layers} of 30 decode layers ({layers * 7} projections, "
-                       f"{done_bytes / 1e6:.1f} MB packed), ActQuant + int dot + epilogue, "
-                       f"{spent:.1f} s")
+                sample=f"the first {max_layers} of 30 decode layers ({len(prepared)} projections, "
+                       f"{sum(nb for *_, nb in prepared) / 1e6:.1f} MB packed) {passes} times over, "
+                       f"ActQuant + int dot + epilogue, {spent:.1f} s")
 
 
 # ------------------------------------------------------------------- prefill
@@ -166,32 +170,35 @@ def bench_prefill(tw, wl, torch, steps, warmup, out_dtype):
         y = torch.empty((w.M, p.N), dtype=out_dtype, device="cuda")
         projs.append((p, pw, x, q, a, r, y))
     ops = sum(2 * w.M * p.N * p.K for p, *_ in projs)
-    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    evs = [[(Ev(), Ev()) for _ in projs] for _ in range(steps)]
-    stream = torch.cuda.current_stream().cuda_stream
 
-    def step(events):
-        for j, (p, pw, x, q, a, r, y) in enumerate(projs):
-            tw._lib.check(tw._lib.lib().bitnet_act_quant(stream, x.data_ptr(), tw._dtype(x), w.M, p.K, p.K,
-                                                         q.data_ptr(), a.data_ptr(), r.data_ptr()))
-            if events:
-                events[j][0].record()
+    def quant(p, x, q, a, r):
+        tw._lib.check(tw._lib.lib().bitnet_act_quant(torch.cuda.current_stream().cuda_stream, x.data_ptr(),
+                                                     tw._dtype(x), w.M, p.K, p.K, q.data_ptr(), a.data_ptr(),
+                                                     r.data_ptr()))
+
+    def step():
+        for p, pw, x, q, a, r, y in projs:
+            quant(p, x, q, a, r)
             tw.linear(q, a, r, pw, out=y)
-            if events:
-                events[j][1].record()
 
-    for _ in range(warmup):
-        step(None)
+    def gemms():
+        for p, pw, x, q, a, r, y in projs:
+            tw.linear(q, a, r, pw, out=y)
+
+    # Both timed regions replay HIP graphs, so host-side submission never leaves
+    # the GPU idle between launches: a step is ActQuant + GEMM per projection;
+    # the GEMM-only graph gives the average duration of one GEMM launch.
+    step()
     torch.cuda.synchronize()
-    start, end = Ev(), Ev()
-    start.record()
-    for s_ in range(steps):
-        step(evs[s_])
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
-    per_launch = [e0.elapsed_time(e1) for row in evs for e0, e1 in row]
-    gemm_ms = sum(per_launch) / len(per_launch)
+    g_step, g_gemm = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        step()
+    reps = 4
+    with torch.cuda.graph(g_gemm):
+        for _ in range(reps):
+            gemms()
+    ms = time_region(torch, g_step.replay, steps, warmup)
+    gemm_ms = time_region(torch, g_gemm.replay, max(steps // 2, 3), 2) / (reps * len(projs))
     ops_per_launch = ops / len(projs)
     achieved = ops_per_launch / (gemm_ms * 1e-3) / 1e12
     tops = ops / (ms * 1e-3) / 1e12
@@ -202,24 +209,30 @@ def bench_prefill(tw, wl, torch, steps, warmup, out_dtype):
                             step="ActQuant + GEMM per projection"),
                 roofline=dict(bound="mfma", achieved=achieved, peak=INT8_PEAK_TOPS, unit="TOPS",
                               frac=achieved / INT8_PEAK_TOPS,
-                              traffic=traffic_from_profile("gemm_bitnet2b_prefill_m4096", src)),
-                gemm_ms_per_launch=gemm_ms, launches_per_step=2 * len(projs))
+                              traffic=traffic_from_profile("prefill_gemm_bitnet2b_m4096", src)),
+                gemm_ms_per_launch=gemm_ms, launches_per_step=2 * len(projs),
+                timing="HIP graph replays: whole steps, and GEMM launches alone")
 
 
 def cpu_baseline_prefill(wl, torch, budget_s: float):
+    """The oracle's ActQuant + int dot + epilogue on slices of 64 tokens of the
+    prefill activations through all three projections, until budget_s of timed
+    work or all 4096 tokens (weights quantised once, untimed)."""
     from oracle.oracle import Oracle
     orc = Oracle()
     w = wl.WORKLOADS["c5"]
     threads = orc.max_threads()
-    ops, spent, tokens = 0, 0.0, 0
-    rows = 16
-    while spent < budget_s and tokens < 256:
-        for i, p in enumerate(w.projections):
-            W = wl.weight_for(w, i, device="cuda").cpu()
-            x = wl.activation_for(w, i, device="cuda")[tokens:tokens + rows].cpu()
-            t, ws, _, _ = orc.weight_quant(W.view(torch.int16).numpy().view("uint16"), p.segments or None)
+    prepared = []
+    for i, p in enumerate(w.projections):
+        W = wl.weight_for(w, i, device="cuda").cpu()
+        t, ws, _, _ = orc.weight_quant(W.view(torch.int16).numpy().view("uint16"), p.segments or None)
+        x = wl.activation_for(w, i, device="cuda").cpu().view(torch.int16).numpy().view("uint16")
+        prepared.append((p, t, ws, x))
+    ops, spent, tokens, rows = 0, 0.0, 0, 64
+    while spent < budget_s and tokens < w.M:
+        for p, t, ws, x in prepared:
             t0 = time.perf_counter()
-            q, a, _ = orc.act_quant(x.view(torch.int16).numpy().view("uint16"))
+            q, a, _ = orc.act_quant(x[tokens:tokens + rows])
             acc = orc.int_dot(q, t, nthreads=threads)
             orc.epilogue(acc, a, ws)
             spent += time.perf_counter() - t0
