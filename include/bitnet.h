@@ -223,6 +223,14 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
  */
 bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_plan_t* plan);
 
+/* Name of the kernel a plan launches: "stream" (each workgroup streams an
+ * equal share of all packed bytes through per-wave LDS rings; chosen when
+ * every workgroup's token rows fit its LDS share) or "persistent" (the
+ * fallback); "" for a handle not made by bitnet_group_plan.  The environment
+ * variable BITNET_GROUP_KERNEL=persistent, read by bitnet_group_plan, forces
+ * the fallback (for comparisons; results are identical). */
+const char* bitnet_group_plan_kernel(const bitnet_group_plan_t* plan);
+
 /* Static text for a status code. */
 const char* bitnet_status_string(bitnet_status_t s);
 

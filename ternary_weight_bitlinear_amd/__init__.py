@@ -180,6 +180,8 @@ class GroupedBitLinear:
                 _stream(x0), ctypes.cast(arr, ctypes.c_void_p), len(items), M, _dtype(x0),
                 _dtype(items[0][2]), self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
         self.bytes = sum(w.N * w.K // 4 for _, w, _ in items)
+        # which kernel the plan launches: "dynamic", "stream" or "persistent"
+        self.kernel = _lib.lib().bitnet_group_plan_kernel(ctypes.byref(self.plan)).decode()
 
     def __call__(self):
         with torch.cuda.device(self.device):

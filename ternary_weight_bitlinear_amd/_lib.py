@@ -31,6 +31,7 @@ SIGNATURES = {
     "bitnet_group_table_bytes": (_i64, [_i32]),
     "bitnet_group_plan": (ctypes.c_int, [_vp, _vp, _i32, _i64, ctypes.c_int, ctypes.c_int, _vp, _i64, _vp]),
     "bitnet_bitlinear_grouped": (ctypes.c_int, [_vp, _vp]),
+    "bitnet_group_plan_kernel": (ctypes.c_char_p, [_vp]),
     "bitnet_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bitnet_last_error": (ctypes.c_char_p, []),
 }

@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -336,6 +337,15 @@ bitnet_status_t bitnet_bitlinear_forward(hipStream_t stream, const void* x, bitn
     return run_linear(stream, q, a_scale, q_rowsum, M, K, packed, w_scale, N, y, y_dtype, ldy, nullptr, fn);
 }
 
+// Kernels of a grouped plan.  BITNET_GROUP_KERNEL=persistent, read when a
+// plan is made, skips the streaming kernel (for comparisons; results are
+// identical).
+enum { kGroupPersistent = 0, kGroupStream = 1 };
+static bool persistent_forced() {
+    const char* v = getenv("BITNET_GROUP_KERNEL");
+    return v && strcmp(v, "persistent") == 0;
+}
+
 int64_t bitnet_group_table_bytes(int32_t count) {
     if (count <= 0) return -1;
     return static_cast<int64_t>(count) * static_cast<int64_t>(sizeof(bitnet::GemvProblem));
@@ -385,10 +395,14 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
         if (tiles > kMaxMN) return fail(BITNET_ERR_INVALID_ARG, "%s: too many tiles in the group", fn);
         if (Kp > max_kp) max_kp = Kp;
     }
-    int stream_grid = 0;
+    // Kernel choice: the streaming kernel where every workgroup's problems
+    // fit its LDS share, else the persistent one.
+    int kind = kGroupPersistent, grid = 0;
     size_t lds = bitnet::gemv_group_lds(M, max_kp);
-    if (!bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &stream_grid, &lds)) {
-        stream_grid = 0;
+    if (!persistent_forced() && bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &grid, &lds)) {
+        kind = kGroupStream;
+    } else {
+        grid = 0;
         lds = bitnet::gemv_group_lds(M, max_kp);
     }
     hipError_t e = hipMemcpyAsync(table_dev, table.data(), table.size() * sizeof(bitnet::GemvProblem),
@@ -402,7 +416,7 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
     plan->opaque[4] = tiles;
     plan->opaque[5] = static_cast<int64_t>(lds);
     plan->opaque[6] = static_cast<int64_t>(x_dtype) | (static_cast<int64_t>(y_dtype) << 8) |
-                      (static_cast<int64_t>(stream_grid) << 32);
+                      (static_cast<int64_t>(kind) << 16) | (static_cast<int64_t>(grid) << 32);
     plan->opaque[7] = steps;
     return ok();
 }
@@ -412,13 +426,21 @@ bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_
     if (!plan || plan->opaque[0] != kPlanMagic)
         return fail(BITNET_ERR_INVALID_ARG, "%s: plan was not made by bitnet_group_plan", fn);
     const auto* table = reinterpret_cast<const bitnet::GemvProblem*>(static_cast<uintptr_t>(plan->opaque[1]));
-    hipError_t e = bitnet::launch_gemv_grouped(table, static_cast<int>(plan->opaque[2]), plan->opaque[4],
-                                               plan->opaque[7], static_cast<size_t>(plan->opaque[5]),
-                                               static_cast<int>(plan->opaque[6] >> 32),
-                                               (plan->opaque[6] & 0xFF) == BITNET_BF16,
-                                               ((plan->opaque[6] >> 8) & 0xFF) == BITNET_BF16, stream);
+    const int count = static_cast<int>(plan->opaque[2]);
+    const int kind = static_cast<int>((plan->opaque[6] >> 16) & 0xFF);
+    const int grid = static_cast<int>(plan->opaque[6] >> 32);
+    const bool x_bf16 = (plan->opaque[6] & 0xFF) == BITNET_BF16;
+    const bool y_bf16 = ((plan->opaque[6] >> 8) & 0xFF) == BITNET_BF16;
+    hipError_t e = bitnet::launch_gemv_grouped(table, count, plan->opaque[4], plan->opaque[7],
+                                               static_cast<size_t>(plan->opaque[5]),
+                                               kind == kGroupStream ? grid : 0, x_bf16, y_bf16, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
+}
+
+const char* bitnet_group_plan_kernel(const bitnet_group_plan_t* plan) {
+    if (!plan || plan->opaque[0] != kPlanMagic) return "";
+    return ((plan->opaque[6] >> 16) & 0xFF) == kGroupStream ? "stream" : "persistent";
 }
 
 const char* bitnet_status_string(bitnet_status_t s) {

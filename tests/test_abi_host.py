@@ -45,6 +45,18 @@ def test_sizes_and_strings():
         assert L.bitnet_status_string(s)
 
 
+def test_group_table_and_plan_handle():
+    """The table holds one descriptor per item; a handle that bitnet_group_plan
+    did not fill names no kernel."""
+    L = _lib.lib()
+    assert L.bitnet_group_table_bytes(0) == -1
+    one = L.bitnet_group_table_bytes(1)
+    assert one > 0 and one % 8 == 0
+    assert L.bitnet_group_table_bytes(210) == 210 * one
+    assert L.bitnet_group_plan_kernel(ctypes.byref(_lib.GroupPlan())) == b""
+    assert L.bitnet_group_plan_kernel(None) == b""
+
+
 def _status_and_error(fn, *args):
     st = fn(*args)
     return st, _lib.lib().bitnet_last_error().decode()

@@ -258,10 +258,70 @@ def test_grouped_large_tokens_use_persistent_kernel(orc):
         items.append((x.to(DEV), pw, y))
         refs.append(orc.linear(bits(x), bits(W)))
     group = tw.GroupedBitLinear(items)
+    assert group.kernel == "persistent"
     group()
     torch.cuda.synchronize()
     for (_, _, y), ref in zip(items, refs):
         check_y(y, ref["y"])
+
+
+# Grouped decode items: N values leave ragged last tiles; K=4304 and K=2000
+# are not multiples of 128 (padded tails); small N gives one-tile problems.
+GROUP_SHAPES = [(2560, 2560), (640, 2560), (6912, 2560), (2560, 6912), (2500, 2560), (1000, 4304),
+                (4100, 2000), (64, 2560), (130, 6912)]
+
+
+def _group_case(orc, M, x_dtype, y_dtype, shapes, seed):
+    items, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        x, W = wl.random_case(seed + i, M, N, K, x_dist="normal_outliers")
+        pw = tw.pack(W.to(DEV))
+        items.append((x.to(DEV).to(x_dtype), pw, torch.full((M, N), float("nan"), device=DEV, dtype=y_dtype)))
+        xo = bits(x) if x_dtype == torch.bfloat16 else x.float().numpy()
+        refs.append(orc.linear(xo, bits(W), out="bf16" if y_dtype == torch.bfloat16 else "f32"))
+    return items, refs
+
+
+@pytest.mark.parametrize("M,x_dtype,y_dtype", [(1, torch.bfloat16, torch.float32), (1, torch.float32, torch.bfloat16),
+                                               (2, torch.float32, torch.float32), (3, torch.bfloat16, torch.bfloat16),
+                                               (4, torch.float32, torch.bfloat16)])
+def test_grouped_kernels_agree_with_oracle(orc, M, x_dtype, y_dtype, monkeypatch):
+    """The same group planned for the streaming kernel and for the persistent
+    fallback matches the oracle on every launch of the reused plan."""
+    items, refs = _group_case(orc, M, x_dtype, y_dtype, GROUP_SHAPES, 1300 + 10 * M)
+    for kernel in ("stream", "persistent"):
+        if kernel == "stream":
+            monkeypatch.delenv("BITNET_GROUP_KERNEL", raising=False)
+        else:
+            monkeypatch.setenv("BITNET_GROUP_KERNEL", kernel)
+        group = tw.GroupedBitLinear(items)
+        assert group.kernel == kernel
+        for rep in range(3):
+            for _, _, y in items:
+                y.fill_(float("nan"))
+            group()
+            torch.cuda.synchronize()
+            for (_, _, y), ref in zip(items, refs):
+                check_y(y, ref["y"])
+
+
+def test_grouped_many_problems_per_workgroup(orc):
+    """A six-layer mix of a decoder's projections (each workgroup's share spans
+    several problems) next to a two-item group with fewer tiles than
+    workgroups, launched back to back."""
+    big = [(2560, 2560), (640, 2560), (640, 2560), (2560, 2560), (6912, 2560), (6912, 2560), (2560, 6912)] * 6
+    items, refs = _group_case(orc, 1, torch.bfloat16, torch.bfloat16, big, 1700)
+    small_items, small_refs = _group_case(orc, 1, torch.float32, torch.float32, [(130, 2560), (64, 6912)], 1800)
+    g_big, g_small = tw.GroupedBitLinear(items), tw.GroupedBitLinear(small_items)
+    assert g_big.kernel == "stream" and g_small.kernel == "stream"
+    for rep in range(3):
+        for _, _, y in items + small_items:
+            y.fill_(float("nan"))
+        g_big()
+        g_small()
+        torch.cuda.synchronize()
+        for (_, _, y), ref in zip(items + small_items, refs + small_refs):
+            check_y(y, ref["y"])
 
 
 def test_grouped_plan_rejects_bad_items():
