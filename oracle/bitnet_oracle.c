@@ -45,6 +45,22 @@
  *       element k of a row is in byte 4*(k/16) + (k%4), bits
  *       2*((k%16)/4) .. +1; positions k >= K hold code 1 (weight 0).
  *
+ *
+ * The step before the path [Guide s3.1 "Background"; s3.1 key parameters,
+ * rms_norm_eps]: every projection normalises its input first,
+ * y = ActQuant(RMSNorm(x, g)) with a per-projection weight g [K] and eps; for
+ * the down projection the input is the gated product silu(gate) * up [Guide
+ * s2, model table: SiLU activation].
+ *   R10 RMSNorm(x, g)_k = x_k * g_k * r with r = 1/sqrt(mean_k(x_k^2) + eps)
+ *       (the plain reading; no rounding of the normalised vector to bf16).
+ *       r > 0 is one factor for the whole token, and ActQuant's codes do not
+ *       change when a token is scaled by a positive factor, so the codes are
+ *       taken from z = x*g (fp32 products, R4 on z) and r enters a_scale
+ *       only: a_scale = amax(z) * r / 127, evaluated in fp64 with the sum of
+ *       squares in fp64 (k ascending) and rounded once to fp32.
+ *   R11 silu(a) * u is evaluated in fp64, a / (1 + exp(-a)) * u, and rounded
+ *       once to fp32; that fp32 value is the input of R10.
+ *
  * Everything here is a direct loop over the definition.  No blocking, no
  * fusion, no intrinsics.
  */
@@ -273,6 +289,67 @@ int orc_act_quant(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
         q_rowsum[m] = (int32_t)sum;
     }
     return 0;
+}
+
+/* ------------------------------------------------- RMSNorm -> ActQuant */
+
+/*
+ * q, a_scale and q_rowsum of ActQuant(RMSNorm(x, g)) for M tokens of K (R10):
+ * codes of z = x*g exactly as orc_act_quant, a_scale = amax(z) * r / 127 with
+ * r = 1/sqrt(sum_k x_k^2 / K + eps) in fp64.  x and g are bf16 or fp32; g has
+ * K entries.  Returns -1 for a bad K.
+ */
+int orc_rms_act_quant(const void* x, int x_dtype, const void* g, int g_dtype, int64_t M, int64_t K,
+                      int64_t ldx, float eps, int8_t* q, float* a_scale, int32_t* q_rowsum)
+{
+    int64_t Kp = orc_padded_k(K);
+    if (Kp < 0)
+        return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        /* z = x * g, one fp32 product per element */
+        float amax = 0.0f;
+        double squares = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            float xv = load_elem(x, x_dtype, m * ldx + k);
+            float z = xv * load_elem(g, g_dtype, k);
+            float a = fabsf(z);
+            if (a > amax)
+                amax = a;
+            squares += (double)xv * (double)xv;
+        }
+        double r = 1.0 / sqrt(squares / (double)K + (double)eps);
+        int64_t sum = 0;
+        memset(&q[m * Kp], 0, (size_t)Kp);         /* zero token and the tail k >= K */
+        if (amax == 0.0f) {
+            a_scale[m] = 0.0f;
+        } else {
+            float sa = 127.0f / amax;
+            for (int64_t k = 0; k < K; ++k) {
+                float z = load_elem(x, x_dtype, m * ldx + k) * load_elem(g, g_dtype, k);
+                float c = round_half_even(z * sa);
+                if (c > 127.0f)
+                    c = 127.0f;
+                if (c < -128.0f)
+                    c = -128.0f;
+                q[m * Kp + k] = (int8_t)c;
+                sum += (int8_t)c;
+            }
+            a_scale[m] = (float)((double)amax * r / 127.0);
+        }
+        q_rowsum[m] = (int32_t)sum;
+    }
+    return 0;
+}
+
+/* h = silu(gate) * up per element (R11), fp32 out [M][K] (row stride K). */
+void orc_swiglu(const void* gate, const void* up, int dtype, int64_t M, int64_t K, int64_t ld, float* h)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            double a = (double)load_elem(gate, dtype, m * ld + k);
+            double u = (double)load_elem(up, dtype, m * ld + k);
+            h[m * K + k] = (float)(a / (1.0 + exp(-a)) * u);
+        }
 }
 
 /* ----------------------------------------------------------- integer dot */

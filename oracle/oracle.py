@@ -70,6 +70,10 @@ class Oracle:
         lib.orc_unpack.argtypes, lib.orc_unpack.restype = [vp, i64, i64, vp], i64
         lib.orc_act_quant.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp]
         lib.orc_act_quant.restype = ctypes.c_int
+        lib.orc_rms_act_quant.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, f32, vp, vp, vp]
+        lib.orc_rms_act_quant.restype = ctypes.c_int
+        lib.orc_swiglu.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp]
+        lib.orc_swiglu.restype = None
         lib.orc_int_dot.argtypes = [vp, i64, i64, vp, i64, vp, ctypes.c_int]
         lib.orc_int_dot.restype = ctypes.c_int
         lib.orc_int_dot_pairs.argtypes = [vp, i64, vp, i64, vp, vp, vp]
@@ -153,6 +157,38 @@ class Oracle:
         rowsum = np.empty(M, dtype=np.int32)
         self.lib.orc_act_quant(_ptr(x), _dtype_code(x), M, K, K, _ptr(q), _ptr(a_scale), _ptr(rowsum))
         return q, a_scale, rowsum
+
+    def rms_act_quant(self, x: np.ndarray, g: np.ndarray, eps: float = 1e-6):
+        """ActQuant(RMSNorm(x, g)): q [M, Kp] int8, a_scale [M] f32, q_rowsum [M] i32."""
+        x = np.ascontiguousarray(x)
+        g = np.ascontiguousarray(g)
+        M, K = x.shape
+        if g.shape != (K,):
+            raise ValueError("g must have K entries")
+        Kp = self.padded_k(K)
+        if Kp < 0:
+            raise ValueError("K must be a positive multiple of 16")
+        q = np.empty((M, Kp), dtype=np.int8)
+        a_scale = np.empty(M, dtype=np.float32)
+        rowsum = np.empty(M, dtype=np.int32)
+        self.lib.orc_rms_act_quant(_ptr(x), _dtype_code(x), _ptr(g), _dtype_code(g), M, K, K, float(eps),
+                                   _ptr(q), _ptr(a_scale), _ptr(rowsum))
+        return q, a_scale, rowsum
+
+    def swiglu(self, gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+        """silu(gate) * up, fp32 [M, K] (gate and up of one dtype and shape)."""
+        gate = np.ascontiguousarray(gate)
+        up = np.ascontiguousarray(up)
+        if gate.shape != up.shape or gate.dtype != up.dtype:
+            raise ValueError("gate and up must match")
+        M, K = gate.shape
+        h = np.empty((M, K), dtype=np.float32)
+        self.lib.orc_swiglu(_ptr(gate), _ptr(up), _dtype_code(gate), M, K, K, _ptr(h))
+        return h
+
+    def swiglu_rms_act_quant(self, gate: np.ndarray, up: np.ndarray, g: np.ndarray, eps: float = 1e-6):
+        """ActQuant(RMSNorm(silu(gate) * up, g)) for the down projection."""
+        return self.rms_act_quant(self.swiglu(gate, up), g, eps)
 
     # ------------------------------------------------------ integer dot
     def int_dot(self, q: np.ndarray, t: np.ndarray, nthreads: int = 1) -> np.ndarray:

@@ -319,6 +319,108 @@ def pin_act_quant_exact_rational(orc):
     assert np.array_equal(r, want.astype(np.int64).sum(1).astype(np.int32))
 
 
+# ------------------------------------------- RMSNorm -> ActQuant, SwiGLU
+
+def _rms_literal(xv: np.ndarray, gv: np.ndarray, eps: float):
+    """The composition written out in fp64, straight from the page's pipeline
+    (x -> RMSNorm(x, g) -> ActQuant): the normalised vector y, its codes before
+    rounding v = y*127/max|y|, and amax(y)/127."""
+    x64, g64 = xv.astype(np.float64), gv.astype(np.float64)
+    ms = np.array([math.fsum(row) for row in x64 * x64]) / xv.shape[1]
+    y = x64 * g64[None, :] / np.sqrt(ms + eps)[:, None]
+    amax = np.abs(y).max(1)
+    v = y * (127.0 / np.where(amax > 0, amax, 1.0))[:, None]
+    return y, v, amax / 127.0
+
+
+def pin_rms_constant_token(orc):
+    """x = c on every k, g = 1: every code is +-127 and a_scale = |c| / sqrt(c^2 + eps) / 127
+    (closed form, evaluated with Python's decimal module)."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    K, eps = 256, 1e-6
+    for c in (0.75, -3.5, 0.001953125, 40.0):
+        x = f32_to_bf16_bits(np.full((1, K), c, dtype=np.float32))
+        g = f32_to_bf16_bits(np.ones(K, dtype=np.float32))
+        q, a, r = orc.rms_act_quant(x, g, eps)
+        sign = 1 if c > 0 else -1
+        assert np.all(q[0, :K] == 127 * sign) and np.all(q[0, K:] == 0)
+        assert r[0] == 127 * K * sign
+        dc, de = Decimal(abs(c)), Decimal(np.float32(eps).item())
+        want = float(dc / (dc * dc + de).sqrt() / Decimal(127))
+        assert abs(float(a[0]) - want) <= 2 * np.spacing(np.float32(want)), (c, float(a[0]), want)
+
+
+def pin_rms_matches_literal_composition(orc):
+    """Codes equal the fp64 composition RMSNorm then ActQuant wherever the value
+    before rounding is not within 2e-5 of a .5 tie (the fp32 product decides those),
+    and a_scale equals amax(y)/127 to 2 fp32 ulps."""
+    rng = np.random.default_rng(41)
+    M, K, eps = 24, 384, 1e-6
+    x = rng_bf16(rng, (M, K))
+    x[3] = rng_bf16(rng, (1, K), scale=1e-4)          # eps matters for this token
+    x[5, 17] = f32_to_bf16_bits(np.array([60.0], dtype=np.float32))[0]   # an outlier
+    g = rng_bf16(rng, (K,), scale=0.2)
+    gv = bf16_bits_to_f32(g) + np.float32(1.0)
+    g = f32_to_bf16_bits(bf16_bits_to_f32(rng_bf16_from(gv)))
+    xv, gv = bf16_bits_to_f32(x), bf16_bits_to_f32(g)
+    q, a, rs = orc.rms_act_quant(x, g, eps)
+    _, v, a_lit = _rms_literal(xv, gv, np.float64(np.float32(eps)))
+    clear = np.abs(np.abs(v - np.trunc(v)) - 0.5) > 2e-5
+    want = np.clip(np.rint(v), -128, 127)
+    assert clear.mean() > 0.99
+    assert np.array_equal(q[:, :K][clear], want[clear].astype(np.int8))
+    assert np.all(np.abs(a.astype(np.float64) - a_lit) <= 2 * np.spacing(a))
+    assert np.array_equal(rs, q.astype(np.int64).sum(1).astype(np.int32))
+
+
+def pin_rms_eps_and_zero_weight(orc):
+    """A token far below sqrt(eps) is scaled by about 1/sqrt(eps); a zero norm
+    weight gives zero codes and a zero scale; eps = 0 with power-of-two scaling
+    of x leaves codes and a_scale unchanged."""
+    rng = np.random.default_rng(43)
+    K = 128
+    x = rng_bf16(rng, (1, K), scale=1e-6)
+    g = f32_to_bf16_bits(np.ones(K, dtype=np.float32))
+    q, a, _ = orc.rms_act_quant(x, g, 1e-6)
+    xv = bf16_bits_to_f32(x).astype(np.float64)
+    ms = math.fsum(xv[0] ** 2) / K
+    want = np.abs(xv).max() / math.sqrt(ms + float(np.float32(1e-6))) / 127
+    assert abs(float(a[0]) - want) <= 2 * np.spacing(np.float32(want))
+    q0, a0, r0 = orc.rms_act_quant(rng_bf16(rng, (2, K)), np.zeros(K, dtype=np.float32), 1e-6)
+    assert not q0.any() and not a0.any() and not r0.any()
+    x = rng_bf16(rng, (3, K))
+    base = orc.rms_act_quant(x, g, 0.0)
+    for j in (-3, 5):
+        xs = f32_to_bf16_bits(bf16_bits_to_f32(x) * np.float32(2.0 ** j))
+        got = orc.rms_act_quant(xs, g, 0.0)
+        assert np.array_equal(got[0], base[0]) and np.array_equal(got[1], base[1])
+
+
+def pin_swiglu_decimal(orc):
+    """silu(a)*u against Python's decimal module (50 digits): within half an fp32
+    ulp plus a hair, and exact for the closed forms silu(0) = 0, u = 0 and
+    silu(a) = a for a = 60 (e^-60 is far below an ulp)."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    rng = np.random.default_rng(47)
+    a = rng_bf16(rng, (4, 48), scale=3.0)
+    u = rng_bf16(rng, (4, 48))
+    a[0, :4] = f32_to_bf16_bits(np.array([0.0, -0.0, 60.0, -60.0], dtype=np.float32))
+    u[1, :3] = 0
+    h = orc.swiglu(a, u)
+    av, uv = bf16_bits_to_f32(a), bf16_bits_to_f32(u)
+    for i in range(av.shape[0]):
+        for k in range(av.shape[1]):
+            da, du = Decimal(float(av[i, k])), Decimal(float(uv[i, k]))
+            exact = da / (1 + (-da).exp()) * du
+            err = abs(Decimal(float(h[i, k])) - exact)
+            ulp = Decimal(float(np.spacing(np.float32(abs(float(exact)))))) if exact != 0 else Decimal(0)
+            assert err <= ulp * Decimal("0.5000001") or (exact == 0 and h[i, k] == 0), (i, k)
+    assert h[0, 0] == 0 and h[0, 1] == 0 and np.all(h[1, :3] == 0)
+    assert h[0, 2] == np.float32(60.0) * uv[0, 2]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

@@ -66,6 +66,26 @@ MUTANTS = [
      "if (r > 2.0f)\n        r = 2.0f;\n    if (r < -2.0f)\n        r = -2.0f;"),
     ("zero count counts non-zeros", "zeros += (c == 0);", "zeros += (c != 0);"),
     ("unpack offset wrong", "t[n * K + k] = (int8_t)((int)u - 1);", "t[n * K + k] = (int8_t)((int)u - 2);"),
+    ("RMSNorm drops eps",
+     "double r = 1.0 / sqrt(squares / (double)K + (double)eps);",
+     "double r = 1.0 / sqrt(squares / (double)K);"),
+    ("RMSNorm sums instead of averaging",
+     "double r = 1.0 / sqrt(squares / (double)K + (double)eps);",
+     "double r = 1.0 / sqrt(squares + (double)eps);"),
+    ("RMSNorm without the square root",
+     "double r = 1.0 / sqrt(squares / (double)K + (double)eps);",
+     "double r = 1.0 / (squares / (double)K + (double)eps);"),
+    ("RMSNorm codes ignore the norm weight",
+     "float z = load_elem(x, x_dtype, m * ldx + k) * load_elem(g, g_dtype, k);\n                float c",
+     "float z = load_elem(x, x_dtype, m * ldx + k);\n                float c"),
+    ("RMSNorm scale leaves out r",
+     "a_scale[m] = (float)((double)amax * r / 127.0);", "a_scale[m] = (float)((double)amax / 127.0);"),
+    ("RMSNorm squares the weighted value",
+     "squares += (double)xv * (double)xv;", "squares += (double)z * (double)z;"),
+    ("silu sign flipped", "h[m * K + k] = (float)(a / (1.0 + exp(-a)) * u);",
+     "h[m * K + k] = (float)(a / (1.0 + exp(a)) * u);"),
+    ("gated product drops up", "h[m * K + k] = (float)(a / (1.0 + exp(-a)) * u);",
+     "h[m * K + k] = (float)(a / (1.0 + exp(-a)));"),
 ]
 
 
