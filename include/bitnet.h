@@ -136,6 +136,29 @@ bitnet_status_t bitnet_act_quant(hipStream_t stream, const void* x, bitnet_dtype
                                  int8_t* q, float* a_scale, int32_t* q_rowsum);
 
 /*
+ * ActQuant of the normalised input of a projection [Guide s3.1: every
+ * projection applies RMSNorm with its own weight and rms_norm_eps (1e-6 in
+ * the guide's models) before ActQuant; Guide s2: SiLU gating before the down
+ * projection].  Device memory throughout; results as bitnet_act_quant's.
+ *
+ * x        [M, K], row stride ldx >= K, dtype x_dtype (BF16 or F32).
+ * up       NULL, or [M, K] with x's dtype and row stride: the input is then
+ *          h = silu(x) * up (x being the gate), evaluated in fp64 as
+ *          x / (1 + exp(-x)) * up and rounded once to fp32.
+ * norm_w   [K] RMSNorm weight g, dtype norm_dtype (BF16 or F32).
+ * eps      finite, >= 0.
+ * RMSNorm(h)_k = h_k * g_k * r with r = 1/sqrt(mean_k(h_k^2) + eps).  r is
+ * one positive factor per token, so the int8 codes are those of z = h * g
+ * (fp32 products, then ActQuant exactly as bitnet_act_quant) and
+ * a_scale = amax(z) * r / 127, with the sum of squares and r in fp64 and one
+ * rounding to fp32 at the end (0 for a token whose z is all zero).
+ */
+bitnet_status_t bitnet_rmsnorm_act_quant(hipStream_t stream, const void* x, const void* up,
+                                         bitnet_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                         const void* norm_w, bitnet_dtype_t norm_dtype, float eps,
+                                         int8_t* q, float* a_scale, int32_t* q_rowsum);
+
+/*
  * Ternary linear on quantised operands + dequant epilogue [BitVLA s1, s2;
  * Guide s2 (no bias)].  Device memory throughout.
  *

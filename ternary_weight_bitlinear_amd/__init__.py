@@ -112,6 +112,28 @@ def act_quant(x: torch.Tensor):
     return q, a_scale, rowsum
 
 
+def rmsnorm_act_quant(x: torch.Tensor, norm_w: torch.Tensor, eps: float = 1e-6, up: torch.Tensor | None = None):
+    """ActQuant(RMSNorm(h, norm_w)) with h = x, or h = silu(x) * up when ``up`` is given
+    (same shape, dtype and row stride as x) -> (q [M, Kp] int8, a_scale [M], q_rowsum [M])."""
+    ldx = _rows(x, "x")
+    M, K = x.shape
+    Kp = padded_k(K)
+    if Kp < 0:
+        raise ValueError(f"K={K} must be a positive multiple of 16")
+    if norm_w.shape != (K,) or not norm_w.is_contiguous():
+        raise ValueError("norm_w must be a contiguous [K] tensor")
+    if up is not None and (up.shape != x.shape or up.dtype != x.dtype or _rows(up, "up") != ldx):
+        raise ValueError("up must match x in shape, dtype and row stride")
+    q = torch.empty((M, Kp), dtype=torch.int8, device=x.device)
+    a_scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    rowsum = torch.empty(M, dtype=torch.int32, device=x.device)
+    with torch.cuda.device(x.device):
+        _lib.check(_lib.lib().bitnet_rmsnorm_act_quant(
+            _stream(x), x.data_ptr(), up.data_ptr() if up is not None else None, _dtype(x), M, K, ldx,
+            norm_w.data_ptr(), _dtype(norm_w), float(eps), q.data_ptr(), a_scale.data_ptr(), rowsum.data_ptr()))
+    return q, a_scale, rowsum
+
+
 def linear(q: torch.Tensor, a_scale: torch.Tensor, q_rowsum: torch.Tensor, w: PackedWeight,
            out_dtype=torch.float32, out: torch.Tensor | None = None, acc_debug: bool = False):
     """y [M, N] = (acc) * (a_scale[m] * w_scale[n]) with acc the exact int32 sum of q*t.

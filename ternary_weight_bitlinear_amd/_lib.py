@@ -24,6 +24,8 @@ SIGNATURES = {
     "bitnet_pack_weights": (ctypes.c_int, [ctypes.c_int, _vp, _vp, ctypes.c_int, _i64, _i64, _i64,
                                            _vp, _i32, _vp, _vp, _vp, _vp]),
     "bitnet_act_quant": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "bitnet_rmsnorm_act_quant": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp,
+                                                ctypes.c_int, ctypes.c_float, _vp, _vp, _vp]),
     "bitnet_linear_forward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64,
                                              _vp, ctypes.c_int, _i64, _vp]),
     "bitnet_bitlinear_forward": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp,

@@ -7,6 +7,17 @@
 // factor sa = 127/amax, q = rne(x*sa), a_scale = amax/127, q = 0 and
 // a_scale = 0 for an all-zero token.
 //
+// The same kernel also runs the step before the path, per-projection RMSNorm
+// ("BitNet-Embeddings-0.6B/270M: I2_S Conversion and Inference Optimization
+// Guide", s3.1: every projection normalises its input with its own weight g
+// and rms_norm_eps before ActQuant), optionally on the gated product
+// silu(gate) * up that feeds the down projection (same guide, s2: SiLU).
+// RMSNorm scales a token by one positive factor r = 1/sqrt(mean(x^2) + eps),
+// which ActQuant's codes do not see: the codes are those of z = x * g (fp32
+// products) and r enters a_scale = amax(z) * r / 127, evaluated in fp64 with
+// the squares summed in fp64.  silu(a) * u is evaluated in fp64 and rounded
+// once to fp32.
+//
 // One 256-thread workgroup per token.  Each thread holds up to VPT vectors of
 // 8 elements in registers, so the token is read from HBM once: absmax is a
 // wave butterfly (v_max over __shfl_xor) plus a 4-entry LDS step, and the
@@ -99,41 +110,88 @@ __device__ __forceinline__ int block_sum(int v, int* red) {
     return r;
 }
 
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) == 0) red[w] = v;
+    __syncthreads();
+    double r = 0.0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) r += red[i];
+    return r;
+}
+
+// Input modes: the token itself; RMSNorm of it; RMSNorm of silu(x) * up.
+enum { kPlain = 0, kNorm = 1, kGatedNorm = 2 };
+
+// The 8 values whose codes are taken (x, or x * g, or silu(x) * up * g) of
+// vector vi, and the fp64 sum of squares of the normalised input's 8 values.
+template <typename T, bool kAligned, int kMode>
+__device__ __forceinline__ void load_input8(const T* xr, const T* ur, const void* g, bool g_bf16, int vi,
+                                            float (&z)[8], double& squares) {
+    load8<T, kAligned>(xr + vi * 8, z);
+    if constexpr (kMode == kGatedNorm) {
+        float u[8];
+        load8<T, kAligned>(ur + vi * 8, u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double a = z[e];
+            z[e] = static_cast<float>(a / (1.0 + exp(-a)) * static_cast<double>(u[e]));
+        }
+    }
+    if constexpr (kMode != kPlain) {
+        float gv[8];
+        if (g_bf16) load8<uint16_t, false>(static_cast<const uint16_t*>(g) + vi * 8, gv);
+        else load8<float, false>(static_cast<const float*>(g) + vi * 8, gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            squares += static_cast<double>(z[e]) * static_cast<double>(z[e]);
+            z[e] = z[e] * gv[e];
+        }
+    }
+}
+
 // VPT > 0: the token stays in registers (K <= 8 * 256 * VPT).
 // VPT == 0: any K; the row is read twice (the second read hits L2).
-template <typename T, int VPT, bool kAligned>
+template <typename T, int VPT, bool kAligned, int kMode>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(
-    const T* __restrict__ x, int64_t ldx, int K, int Kp,
+    const T* __restrict__ x, const T* __restrict__ up, int64_t ldx, int K, int Kp,
+    const void* __restrict__ g, bool g_bf16, float eps,
     int8_t* __restrict__ q, float* __restrict__ a_scale, int32_t* __restrict__ q_rowsum) {
     __shared__ float red_f[kWaves];
     __shared__ int red_i[kWaves];
+    __shared__ double red_d[kWaves];
     const int64_t m = blockIdx.x;
     const T* xr = x + m * ldx;
+    const T* ur = kMode == kGatedNorm ? up + m * ldx : nullptr;
     int8_t* qr = q + m * static_cast<int64_t>(Kp);
     const int nvec = K / 8;
     const int tid = threadIdx.x;
 
     float amax_local = 0.0f;
+    double squares = 0.0;
     float v[VPT > 0 ? VPT : 1][8];
     if constexpr (VPT > 0) {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int vi = tid + i * kThreads;
             if (vi < nvec) {
-                load8<T, kAligned>(xr + vi * 8, v[i]);
+                load_input8<T, kAligned, kMode>(xr, ur, g, g_bf16, vi, v[i], squares);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) amax_local = fmaxf(amax_local, fabsf(v[i][e]));
             }
         }
     } else {
         for (int vi = tid; vi < nvec; vi += kThreads) {
-            load8<T, kAligned>(xr + vi * 8, v[0]);
+            load_input8<T, kAligned, kMode>(xr, ur, g, g_bf16, vi, v[0], squares);
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax_local = fmaxf(amax_local, fabsf(v[0][e]));
         }
     }
     const float amax = block_max(amax_local, red_f);
-    // amax == 0: every x is +-0 and sa = 0 gives q = 0 exactly.
+    if constexpr (kMode != kPlain) squares = block_sum_f64(squares, red_d);
+    // amax == 0: every value is +-0 and sa = 0 gives q = 0 exactly.
     const float sa = (amax == 0.0f) ? 0.0f : 127.0f / amax;
 
     int sum_local = 0;
@@ -148,8 +206,9 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
             }
         }
     } else {
+        double unused = 0.0;
         for (int vi = tid; vi < nvec; vi += kThreads) {
-            load8<T, kAligned>(xr + vi * 8, v[0]);
+            load_input8<T, kAligned, kMode>(xr, ur, g, g_bf16, vi, v[0], unused);
             uint2 out;
             sum_local += quant8(v[0], sa, out);
             *reinterpret_cast<uint2*>(qr + vi * 8) = out;
@@ -162,27 +221,63 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const int total = block_sum(sum_local, red_i);
     if (tid == 0) {
         q_rowsum[m] = total;
-        a_scale[m] = (amax == 0.0f) ? 0.0f : amax / 127.0f;
+        if (amax == 0.0f) {
+            a_scale[m] = 0.0f;
+        } else if constexpr (kMode == kPlain) {
+            a_scale[m] = amax / 127.0f;
+        } else {
+            const double r = 1.0 / sqrt(squares / static_cast<double>(K) + static_cast<double>(eps));
+            a_scale[m] = static_cast<float>(static_cast<double>(amax) * r / 127.0);
+        }
     }
 }
 
-template <typename T, bool kAligned>
-hipError_t launch_t(const T* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, float* a_scale,
-                    int32_t* q_rowsum, int Kp, hipStream_t stream) {
+template <typename T, bool kAligned, int kMode>
+hipError_t launch_t(const T* x, const T* up, int64_t M, int64_t K, int64_t ldx, const void* g, bool g_bf16,
+                    float eps, int8_t* q, float* a_scale, int32_t* q_rowsum, int Kp, hipStream_t stream) {
     const int nvec = static_cast<int>(K / 8);
     const dim3 grid(static_cast<unsigned>(M)), block(kThreads);
     const int vpt = (nvec + kThreads - 1) / kThreads;
+    const int k = static_cast<int>(K);
     if (vpt <= 1)
-        act_quant_kernel<T, 1, kAligned><<<grid, block, 0, stream>>>(x, ldx, (int)K, Kp, q, a_scale, q_rowsum);
+        act_quant_kernel<T, 1, kAligned, kMode>
+            <<<grid, block, 0, stream>>>(x, up, ldx, k, Kp, g, g_bf16, eps, q, a_scale, q_rowsum);
     else if (vpt <= 2)
-        act_quant_kernel<T, 2, kAligned><<<grid, block, 0, stream>>>(x, ldx, (int)K, Kp, q, a_scale, q_rowsum);
+        act_quant_kernel<T, 2, kAligned, kMode>
+            <<<grid, block, 0, stream>>>(x, up, ldx, k, Kp, g, g_bf16, eps, q, a_scale, q_rowsum);
     else if (vpt <= 4)
-        act_quant_kernel<T, 4, kAligned><<<grid, block, 0, stream>>>(x, ldx, (int)K, Kp, q, a_scale, q_rowsum);
+        act_quant_kernel<T, 4, kAligned, kMode>
+            <<<grid, block, 0, stream>>>(x, up, ldx, k, Kp, g, g_bf16, eps, q, a_scale, q_rowsum);
     else if (vpt <= 8)
-        act_quant_kernel<T, 8, kAligned><<<grid, block, 0, stream>>>(x, ldx, (int)K, Kp, q, a_scale, q_rowsum);
+        act_quant_kernel<T, 8, kAligned, kMode>
+            <<<grid, block, 0, stream>>>(x, up, ldx, k, Kp, g, g_bf16, eps, q, a_scale, q_rowsum);
     else
-        act_quant_kernel<T, 0, kAligned><<<grid, block, 0, stream>>>(x, ldx, (int)K, Kp, q, a_scale, q_rowsum);
+        act_quant_kernel<T, 0, kAligned, kMode>
+            <<<grid, block, 0, stream>>>(x, up, ldx, k, Kp, g, g_bf16, eps, q, a_scale, q_rowsum);
     return hipGetLastError();
+}
+
+template <int kMode>
+hipError_t launch_mode(const void* x, const void* up, bool x_bf16, int64_t M, int64_t K, int64_t ldx,
+                       const void* g, bool g_bf16, float eps, int8_t* q, float* a_scale, int32_t* q_rowsum,
+                       int64_t Kp, hipStream_t stream) {
+    const size_t esize = x_bf16 ? 2 : 4;
+    const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(up) % 16 == 0) &&
+                         ((ldx * esize) % 16 == 0);
+    if (x_bf16) {
+        auto* p = static_cast<const uint16_t*>(x);
+        auto* u = static_cast<const uint16_t*>(up);
+        return aligned ? launch_t<uint16_t, true, kMode>(p, u, M, K, ldx, g, g_bf16, eps, q, a_scale, q_rowsum,
+                                                          (int)Kp, stream)
+                       : launch_t<uint16_t, false, kMode>(p, u, M, K, ldx, g, g_bf16, eps, q, a_scale, q_rowsum,
+                                                           (int)Kp, stream);
+    }
+    auto* p = static_cast<const float*>(x);
+    auto* u = static_cast<const float*>(up);
+    return aligned ? launch_t<float, true, kMode>(p, u, M, K, ldx, g, g_bf16, eps, q, a_scale, q_rowsum, (int)Kp,
+                                                   stream)
+                   : launch_t<float, false, kMode>(p, u, M, K, ldx, g, g_bf16, eps, q, a_scale, q_rowsum, (int)Kp,
+                                                    stream);
 }
 
 }  // namespace
@@ -190,16 +285,18 @@ hipError_t launch_t(const T* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, fl
 hipError_t launch_act_quant(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx,
                             int8_t* q, float* a_scale, int32_t* q_rowsum, int64_t Kp,
                             hipStream_t stream) {
-    const size_t esize = x_bf16 ? 2 : 4;
-    const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && ((ldx * esize) % 16 == 0);
-    if (x_bf16) {
-        auto* p = static_cast<const uint16_t*>(x);
-        return aligned ? launch_t<uint16_t, true>(p, M, K, ldx, q, a_scale, q_rowsum, (int)Kp, stream)
-                       : launch_t<uint16_t, false>(p, M, K, ldx, q, a_scale, q_rowsum, (int)Kp, stream);
-    }
-    auto* p = static_cast<const float*>(x);
-    return aligned ? launch_t<float, true>(p, M, K, ldx, q, a_scale, q_rowsum, (int)Kp, stream)
-                   : launch_t<float, false>(p, M, K, ldx, q, a_scale, q_rowsum, (int)Kp, stream);
+    return launch_mode<kPlain>(x, nullptr, x_bf16, M, K, ldx, nullptr, false, 0.0f, q, a_scale, q_rowsum, Kp,
+                               stream);
+}
+
+hipError_t launch_norm_act_quant(const void* x, const void* up, bool x_bf16, int64_t M, int64_t K, int64_t ldx,
+                                 const void* norm_w, bool norm_bf16, float eps, int8_t* q, float* a_scale,
+                                 int32_t* q_rowsum, int64_t Kp, hipStream_t stream) {
+    if (up)
+        return launch_mode<kGatedNorm>(x, up, x_bf16, M, K, ldx, norm_w, norm_bf16, eps, q, a_scale, q_rowsum,
+                                       Kp, stream);
+    return launch_mode<kNorm>(x, nullptr, x_bf16, M, K, ldx, norm_w, norm_bf16, eps, q, a_scale, q_rowsum, Kp,
+                              stream);
 }
 
 }  // namespace bitnet

@@ -298,6 +298,34 @@ bitnet_status_t bitnet_act_quant(hipStream_t stream, const void* x, bitnet_dtype
     return ok();
 }
 
+static bitnet_status_t check_norm(const void* x, const void* up, bitnet_dtype_t x_dtype, const void* norm_w,
+                                  bitnet_dtype_t norm_dtype, float eps, const char* fn) {
+    if (!norm_w) return fail(BITNET_ERR_INVALID_ARG, "%s: norm_w is NULL", fn);
+    if (!valid_dtype(norm_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad norm_w dtype %d", fn, (int)norm_dtype);
+    if (!aligned(norm_w, norm_dtype == BITNET_F32 ? 4 : 2))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned norm_w", fn);
+    if (up && !aligned(up, x_dtype == BITNET_F32 ? 4 : 2)) return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned up", fn);
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+    (void)x;
+    return BITNET_OK;
+}
+
+bitnet_status_t bitnet_rmsnorm_act_quant(hipStream_t stream, const void* x, const void* up, bitnet_dtype_t x_dtype,
+                                         int64_t M, int64_t K, int64_t ldx, const void* norm_w,
+                                         bitnet_dtype_t norm_dtype, float eps, int8_t* q, float* a_scale,
+                                         int32_t* q_rowsum) {
+    const char* fn = "bitnet_rmsnorm_act_quant";
+    bitnet_status_t s = check_act_quant(x, x_dtype, M, K, ldx, q, a_scale, q_rowsum, fn);
+    if (s != BITNET_OK) return s;
+    if ((s = check_norm(x, up, x_dtype, norm_w, norm_dtype, eps, fn)) != BITNET_OK) return s;
+    hipError_t e = bitnet::launch_norm_act_quant(x, up, x_dtype == BITNET_BF16, M, K, ldx, norm_w,
+                                                 norm_dtype == BITNET_BF16, eps, q, a_scale, q_rowsum,
+                                                 padded_k(K), stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
 bitnet_status_t bitnet_linear_forward(hipStream_t stream, const int8_t* q, const float* a_scale,
                                       const int32_t* q_rowsum, int64_t M, int64_t K, const uint8_t* packed,
                                       const float* w_scale, int64_t N, void* y, bitnet_dtype_t y_dtype, int64_t ldy,

@@ -13,6 +13,12 @@ hipError_t launch_act_quant(const void* x, bool x_bf16, int64_t M, int64_t K, in
                             int8_t* q, float* a_scale, int32_t* q_rowsum, int64_t Kp,
                             hipStream_t stream);
 
+// ActQuant(RMSNorm(input, norm_w)) of M tokens: input = x, or silu(x) * up
+// when up is given (same dtype and row stride as x); norm_w has K entries.
+hipError_t launch_norm_act_quant(const void* x, const void* up, bool x_bf16, int64_t M, int64_t K, int64_t ldx,
+                                 const void* norm_w, bool norm_bf16, float eps, int8_t* q, float* a_scale,
+                                 int32_t* q_rowsum, int64_t Kp, hipStream_t stream);
+
 // Linear on quantised operands, M <= 16: one streaming pass over packed.
 hipError_t launch_gemv(const int8_t* q, const float* a_scale, const int32_t* q_rowsum,
                        int64_t M, int64_t Kp, const uint8_t* packed, const float* w_scale,

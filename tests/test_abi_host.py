@@ -82,6 +82,18 @@ def test_argument_errors_launch_nothing():
         (L.bitnet_linear_forward, (None, p16, p16, p16, 1, 16, p16, p16, 4, p16, 5, 4, None), "dtype"),
         (L.bitnet_bitlinear_forward, (None, p16, _lib.BF16, 2, 32, 32, p16, p16, 4, p16, _lib.F32, 2,
                                       p16, p16, p16), "ldy"),
+        (L.bitnet_rmsnorm_act_quant, (None, p16, None, _lib.BF16, 1, 16, 16, None, _lib.BF16, 1e-6,
+                                      p16, p16, p16), "norm_w is NULL"),
+        (L.bitnet_rmsnorm_act_quant, (None, p16, None, _lib.BF16, 1, 16, 16, p16, 3, 1e-6, p16, p16, p16),
+         "norm_w dtype"),
+        (L.bitnet_rmsnorm_act_quant, (None, p16, None, _lib.BF16, 1, 16, 16, p16, _lib.BF16, -1.0,
+                                      p16, p16, p16), "eps"),
+        (L.bitnet_rmsnorm_act_quant, (None, p16, None, _lib.BF16, 1, 16, 16, p16, _lib.BF16, float("nan"),
+                                      p16, p16, p16), "eps"),
+        (L.bitnet_rmsnorm_act_quant, (None, p16, p16 + 1, _lib.BF16, 1, 16, 16, p16, _lib.BF16, 1e-6,
+                                      p16, p16, p16), "misaligned up"),
+        (L.bitnet_rmsnorm_act_quant, (None, p16, None, _lib.BF16, 1, 20, 20, p16, _lib.BF16, 1e-6,
+                                      p16, p16, p16), "K=20"),
         (L.bitnet_pack_weights, (_lib.MEM_HOST, None, p16, _lib.BF16, 4, 16, 16,
                                  (ctypes.c_int64 * 2)(2, 1), 2, p16, p16, None, None), "segment"),
         (L.bitnet_pack_weights, (_lib.MEM_HOST, None, p16, _lib.BF16, 4, 16, 16,

@@ -125,6 +125,97 @@ def test_device_pack_rejects_non_finite():
     assert e.value.status == _lib.ERR_NONFINITE
 
 
+# ------------------------------------------------------ RMSNorm -> ActQuant
+
+def _norm_weight(K: int, seed: int, dtype) -> torch.Tensor:
+    g = 1.0 + 0.2 * wl.draw_activation((1, K), seed=seed).float()[0]
+    return g.to(dtype)
+
+
+def _check_scale(a_dev: torch.Tensor, a_orc: np.ndarray):
+    """a_scale: the codes decide nothing here; the fp64 sums differ only in order, so
+    the fp32 result is expected bit-exact and must be within 1e-5 relative."""
+    a = a_dev.cpu().numpy()
+    rel = np.abs(a.astype(np.float64) - a_orc) / np.maximum(np.abs(a_orc.astype(np.float64)), 1e-30)
+    assert np.all((rel <= 1e-5) | (a == a_orc)), float(rel.max())
+
+
+def check_y_tol(y_dev: torch.Tensor, y_orc: np.ndarray, rel_tol: float = 1e-5):
+    y = y_dev.cpu().numpy().astype(np.float64)
+    rel = np.abs(y - y_orc) / np.maximum(np.abs(y_orc.astype(np.float64)), 1e-30)
+    assert np.all((rel <= rel_tol) | (y == y_orc)), float(rel.max())
+
+
+@pytest.mark.parametrize("M,K,dist", [
+    (1, 16, "normal"), (1, 2560, "normal_outliers"), (3, 1152, "normal"), (17, 4304, "student_t_channels"),
+    (5, 6912, "normal"), (2, 20480, "normal"), (64, 1024, "normal_outliers"),
+])
+@pytest.mark.parametrize("x_dtype,g_dtype", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
+                                             (torch.bfloat16, torch.float32)])
+def test_rmsnorm_act_quant(orc, M, K, dist, x_dtype, g_dtype):
+    x = wl.draw_activation((M, K), seed=M * 13 + K, dist=dist)
+    if M > 2:
+        x[1] = 0                                   # an all-zero token
+        x[2] *= 1e-5                               # eps dominates
+    g = _norm_weight(K, K + 1, g_dtype)
+    xd = x.to(DEV).to(x_dtype)
+    q, a, r = tw.rmsnorm_act_quant(xd, g.to(DEV), 1e-6)
+    xo = bits(x.to(x_dtype)) if x_dtype == torch.bfloat16 else x.float().numpy()
+    go = bits(g) if g_dtype == torch.bfloat16 else g.numpy()
+    qo, ao, ro = orc.rms_act_quant(xo, go, 1e-6)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(r.cpu().numpy(), ro)
+    _check_scale(a, ao)
+
+
+@pytest.mark.parametrize("M,K", [(1, 6912), (4, 2048), (9, 16), (2, 20480)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gated_rmsnorm_act_quant(orc, M, K, dtype):
+    """The down projection's input: silu(gate) * up, then RMSNorm and ActQuant;
+    gate and up are strided views of one [M, 2K] buffer (the fused gate|up output)."""
+    gu = (wl.draw_activation((M, 2 * K), seed=K + M, dist="normal").float() * 3).to(dtype)
+    g = _norm_weight(K, K + 7, torch.bfloat16)
+    gud = gu.to(DEV)
+    q, a, r = tw.rmsnorm_act_quant(gud[:, :K], g.to(DEV), 1e-6, up=gud[:, K:])
+    if dtype == torch.bfloat16:
+        go, uo = bits(gu[:, :K].contiguous()), bits(gu[:, K:].contiguous())
+    else:
+        go, uo = gu[:, :K].contiguous().numpy(), gu[:, K:].contiguous().numpy()
+    qo, ao, ro = orc.swiglu_rms_act_quant(go, uo, bits(g), 1e-6)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(r.cpu().numpy(), ro)
+    _check_scale(a, ao)
+
+
+def test_rmsnorm_strided_unaligned_and_eps_zero(orc):
+    """x rows at an odd fp32 stride (the unaligned load path), eps = 0, fp32 weight."""
+    M, K = 6, 1152
+    base = wl.draw_activation((M, K + 3), seed=77).float()
+    x = base.to(DEV)[:, 1:K + 1]
+    g = _norm_weight(K, 5, torch.float32)
+    q, a, r = tw.rmsnorm_act_quant(x, g.to(DEV), 0.0)
+    qo, ao, ro = orc.rms_act_quant(base[:, 1:K + 1].contiguous().numpy(), g.numpy(), 0.0)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(r.cpu().numpy(), ro)
+    _check_scale(a, ao)
+
+
+def test_rmsnorm_then_linear(orc):
+    """Normalised, quantised tokens through the decode and GEMM paths against the
+    oracle's integer dot and epilogue on its own codes."""
+    for M, N, K in ((1, 640, 2560), (40, 257, 1152)):
+        x, W = wl.random_case(2100 + M, M, N, K, x_dist="normal_outliers")
+        g = _norm_weight(K, 9, torch.bfloat16)
+        pw = tw.pack(W.to(DEV))
+        q, a, r = tw.rmsnorm_act_quant(x.to(DEV), g.to(DEV), 1e-6)
+        y, acc = tw.linear(q, a, r, pw, acc_debug=True)
+        qo, ao, _ = orc.rms_act_quant(bits(x), bits(g), 1e-6)
+        t, ws, _, _ = orc.weight_quant(bits(W))
+        acc_o = orc.int_dot(qo, t)
+        assert np.array_equal(acc.cpu().numpy(), acc_o)
+        check_y_tol(y, orc.epilogue(acc_o, ao, ws))
+
+
 # -------------------------------------------------------------------- linear
 
 LINEAR_CASES = [
