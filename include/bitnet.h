@@ -196,6 +196,23 @@ bitnet_status_t bitnet_bitlinear_forward(hipStream_t stream,
                                          int8_t* q, float* a_scale, int32_t* q_rowsum);
 
 /*
+ * bitnet_bitlinear_forward with the projection's input norm first:
+ * y = linear(ActQuant(RMSNorm(h, norm_w)), WeightQuant(W)) where h = x, or
+ * h = silu(x) * up when up is given [Guide s3.1, s2].  x, up, norm_w and eps
+ * as in bitnet_rmsnorm_act_quant; every other argument as in
+ * bitnet_bitlinear_forward, including the single-launch condition (for the
+ * single launch, up and norm_w must also be 16-byte aligned).  q, a_scale
+ * and q_rowsum receive bitnet_rmsnorm_act_quant's results.
+ */
+bitnet_status_t bitnet_rmsnorm_bitlinear_forward(hipStream_t stream,
+                                                 const void* x, const void* up, bitnet_dtype_t x_dtype,
+                                                 int64_t M, int64_t K, int64_t ldx,
+                                                 const void* norm_w, bitnet_dtype_t norm_dtype, float eps,
+                                                 const uint8_t* packed, const float* w_scale, int64_t N,
+                                                 void* y, bitnet_dtype_t y_dtype, int64_t ldy,
+                                                 int8_t* q, float* a_scale, int32_t* q_rowsum);
+
+/*
  * Many independent decode-size BitLinears in one launch.  A decoder streams
  * the weights of many projections per token (one position at a time, M = 1:
  * [BitVLA s3]); each matrix alone moves only a few MB, far too little to
@@ -236,6 +253,25 @@ int64_t bitnet_group_table_bytes(int32_t count);
 bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t* items, int32_t count,
                                   int64_t M, bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype,
                                   void* table_dev, int64_t table_bytes, bitnet_group_plan_t* plan);
+
+/* Input norm of one grouped item (see bitnet_rmsnorm_act_quant): norm_w NULL
+ * means none; otherwise norm_w [K] (16-byte aligned), its dtype and eps, and
+ * up NULL or [M, K] with the item's x dtype and row stride (16-byte aligned)
+ * for the gated input silu(x) * up. */
+typedef struct {
+    const void* up;
+    const void* norm_w;
+    bitnet_dtype_t norm_dtype;
+    float eps;
+} bitnet_group_norm_t;
+
+/* bitnet_group_plan with an input norm per item: norms[i] applies to items[i]
+ * (count entries, host memory); the launch then quantises each item's
+ * normalised input, with bitnet_rmsnorm_act_quant's results. */
+bitnet_status_t bitnet_group_plan_rmsnorm(hipStream_t stream, const bitnet_group_item_t* items,
+                                          const bitnet_group_norm_t* norms, int32_t count,
+                                          int64_t M, bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype,
+                                          void* table_dev, int64_t table_bytes, bitnet_group_plan_t* plan);
 
 /*
  * Run every item of a plan in one kernel launch on `stream`: each workgroup

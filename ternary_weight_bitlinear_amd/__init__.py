@@ -174,6 +174,33 @@ def bitlinear(x: torch.Tensor, w: PackedWeight, out_dtype=torch.float32, out: to
     return y
 
 
+def rmsnorm_bitlinear(x: torch.Tensor, norm_w: torch.Tensor, w: PackedWeight, eps: float = 1e-6,
+                      up: torch.Tensor | None = None, out_dtype=torch.float32, out: torch.Tensor | None = None,
+                      workspace=None):
+    """y = linear(ActQuant(RMSNorm(h, norm_w)), WeightQuant(W)) with h = x, or h = silu(x) * up."""
+    ldx = _rows(x, "x")
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError("x and the packed weight disagree on K")
+    if norm_w.shape != (K,) or not norm_w.is_contiguous():
+        raise ValueError("norm_w must be a contiguous [K] tensor")
+    if up is not None and (up.shape != x.shape or up.dtype != x.dtype or _rows(up, "up") != ldx):
+        raise ValueError("up must match x in shape, dtype and row stride")
+    if workspace is None:
+        workspace = (torch.empty((M, padded_k(K)), dtype=torch.int8, device=x.device),
+                     torch.empty(M, dtype=torch.float32, device=x.device),
+                     torch.empty(M, dtype=torch.int32, device=x.device))
+    q, a_scale, rowsum = workspace
+    y = out if out is not None else torch.empty((M, w.N), dtype=out_dtype, device=x.device)
+    ldy = _rows(y, "y")
+    with torch.cuda.device(x.device):
+        _lib.check(_lib.lib().bitnet_rmsnorm_bitlinear_forward(
+            _stream(x), x.data_ptr(), up.data_ptr() if up is not None else None, _dtype(x), M, K, ldx,
+            norm_w.data_ptr(), _dtype(norm_w), float(eps), w.packed.data_ptr(), w.w_scale.data_ptr(),
+            w.N, y.data_ptr(), _dtype(y), ldy, q.data_ptr(), a_scale.data_ptr(), rowsum.data_ptr()))
+    return y
+
+
 class GroupedBitLinear:
     """Many independent decode-size BitLinears (shared M <= 16) run as one launch.
 
@@ -181,9 +208,13 @@ class GroupedBitLinear:
     plan keeps pointers to them, so they must stay alive and in place.  Calling
     the object writes y_i = linear(ActQuant(x_i), WeightQuant(W_i)) for all i."""
 
-    def __init__(self, items):
+    def __init__(self, items, norms=None):
+        """``norms``: None, or one entry per item, each None or (norm_w [K], up or None, eps):
+        the item's input is then RMSNorm(x or silu(x) * up, norm_w) before ActQuant."""
         if not items:
             raise ValueError("need at least one item")
+        if norms is not None and len(norms) != len(items):
+            raise ValueError("norms needs one entry per item")
         x0 = items[0][0]
         M = x0.shape[0]
         self._keep = list(items)
@@ -193,14 +224,34 @@ class GroupedBitLinear:
                 raise ValueError(f"item {i}: shapes do not match")
             arr[i] = _lib.GroupItem(x.data_ptr(), _rows(x, "x"), w.packed.data_ptr(), w.w_scale.data_ptr(),
                                     y.data_ptr(), _rows(y, "y"), w.N, w.K)
+        nrm = None
+        if norms is not None:
+            nrm = (_lib.GroupNorm * len(items))()
+            for i, entry in enumerate(norms):
+                if entry is None:
+                    continue
+                g, up, eps = entry
+                x = items[i][0]
+                if g.shape != (x.shape[1],) or not g.is_contiguous():
+                    raise ValueError(f"item {i}: norm_w must be a contiguous [K] tensor")
+                if up is not None and (up.shape != x.shape or up.dtype != x.dtype or _rows(up, "up") != _rows(x, "x")):
+                    raise ValueError(f"item {i}: up must match x in shape, dtype and row stride")
+                nrm[i] = _lib.GroupNorm(up.data_ptr() if up is not None else None, g.data_ptr(), _dtype(g),
+                                        float(eps))
+                self._keep.append((g, up))
         nbytes = int(_lib.lib().bitnet_group_table_bytes(len(items)))
         self.table = torch.empty(nbytes, dtype=torch.uint8, device=x0.device)
         self.plan = _lib.GroupPlan()
         self.device = x0.device
         with torch.cuda.device(x0.device):
-            _lib.check(_lib.lib().bitnet_group_plan(
-                _stream(x0), ctypes.cast(arr, ctypes.c_void_p), len(items), M, _dtype(x0),
-                _dtype(items[0][2]), self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
+            if nrm is None:
+                _lib.check(_lib.lib().bitnet_group_plan(
+                    _stream(x0), ctypes.cast(arr, ctypes.c_void_p), len(items), M, _dtype(x0),
+                    _dtype(items[0][2]), self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
+            else:
+                _lib.check(_lib.lib().bitnet_group_plan_rmsnorm(
+                    _stream(x0), ctypes.cast(arr, ctypes.c_void_p), ctypes.cast(nrm, ctypes.c_void_p), len(items),
+                    M, _dtype(x0), _dtype(items[0][2]), self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
         self.bytes = sum(w.N * w.K // 4 for _, w, _ in items)
         # which kernel the plan launches: "dynamic", "stream" or "persistent"
         self.kernel = _lib.lib().bitnet_group_plan_kernel(ctypes.byref(self.plan)).decode()

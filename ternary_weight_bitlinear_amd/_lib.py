@@ -30,8 +30,13 @@ SIGNATURES = {
                                              _vp, ctypes.c_int, _i64, _vp]),
     "bitnet_bitlinear_forward": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp,
                                                 _i64, _vp, ctypes.c_int, _i64, _vp, _vp, _vp]),
+    "bitnet_rmsnorm_bitlinear_forward": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp,
+                                                        ctypes.c_int, ctypes.c_float, _vp, _vp, _i64, _vp,
+                                                        ctypes.c_int, _i64, _vp, _vp, _vp]),
     "bitnet_group_table_bytes": (_i64, [_i32]),
     "bitnet_group_plan": (ctypes.c_int, [_vp, _vp, _i32, _i64, ctypes.c_int, ctypes.c_int, _vp, _i64, _vp]),
+    "bitnet_group_plan_rmsnorm": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, ctypes.c_int, ctypes.c_int, _vp, _i64,
+                                                 _vp]),
     "bitnet_bitlinear_grouped": (ctypes.c_int, [_vp, _vp]),
     "bitnet_group_plan_kernel": (ctypes.c_char_p, [_vp]),
     "bitnet_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -43,6 +48,11 @@ class GroupItem(ctypes.Structure):
     """bitnet_group_item_t."""
     _fields_ = [("x", _vp), ("ldx", _i64), ("packed", _vp), ("w_scale", _vp), ("y", _vp),
                 ("ldy", _i64), ("N", _i64), ("K", _i64)]
+
+
+class GroupNorm(ctypes.Structure):
+    """bitnet_group_norm_t."""
+    _fields_ = [("up", _vp), ("norm_w", _vp), ("norm_dtype", ctypes.c_int), ("eps", ctypes.c_float)]
 
 
 class GroupPlan(ctypes.Structure):

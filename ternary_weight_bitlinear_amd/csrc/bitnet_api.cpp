@@ -337,22 +337,26 @@ bitnet_status_t bitnet_linear_forward(hipStream_t stream, const int8_t* q, const
     return run_linear(stream, q, a_scale, q_rowsum, M, K, packed, w_scale, N, y, y_dtype, ldy, acc_debug, fn);
 }
 
-bitnet_status_t bitnet_bitlinear_forward(hipStream_t stream, const void* x, bitnet_dtype_t x_dtype, int64_t M,
-                                         int64_t K, int64_t ldx, const uint8_t* packed, const float* w_scale,
-                                         int64_t N, void* y, bitnet_dtype_t y_dtype, int64_t ldy, int8_t* q,
-                                         float* a_scale, int32_t* q_rowsum) {
-    const char* fn = "bitnet_bitlinear_forward";
+static bitnet_status_t bitlinear_impl(hipStream_t stream, const void* x, const void* up, bitnet_dtype_t x_dtype,
+                                      int64_t M, int64_t K, int64_t ldx, const void* norm_w,
+                                      bitnet_dtype_t norm_dtype, float eps, const uint8_t* packed,
+                                      const float* w_scale, int64_t N, void* y, bitnet_dtype_t y_dtype, int64_t ldy,
+                                      int8_t* q, float* a_scale, int32_t* q_rowsum, const char* fn) {
     bitnet_status_t s = check_act_quant(x, x_dtype, M, K, ldx, q, a_scale, q_rowsum, fn);
     if (s != BITNET_OK) return s;
+    if (norm_w && (s = check_norm(x, up, x_dtype, norm_w, norm_dtype, eps, fn)) != BITNET_OK) return s;
     s = check_linear(q, a_scale, q_rowsum, M, K, packed, w_scale, N, y, y_dtype, ldy, fn);
     if (s != BITNET_OK) return s;
     const int64_t Kp = padded_k(K);
     const int64_t esize = x_dtype == BITNET_BF16 ? 2 : 4;
-    const bool fuse = M <= kGemvMaxM && M * Kp <= kFusedLdsBytes && aligned(x, 16) && (ldx * esize) % 16 == 0;
+    const bool fuse = M <= kGemvMaxM && M * Kp <= kFusedLdsBytes && aligned(x, 16) && (ldx * esize) % 16 == 0 &&
+                      (!up || aligned(up, 16)) && (!norm_w || aligned(norm_w, 16));
     hipError_t e;
     if (fuse) {
         bitnet::GemvProblem p{};
         p.x = x; p.ldx = ldx;
+        p.up = norm_w ? up : nullptr;
+        p.norm_w = norm_w; p.eps = eps; p.norm_bf16 = norm_dtype == BITNET_BF16;
         p.q_out = q; p.a_scale_out = a_scale; p.rowsum_out = q_rowsum;
         p.packed = packed; p.w_scale = w_scale; p.y = y; p.ldy = ldy;
         p.M = (int)M; p.N = (int)N; p.K = (int)K; p.Kp = (int)Kp;
@@ -360,9 +364,31 @@ bitnet_status_t bitnet_bitlinear_forward(hipStream_t stream, const void* x, bitn
         if (e != hipSuccess) return hip_fail(e, fn);
         return ok();
     }
-    e = bitnet::launch_act_quant(x, x_dtype == BITNET_BF16, M, K, ldx, q, a_scale, q_rowsum, Kp, stream);
+    e = norm_w ? bitnet::launch_norm_act_quant(x, up, x_dtype == BITNET_BF16, M, K, ldx, norm_w,
+                                               norm_dtype == BITNET_BF16, eps, q, a_scale, q_rowsum, Kp, stream)
+               : bitnet::launch_act_quant(x, x_dtype == BITNET_BF16, M, K, ldx, q, a_scale, q_rowsum, Kp, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return run_linear(stream, q, a_scale, q_rowsum, M, K, packed, w_scale, N, y, y_dtype, ldy, nullptr, fn);
+}
+
+bitnet_status_t bitnet_bitlinear_forward(hipStream_t stream, const void* x, bitnet_dtype_t x_dtype, int64_t M,
+                                         int64_t K, int64_t ldx, const uint8_t* packed, const float* w_scale,
+                                         int64_t N, void* y, bitnet_dtype_t y_dtype, int64_t ldy, int8_t* q,
+                                         float* a_scale, int32_t* q_rowsum) {
+    return bitlinear_impl(stream, x, nullptr, x_dtype, M, K, ldx, nullptr, BITNET_F32, 0.0f, packed, w_scale, N, y,
+                          y_dtype, ldy, q, a_scale, q_rowsum, "bitnet_bitlinear_forward");
+}
+
+bitnet_status_t bitnet_rmsnorm_bitlinear_forward(hipStream_t stream, const void* x, const void* up,
+                                                 bitnet_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                                 const void* norm_w, bitnet_dtype_t norm_dtype, float eps,
+                                                 const uint8_t* packed, const float* w_scale, int64_t N, void* y,
+                                                 bitnet_dtype_t y_dtype, int64_t ldy, int8_t* q, float* a_scale,
+                                                 int32_t* q_rowsum) {
+    const char* fn = "bitnet_rmsnorm_bitlinear_forward";
+    if (!norm_w) return fail(BITNET_ERR_INVALID_ARG, "%s: norm_w is NULL", fn);
+    return bitlinear_impl(stream, x, up, x_dtype, M, K, ldx, norm_w, norm_dtype, eps, packed, w_scale, N, y,
+                          y_dtype, ldy, q, a_scale, q_rowsum, fn);
 }
 
 // Kernels of a grouped plan.  BITNET_GROUP_KERNEL=persistent, read when a
@@ -379,10 +405,10 @@ int64_t bitnet_group_table_bytes(int32_t count) {
     return static_cast<int64_t>(count) * static_cast<int64_t>(sizeof(bitnet::GemvProblem));
 }
 
-bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t* items, int32_t count, int64_t M,
-                                  bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype, void* table_dev,
-                                  int64_t table_bytes, bitnet_group_plan_t* plan) {
-    const char* fn = "bitnet_group_plan";
+static bitnet_status_t group_plan_impl(hipStream_t stream, const bitnet_group_item_t* items,
+                                       const bitnet_group_norm_t* norms, int32_t count, int64_t M,
+                                       bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype, void* table_dev,
+                                       int64_t table_bytes, bitnet_group_plan_t* plan, const char* fn) {
     if (count <= 0 || !items || !plan || !table_dev)
         return fail(BITNET_ERR_INVALID_ARG, "%s: need count > 0, items, table_dev and plan", fn);
     if (!aligned(table_dev, 16) || table_bytes < bitnet_group_table_bytes(count))
@@ -409,8 +435,18 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
         if (static_cast<int64_t>(bitnet::gemv_group_lds(M, Kp)) > kGroupLdsBytes)
             return fail(BITNET_ERR_UNSUPPORTED, "%s: M tokens of K=%lld need more than %lld bytes of LDS", where,
                         (long long)it.K, (long long)kGroupLdsBytes);
+        const bitnet_group_norm_t* nm = norms && norms[i].norm_w ? &norms[i] : nullptr;
+        if (nm) {
+            if ((s = check_norm(it.x, nm->up, x_dtype, nm->norm_w, nm->norm_dtype, nm->eps, where)) != BITNET_OK)
+                return s;
+            if (!aligned(nm->norm_w, 16) || (nm->up && !aligned(nm->up, 16)))
+                return fail(BITNET_ERR_INVALID_ARG, "%s: norm_w and up must be 16-byte aligned", where);
+        }
         bitnet::GemvProblem& p = table[static_cast<size_t>(i)];
         p = bitnet::GemvProblem{};
+        if (nm) {
+            p.up = nm->up; p.norm_w = nm->norm_w; p.eps = nm->eps; p.norm_bf16 = nm->norm_dtype == BITNET_BF16;
+        }
         p.x = it.x; p.ldx = it.ldx; p.packed = it.packed; p.w_scale = it.w_scale;
         p.y = it.y; p.ldy = it.ldy;
         p.M = (int)M; p.N = (int)it.N; p.K = (int)it.K; p.Kp = (int)Kp;
@@ -447,6 +483,22 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
                       (static_cast<int64_t>(kind) << 16) | (static_cast<int64_t>(grid) << 32);
     plan->opaque[7] = steps;
     return ok();
+}
+
+bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t* items, int32_t count, int64_t M,
+                                  bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype, void* table_dev,
+                                  int64_t table_bytes, bitnet_group_plan_t* plan) {
+    return group_plan_impl(stream, items, nullptr, count, M, x_dtype, y_dtype, table_dev, table_bytes, plan,
+                           "bitnet_group_plan");
+}
+
+bitnet_status_t bitnet_group_plan_rmsnorm(hipStream_t stream, const bitnet_group_item_t* items,
+                                          const bitnet_group_norm_t* norms, int32_t count, int64_t M,
+                                          bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype, void* table_dev,
+                                          int64_t table_bytes, bitnet_group_plan_t* plan) {
+    if (!norms) return fail(BITNET_ERR_INVALID_ARG, "bitnet_group_plan_rmsnorm: norms is NULL");
+    return group_plan_impl(stream, items, norms, count, M, x_dtype, y_dtype, table_dev, table_bytes, plan,
+                           "bitnet_group_plan_rmsnorm");
 }
 
 bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_plan_t* plan) {

@@ -21,6 +21,10 @@ struct GemvProblem {
     void* y;                   // [M, N], row stride ldy
     int64_t ldy;
     int32_t* acc_debug;        // optional [M][N]
+    const void* up;            // fused, optional: input is silu(x) * up (x's dtype and stride)
+    const void* norm_w;        // fused, optional: RMSNorm weight [K] applied before ActQuant
+    float eps;                 // fused: RMSNorm epsilon
+    int32_t norm_bf16;         // fused: norm_w is bf16 (else fp32)
     int32_t M, N, K, Kp;
     int32_t tile0;             // grouped: global index of this problem's first 64-row tile
     int32_t ntiles;            // grouped: tiles of this problem

@@ -100,34 +100,83 @@ __host__ __device__ __forceinline__ int padded_q_row(int Kp) {
     return (Kp + 256 * kBatch - 1) / (256 * kBatch) * (256 * kBatch);
 }
 
+// 8 values whose codes are taken, of vector vi of token row m: x, or with a
+// norm weight z = h * g where h = x or h = silu(x) * up (fp64, rounded once to
+// fp32); `squares` gathers the fp64 sum of h^2 that RMSNorm needs.  The norm
+// factor r > 0 is common to the token, so the codes of RMSNorm(h) are those of
+// z and r enters a_scale only ("BitNet-Embeddings-0.6B/270M: I2_S Conversion
+// and Inference Optimization Guide", s3.1: each projection normalises its
+// input with its own weight before ActQuant).
+template <bool kXBf16>
+__device__ __forceinline__ void load_input8(const GemvProblem& p, const void* xrow, const void* urow, int vi,
+                                            float (&z)[8], double& squares) {
+    load_x8<kXBf16>(xrow, vi, z);
+    if (!p.norm_w) return;
+    if (urow) {
+        float u[8];
+        load_x8<kXBf16>(urow, vi, u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double a = z[e];
+            z[e] = static_cast<float>(a / (1.0 + exp(-a)) * static_cast<double>(u[e]));
+        }
+    }
+    float g[8];
+    if (p.norm_bf16) {
+        const u32x4 w = gload<u32x4>(static_cast<const char*>(p.norm_w) + 16 * vi);
+        g[0] = bf16_lo(w.x); g[1] = bf16_hi(w.x); g[2] = bf16_lo(w.y); g[3] = bf16_hi(w.y);
+        g[4] = bf16_lo(w.z); g[5] = bf16_hi(w.z); g[6] = bf16_lo(w.w); g[7] = bf16_hi(w.w);
+    } else {
+        const f32x4 lo = gload<f32x4>(static_cast<const char*>(p.norm_w) + 32 * vi);
+        const f32x4 hi = gload<f32x4>(static_cast<const char*>(p.norm_w) + 32 * vi + 16);
+        g[0] = lo.x; g[1] = lo.y; g[2] = lo.z; g[3] = lo.w; g[4] = hi.x; g[5] = hi.y; g[6] = hi.z; g[7] = hi.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        squares += static_cast<double>(z[e]) * static_cast<double>(z[e]);
+        z[e] = z[e] * g[e];
+    }
+}
+
 template <bool kXBf16, int kCache, bool kPerm>
 __device__ void quantise_tokens(const GemvProblem& p, int8_t* q_lds, float* as_lds, int* rs_lds,
-                                float* red_f, int* red_i, bool store) {
+                                float* red_f, int* red_i, double* red_d, bool store) {
     const int ldq = kPerm ? padded_q_row(p.Kp) : p.Kp;
     const int tid = threadIdx.x;
     const int nvec = p.K / 8;
     const size_t esize = kXBf16 ? 2 : 4;
+    const bool norm = p.norm_w != nullptr;
     for (int m = 0; m < p.M; ++m) {
         const void* xrow = static_cast<const char*>(p.x) + static_cast<int64_t>(m) * p.ldx * esize;
+        const void* urow = p.up ? static_cast<const char*>(p.up) + static_cast<int64_t>(m) * p.ldx * esize
+                                : nullptr;
         float cache[kCache][8];
         float amax = 0.0f;
+        double squares = 0.0;
 #pragma unroll
         for (int i = 0; i < kCache; ++i) {
             const int vi = tid + i * kThreads;
             if (vi < nvec) {
-                load_x8<kXBf16>(xrow, vi, cache[i]);
+                load_input8<kXBf16>(p, xrow, urow, vi, cache[i], squares);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(cache[i][e]));
             }
         }
         for (int vi = tid + kCache * kThreads; vi < nvec; vi += kThreads) {
             float v[8];
-            load_x8<kXBf16>(xrow, vi, v);
+            load_input8<kXBf16>(p, xrow, urow, vi, v, squares);
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
         }
         amax = wave_max(amax);
-        if (tid % kWave == 0) red_f[tid / kWave] = amax;
+        if (norm) {
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) squares += __shfl_xor(squares, o, kWave);
+        }
+        if (tid % kWave == 0) {
+            red_f[tid / kWave] = amax;
+            red_d[tid / kWave] = squares;
+        }
         __syncthreads();
         amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
         const float sa = (amax == 0.0f) ? 0.0f : 127.0f / amax;
@@ -156,7 +205,8 @@ __device__ void quantise_tokens(const GemvProblem& p, int8_t* q_lds, float* as_l
                         if (c == i) packed8 = quant8(cache[c]);
                 } else {
                     float v[8];
-                    load_x8<kXBf16>(xrow, vi, v);
+                    double unused = 0.0;
+                    load_input8<kXBf16>(p, xrow, urow, vi, v, unused);
                     packed8 = quant8(v);
                 }
             }
@@ -173,7 +223,16 @@ __device__ void quantise_tokens(const GemvProblem& p, int8_t* q_lds, float* as_l
         __syncthreads();
         if (tid == 0) {
             const int total = red_i[0] + red_i[1] + red_i[2] + red_i[3];
-            const float as = (amax == 0.0f) ? 0.0f : amax / 127.0f;
+            float as = 0.0f;
+            if (amax != 0.0f) {
+                if (norm) {
+                    const double ss = red_d[0] + red_d[1] + red_d[2] + red_d[3];
+                    const double r = 1.0 / sqrt(ss / static_cast<double>(p.K) + static_cast<double>(p.eps));
+                    as = static_cast<float>(static_cast<double>(amax) * r / 127.0);
+                } else {
+                    as = amax / 127.0f;
+                }
+            }
             as_lds[m] = as;
             rs_lds[m] = total;
             if (store) {
@@ -181,7 +240,7 @@ __device__ void quantise_tokens(const GemvProblem& p, int8_t* q_lds, float* as_l
                 gstore<int32_t>(p.rowsum_out + m, total);
             }
         }
-        __syncthreads();   // red_f / red_i are reused by the next token
+        __syncthreads();   // red_f / red_i / red_d are reused by the next token
     }
 }
 
@@ -244,6 +303,7 @@ __global__ __launch_bounds__(kThreads) void gemv_splitk_kernel(GemvProblem p) {
     __shared__ int part[kWaves][16][17];
     __shared__ float red_f[kWaves];
     __shared__ int red_i[kWaves];
+    __shared__ double red_d[kWaves];
     __shared__ float as_lds[16];
     __shared__ int rs_lds[16];
     constexpr int kUnroll = 4;
@@ -271,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void gemv_splitk_kernel(GemvProblem p) {
     };
     load_b(0);   // in flight during the fused quantisation
     if constexpr (kFused)
-        quantise_tokens<kXBf16, 4, false>(p, q_lds, as_lds, rs_lds, red_f, red_i,
+        quantise_tokens<kXBf16, 4, false>(p, q_lds, as_lds, rs_lds, red_f, red_i, red_d,
                                           p.q_out != nullptr && blockIdx.x == 0);
 
     v4i acc = {0, 0, 0, 0};
@@ -390,6 +450,7 @@ __global__ __launch_bounds__(kThreads) void gemv_persistent_kernel(GemvProblem s
     extern __shared__ __attribute__((aligned(16))) int8_t q_lds[];   // [M][padded_q_row(Kp)], permuted
     __shared__ float red_f[kWaves];
     __shared__ int red_i[kWaves];
+    __shared__ double red_d[kWaves];
     __shared__ float as_lds[16];
     __shared__ int rs_lds[16];
 
@@ -530,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void gemv_persistent_kernel(GemvProblem s
         load_batch(bufB);
         prefetch_epilogue();
         if constexpr (kFused)
-            quantise_tokens<kXBf16, 2, true>(P, q_lds, as_lds, rs_lds, red_f, red_i,
+            quantise_tokens<kXBf16, 2, true>(P, q_lds, as_lds, rs_lds, red_f, red_i, red_d,
                                              P.q_out != nullptr && seg_begin == P.tile0);
         else
             stage_tokens(P, q_lds, as_lds, rs_lds);
@@ -579,7 +640,7 @@ __shared__ __attribute__((aligned(1024))) int8_t g_stream_ring[kDepth * kThreads
 
 // Token rows of the workgroup's problems, then the w_scale of its rows: a
 // static array sized to the workgroup's LDS share.
-constexpr int kStreamStaticOther = 2 * 4 * kStreamMaxProblems * 16 + 2 * 4 * kWaves;
+constexpr int kStreamStaticOther = 2 * 4 * kStreamMaxProblems * 16 + 2 * 4 * kWaves + 8 * kWaves;
 constexpr int kStreamQBytes = (160 * 1024 / BITNET_STREAM_PER_CU - kDepth * kThreads * 16 - kStreamStaticOther - 256) / 256 * 256;
 static_assert(kStreamQBytes >= 8192, "streaming kernel: too little LDS left for token rows");
 static_assert(kThreads * 16 == 4096 && kDepth % 2 == 0, "ring slot stride and pairs of steps");
@@ -655,6 +716,7 @@ void gemv_stream_kernel(GemvProblem single,
     int8_t* const q_lds = g_stream_q;                   // the workgroup's problems' token rows
     __shared__ float red_f[kWaves];
     __shared__ int red_i[kWaves];
+    __shared__ double red_d[kWaves];
     __shared__ __attribute__((aligned(16))) float as_lds[kStreamMaxProblems * 16];
     __shared__ __attribute__((aligned(16))) int rs_lds[kStreamMaxProblems * 16];
 
@@ -731,7 +793,7 @@ void gemv_stream_kernel(GemvProblem single,
             const GemvProblem Pi = ps.get(pi);
             const int j = pi - p_first;
             if constexpr (kFused)
-                quantise_tokens<kXBf16, 2, true>(Pi, q_lds + off, as_lds + 16 * j, rs_lds + 16 * j, red_f, red_i,
+                quantise_tokens<kXBf16, 2, true>(Pi, q_lds + off, as_lds + 16 * j, rs_lds + 16 * j, red_f, red_i, red_d,
                                                  Pi.q_out != nullptr && t_begin <= Pi.tile0);
             else
                 stage_tokens(Pi, q_lds + off, as_lds + 16 * j, rs_lds + 16 * j);

@@ -216,6 +216,76 @@ def test_rmsnorm_then_linear(orc):
         check_y_tol(y, orc.epilogue(acc_o, ao, ws))
 
 
+@pytest.mark.parametrize("M,N,K,gated", [
+    (1, 640, 2560, False), (3, 257, 1152, False), (16, 100, 2048, False),    # split-K decode kernel
+    (1, 13824, 2560, False), (2, 8200, 4096, False),                          # streaming decode kernel
+    (1, 2560, 6912, True), (1, 5120, 6912, True), (4, 96, 2048, True),       # down projection inputs
+    (17, 130, 1152, False), (20, 64, 2048, True),                            # ActQuant launch + GEMM
+])
+def test_rmsnorm_bitlinear(orc, M, N, K, gated):
+    """Input norm fused into the decode kernels' token prologue (or a separate
+    launch for larger M) against the oracle: codes and sums bit-exact, a_scale
+    and y within 1e-5 relative."""
+    x, W = wl.random_case(3100 + M * 7 + N, M, N, K, x_dist="normal_outliers")
+    g = _norm_weight(K, K + 11, torch.bfloat16)
+    pw = tw.pack(W.to(DEV))
+    xd = x.to(DEV)
+    up = wl.draw_activation((M, K), seed=N + 5).to(DEV) if gated else None
+    ws = (torch.empty((M, tw.padded_k(K)), dtype=torch.int8, device=DEV),
+          torch.empty(M, dtype=torch.float32, device=DEV), torch.empty(M, dtype=torch.int32, device=DEV))
+    y = tw.rmsnorm_bitlinear(xd, g.to(DEV), pw, 1e-6, up=up, workspace=ws)
+    if gated:
+        qo, ao, ro = orc.swiglu_rms_act_quant(bits(x), bits(up), bits(g), 1e-6)
+    else:
+        qo, ao, ro = orc.rms_act_quant(bits(x), bits(g), 1e-6)
+    assert np.array_equal(ws[0].cpu().numpy(), qo)
+    assert np.array_equal(ws[2].cpu().numpy(), ro)
+    _check_scale(ws[1], ao)
+    t, wsc, _, _ = orc.weight_quant(bits(W))
+    check_y_tol(y, orc.epilogue(orc.int_dot(qo, t), ao, wsc))
+
+
+@pytest.mark.parametrize("kernel", ["stream", "persistent"])
+def test_grouped_rmsnorm(orc, kernel, monkeypatch):
+    """A layer's projections with their input norms in one grouped launch: plain,
+    normalised and gated (down) inputs mixed, on both grouped kernels."""
+    if kernel == "persistent":
+        monkeypatch.setenv("BITNET_GROUP_KERNEL", "persistent")
+    else:
+        monkeypatch.delenv("BITNET_GROUP_KERNEL", raising=False)
+    shapes = [(2560, 2560, "norm"), (640, 2560, "norm"), (640, 2560, None), (2560, 2560, "norm"),
+              (6912, 2560, "norm"), (6912, 2560, "norm"), (2560, 6912, "gated"), (130, 1152, "gated")]
+    items, norms, refs = [], [], []
+    for i, (N, K, kind) in enumerate(shapes):
+        x, W = wl.random_case(4100 + i, 1, N, K, x_dist="normal_outliers")
+        pw = tw.pack(W.to(DEV))
+        y = torch.full((1, N), float("nan"), device=DEV)
+        items.append((x.to(DEV), pw, y))
+        t, wsc, _, _ = orc.weight_quant(bits(W))
+        if kind is None:
+            norms.append(None)
+            qo, ao, _ = orc.act_quant(bits(x))
+        else:
+            g = _norm_weight(K, 50 + i, torch.bfloat16 if i % 2 else torch.float32)
+            up = wl.draw_activation((1, K), seed=60 + i).to(DEV) if kind == "gated" else None
+            norms.append((g.to(DEV), up, 1e-6))
+            go = bits(g) if g.dtype == torch.bfloat16 else g.numpy()
+            if kind == "gated":
+                qo, ao, _ = orc.swiglu_rms_act_quant(bits(x), bits(up), go, 1e-6)
+            else:
+                qo, ao, _ = orc.rms_act_quant(bits(x), go, 1e-6)
+        refs.append(orc.epilogue(orc.int_dot(qo, t), ao, wsc))
+    group = tw.GroupedBitLinear(items, norms)
+    assert group.kernel == kernel
+    for rep in range(2):
+        for _, _, y in items:
+            y.fill_(float("nan"))
+        group()
+        torch.cuda.synchronize()
+        for (_, _, y), ref in zip(items, refs):
+            check_y_tol(y, ref)
+
+
 # -------------------------------------------------------------------- linear
 
 LINEAR_CASES = [
