@@ -58,8 +58,10 @@
  *       taken from z = x*g (fp32 products, R4 on z) and r enters a_scale
  *       only: a_scale = amax(z) * r / 127, evaluated in fp64 with the sum of
  *       squares in fp64 (k ascending) and rounded once to fp32.
- *   R11 silu(a) * u is evaluated in fp64, a / (1 + exp(-a)) * u, and rounded
- *       once to fp32; that fp32 value is the input of R10.
+ *   R11 silu(a) * u = a / (1 + e) * u in fp32, with e = exp(-a) by the
+ *       fp32 steps of orc_exp_f32 below (Cody-Waite reduction by ln 2 and a
+ *       degree-7 Taylor polynomial), so that both implementations reach the
+ *       same bits; the fp32 result is the input of R10.
  *
  * Everything here is a direct loop over the definition.  No blocking, no
  * fusion, no intrinsics.
@@ -341,14 +343,41 @@ int orc_rms_act_quant(const void* x, int x_dtype, const void* g, int g_dtype, in
     return 0;
 }
 
+/*
+ * exp(t) in fp32 (R11): above 88 the result is +inf and below -88 it is 0;
+ * otherwise n = rint(t * log2(e)), the reduced argument
+ * r = (t - n * ln2_hi) - n * ln2_lo (ln2_hi has 15 significant bits, so
+ * n * ln2_hi is exact for the |n| <= 127 used here), the Taylor polynomial of
+ * exp to degree 7 at r (|r| <= ln2/2: truncation below 2^-27 relative) in
+ * Horner form, and a scaling by 2^n.  Every step is one IEEE fp32 operation.
+ */
+float orc_exp_f32(float t)
+{
+    if (t > 88.0f)
+        return INFINITY;
+    if (t < -88.0f)
+        return 0.0f;
+    float n = nearbyintf(t * 1.44269502f);
+    float r = (t - n * 0.693145752f) - n * 1.42860677e-06f;
+    float p = 1.0f / 5040.0f;
+    p = p * r + 1.0f / 720.0f;
+    p = p * r + 1.0f / 120.0f;
+    p = p * r + 1.0f / 24.0f;
+    p = p * r + 1.0f / 6.0f;
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    return ldexpf(p, (int)n);
+}
+
 /* h = silu(gate) * up per element (R11), fp32 out [M][K] (row stride K). */
 void orc_swiglu(const void* gate, const void* up, int dtype, int64_t M, int64_t K, int64_t ld, float* h)
 {
     for (int64_t m = 0; m < M; ++m)
         for (int64_t k = 0; k < K; ++k) {
-            double a = (double)load_elem(gate, dtype, m * ld + k);
-            double u = (double)load_elem(up, dtype, m * ld + k);
-            h[m * K + k] = (float)(a / (1.0 + exp(-a)) * u);
+            float a = load_elem(gate, dtype, m * ld + k);
+            float u = load_elem(up, dtype, m * ld + k);
+            h[m * K + k] = a / (1.0f + orc_exp_f32(-a)) * u;
         }
 }
 

@@ -72,6 +72,7 @@ class Oracle:
         lib.orc_act_quant.restype = ctypes.c_int
         lib.orc_rms_act_quant.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, f32, vp, vp, vp]
         lib.orc_rms_act_quant.restype = ctypes.c_int
+        lib.orc_exp_f32.argtypes, lib.orc_exp_f32.restype = [f32], f32
         lib.orc_swiglu.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp]
         lib.orc_swiglu.restype = None
         lib.orc_int_dot.argtypes = [vp, i64, i64, vp, i64, vp, ctypes.c_int]
@@ -174,6 +175,10 @@ class Oracle:
         self.lib.orc_rms_act_quant(_ptr(x), _dtype_code(x), _ptr(g), _dtype_code(g), M, K, K, float(eps),
                                    _ptr(q), _ptr(a_scale), _ptr(rowsum))
         return q, a_scale, rowsum
+
+    def exp_f32(self, t: float) -> np.float32:
+        """The fp32 exp the gated input uses (Cody-Waite reduction, degree-7 Taylor)."""
+        return np.float32(self.lib.orc_exp_f32(float(t)))
 
     def swiglu(self, gate: np.ndarray, up: np.ndarray) -> np.ndarray:
         """silu(gate) * up, fp32 [M, K] (gate and up of one dtype and shape)."""

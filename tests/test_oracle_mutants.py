@@ -82,10 +82,14 @@ MUTANTS = [
      "a_scale[m] = (float)((double)amax * r / 127.0);", "a_scale[m] = (float)((double)amax / 127.0);"),
     ("RMSNorm squares the weighted value",
      "squares += (double)xv * (double)xv;", "squares += (double)z * (double)z;"),
-    ("silu sign flipped", "h[m * K + k] = (float)(a / (1.0 + exp(-a)) * u);",
-     "h[m * K + k] = (float)(a / (1.0 + exp(a)) * u);"),
-    ("gated product drops up", "h[m * K + k] = (float)(a / (1.0 + exp(-a)) * u);",
-     "h[m * K + k] = (float)(a / (1.0 + exp(-a)));"),
+    ("silu sign flipped", "h[m * K + k] = a / (1.0f + orc_exp_f32(-a)) * u;",
+     "h[m * K + k] = a / (1.0f + orc_exp_f32(a)) * u;"),
+    ("gated product drops up", "h[m * K + k] = a / (1.0f + orc_exp_f32(-a)) * u;",
+     "h[m * K + k] = a / (1.0f + orc_exp_f32(-a));"),
+    ("exp drops the low part of ln 2", "float r = (t - n * 0.693145752f) - n * 1.42860677e-06f;",
+     "float r = t - n * 0.693145752f;"),
+    ("exp polynomial one degree short", "    p = p * r + 1.0f / 24.0f;\n", "    p = 1.0f / 24.0f;\n"),
+    ("exp scaled by 2^(n+1)", "return ldexpf(p, (int)n);", "return ldexpf(p, (int)n + 1);"),
 ]
 
 
