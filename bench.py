@@ -126,6 +126,54 @@ def bench_decode(tw, wl, torch, steps, warmup, per_call: bool):
     return out
 
 
+def bench_norm(tw, wl, torch, steps, warmup):
+    """The projections' input norm ("BitNet-Embeddings" guide, s3.1): the c2 grouped
+    decode with an RMSNorm before every projection (the down projection's input being
+    silu(gate) * up), and the standalone RMSNorm -> ActQuant kernel at the prefill
+    token count."""
+    items, nbytes = setup_decode(tw, wl, torch, 30)
+    norms = []
+    for x, pw, _ in items:
+        K = pw.K
+        g = (1.0 + 0.2 * torch.randn(K, device="cuda")).to(torch.bfloat16)
+        up = torch.randn_like(x) if K == 6912 else None
+        norms.append((g, up, 1e-6))
+    group = tw.GroupedBitLinear(items, norms)
+    ms = time_region(torch, group, steps, warmup)
+    out = dict(decode=dict(value=nbytes / (ms * 1e-3) / 1e9, unit="GB/s", ms_per_step=ms, kernel=group.kernel,
+                           note="c2 grouped decode with a per-projection RMSNorm (down: silu(gate)*up) "
+                                "fused into the token prologue; GB/s of packed weights"))
+    del group, items, norms
+    torch.cuda.empty_cache()
+    # standalone RMSNorm -> ActQuant at M = 4096 (prefill): HBM-bound, bytes = inputs + g + q + scales
+    res = {}
+    for name, K, gated in (("qkv_gate_up_input", 2560, False), ("down_input", 6912, True)):
+        M = 4096
+        x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        up = torch.randn_like(x) if gated else None
+        g = (1.0 + 0.2 * torch.randn(K, device="cuda")).to(torch.bfloat16)
+        q = torch.empty((M, tw.padded_k(K)), dtype=torch.int8, device="cuda")
+        a = torch.empty(M, dtype=torch.float32, device="cuda")
+        r = torch.empty(M, dtype=torch.int32, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        L = tw._lib.lib()
+
+        def run():
+            tw._lib.check(L.bitnet_rmsnorm_act_quant(stream, x.data_ptr(), up.data_ptr() if gated else None,
+                                                     tw._lib.BF16, M, K, K, g.data_ptr(), tw._lib.BF16, 1e-6,
+                                                     q.data_ptr(), a.data_ptr(), r.data_ptr()))
+        ms_k = time_region(torch, run, steps * 5, warmup)
+        nb = (2 if gated else 1) * 2 * M * K + 2 * K + M * tw.padded_k(K) + 8 * M
+        gbps = nb / (ms_k * 1e-3) / 1e9
+        res[name] = dict(M=M, K=K, gated=gated, us_per_launch=ms_k * 1e3, value=gbps, unit="GB/s",
+                         roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s",
+                                       frac=gbps / HBM_PEAK_GBPS, traffic=None))
+        del x, up, g, q, a, r
+    out["rmsnorm_act_quant"] = res
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline_decode(wl, torch, budget_s: float, max_layers: int = 3):
     """The oracle's ActQuant + int dot + epilogue over the first layers' projections
     (weights quantised once, untimed), cycled until budget_s of timed work."""
@@ -251,6 +299,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget per CPU-baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-call", action="store_true")
+    ap.add_argument("--no-norm", action="store_true", help="skip the input-norm measurements")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first fill and copy a buffer of this many MiB three times: plain kernels of "
@@ -295,6 +344,8 @@ def main() -> int:
             line["per_call"] = d["per_call"]
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_decode(wl, torch, args.cpu_seconds)
+        if not args.no_norm:
+            line["input_norm"] = bench_norm(tw, wl, torch, args.steps, args.warmup)
     if args.only in (None, "prefill"):
         g = bench_prefill(tw, wl, torch, args.steps, args.warmup, torch.bfloat16)
         if not args.no_cpu_baseline:

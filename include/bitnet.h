@@ -143,8 +143,10 @@ bitnet_status_t bitnet_act_quant(hipStream_t stream, const void* x, bitnet_dtype
  *
  * x        [M, K], row stride ldx >= K, dtype x_dtype (BF16 or F32).
  * up       NULL, or [M, K] with x's dtype and row stride: the input is then
- *          h = silu(x) * up (x being the gate), evaluated in fp64 as
- *          x / (1 + exp(-x)) * up and rounded once to fp32.
+ *          h = silu(x) * up (x being the gate) = x / (1 + e) * up in fp32,
+ *          with e = exp(-x) by fixed fp32 steps (Cody-Waite reduction by
+ *          ln 2, degree-7 Taylor polynomial, scaling by 2^n; +inf above 88,
+ *          0 below -88), so results do not depend on a math library.
  * norm_w   [K] RMSNorm weight g, dtype norm_dtype (BF16 or F32).
  * eps      finite, >= 0.
  * RMSNorm(h)_k = h_k * g_k * r with r = 1/sqrt(mean_k(h_k^2) + eps).  r is

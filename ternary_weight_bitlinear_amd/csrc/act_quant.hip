@@ -15,14 +15,11 @@
 // RMSNorm scales a token by one positive factor r = 1/sqrt(mean(x^2) + eps),
 // which ActQuant's codes do not see: the codes are those of z = x * g (fp32
 // products) and r enters a_scale = amax(z) * r / 127, evaluated in fp64 with
-// the squares summed in fp64.  silu(a) * u is evaluated in fp64 and rounded
-// once to fp32.
+// the squares summed in fp64.  silu(a) * u is evaluated in fp32 with the
+// fixed-step exp of device_common.h.
 //
-// One 256-thread workgroup per token.  Each thread holds up to VPT vectors of
-// 8 elements in registers, so the token is read from HBM once: absmax is a
-// wave butterfly (v_max over __shfl_xor) plus a 4-entry LDS step, and the
-// quantised row, its int32 sum and the scale are written in the same pass.
-// The kernel is HBM-bound: 2 B read + 1 B written per element (bf16 input).
+// One wave per token (below).  The kernel is HBM-bound: 2 B read + 1 B
+// written per element for bf16 input.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -30,7 +27,6 @@ namespace bitnet {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 
 // 8 consecutive elements as fp32, from bf16 or fp32 storage.
 template <typename T>
@@ -88,40 +84,6 @@ __device__ __forceinline__ int quant8(const float (&v)[8], float sa, uint2& out)
     return sum;
 }
 
-__device__ __forceinline__ float block_max(float v, float* red) {
-    v = wave_max(v);
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x % kWave) == 0) red[w] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) r = fmaxf(r, red[i]);
-    return r;
-}
-
-__device__ __forceinline__ int block_sum(int v, int* red) {
-    v = wave_sum(v);
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x % kWave) == 0) red[w] = v;
-    __syncthreads();
-    int r = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) r += red[i];
-    return r;
-}
-
-__device__ __forceinline__ double block_sum_f64(double v, double* red) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x % kWave) == 0) red[w] = v;
-    __syncthreads();
-    double r = 0.0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) r += red[i];
-    return r;
-}
-
 // Input modes: the token itself; RMSNorm of it; RMSNorm of silu(x) * up.
 enum { kPlain = 0, kNorm = 1, kGatedNorm = 2 };
 
@@ -135,10 +97,7 @@ __device__ __forceinline__ void load_input8(const T* xr, const T* ur, const void
         float u[8];
         load8<T, kAligned>(ur + vi * 8, u);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const double a = z[e];
-            z[e] = static_cast<float>(a / (1.0 + exp(-a)) * static_cast<double>(u[e]));
-        }
+        for (int e = 0; e < 8; ++e) z[e] = silu_mul(z[e], u[e]);
     }
     if constexpr (kMode != kPlain) {
         float gv[8];
@@ -152,75 +111,82 @@ __device__ __forceinline__ void load_input8(const T* xr, const T* ur, const void
     }
 }
 
-// VPT > 0: the token stays in registers (K <= 8 * 256 * VPT).
-// VPT == 0: any K; the row is read twice (the second read hits L2).
+// One wave per token, four tokens per workgroup: the reductions (absmax, the
+// code sum, the fp64 sum of squares) are wave butterflies with no barrier, and
+// a lane keeps VPT vectors of 8 values in registers, so a token of up to
+// 8 * 64 * VPT elements is read from HBM once with all of its loads in flight
+// together.  VPT == 0: any K; the row is read twice (the second read hits L2).
+constexpr int kTokensPerBlock = kThreads / kWave;
+
 template <typename T, int VPT, bool kAligned, int kMode>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(
-    const T* __restrict__ x, const T* __restrict__ up, int64_t ldx, int K, int Kp,
+    const T* __restrict__ x, const T* __restrict__ up, int64_t ldx, int M, int K, int Kp,
     const void* __restrict__ g, bool g_bf16, float eps,
     int8_t* __restrict__ q, float* __restrict__ a_scale, int32_t* __restrict__ q_rowsum) {
-    __shared__ float red_f[kWaves];
-    __shared__ int red_i[kWaves];
-    __shared__ double red_d[kWaves];
-    const int64_t m = blockIdx.x;
+    const int lane = threadIdx.x % kWave;
+    const int64_t m = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + threadIdx.x / kWave;
+    if (m >= M) return;                                 // wave-uniform
     const T* xr = x + m * ldx;
     const T* ur = kMode == kGatedNorm ? up + m * ldx : nullptr;
     int8_t* qr = q + m * static_cast<int64_t>(Kp);
     const int nvec = K / 8;
-    const int tid = threadIdx.x;
 
-    float amax_local = 0.0f;
+    float amax = 0.0f;
     double squares = 0.0;
     float v[VPT > 0 ? VPT : 1][8];
     if constexpr (VPT > 0) {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int vi = tid + i * kThreads;
-            if (vi < nvec) {
-                load_input8<T, kAligned, kMode>(xr, ur, g, g_bf16, vi, v[i], squares);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) amax_local = fmaxf(amax_local, fabsf(v[i][e]));
-            }
+            const int vi = lane + i * kWave;
+            if (vi < nvec) load_input8<T, kAligned, kMode>(xr, ur, g, g_bf16, vi, v[i], squares);
         }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+            if (lane + i * kWave < nvec)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
     } else {
-        for (int vi = tid; vi < nvec; vi += kThreads) {
+        for (int vi = lane; vi < nvec; vi += kWave) {
             load_input8<T, kAligned, kMode>(xr, ur, g, g_bf16, vi, v[0], squares);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) amax_local = fmaxf(amax_local, fabsf(v[0][e]));
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[0][e]));
         }
     }
-    const float amax = block_max(amax_local, red_f);
-    if constexpr (kMode != kPlain) squares = block_sum_f64(squares, red_d);
+    amax = wave_max(amax);
+    if constexpr (kMode != kPlain) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) squares += __shfl_xor(squares, o, kWave);
+    }
     // amax == 0: every value is +-0 and sa = 0 gives q = 0 exactly.
     const float sa = (amax == 0.0f) ? 0.0f : 127.0f / amax;
 
-    int sum_local = 0;
+    int sum = 0;
     if constexpr (VPT > 0) {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int vi = tid + i * kThreads;
+            const int vi = lane + i * kWave;
             if (vi < nvec) {
                 uint2 out;
-                sum_local += quant8(v[i], sa, out);
+                sum += quant8(v[i], sa, out);
                 *reinterpret_cast<uint2*>(qr + vi * 8) = out;
             }
         }
     } else {
         double unused = 0.0;
-        for (int vi = tid; vi < nvec; vi += kThreads) {
+        for (int vi = lane; vi < nvec; vi += kWave) {
             load_input8<T, kAligned, kMode>(xr, ur, g, g_bf16, vi, v[0], unused);
             uint2 out;
-            sum_local += quant8(v[0], sa, out);
+            sum += quant8(v[0], sa, out);
             *reinterpret_cast<uint2*>(qr + vi * 8) = out;
         }
     }
     // zero tail K..Kp-1 (at most 112 bytes, 8-byte stores)
-    for (int vi = nvec + tid; vi < Kp / 8; vi += kThreads)
+    for (int vi = nvec + lane; vi < Kp / 8; vi += kWave)
         *reinterpret_cast<uint2*>(qr + vi * 8) = make_uint2(0u, 0u);
 
-    const int total = block_sum(sum_local, red_i);
-    if (tid == 0) {
-        q_rowsum[m] = total;
+    sum = wave_sum(sum);
+    if (lane == 0) {
+        q_rowsum[m] = sum;
         if (amax == 0.0f) {
             a_scale[m] = 0.0f;
         } else if constexpr (kMode == kPlain) {
@@ -236,24 +202,18 @@ template <typename T, bool kAligned, int kMode>
 hipError_t launch_t(const T* x, const T* up, int64_t M, int64_t K, int64_t ldx, const void* g, bool g_bf16,
                     float eps, int8_t* q, float* a_scale, int32_t* q_rowsum, int Kp, hipStream_t stream) {
     const int nvec = static_cast<int>(K / 8);
-    const dim3 grid(static_cast<unsigned>(M)), block(kThreads);
-    const int vpt = (nvec + kThreads - 1) / kThreads;
-    const int k = static_cast<int>(K);
-    if (vpt <= 1)
-        act_quant_kernel<T, 1, kAligned, kMode>
-            <<<grid, block, 0, stream>>>(x, up, ldx, k, Kp, g, g_bf16, eps, q, a_scale, q_rowsum);
-    else if (vpt <= 2)
-        act_quant_kernel<T, 2, kAligned, kMode>
-            <<<grid, block, 0, stream>>>(x, up, ldx, k, Kp, g, g_bf16, eps, q, a_scale, q_rowsum);
-    else if (vpt <= 4)
-        act_quant_kernel<T, 4, kAligned, kMode>
-            <<<grid, block, 0, stream>>>(x, up, ldx, k, Kp, g, g_bf16, eps, q, a_scale, q_rowsum);
-    else if (vpt <= 8)
-        act_quant_kernel<T, 8, kAligned, kMode>
-            <<<grid, block, 0, stream>>>(x, up, ldx, k, Kp, g, g_bf16, eps, q, a_scale, q_rowsum);
-    else
-        act_quant_kernel<T, 0, kAligned, kMode>
-            <<<grid, block, 0, stream>>>(x, up, ldx, k, Kp, g, g_bf16, eps, q, a_scale, q_rowsum);
+    const dim3 grid(static_cast<unsigned>((M + kTokensPerBlock - 1) / kTokensPerBlock)), block(kThreads);
+    const int vpt = (nvec + kWave - 1) / kWave;
+    const int m = static_cast<int>(M), k = static_cast<int>(K);
+#define BITNET_AQ_LAUNCH(V)                                                                                    \
+    act_quant_kernel<T, V, kAligned, kMode><<<grid, block, 0, stream>>>(x, up, ldx, m, k, Kp, g, g_bf16, eps, q, \
+                                                                         a_scale, q_rowsum)
+    if (vpt <= 2) BITNET_AQ_LAUNCH(2);
+    else if (vpt <= 4) BITNET_AQ_LAUNCH(4);
+    else if (vpt <= 8) BITNET_AQ_LAUNCH(8);
+    else if (vpt <= 16) BITNET_AQ_LAUNCH(16);
+    else BITNET_AQ_LAUNCH(0);
+#undef BITNET_AQ_LAUNCH
     return hipGetLastError();
 }
 

@@ -71,6 +71,32 @@ __device__ __forceinline__ v4i expand_word(uint32_t w) {
     return r;
 }
 
+// exp(t) in fp32 by fixed IEEE steps, so that the gated input silu(a) * u of
+// the down projection has the same bits on every implementation of them:
+// +inf above 88 and 0 below -88; else n = rint(t * log2 e), reduced argument
+// r = (t - n * ln2_hi) - n * ln2_lo with a 15-bit ln2_hi (n * ln2_hi exact),
+// the degree-7 Taylor polynomial of exp at r in Horner form (|r| <= ln2/2),
+// times 2^n.  Each line is one correctly rounded fp32 operation (contraction
+// is off for these sources).
+__device__ __forceinline__ float exp_f32_fixed(float t) {
+    if (t > 88.0f) return __builtin_inff();
+    if (t < -88.0f) return 0.0f;
+    const float n = rne(t * 1.44269502f);
+    const float r = (t - n * 0.693145752f) - n * 1.42860677e-06f;
+    float p = 1.0f / 5040.0f;
+    p = p * r + 1.0f / 720.0f;
+    p = p * r + 1.0f / 120.0f;
+    p = p * r + 1.0f / 24.0f;
+    p = p * r + 1.0f / 6.0f;
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    return __builtin_ldexpf(p, static_cast<int>(n));
+}
+
+// silu(a) * u = a / (1 + exp(-a)) * u, fp32.
+__device__ __forceinline__ float silu_mul(float a, float u) { return a / (1.0f + exp_f32_fixed(-a)) * u; }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

@@ -101,8 +101,8 @@ __host__ __device__ __forceinline__ int padded_q_row(int Kp) {
 }
 
 // 8 values whose codes are taken, of vector vi of token row m: x, or with a
-// norm weight z = h * g where h = x or h = silu(x) * up (fp64, rounded once to
-// fp32); `squares` gathers the fp64 sum of h^2 that RMSNorm needs.  The norm
+// norm weight z = h * g where h = x or h = silu(x) * up (fp32, fixed-step
+// exp); `squares` gathers the fp64 sum of h^2 that RMSNorm needs.  The norm
 // factor r > 0 is common to the token, so the codes of RMSNorm(h) are those of
 // z and r enters a_scale only ("BitNet-Embeddings-0.6B/270M: I2_S Conversion
 // and Inference Optimization Guide", s3.1: each projection normalises its
@@ -116,10 +116,7 @@ __device__ __forceinline__ void load_input8(const GemvProblem& p, const void* xr
         float u[8];
         load_x8<kXBf16>(urow, vi, u);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const double a = z[e];
-            z[e] = static_cast<float>(a / (1.0 + exp(-a)) * static_cast<double>(u[e]));
-        }
+        for (int e = 0; e < 8; ++e) z[e] = silu_mul(z[e], u[e]);
     }
     float g[8];
     if (p.norm_bf16) {
