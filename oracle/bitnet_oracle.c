@@ -63,6 +63,18 @@
  *       degree-7 Taylor polynomial), so that both implementations reach the
  *       same bits; the fp32 result is the input of R10.
  *
+ * The I2_S interchange format [Guide s3.3 "I2_S Ternary Packing"]: the
+ * tensor's values, flattened row-major, form blocks of 128; a block is 32
+ * bytes; byte = (c0 << 6) | (c1 << 4) | (c2 << 2) | c3 with the stored codes
+ * -1 -> 0, 0 -> 1, +1 -> 2; the fp32 scale 1/mean|W| follows the codes.
+ *   R12 Which four values of a block share a byte is not stated.  Reading
+ *       "strided" (the default): byte j of a block holds values j, j+32,
+ *       j+64, j+96 as c0..c3 -- a block size only matters to a layout of
+ *       this kind.  Reading "consecutive": byte j holds values 4j..4j+3.
+ *       Both are provided.
+ *   R13 The appended float is the quantisation scale s = 1/mean|W| as the
+ *       page names it; the dequantisation factor is 1/s.
+ *
  * Everything here is a direct loop over the definition.  No blocking, no
  * fusion, no intrinsics.
  */
@@ -245,6 +257,49 @@ int64_t orc_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* t)
             t[n * K + k] = (int8_t)((int)u - 1);
         }
     }
+    return bad;
+}
+
+/* ----------------------------------------------------------------- I2_S */
+
+/* Byte index inside a block and shift of value v (0..127) of the block (R12). */
+static int64_t i2s_byte(int64_t v, int consecutive) { return consecutive ? v / 4 : v % 32; }
+static int i2s_shift(int64_t v, int consecutive) { return consecutive ? 6 - 2 * (int)(v % 4) : 6 - 2 * (int)(v / 32); }
+
+/*
+ * Codes t [N, K] (-1, 0, +1) and the scale s = 1/mean|W| as an I2_S buffer:
+ * N*K/4 code bytes, then s as 4 little-endian bytes (R12, R13).  N*K must be
+ * a multiple of 128.  Returns -1 otherwise.
+ */
+int orc_i2s_pack(const int8_t* t, int64_t N, int64_t K, float s, int consecutive, uint8_t* out)
+{
+    int64_t total = N * K;
+    if (total <= 0 || total % 128 != 0)
+        return -1;
+    memset(out, 0, (size_t)(total / 4));
+    for (int64_t i = 0; i < total; ++i) {
+        int64_t block = i / 128, v = i % 128;
+        unsigned c = (unsigned)(t[i] + 1);
+        out[block * 32 + i2s_byte(v, consecutive)] |= (uint8_t)(c << i2s_shift(v, consecutive));
+    }
+    memcpy(out + total / 4, &s, sizeof s);
+    return 0;
+}
+
+/* Inverse of orc_i2s_pack: codes t [N, K] and *s.  Returns -1 for a bad size,
+ * else the number of fields holding the unused value 3. */
+int64_t orc_i2s_unpack(const uint8_t* in, int64_t N, int64_t K, int consecutive, int8_t* t, float* s)
+{
+    int64_t total = N * K, bad = 0;
+    if (total <= 0 || total % 128 != 0)
+        return -1;
+    for (int64_t i = 0; i < total; ++i) {
+        int64_t block = i / 128, v = i % 128;
+        unsigned c = (in[block * 32 + i2s_byte(v, consecutive)] >> i2s_shift(v, consecutive)) & 3u;
+        bad += (c == 3u);
+        t[i] = (int8_t)((int)c - 1);
+    }
+    memcpy(s, in + total / 4, sizeof *s);
     return bad;
 }
 

@@ -68,6 +68,9 @@ class Oracle:
         lib.orc_weight_quant.restype = ctypes.c_int
         lib.orc_pack.argtypes, lib.orc_pack.restype = [vp, i64, i64, vp], ctypes.c_int
         lib.orc_unpack.argtypes, lib.orc_unpack.restype = [vp, i64, i64, vp], i64
+        lib.orc_i2s_pack.argtypes, lib.orc_i2s_pack.restype = [vp, i64, i64, f32, ctypes.c_int, vp], ctypes.c_int
+        lib.orc_i2s_unpack.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
+        lib.orc_i2s_unpack.restype = i64
         lib.orc_act_quant.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp]
         lib.orc_act_quant.restype = ctypes.c_int
         lib.orc_rms_act_quant.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, f32, vp, vp, vp]
@@ -144,6 +147,28 @@ class Oracle:
         if bad < 0:
             raise ValueError("K must be a positive multiple of 16")
         return t, int(bad)
+
+    # ------------------------------------------------------------- I2_S
+    def i2s_pack(self, t: np.ndarray, s: float, order: str = "strided") -> np.ndarray:
+        """I2_S bytes of codes t [N, K] (N*K % 128 == 0) and scale s = 1/mean|W|."""
+        t = np.ascontiguousarray(t, dtype=np.int8)
+        N, K = t.shape
+        out = np.empty(N * K // 4 + 4, dtype=np.uint8)
+        if self.lib.orc_i2s_pack(_ptr(t), N, K, float(s), int(order == "consecutive"), _ptr(out)) != 0:
+            raise ValueError("N*K must be a positive multiple of 128")
+        return out
+
+    def i2s_unpack(self, buf: np.ndarray, N: int, K: int, order: str = "strided"):
+        """Codes t [N, K], the scale s, and the count of invalid fields (value 3)."""
+        buf = np.ascontiguousarray(buf, dtype=np.uint8)
+        if buf.size < N * K // 4 + 4:
+            raise ValueError("buffer too small")
+        t = np.empty((N, K), dtype=np.int8)
+        s = np.empty(1, dtype=np.float32)
+        bad = self.lib.orc_i2s_unpack(_ptr(buf), N, K, int(order == "consecutive"), _ptr(t), _ptr(s))
+        if bad < 0:
+            raise ValueError("N*K must be a positive multiple of 128")
+        return t, np.float32(s[0]), int(bad)
 
     # --------------------------------------------------------- ActQuant
     def act_quant(self, x: np.ndarray):

@@ -442,6 +442,49 @@ def pin_swiglu_decimal(orc):
     assert h[0, 4] == 0
 
 
+# --------------------------------------------------------------------- I2_S
+
+def pin_i2s_golden(orc):
+    """One block worked by hand from the page's byte formula, both readings of
+    which values share a byte (tests/golden/i2s_block.txt)."""
+    g = read_golden("i2s_block.txt")
+    t = np.array([int(v) for v in g["T"][0]], dtype=np.int8).reshape(1, 128)
+    scale = float(g["SCALE"][0][0])
+    for order, key in (("strided", "STRIDED"), ("consecutive", "CONSECUTIVE")):
+        want = np.array([int(b, 16) for b in g[key][0]], dtype=np.uint8)
+        got = orc.i2s_pack(t, scale, order)
+        assert np.array_equal(got, want), order
+        t2, s2, bad = orc.i2s_unpack(want, 1, 128, order)
+        assert np.array_equal(t2, t) and s2 == np.float32(scale) and bad == 0
+
+
+def pin_i2s_roundtrip_and_blocks(orc):
+    """unpack(pack(t)) = t with blocks that cross rows (K = 48); each 32-byte block
+    holds the same multiset of codes under both readings (they only permute
+    values inside a block); codes of other blocks do not move; fields never hold 3."""
+    rng = np.random.default_rng(53)
+    N, K = 16, 48
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    for order in ("strided", "consecutive"):
+        buf = orc.i2s_pack(t, 0.25, order)
+        t2, s2, bad = orc.i2s_unpack(buf, N, K, order)
+        assert np.array_equal(t2, t) and s2 == np.float32(0.25) and bad == 0
+        fields = np.stack([(buf[:-4] >> sh) & 3 for sh in (6, 4, 2, 0)], 1)
+        assert fields.max() <= 2
+    a, b = orc.i2s_pack(t, 1.0, "strided"), orc.i2s_pack(t, 1.0, "consecutive")
+    flat = t.reshape(-1)
+    for blk in range(flat.size // 128):
+        def counts(buf):
+            f = np.stack([(buf[32 * blk:32 * blk + 32] >> sh) & 3 for sh in (6, 4, 2, 0)], 1).reshape(-1)
+            return np.bincount(f, minlength=3)
+        want = np.bincount(flat[128 * blk:128 * blk + 128] + 1, minlength=3)
+        assert np.array_equal(counts(a), want) and np.array_equal(counts(b), want)
+    t3 = t.copy()
+    t3.reshape(-1)[200] = -t3.reshape(-1)[200] if t3.reshape(-1)[200] else 1
+    d = np.nonzero(orc.i2s_pack(t3, 1.0, "strided") != a)[0]
+    assert d.size == 1 and d[0] // 32 == 200 // 128
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

@@ -90,6 +90,11 @@ MUTANTS = [
      "float r = t - n * 0.693145752f;"),
     ("exp polynomial one degree short", "    p = p * r + 1.0f / 24.0f;\n", "    p = 1.0f / 24.0f;\n"),
     ("exp scaled by 2^(n+1)", "return ldexpf(p, (int)n);", "return ldexpf(p, (int)n + 1);"),
+    ("I2_S strided fields in reversed bit order", "6 - 2 * (int)(v / 32)", "2 * (int)(v / 32)"),
+    ("I2_S consecutive fields in reversed bit order", "6 - 2 * (int)(v % 4)", "2 * (int)(v % 4)"),
+    ("I2_S stride of 16", "return consecutive ? v / 4 : v % 32;", "return consecutive ? v / 4 : v % 16;"),
+    ("I2_S scale not stored", "memcpy(out + total / 4, &s, sizeof s);", "(void)s;"),
+    ("I2_S codes offset by 2", "unsigned c = (unsigned)(t[i] + 1);", "unsigned c = (unsigned)(t[i] + 2) & 3u;"),
 ]
 
 
