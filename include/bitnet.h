@@ -292,6 +292,47 @@ bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_
  * the fallback (for comparisons; results are identical). */
 const char* bitnet_group_plan_kernel(const bitnet_group_plan_t* plan);
 
+/*
+ * I2_S interchange [Guide s3.3 "I2_S Ternary Packing"], for weights
+ * converted by bitnet.cpp's tooling.  An I2_S buffer of one [N, K] tensor is
+ * N*K/4 code bytes followed by one fp32 scale s = 1/mean|W| (little-endian),
+ * bitnet_i2s_bytes(N, K) bytes in all.  The tensor's values, flattened
+ * row-major, form blocks of 128; block b is bytes 32b..32b+31; a byte holds
+ * four stored codes (-1 -> 0, 0 -> 1, +1 -> 2, the codes of layout v1) as
+ * (c0 << 6) | (c1 << 4) | (c2 << 2) | c3.  The page does not say which four
+ * values of a block share a byte:
+ *   BITNET_I2S_STRIDED      byte j of a block holds values j, j+32, j+64,
+ *                           j+96 as c0..c3 (a block size only matters to a
+ *                           layout of this kind, so this is the default);
+ *   BITNET_I2S_CONSECUTIVE  byte j holds values 4j, 4j+1, 4j+2, 4j+3.
+ */
+typedef enum { BITNET_I2S_STRIDED = 0, BITNET_I2S_CONSECUTIVE = 1 } bitnet_i2s_order_t;
+
+/* Bytes of the I2_S buffer of an [N, K] tensor; -1 unless K % 16 == 0 and
+ * N*K % 128 == 0. */
+int64_t bitnet_i2s_bytes(int64_t N, int64_t K);
+
+/*
+ * I2_S buffer -> layout v1 (packed [N][Kp/4], w_scale[n] = 1/s for every row,
+ * codes k >= K set to 1).  `where` says whether all three buffers are host or
+ * device memory (device: 4-byte aligned i2s and w_scale; synchronous on
+ * `stream`).  Errors: INVALID_ARG for bad sizes, a field holding 3 or a scale
+ * that is not positive (outputs then partly written); HIP.
+ */
+bitnet_status_t bitnet_i2s_import(bitnet_mem_t where, hipStream_t stream, const uint8_t* i2s,
+                                  int64_t N, int64_t K, bitnet_i2s_order_t order,
+                                  uint8_t* packed, float* w_scale);
+
+/*
+ * Layout v1 -> I2_S buffer of bitnet_i2s_bytes(N, K) bytes, with
+ * s = 1/w_scale[0].  I2_S has one scale per tensor: every w_scale[n] must be
+ * equal (export the segments of a fused tensor one at a time, by rows).
+ * Same memory rules and errors as bitnet_i2s_import.
+ */
+bitnet_status_t bitnet_i2s_export(bitnet_mem_t where, hipStream_t stream, const uint8_t* packed,
+                                  const float* w_scale, int64_t N, int64_t K, bitnet_i2s_order_t order,
+                                  uint8_t* i2s);
+
 /* Static text for a status code. */
 const char* bitnet_status_string(bitnet_status_t s);
 

@@ -88,6 +88,43 @@ def pack(W: torch.Tensor, segments=None) -> PackedWeight:
     return PackedWeight(packed, w_scale, N, K, seg_mean, zeros)
 
 
+_I2S_ORDERS = {"strided": 0, "consecutive": 1}
+
+
+def i2s_import(buf: torch.Tensor, N: int, K: int, order: str = "strided") -> PackedWeight:
+    """An I2_S buffer (uint8, bitnet_i2s_bytes(N, K) bytes, CPU or CUDA) of one [N, K]
+    tensor as a layout-v1 PackedWeight on the same device.  seg_mean holds 1/s; the
+    zero count is not known for imported weights (-1)."""
+    nbytes = int(_lib.lib().bitnet_i2s_bytes(N, K))
+    if nbytes < 0:
+        raise ValueError("need K % 16 == 0 and N*K % 128 == 0")
+    if buf.dtype != torch.uint8 or buf.numel() < nbytes or not buf.is_contiguous():
+        raise ValueError(f"buf must be a contiguous uint8 tensor of at least {nbytes} bytes")
+    Kp = padded_k(K)
+    packed = torch.empty((N, Kp // 4), dtype=torch.uint8, device=buf.device)
+    w_scale = torch.empty(N, dtype=torch.float32, device=buf.device)
+    on_gpu = buf.is_cuda
+    with torch.cuda.device(buf.device) if on_gpu else _nullctx():
+        _lib.check(_lib.lib().bitnet_i2s_import(
+            _lib.MEM_DEVICE if on_gpu else _lib.MEM_HOST, _stream(buf) if on_gpu else None, buf.data_ptr(),
+            N, K, _I2S_ORDERS[order], packed.data_ptr(), w_scale.data_ptr()))
+    return PackedWeight(packed, w_scale, N, K, w_scale[:1].cpu().clone(), torch.tensor([-1], dtype=torch.int64))
+
+
+def i2s_export(w: PackedWeight, order: str = "strided") -> torch.Tensor:
+    """The I2_S buffer (uint8, on w's device) of a single-tensor PackedWeight."""
+    nbytes = int(_lib.lib().bitnet_i2s_bytes(w.N, w.K))
+    if nbytes < 0:
+        raise ValueError("need K % 16 == 0 and N*K % 128 == 0")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w.packed.device)
+    on_gpu = w.packed.is_cuda
+    with torch.cuda.device(w.packed.device) if on_gpu else _nullctx():
+        _lib.check(_lib.lib().bitnet_i2s_export(
+            _lib.MEM_DEVICE if on_gpu else _lib.MEM_HOST, _stream(w.packed) if on_gpu else None,
+            w.packed.data_ptr(), w.w_scale.data_ptr(), w.N, w.K, _I2S_ORDERS[order], out.data_ptr()))
+    return out
+
+
 class _nullctx:
     def __enter__(self):
         return None

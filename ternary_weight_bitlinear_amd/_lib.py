@@ -14,6 +14,7 @@ LIBRARY = Path(__file__).resolve().parent / "libbitnet_hip.so"
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NONFINITE = range(5)
 F32, BF16 = 0, 1
 MEM_HOST, MEM_DEVICE = 0, 1
+I2S_STRIDED, I2S_CONSECUTIVE = 0, 1
 
 # name -> (restype, argtypes), in the order of include/bitnet.h
 _i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
@@ -39,6 +40,9 @@ SIGNATURES = {
                                                  _vp]),
     "bitnet_bitlinear_grouped": (ctypes.c_int, [_vp, _vp]),
     "bitnet_group_plan_kernel": (ctypes.c_char_p, [_vp]),
+    "bitnet_i2s_bytes": (_i64, [_i64, _i64]),
+    "bitnet_i2s_import": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
+    "bitnet_i2s_export": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp]),
     "bitnet_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bitnet_last_error": (ctypes.c_char_p, []),
 }

@@ -391,6 +391,120 @@ bitnet_status_t bitnet_rmsnorm_bitlinear_forward(hipStream_t stream, const void*
                           y_dtype, ldy, q, a_scale, q_rowsum, fn);
 }
 
+// ------------------------------------------------------------------ I2_S
+
+int64_t bitnet_i2s_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || K % 16 != 0 || K > kMaxK || N > kMaxMN || (N * K) % 128 != 0) return -1;
+    return N * K / 4 + 4;
+}
+
+static int64_t i2s_byte_at(int64_t v, bool consecutive) { return consecutive ? v / 4 : v % 32; }
+static int i2s_shift_at(int64_t v, bool consecutive) {
+    return consecutive ? 6 - 2 * static_cast<int>(v % 4) : 6 - 2 * static_cast<int>(v / 32);
+}
+
+static bitnet_status_t check_i2s(bitnet_mem_t where, const void* a, const void* b, const void* c, int64_t N,
+                                 int64_t K, bitnet_i2s_order_t order, const char* fn) {
+    if (where != BITNET_MEM_HOST && where != BITNET_MEM_DEVICE)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: bad memory kind %d", fn, (int)where);
+    if (order != BITNET_I2S_STRIDED && order != BITNET_I2S_CONSECUTIVE)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: bad I2_S order %d", fn, (int)order);
+    if (!a || !b || !c) return fail(BITNET_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (bitnet_i2s_bytes(N, K) < 0)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: N=%lld, K=%lld: need K %% 16 == 0 and N*K %% 128 == 0", fn,
+                    (long long)N, (long long)K);
+    return BITNET_OK;
+}
+
+static bitnet_status_t i2s_device(bool import, hipStream_t stream, const uint8_t* in, const float* ws_in,
+                                  int64_t N, int64_t K, bool consecutive, uint8_t* out, float* ws_out,
+                                  const char* fn) {
+    DeviceTemps temps;
+    temps.stream = stream;
+    hipError_t e = hipMallocAsync(&temps.p, sizeof(unsigned int), stream);
+    if (e != hipSuccess) {
+        temps.p = nullptr;
+        return hip_fail(e, fn);
+    }
+    auto* d_status = static_cast<unsigned int*>(temps.p);
+    if ((e = hipMemsetAsync(d_status, 0, sizeof(unsigned int), stream)) != hipSuccess) return hip_fail(e, fn);
+    const int64_t Kp = padded_k(K);
+    e = import ? bitnet::launch_i2s_import(in, N, K, Kp, consecutive, out, ws_out, d_status, stream)
+               : bitnet::launch_i2s_export(in, ws_in, N, K, Kp, consecutive, out, d_status, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    unsigned int status = 0;
+    if ((e = hipMemcpyAsync(&status, d_status, sizeof status, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+        (e = hipStreamSynchronize(stream)) != hipSuccess)
+        return hip_fail(e, fn);
+    if (status & 1u) return fail(BITNET_ERR_INVALID_ARG, "%s: a 2-bit field holds 3, which encodes no weight", fn);
+    if (status & 2u) return fail(BITNET_ERR_INVALID_ARG, "%s: the I2_S scale is not positive", fn);
+    if (status & 4u)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: w_scale differs between rows (export one source tensor at a time)",
+                    fn);
+    return ok();
+}
+
+bitnet_status_t bitnet_i2s_import(bitnet_mem_t where, hipStream_t stream, const uint8_t* i2s, int64_t N, int64_t K,
+                                  bitnet_i2s_order_t order, uint8_t* packed, float* w_scale) {
+    const char* fn = "bitnet_i2s_import";
+    bitnet_status_t st = check_i2s(where, i2s, packed, w_scale, N, K, order, fn);
+    if (st != BITNET_OK) return st;
+    const bool consecutive = order == BITNET_I2S_CONSECUTIVE;
+    if (where == BITNET_MEM_DEVICE) {
+        if (!aligned(i2s, 4) || !aligned(w_scale, 4))
+            return fail(BITNET_ERR_INVALID_ARG, "%s: i2s and w_scale must be 4-byte aligned", fn);
+        return i2s_device(true, stream, i2s, nullptr, N, K, consecutive, packed, w_scale, fn);
+    }
+    const int64_t Kp = padded_k(K), row_bytes = Kp / 4;
+    float s;
+    memcpy(&s, i2s + N * K / 4, sizeof s);
+    if (!(s > 0.0f)) return fail(BITNET_ERR_INVALID_ARG, "%s: the I2_S scale is not positive", fn);
+    memset(packed, 0, static_cast<size_t>(N * row_bytes));
+    for (int64_t n = 0; n < N; ++n) {
+        uint8_t* row = packed + n * row_bytes;
+        for (int64_t k = 0; k < Kp; ++k) {
+            unsigned c = 1u;
+            if (k < K) {
+                const int64_t i = n * K + k, v = i % 128;
+                c = (i2s[(i / 128) * 32 + i2s_byte_at(v, consecutive)] >> i2s_shift_at(v, consecutive)) & 3u;
+                if (c == 3u) return fail(BITNET_ERR_INVALID_ARG, "%s: a 2-bit field holds 3, which encodes no weight", fn);
+            }
+            row[4 * (k / 16) + k % 4] |= static_cast<uint8_t>(c << (2 * ((k % 16) / 4)));
+        }
+        w_scale[n] = 1.0f / s;
+    }
+    return ok();
+}
+
+bitnet_status_t bitnet_i2s_export(bitnet_mem_t where, hipStream_t stream, const uint8_t* packed,
+                                  const float* w_scale, int64_t N, int64_t K, bitnet_i2s_order_t order,
+                                  uint8_t* i2s) {
+    const char* fn = "bitnet_i2s_export";
+    bitnet_status_t st = check_i2s(where, packed, w_scale, i2s, N, K, order, fn);
+    if (st != BITNET_OK) return st;
+    const bool consecutive = order == BITNET_I2S_CONSECUTIVE;
+    if (where == BITNET_MEM_DEVICE) {
+        if (!aligned(i2s, 4) || !aligned(w_scale, 4))
+            return fail(BITNET_ERR_INVALID_ARG, "%s: i2s and w_scale must be 4-byte aligned", fn);
+        return i2s_device(false, stream, packed, w_scale, N, K, consecutive, i2s, nullptr, fn);
+    }
+    for (int64_t n = 1; n < N; ++n)
+        if (w_scale[n] != w_scale[0])
+            return fail(BITNET_ERR_INVALID_ARG, "%s: w_scale differs between rows (export one source tensor at a time)",
+                        fn);
+    const int64_t Kp = padded_k(K), row_bytes = Kp / 4, total = N * K;
+    memset(i2s, 0, static_cast<size_t>(total / 4));
+    for (int64_t i = 0; i < total; ++i) {
+        const int64_t n = i / K, k = i % K, v = i % 128;
+        const unsigned c = (packed[n * row_bytes + 4 * (k / 16) + k % 4] >> (2 * ((k % 16) / 4))) & 3u;
+        if (c == 3u) return fail(BITNET_ERR_INVALID_ARG, "%s: a 2-bit field holds 3, which encodes no weight", fn);
+        i2s[(i / 128) * 32 + i2s_byte_at(v, consecutive)] |= static_cast<uint8_t>(c << i2s_shift_at(v, consecutive));
+    }
+    const float s = 1.0f / w_scale[0];
+    memcpy(i2s + total / 4, &s, sizeof s);
+    return ok();
+}
+
 // Kernels of a grouped plan.  BITNET_GROUP_KERNEL=persistent, read when a
 // plan is made, skips the streaming kernel (for comparisons; results are
 // identical).

@@ -40,4 +40,12 @@ hipError_t launch_pack(const void* W, bool w_bf16, int64_t N, int64_t K, int64_t
                        unsigned int* status_dev, uint8_t* packed, float* w_scale,
                        hipStream_t stream);
 
+// I2_S <-> layout v1 (status bits: 1 a field holds 3, 2 a scale is not
+// positive, 4 rows differ in scale on export).  The grid covers every output
+// byte and every row.
+hipError_t launch_i2s_import(const uint8_t* in, int64_t N, int64_t K, int64_t Kp, bool consecutive, uint8_t* packed,
+                             float* w_scale, unsigned int* status, hipStream_t stream);
+hipError_t launch_i2s_export(const uint8_t* packed, const float* w_scale, int64_t N, int64_t K, int64_t Kp,
+                             bool consecutive, uint8_t* out, unsigned int* status, hipStream_t stream);
+
 }  // namespace bitnet

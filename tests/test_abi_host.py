@@ -153,3 +153,59 @@ def test_host_packer_degenerate_tensors(orc):
     pw = tw.pack(W)
     t, _ = orc.unpack(pw.packed.numpy(), 16)
     assert np.all(t == -1)
+
+
+# ------------------------------------------------------------------ I2_S (host memory)
+
+@pytest.mark.parametrize("N,K", [(1, 128), (24, 48), (40, 2560), (9, 4352)])
+@pytest.mark.parametrize("order", ["strided", "consecutive"])
+def test_host_i2s_matches_oracle(orc, N, K, order):
+    """Export of a host-packed weight equals the oracle's I2_S bytes of the same
+    codes and scale; import of those bytes gives back the layout-v1 bytes."""
+    W = wl.draw_weight((N, K), seed=N * 3 + K, dist="laplace")
+    pw = tw.pack(W)
+    t, ws, _, _ = orc.weight_quant(_bits(W))
+    buf = tw.i2s_export(pw, order)
+    assert np.array_equal(buf.numpy(), orc.i2s_pack(t, np.float32(1) / ws[0], order))
+    back = tw.i2s_import(buf, N, K, order)
+    assert torch.equal(back.packed, pw.packed)
+    assert torch.equal(back.w_scale, torch.full((N,), np.float32(1) / (np.float32(1) / ws[0])))
+
+
+def test_host_i2s_golden_block():
+    """The hand-worked block of tests/golden/i2s_block.txt through the library."""
+    import pins
+    g = pins.read_golden("i2s_block.txt")
+    t = np.array([int(v) for v in g["T"][0]], dtype=np.int8)
+    for order, key in (("strided", "STRIDED"), ("consecutive", "CONSECUTIVE")):
+        raw = torch.tensor([int(b, 16) for b in g[key][0]], dtype=torch.uint8)
+        pw = tw.i2s_import(raw, 1, 128, order)
+        assert pw.w_scale.item() == 2.0                     # 1 / 0.5
+        fields = torch.stack([(pw.packed[0] >> sh) & 3 for sh in (0, 2, 4, 6)], -1)   # [32 bytes, p]
+        k = torch.arange(128)
+        got = fields[4 * (k // 16) + k % 4, (k % 16) // 4].to(torch.int8) - 1
+        assert np.array_equal(got.numpy(), t)
+        assert torch.equal(tw.i2s_export(pw, order), raw)
+
+
+def test_host_i2s_errors():
+    L = _lib.lib()
+    assert L.bitnet_i2s_bytes(3, 16) == -1 and L.bitnet_i2s_bytes(8, 16) == 36 and L.bitnet_i2s_bytes(1, 24) == -1
+    W = wl.draw_weight((4, 64), seed=1)
+    pw = tw.pack(W)
+    buf = tw.i2s_export(pw)
+    bad = buf.clone()
+    bad[5] = 0xFF                                           # fields holding 3
+    with pytest.raises(tw.BitnetError, match="holds 3"):
+        tw.i2s_import(bad, 4, 64)
+    neg = buf.clone()
+    neg[-4:] = torch.tensor(np.array([-1.0], dtype=np.float32).view(np.uint8))
+    with pytest.raises(tw.BitnetError, match="not positive"):
+        tw.i2s_import(neg, 4, 64)
+    two = tw.pack(W, (2, 2))                                # two source tensors: two scales
+    if two.w_scale[0] != two.w_scale[2]:
+        with pytest.raises(tw.BitnetError, match="differs between rows"):
+            tw.i2s_export(two)
+    st = L.bitnet_i2s_import(_lib.MEM_HOST, None, buf.data_ptr(), 4, 64, 7, pw.packed.data_ptr(),
+                             pw.w_scale.data_ptr())
+    assert st == _lib.ERR_INVALID_ARG and b"order" in L.bitnet_last_error()

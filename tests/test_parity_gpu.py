@@ -286,6 +286,45 @@ def test_grouped_rmsnorm(orc, kernel, monkeypatch):
             check_y_tol(y, ref)
 
 
+# ------------------------------------------------------------------- I2_S
+
+@pytest.mark.parametrize("N,K", [(24, 48), (2560, 2560), (3, 4352), (6912, 2560), (640, 6912)])
+@pytest.mark.parametrize("order", ["strided", "consecutive"])
+def test_i2s_device(orc, N, K, order):
+    """Device export of a packed weight equals the oracle's I2_S bytes; device import
+    of them gives back the layout-v1 bytes and the scale, and the imported weight
+    runs through linear to the oracle's outputs."""
+    W = wl.draw_weight((N, K), seed=N + 7 * K, dist="normal")
+    pw = tw.pack(W.to(DEV))
+    t, ws, _, _ = orc.weight_quant(bits(W))
+    s = np.float32(1) / ws[0]
+    buf = tw.i2s_export(pw, order)
+    assert np.array_equal(buf.cpu().numpy(), orc.i2s_pack(t, s, order))
+    back = tw.i2s_import(buf, N, K, order)
+    assert torch.equal(back.packed, pw.packed)
+    assert np.array_equal(f32bits(back.w_scale.cpu().numpy()), f32bits(np.full(N, np.float32(1) / s)))
+    if N <= 2560:
+        x = wl.draw_activation((2, K), seed=N)
+        y = tw.bitlinear(x.to(DEV), back)
+        qo, ao, _ = orc.act_quant(bits(x))
+        check_y(y, orc.epilogue(orc.int_dot(qo, t), ao, np.full(N, np.float32(1) / s)))
+
+
+def test_i2s_device_rejects_bad_fields():
+    W = wl.draw_weight((8, 64), seed=2).to(DEV)
+    buf = tw.i2s_export(tw.pack(W))
+    buf[3] = 0xFF
+    with pytest.raises(tw.BitnetError, match="holds 3"):
+        tw.i2s_import(buf, 8, 64)
+    buf = tw.i2s_export(tw.pack(W))
+    buf[-4:] = 0                                         # scale +0
+    with pytest.raises(tw.BitnetError, match="not positive"):
+        tw.i2s_import(buf, 8, 64)
+    two = tw.pack((W.float() * torch.tensor([[1.0]] * 4 + [[3.0]] * 4, device=DEV)).to(torch.bfloat16), (4, 4))
+    with pytest.raises(tw.BitnetError, match="differs between rows"):
+        tw.i2s_export(two)
+
+
 # -------------------------------------------------------------------- linear
 
 LINEAR_CASES = [
