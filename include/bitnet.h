@@ -333,6 +333,25 @@ bitnet_status_t bitnet_i2s_export(bitnet_mem_t where, hipStream_t stream, const 
                                   const float* w_scale, int64_t N, int64_t K, bitnet_i2s_order_t order,
                                   uint8_t* i2s);
 
+/*
+ * Packed-weight files: a versioned container for layout v1, so packing (an
+ * offline conversion [Guide s3.3]) is done once.  Host memory, synchronous.
+ * Format (little-endian): a 64-byte header -- magic "BTNLV1\0\0", u32
+ * version (1), u32 header size (64), i64 N, K, Kp, i32 segment count, u32
+ * layout (1 = layout v1), u64 FNV-1a-64 of every byte after the header, u64
+ * reserved (0) -- then packed [N][Kp/4], w_scale [N] fp32, the segments' row
+ * counts (i64) and means (fp32).
+ * bitnet_load_packed with packed == NULL only reads the header into N, K and
+ * n_segs (to size the buffers); otherwise it fills all four arrays and checks
+ * the checksum.  Errors: INVALID_ARG (I/O, bad or inconsistent file,
+ * checksum), UNSUPPORTED (another version or layout).
+ */
+bitnet_status_t bitnet_save_packed(const char* path, const uint8_t* packed, const float* w_scale,
+                                   int64_t N, int64_t K, const int64_t* seg_rows, const float* seg_mean,
+                                   int32_t n_segs);
+bitnet_status_t bitnet_load_packed(const char* path, int64_t* N, int64_t* K, int32_t* n_segs,
+                                   uint8_t* packed, float* w_scale, int64_t* seg_rows, float* seg_mean);
+
 /* Static text for a status code. */
 const char* bitnet_status_string(bitnet_status_t s);
 

@@ -125,6 +125,36 @@ def i2s_export(w: PackedWeight, order: str = "strided") -> torch.Tensor:
     return out
 
 
+def save_packed(path, w: PackedWeight, segments=None):
+    """Write w (with the row counts of its source tensors, default one) to a
+    versioned packed-weight file."""
+    segs = torch.tensor(list(segments) if segments else [w.N], dtype=torch.int64)
+    if segs.numel() != w.seg_mean.numel():
+        raise ValueError("one row count per segment of w")
+    packed, w_scale = w.packed.cpu().contiguous(), w.w_scale.cpu().contiguous()
+    seg_mean = w.seg_mean.to(torch.float32).contiguous()
+    _lib.check(_lib.lib().bitnet_save_packed(str(path).encode(), packed.data_ptr(), w_scale.data_ptr(), w.N, w.K,
+                                             segs.data_ptr(), seg_mean.data_ptr(), segs.numel()))
+
+
+def load_packed(path, device="cpu"):
+    """(PackedWeight, segment row counts) from a packed-weight file; tensors on ``device``."""
+    L = _lib.lib()
+    N, K, ns = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _lib.check(L.bitnet_load_packed(str(path).encode(), ctypes.byref(N), ctypes.byref(K), ctypes.byref(ns),
+                                    None, None, None, None))
+    N, K, ns = N.value, K.value, ns.value
+    packed = torch.empty((N, padded_k(K) // 4), dtype=torch.uint8)
+    w_scale = torch.empty(N, dtype=torch.float32)
+    segs = torch.empty(ns, dtype=torch.int64)
+    seg_mean = torch.empty(ns, dtype=torch.float32)
+    _lib.check(L.bitnet_load_packed(str(path).encode(), ctypes.byref(ctypes.c_int64()), ctypes.byref(ctypes.c_int64()),
+                                    ctypes.byref(ctypes.c_int32()), packed.data_ptr(), w_scale.data_ptr(),
+                                    segs.data_ptr(), seg_mean.data_ptr()))
+    w = PackedWeight(packed.to(device), w_scale.to(device), N, K, seg_mean, torch.full((ns,), -1, dtype=torch.int64))
+    return w, segs.tolist()
+
+
 class _nullctx:
     def __enter__(self):
         return None

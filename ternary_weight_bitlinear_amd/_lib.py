@@ -43,6 +43,8 @@ SIGNATURES = {
     "bitnet_i2s_bytes": (_i64, [_i64, _i64]),
     "bitnet_i2s_import": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
     "bitnet_i2s_export": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp]),
+    "bitnet_save_packed": (ctypes.c_int, [ctypes.c_char_p, _vp, _vp, _i64, _i64, _vp, _vp, _i32]),
+    "bitnet_load_packed": (ctypes.c_int, [ctypes.c_char_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "bitnet_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bitnet_last_error": (ctypes.c_char_p, []),
 }

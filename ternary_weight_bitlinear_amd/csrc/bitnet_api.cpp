@@ -505,6 +505,118 @@ bitnet_status_t bitnet_i2s_export(bitnet_mem_t where, hipStream_t stream, const 
     return ok();
 }
 
+// ------------------------------------------------------- packed-weight files
+
+namespace {
+
+constexpr char kFileMagic[8] = {'B', 'T', 'N', 'L', 'V', '1', 0, 0};
+constexpr uint32_t kFileVersion = 1;
+constexpr uint32_t kFileHeaderBytes = 64;
+
+struct FileHeader {                 // little-endian, 64 bytes
+    char magic[8];
+    uint32_t version;
+    uint32_t header_bytes;
+    int64_t N, K, Kp;
+    int32_t n_segs;
+    uint32_t layout;                // 1: layout v1
+    uint64_t payload_fnv1a;         // FNV-1a 64 over every byte after the header
+    uint64_t reserved;
+};
+static_assert(sizeof(FileHeader) == kFileHeaderBytes, "file header layout");
+
+uint64_t fnv1a(uint64_t h, const void* p, size_t n) {
+    const auto* b = static_cast<const unsigned char*>(p);
+    for (size_t i = 0; i < n; ++i) h = (h ^ b[i]) * 0x100000001b3ull;
+    return h;
+}
+
+struct File {
+    FILE* f = nullptr;
+    ~File() {
+        if (f) fclose(f);
+    }
+};
+
+}  // namespace
+
+bitnet_status_t bitnet_save_packed(const char* path, const uint8_t* packed, const float* w_scale, int64_t N,
+                                   int64_t K, const int64_t* seg_rows, const float* seg_mean, int32_t n_segs) {
+    const char* fn = "bitnet_save_packed";
+    bitnet_status_t s = check_dims(fn, 1, N, K);
+    if (s != BITNET_OK) return s;
+    if (!path || !packed || !w_scale || !seg_rows || !seg_mean || n_segs <= 0)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: need path, packed, w_scale, seg_rows, seg_mean and n_segs > 0", fn);
+    int64_t rows = 0;
+    for (int32_t i = 0; i < n_segs; ++i) {
+        if (seg_rows[i] <= 0) return fail(BITNET_ERR_INVALID_ARG, "%s: segment %d is empty", fn, i);
+        rows += seg_rows[i];
+    }
+    if (rows != N) return fail(BITNET_ERR_INVALID_ARG, "%s: segment rows sum to %lld, not N", fn, (long long)rows);
+    const int64_t Kp = padded_k(K);
+    const size_t nb_packed = static_cast<size_t>(N * (Kp / 4)), nb_scale = static_cast<size_t>(N) * 4;
+    FileHeader h{};
+    memcpy(h.magic, kFileMagic, sizeof h.magic);
+    h.version = kFileVersion;
+    h.header_bytes = kFileHeaderBytes;
+    h.N = N; h.K = K; h.Kp = Kp; h.n_segs = n_segs; h.layout = 1;
+    uint64_t c = 0xcbf29ce484222325ull;
+    c = fnv1a(c, packed, nb_packed);
+    c = fnv1a(c, w_scale, nb_scale);
+    c = fnv1a(c, seg_rows, static_cast<size_t>(n_segs) * 8);
+    c = fnv1a(c, seg_mean, static_cast<size_t>(n_segs) * 4);
+    h.payload_fnv1a = c;
+    File f;
+    f.f = fopen(path, "wb");
+    if (!f.f) return fail(BITNET_ERR_INVALID_ARG, "%s: cannot open %s for writing", fn, path);
+    if (fwrite(&h, sizeof h, 1, f.f) != 1 || fwrite(packed, 1, nb_packed, f.f) != nb_packed ||
+        fwrite(w_scale, 1, nb_scale, f.f) != nb_scale ||
+        fwrite(seg_rows, 8, static_cast<size_t>(n_segs), f.f) != static_cast<size_t>(n_segs) ||
+        fwrite(seg_mean, 4, static_cast<size_t>(n_segs), f.f) != static_cast<size_t>(n_segs))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: short write to %s", fn, path);
+    if (fclose(f.f) != 0) {
+        f.f = nullptr;
+        return fail(BITNET_ERR_INVALID_ARG, "%s: closing %s failed", fn, path);
+    }
+    f.f = nullptr;
+    return ok();
+}
+
+bitnet_status_t bitnet_load_packed(const char* path, int64_t* N, int64_t* K, int32_t* n_segs, uint8_t* packed,
+                                   float* w_scale, int64_t* seg_rows, float* seg_mean) {
+    const char* fn = "bitnet_load_packed";
+    if (!path || !N || !K || !n_segs) return fail(BITNET_ERR_INVALID_ARG, "%s: need path, N, K and n_segs", fn);
+    File f;
+    f.f = fopen(path, "rb");
+    if (!f.f) return fail(BITNET_ERR_INVALID_ARG, "%s: cannot open %s", fn, path);
+    FileHeader h{};
+    if (fread(&h, sizeof h, 1, f.f) != 1 || memcmp(h.magic, kFileMagic, sizeof h.magic) != 0)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: %s is not a packed-weight file", fn, path);
+    if (h.version != kFileVersion || h.header_bytes != kFileHeaderBytes || h.layout != 1)
+        return fail(BITNET_ERR_UNSUPPORTED, "%s: file version %u, layout %u not supported (this library: %u, 1)", fn,
+                    h.version, h.layout, kFileVersion);
+    if (check_dims(fn, 1, h.N, h.K) != BITNET_OK || h.Kp != padded_k(h.K) || h.n_segs <= 0 || h.n_segs > h.N)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: %s has an inconsistent header", fn, path);
+    *N = h.N;
+    *K = h.K;
+    *n_segs = h.n_segs;
+    if (!packed) return ok();                       // header query
+    if (!w_scale || !seg_rows || !seg_mean)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: need packed, w_scale, seg_rows and seg_mean", fn);
+    const size_t nb_packed = static_cast<size_t>(h.N * (h.Kp / 4)), nb_scale = static_cast<size_t>(h.N) * 4;
+    const size_t ns = static_cast<size_t>(h.n_segs);
+    if (fread(packed, 1, nb_packed, f.f) != nb_packed || fread(w_scale, 1, nb_scale, f.f) != nb_scale ||
+        fread(seg_rows, 8, ns, f.f) != ns || fread(seg_mean, 4, ns, f.f) != ns)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: %s is truncated", fn, path);
+    uint64_t c = 0xcbf29ce484222325ull;
+    c = fnv1a(c, packed, nb_packed);
+    c = fnv1a(c, w_scale, nb_scale);
+    c = fnv1a(c, seg_rows, ns * 8);
+    c = fnv1a(c, seg_mean, ns * 4);
+    if (c != h.payload_fnv1a) return fail(BITNET_ERR_INVALID_ARG, "%s: %s fails its checksum", fn, path);
+    return ok();
+}
+
 // Kernels of a grouped plan.  BITNET_GROUP_KERNEL=persistent, read when a
 // plan is made, skips the streaming kernel (for comparisons; results are
 // identical).

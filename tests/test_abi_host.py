@@ -209,3 +209,37 @@ def test_host_i2s_errors():
     st = L.bitnet_i2s_import(_lib.MEM_HOST, None, buf.data_ptr(), 4, 64, 7, pw.packed.data_ptr(),
                              pw.w_scale.data_ptr())
     assert st == _lib.ERR_INVALID_ARG and b"order" in L.bitnet_last_error()
+
+
+# -------------------------------------------------------------- packed-weight files
+
+def test_packed_file_roundtrip_and_damage(tmp_path):
+    W = wl.draw_weight((70, 304), seed=9, dist="laplace")
+    pw = tw.pack(W, (30, 40))
+    f = tmp_path / "w.btnl"
+    tw.save_packed(f, pw, (30, 40))
+    raw = f.read_bytes()
+    assert raw[:8] == b"BTNLV1\0\0" and len(raw) == 64 + 70 * tw.padded_k(304) // 4 + 70 * 4 + 2 * 8 + 2 * 4
+    back, segs = tw.load_packed(f)
+    assert segs == [30, 40] and (back.N, back.K) == (70, 304)
+    assert torch.equal(back.packed, pw.packed) and torch.equal(back.w_scale, pw.w_scale)
+    assert torch.equal(back.seg_mean, pw.seg_mean)
+    damaged = bytearray(raw)
+    damaged[64 + 100] ^= 0x04                          # one code field changed
+    (tmp_path / "d.btnl").write_bytes(bytes(damaged))
+    with pytest.raises(tw.BitnetError, match="checksum"):
+        tw.load_packed(tmp_path / "d.btnl")
+    newer = bytearray(raw)
+    newer[8] = 2                                       # version 2
+    (tmp_path / "v.btnl").write_bytes(bytes(newer))
+    with pytest.raises(tw.BitnetError) as e:
+        tw.load_packed(tmp_path / "v.btnl")
+    assert e.value.status == _lib.ERR_UNSUPPORTED
+    (tmp_path / "t.btnl").write_bytes(raw[:-10])
+    with pytest.raises(tw.BitnetError, match="truncated"):
+        tw.load_packed(tmp_path / "t.btnl")
+    (tmp_path / "m.btnl").write_bytes(b"NOTAFILE" + raw[8:])
+    with pytest.raises(tw.BitnetError, match="not a packed-weight file"):
+        tw.load_packed(tmp_path / "m.btnl")
+    with pytest.raises(ValueError):
+        tw.save_packed(f, pw)                          # two segments need two row counts
