@@ -75,6 +75,14 @@
  *   R13 The appended float is the quantisation scale s = 1/mean|W| as the
  *       page names it; the dequantisation factor is 1/s.
  *
+ * The W1.58A16 variant [BitVLA s5 "On-device gotchas": where the in-graph
+ * 8-bit activation quantiser stalled the GPU, the path kept the activations
+ * in 16-bit and quantised only the weights]:
+ *   R14 y[m][n] = w_scale[n] * sum_k x[m][k] * t[n][k] with the activations
+ *       as given; the oracle evaluates it in fp64 (each product exact, one
+ *       rounding per addition, k ascending) -- the reference value that a
+ *       kernel summing in fp32, in its own order, is held to within a bound.
+ *
  * Everything here is a direct loop over the definition.  No blocking, no
  * fusion, no intrinsics.
  */
@@ -433,6 +441,29 @@ void orc_swiglu(const void* gate, const void* up, int dtype, int64_t M, int64_t 
             float a = load_elem(gate, dtype, m * ld + k);
             float u = load_elem(up, dtype, m * ld + k);
             h[m * K + k] = a / (1.0f + orc_exp_f32(-a)) * u;
+        }
+}
+
+/* ------------------------------------------------------------- W1.58A16 */
+
+/*
+ * y [M][N] fp64 = w_scale[n] * sum_{k<K} x[m][k] * t[n][k] (R14); also the
+ * magnitude sum_k |x[m][k] * t[n][k]| into mag [M][N] (for error bounds).
+ * x is bf16 or fp32 with row stride ldx; t has row stride K.
+ */
+void orc_linear_a16(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, const int8_t* t, int64_t N,
+                    const float* w_scale, double* y, double* mag)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0, a = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = (double)load_elem(x, dtype, m * ldx + k) * (double)t[n * K + k];
+                s += p;
+                a += fabs(p);
+            }
+            y[m * N + n] = s * (double)w_scale[n];
+            mag[m * N + n] = a;
         }
 }
 

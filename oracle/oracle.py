@@ -78,6 +78,8 @@ class Oracle:
         lib.orc_exp_f32.argtypes, lib.orc_exp_f32.restype = [f32], f32
         lib.orc_swiglu.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp]
         lib.orc_swiglu.restype = None
+        lib.orc_linear_a16.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, vp, vp, vp]
+        lib.orc_linear_a16.restype = None
         lib.orc_int_dot.argtypes = [vp, i64, i64, vp, i64, vp, ctypes.c_int]
         lib.orc_int_dot.restype = ctypes.c_int
         lib.orc_int_dot_pairs.argtypes = [vp, i64, vp, i64, vp, vp, vp]
@@ -219,6 +221,19 @@ class Oracle:
     def swiglu_rms_act_quant(self, gate: np.ndarray, up: np.ndarray, g: np.ndarray, eps: float = 1e-6):
         """ActQuant(RMSNorm(silu(gate) * up, g)) for the down projection."""
         return self.rms_act_quant(self.swiglu(gate, up), g, eps)
+
+    # --------------------------------------------------------- W1.58A16
+    def linear_a16(self, x: np.ndarray, t: np.ndarray, w_scale: np.ndarray):
+        """fp64 y [M, N] = w_scale * (x @ t.T) with bf16/fp32 x, and sum |x*t| per output."""
+        x = np.ascontiguousarray(x)
+        t = np.ascontiguousarray(t, dtype=np.int8)
+        w_scale = np.ascontiguousarray(w_scale, dtype=np.float32)
+        M, K = x.shape
+        N = t.shape[0]
+        y = np.empty((M, N), dtype=np.float64)
+        mag = np.empty((M, N), dtype=np.float64)
+        self.lib.orc_linear_a16(_ptr(x), _dtype_code(x), M, K, K, _ptr(t), N, _ptr(w_scale), _ptr(y), _ptr(mag))
+        return y, mag
 
     # ------------------------------------------------------ integer dot
     def int_dot(self, q: np.ndarray, t: np.ndarray, nthreads: int = 1) -> np.ndarray:

@@ -442,6 +442,34 @@ def pin_swiglu_decimal(orc):
     assert h[0, 4] == 0
 
 
+# ----------------------------------------------------------------- W1.58A16
+
+def pin_a16_closed_forms_and_matmul(orc):
+    """W = permutation P gives y = x[:, pi] * w_scale exactly; constant codes give
+    y = (sum_k x) * w_scale; random codes agree with numpy's fp64 matmul to 1e-12
+    of sum |x*t| (a library routine on a special case); mag is that sum."""
+    rng = np.random.default_rng(59)
+    K = 64
+    x = rng_bf16(rng, (3, K))
+    xv = bf16_bits_to_f32(x).astype(np.float64)
+    perm = rng.permutation(K)
+    t = np.zeros((K, K), dtype=np.int8)
+    t[np.arange(K), perm] = 1
+    ws = np.full(K, 0.375, dtype=np.float32)
+    y, mag = orc.linear_a16(x, t, ws)
+    assert np.array_equal(y, xv[:, perm] * 0.375)
+    tc = -np.ones((5, K), dtype=np.int8)
+    y, _ = orc.linear_a16(x, tc, np.ones(5, dtype=np.float32))
+    assert np.allclose(y, -xv.sum(1)[:, None], rtol=0, atol=1e-12)
+    t = rng.integers(-1, 2, size=(40, K)).astype(np.int8)
+    ws = rng.random(40).astype(np.float32)
+    y, mag = orc.linear_a16(x, t, ws)
+    want = (xv @ t.T.astype(np.float64)) * ws.astype(np.float64)
+    absum = np.abs(xv) @ np.abs(t.T.astype(np.float64))
+    assert np.all(np.abs(y - want) <= 1e-12 * absum * ws + 1e-300)
+    assert np.allclose(mag, absum, rtol=1e-15, atol=0)
+
+
 # --------------------------------------------------------------------- I2_S
 
 def pin_i2s_golden(orc):

@@ -90,6 +90,12 @@ MUTANTS = [
      "float r = t - n * 0.693145752f;"),
     ("exp polynomial one degree short", "    p = p * r + 1.0f / 24.0f;\n", "    p = 1.0f / 24.0f;\n"),
     ("exp scaled by 2^(n+1)", "return ldexpf(p, (int)n);", "return ldexpf(p, (int)n + 1);"),
+    ("A16 product transposed",
+     "double p = (double)load_elem(x, dtype, m * ldx + k) * (double)t[n * K + k];",
+     "double p = (double)load_elem(x, dtype, m * ldx + k) * (double)t[(k % N) * K + (n % K)];"),
+    ("A16 scale left out", "y[m * N + n] = s * (double)w_scale[n];", "y[m * N + n] = s;"),
+    ("A16 drops the last k", "for (int64_t k = 0; k < K; ++k) {\n                double p",
+     "for (int64_t k = 0; k < K - 1; ++k) {\n                double p"),
     ("I2_S strided fields in reversed bit order", "6 - 2 * (int)(v / 32)", "2 * (int)(v / 32)"),
     ("I2_S consecutive fields in reversed bit order", "6 - 2 * (int)(v % 4)", "2 * (int)(v % 4)"),
     ("I2_S stride of 16", "return consecutive ? v / 4 : v % 32;", "return consecutive ? v / 4 : v % 16;"),
