@@ -174,6 +174,37 @@ def bench_norm(tw, wl, torch, steps, warmup):
     return out
 
 
+def bench_a16(tw, wl, torch, steps, warmup):
+    """The W1.58A16 variant (BitVLA s5: bf16 activations, ternary weights) at M = 1:
+    the c2 30-layer stream as a HIP graph of 210 launches, and one large projection
+    (gate|up 13824 x 2560) alone; GB/s of packed weights."""
+    items, nbytes = setup_decode(tw, wl, torch, 30)
+
+    def calls():
+        for x, pw, y in items:
+            tw.linear_a16(x, pw, out=y)
+    calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    ms = time_region(torch, g.replay, steps, warmup)
+    out = dict(stream=dict(value=nbytes / (ms * 1e-3) / 1e9, unit="GB/s", ms_per_step=ms, launches_per_step=210))
+    del g, items
+    torch.cuda.empty_cache()
+    W = wl.draw_weight((13824, 2560), seed=3, device="cuda")
+    pw = tw.pack(W)
+    x = wl.draw_activation((1, 2560), seed=4, device="cuda")
+    y = torch.empty((1, 13824), device="cuda")
+    ms1 = time_region(torch, lambda: tw.linear_a16(x, pw, out=y), steps * 5, warmup)
+    nb = 13824 * 2560 // 4
+    gbps = nb / (ms1 * 1e-3) / 1e9
+    out["gate_up_13824x2560"] = dict(value=gbps, unit="GB/s", us_per_launch=ms1 * 1e3,
+                                     roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s",
+                                                   frac=gbps / HBM_PEAK_GBPS, traffic=None))
+    return out
+
+
 def cpu_baseline_decode(wl, torch, budget_s: float, max_layers: int = 3):
     """The oracle's ActQuant + int dot + epilogue over the first layers' projections
     (weights quantised once, untimed), cycled until budget_s of timed work."""
@@ -300,6 +331,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-call", action="store_true")
     ap.add_argument("--no-norm", action="store_true", help="skip the input-norm measurements")
+    ap.add_argument("--no-a16", action="store_true", help="skip the W1.58A16 measurements")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first fill and copy a buffer of this many MiB three times: plain kernels of "
@@ -346,6 +378,8 @@ def main() -> int:
             line["cpu_baseline"] = cpu_baseline_decode(wl, torch, args.cpu_seconds)
         if not args.no_norm:
             line["input_norm"] = bench_norm(tw, wl, torch, args.steps, args.warmup)
+        if not args.no_a16:
+            line["w158a16"] = bench_a16(tw, wl, torch, args.steps, args.warmup)
     if args.only in (None, "prefill"):
         g = bench_prefill(tw, wl, torch, args.steps, args.warmup, torch.bfloat16)
         if not args.no_cpu_baseline:

@@ -293,6 +293,22 @@ bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_
 const char* bitnet_group_plan_kernel(const bitnet_group_plan_t* plan);
 
 /*
+ * The W1.58A16 variant [BitVLA s5: where the 8-bit activation quantiser
+ * stalled the GPU, activations stayed in 16 bits]:
+ * y[m][n] = w_scale[n] * sum_k x[m][k] * t[n][k], x bf16 [M, K] (row stride
+ * ldx, rows 16-byte aligned), packed / w_scale as for bitnet_linear_forward,
+ * y fp32 or bf16 [M, N] (ldy).  The sum runs in fp32 on the matrix cores in
+ * the hardware's order: |y - exact| <= w_scale[n] * (K/32 + 64) * 2^-24 *
+ * sum_k |x[m][k] * t[n][k]| (+ the bf16 rounding for bf16 y).  A decode-size
+ * kernel: every 16 tokens re-read the packed weight.  Errors: UNSUPPORTED for
+ * a non-bf16 x; INVALID_ARG as bitnet_linear_forward; HIP.
+ */
+bitnet_status_t bitnet_linear_a16(hipStream_t stream, const void* x, bitnet_dtype_t x_dtype,
+                                  int64_t M, int64_t K, int64_t ldx,
+                                  const uint8_t* packed, const float* w_scale, int64_t N,
+                                  void* y, bitnet_dtype_t y_dtype, int64_t ldy);
+
+/*
  * I2_S interchange [Guide s3.3 "I2_S Ternary Packing"], for weights
  * converted by bitnet.cpp's tooling.  An I2_S buffer of one [N, K] tensor is
  * N*K/4 code bytes followed by one fp32 scale s = 1/mean|W| (little-endian),

@@ -241,6 +241,19 @@ def bitlinear(x: torch.Tensor, w: PackedWeight, out_dtype=torch.float32, out: to
     return y
 
 
+def linear_a16(x: torch.Tensor, w: PackedWeight, out_dtype=torch.float32, out: torch.Tensor | None = None):
+    """W1.58A16: y = w_scale * (x . t) with bf16 activations x [M, K] kept unquantised."""
+    ldx = _rows(x, "x")
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError("x and the packed weight disagree on K")
+    y = out if out is not None else torch.empty((M, w.N), dtype=out_dtype, device=x.device)
+    with torch.cuda.device(x.device):
+        _lib.check(_lib.lib().bitnet_linear_a16(_stream(x), x.data_ptr(), _dtype(x), M, K, ldx, w.packed.data_ptr(),
+                                                w.w_scale.data_ptr(), w.N, y.data_ptr(), _dtype(y), _rows(y, "y")))
+    return y
+
+
 def rmsnorm_bitlinear(x: torch.Tensor, norm_w: torch.Tensor, w: PackedWeight, eps: float = 1e-6,
                       up: torch.Tensor | None = None, out_dtype=torch.float32, out: torch.Tensor | None = None,
                       workspace=None):

@@ -40,6 +40,8 @@ SIGNATURES = {
                                                  _vp]),
     "bitnet_bitlinear_grouped": (ctypes.c_int, [_vp, _vp]),
     "bitnet_group_plan_kernel": (ctypes.c_char_p, [_vp]),
+    "bitnet_linear_a16": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _i64, _vp,
+                                         ctypes.c_int, _i64]),
     "bitnet_i2s_bytes": (_i64, [_i64, _i64]),
     "bitnet_i2s_import": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
     "bitnet_i2s_export": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp]),

@@ -23,7 +23,7 @@ BUILD = PKG / "_build"
 LIBRARY = PKG / "libbitnet_hip.so"
 ARCH = "gfx950"
 
-SOURCES = ["bitnet_api.cpp", "act_quant.hip", "gemv.hip", "gemm.hip", "pack.hip", "i2s.hip"]
+SOURCES = ["bitnet_api.cpp", "act_quant.hip", "gemv.hip", "gemm.hip", "pack.hip", "i2s.hip", "gemv_a16.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

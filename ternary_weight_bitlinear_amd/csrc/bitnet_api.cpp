@@ -391,6 +391,28 @@ bitnet_status_t bitnet_rmsnorm_bitlinear_forward(hipStream_t stream, const void*
                           y_dtype, ldy, q, a_scale, q_rowsum, fn);
 }
 
+// -------------------------------------------------------------- W1.58A16
+
+bitnet_status_t bitnet_linear_a16(hipStream_t stream, const void* x, bitnet_dtype_t x_dtype, int64_t M, int64_t K,
+                                  int64_t ldx, const uint8_t* packed, const float* w_scale, int64_t N, void* y,
+                                  bitnet_dtype_t y_dtype, int64_t ldy) {
+    const char* fn = "bitnet_linear_a16";
+    bitnet_status_t s = check_dims(fn, M, N, K);
+    if (s != BITNET_OK) return s;
+    if (!x || !packed || !w_scale || !y) return fail(BITNET_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (x_dtype != BITNET_BF16)
+        return fail(BITNET_ERR_UNSUPPORTED, "%s: W1.58A16 takes bf16 activations (x_dtype %d)", fn, (int)x_dtype);
+    if (!valid_dtype(y_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad y dtype %d", fn, (int)y_dtype);
+    if (ldx < K || ldy < N) return fail(BITNET_ERR_INVALID_ARG, "%s: ldx < K or ldy < N", fn);
+    if (!aligned(x, 16) || (ldx * 2) % 16 != 0 || !aligned(packed, 16) || !aligned(w_scale, 4) ||
+        !aligned(y, y_dtype == BITNET_F32 ? 4 : 2))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned pointer (x rows and packed must be 16-byte aligned)", fn);
+    hipError_t e = bitnet::launch_gemv_a16(static_cast<const uint16_t*>(x), ldx, M, K, padded_k(K), packed, w_scale,
+                                           N, y, y_dtype == BITNET_BF16, ldy, stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
 // ------------------------------------------------------------------ I2_S
 
 int64_t bitnet_i2s_bytes(int64_t N, int64_t K) {

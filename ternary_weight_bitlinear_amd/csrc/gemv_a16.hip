@@ -1,0 +1,135 @@
+// gemv_a16.hip -- the W1.58A16 variant: bf16 activations x ternary weights.
+//
+// "BitVLA -- 1.58-bit Vision-Language-Action on Core AI", s5 (On-device
+// gotchas): where the in-graph 8-bit activation quantiser stalled the GPU,
+// the path ran with 16-bit activations and ternary weights.  Here
+// y[m][n] = w_scale[n] * sum_k x[m][k] * t[n][k] with x in bf16 as given and
+// the sum in fp32 on the matrix cores (v_mfma_f32_16x16x32_bf16); the order
+// of that sum is the hardware's, so results are held to a bound derived from
+// it rather than to exact bits.
+//
+// Layout as the A8 split-K decode kernel: a workgroup owns 16 output rows and
+// 16 tokens; lane group g of wave w takes every 16th 64-code chunk of the row,
+// starting at 4w + g, so the 4 waves read contiguous 256-byte runs; partial
+// 16 x 16 tiles meet in LDS.  The packed codes go straight into MFMA operands:
+// two 2-bit fields of a word (8 consecutive k) become 8 bf16 values of t in 12
+// VALU ops, each pair by two byte permutes against a 3-entry table of the bf16
+// bytes of -1, 0, +1.  A operands are 8 consecutive bf16 of the token row,
+// read from global memory (L1/L2-resident: every workgroup reads the same
+// rows).  Token tiles beyond the first 16 re-read the packed rows, so this is
+// a decode-size kernel.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace bitnet {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kUnroll = 4;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 bytes of t = u - 1 for stored codes u = 0, 1, 2 (-1.0, 0.0, +1.0):
+// low bytes 0x80, 0x00, 0x80 and high bytes 0xBF, 0x00, 0x3F.
+constexpr uint32_t kTableLo = 0x00800080u;
+constexpr uint32_t kTableHi = 0x003F00BFu;
+
+// Two bf16 values of t from the codes in bytes i0 and i1 of f (each 0..2):
+// a byte permute spreads them to [u0, u0, u1, u1], +4 on the odd bytes picks
+// the high-byte table, and a second permute looks both tables up.
+template <uint32_t kSpread>
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t f) {
+    const uint32_t sel = __builtin_amdgcn_perm(f, f, kSpread) + 0x04000400u;
+    return __builtin_amdgcn_perm(kTableHi, kTableLo, sel);
+}
+
+// B operand (8 bf16 of t, k ascending) from fields 2h and 2h+1 of a packed
+// word: field p holds k = 16j + 4p + b in byte b, so the two fields cover the
+// 8 consecutive k from 16j + 8h.
+__device__ __forceinline__ u32x4 expand_bf16(uint32_t w, int h) {
+    const uint32_t f0 = (w >> (4 * h)) & 0x03030303u;
+    const uint32_t f1 = (w >> (4 * h + 2)) & 0x03030303u;
+    return u32x4{bf16_pair<0x01010000u>(f0), bf16_pair<0x03030202u>(f0), bf16_pair<0x01010000u>(f1),
+                 bf16_pair<0x03030202u>(f1)};
+}
+
+template <bool kOutBf16>
+__global__ __launch_bounds__(kThreads) void gemv_a16_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
+                                                            int K, int Kp, const uint8_t* __restrict__ packed,
+                                                            const float* __restrict__ w_scale, int N, void* y,
+                                                            int64_t ldy) {
+    __shared__ float part[kWaves][16][17];
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int col = lane % 16;                          // token row (A) and output row (B) of this lane
+    const int grp = lane / 16;
+    const int n0 = blockIdx.x * 16;
+    const int m0 = blockIdx.y * 16;
+    const bool n_ok = n0 + col < N;
+    const bool m_ok = m0 + col < M;
+    const int chunks = Kp / 64;
+    const uint8_t* brow = packed + static_cast<int64_t>(n_ok ? n0 + col : 0) * (Kp / 4);
+    const uint16_t* xrow = x + static_cast<int64_t>(m_ok ? m0 + col : 0) * ldx;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // The loop and its exits are wave-uniform (an MFMA needs the whole wave);
+    // a lane group past the last chunk multiplies zeros.
+    for (int cw = 4 * wave; cw < chunks; cw += 16 * kUnroll) {
+        u32x4 bw[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int c = cw + grp + 16 * u;
+            bw[u] = (n_ok && c < chunks) ? gload<u32x4>(brow + 16 * c) : zero;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int c = cw + grp + 16 * u;
+            if (cw + 16 * u >= chunks) break;           // wave-uniform: nothing left
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = 64 * c + 16 * j + 8 * h;       // 8 consecutive k; K % 8 == 0
+                    const u32x4 a = (m_ok && c < chunks && k < K) ? gload<u32x4>(xrow + k) : zero;
+                    const u32x4 b = expand_bf16(bw[u][j], h);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+                }
+            }
+        }
+    }
+    // lane holds C[m = 4*grp + r][n = col] of this wave's share of k
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave][4 * grp + r][col] = acc[r];
+    __syncthreads();
+    const int m = threadIdx.x / 16, nc = threadIdx.x % 16;
+    const int n = n0 + nc;
+    if (m0 + m < M && n < N) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s += part[w][m][nc];
+        const float v = s * gload<float>(w_scale + n);
+        if constexpr (kOutBf16)
+            gstore<uint16_t>(static_cast<uint16_t*>(y) + (m0 + m) * ldy + n, f32_to_bf16(v));
+        else
+            gstore<float>(static_cast<float*>(y) + (m0 + m) * ldy + n, v);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_a16(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, int64_t Kp, const uint8_t* packed,
+                           const float* w_scale, int64_t N, void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((N + 15) / 16), static_cast<unsigned>((M + 15) / 16)), block(kThreads);
+    if (y_bf16)
+        gemv_a16_kernel<true><<<grid, block, 0, stream>>>(x, ldx, (int)M, (int)K, (int)Kp, packed, w_scale, (int)N, y,
+                                                          ldy);
+    else
+        gemv_a16_kernel<false><<<grid, block, 0, stream>>>(x, ldx, (int)M, (int)K, (int)Kp, packed, w_scale, (int)N,
+                                                           y, ldy);
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

@@ -40,6 +40,11 @@ hipError_t launch_pack(const void* W, bool w_bf16, int64_t N, int64_t K, int64_t
                        unsigned int* status_dev, uint8_t* packed, float* w_scale,
                        hipStream_t stream);
 
+// W1.58A16: y = w_scale * (x_bf16 . t), fp32 accumulation on bf16 MFMA; x rows
+// 16-byte aligned (ldx * 2 % 16 == 0).
+hipError_t launch_gemv_a16(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, int64_t Kp, const uint8_t* packed,
+                           const float* w_scale, int64_t N, void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
+
 // I2_S <-> layout v1 (status bits: 1 a field holds 3, 2 a scale is not
 // positive, 4 rows differ in scale on export).  The grid covers every output
 // byte and every row.

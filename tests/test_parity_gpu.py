@@ -325,6 +325,39 @@ def test_i2s_device_rejects_bad_fields():
         tw.i2s_export(two)
 
 
+# --------------------------------------------------------------- W1.58A16
+
+@pytest.mark.parametrize("M,N,K", [(1, 640, 2560), (3, 257, 1152), (16, 100, 2048), (1, 2560, 6912),
+                                   (20, 130, 1152), (1, 1, 16), (2, 4352, 4304)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_linear_a16(orc, M, N, K, out):
+    """bf16 activations x ternary weights against the oracle's fp64 value, within the
+    bound the header states for an fp32 sum in the hardware's order."""
+    x, W = wl.random_case(5100 + M * 3 + N, M, N, K, x_dist="normal_outliers")
+    pw = tw.pack(W.to(DEV))
+    base = torch.zeros((M, K + 8), dtype=torch.bfloat16, device=DEV)
+    base[:, :K] = x.to(DEV)
+    y = tw.linear_a16(base[:, :K], pw, out_dtype=out)          # ldx = K + 8: strided rows
+    t, ws, _, _ = orc.weight_quant(bits(W))
+    ye, mag = orc.linear_a16(bits(x), t, ws)
+    tol = ws.astype(np.float64)[None, :] * (K / 32 + 64) * 2.0 ** -24 * mag
+    got = y.float().cpu().numpy().astype(np.float64)
+    if out == torch.bfloat16:
+        tol = tol + np.abs(ye) * 2.0 ** -8
+    else:
+        tol = tol + np.abs(ye) * 2.0 ** -24
+    err = np.abs(got - ye)
+    assert np.all(err <= tol), float((err / np.maximum(tol, 1e-300)).max())
+
+
+def test_linear_a16_rejects_fp32_activations():
+    x = torch.zeros((1, 64), device=DEV)
+    pw = tw.pack(torch.ones((8, 64), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(tw.BitnetError) as e:
+        tw.linear_a16(x, pw)
+    assert e.value.status == _lib.ERR_UNSUPPORTED
+
+
 # -------------------------------------------------------------------- linear
 
 LINEAR_CASES = [
