@@ -401,7 +401,10 @@ __device__ __forceinline__ int find_problem(const Problems<kGrouped>& ps, int ti
     return lo;
 }
 
-// First tile whose first k step is at or after `s` (total_tiles if none).
+// The tile boundary nearest to batch `s`: the first tile of the workgroup
+// whose share starts at s (total_tiles if none).  Rounding to the nearest
+// boundary rather than the next one halves the largest excess of a share over
+// its exact part.
 template <bool kGrouped>
 __device__ __forceinline__ int first_tile_from_step(const Problems<kGrouped>& ps, int64_t s, int total_tiles) {
     int lo = 0, hi = ps.count - 1;              // last problem with step0 <= s
@@ -411,7 +414,7 @@ __device__ __forceinline__ int first_tile_from_step(const Problems<kGrouped>& ps
         else hi = mid - 1;
     }
     const GemvProblem p = ps.get(lo);
-    const int64_t t = (s - p.step0 + p.steps - 1) / p.steps;   // tiles of p that start before s
+    const int64_t t = (2 * (s - p.step0) + p.steps) / (2 * p.steps);   // nearest tile start, ties up
     if (t >= p.ntiles) return (lo + 1 < ps.count) ? ps.get(lo + 1).tile0 : total_tiles;
     return p.tile0 + static_cast<int>(t);
 }
@@ -627,6 +630,11 @@ __global__ __launch_bounds__(kThreads) void gemv_persistent_kernel(GemvProblem s
 #ifndef BITNET_STREAM_PER_CU
 #define BITNET_STREAM_PER_CU 2
 #endif
+// Share of a CU's first workgroup relative to its second, in percent (see
+// share_start).
+#ifndef BITNET_STREAM_FIRST_WEIGHT
+#define BITNET_STREAM_FIRST_WEIGHT 120
+#endif
 constexpr int kDepth = BITNET_STREAM_DEPTH;
 constexpr int kStreamMaxProblems = 16;          // problems one workgroup may touch
 constexpr uint32_t kStreamOutOfRange = 0x80000000u;
@@ -697,6 +705,19 @@ __device__ __forceinline__ void lds_read64(const void* p, v4i (&a)[4]) {
         : "memory");
 }
 
+// First batch of workgroup b's share of the launch's total_steps batches.
+// With two workgroups per CU the first n_first workgroups of the grid go one
+// to each CU and the rest second.  Measured on MI355X, the first workgroup on
+// a CU wins the CU's arbitration and streams about 1.2 to 1.3 times as fast as
+// the second, so it gets a share BITNET_STREAM_FIRST_WEIGHT percent of the
+// second's and the two finish closer together.  n_first = grid: equal shares.
+__host__ __device__ __forceinline__ int64_t share_start(int64_t total_steps, int b, int grid, int n_first) {
+    const int64_t f = b < n_first ? b : n_first;
+    const int64_t w = BITNET_STREAM_FIRST_WEIGHT * f + 100 * (b - f);
+    const int64_t all = BITNET_STREAM_FIRST_WEIGHT * static_cast<int64_t>(n_first) + 100 * (grid - n_first);
+    return total_steps * w / all;
+}
+
 // k steps of a tile, rounded up to whole pairs (the loop takes two per pass;
 // the token rows are zero padded that far, see padded_q_row).
 __device__ __forceinline__ int stream_steps(int Kp) { return ((Kp / 64 + 3) / 4 + 1) / 2 * 2; }
@@ -707,9 +728,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t packed_rsrc(const GemvProblem&
 
 template <bool kFused, bool kGrouped, bool kXBf16, bool kOutBf16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITNET_STREAM_PER_CU)))
-void gemv_stream_kernel(GemvProblem single,
-                                                               const GemvProblem* __restrict__ table,
-                                                               int count, int total_tiles, int64_t total_steps) {
+void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ table, int count, int total_tiles,
+                        int64_t total_steps, int n_first) {
     int8_t* const q_lds = g_stream_q;                   // the workgroup's problems' token rows
     __shared__ float red_f[kWaves];
     __shared__ int red_i[kWaves];
@@ -718,10 +738,9 @@ void gemv_stream_kernel(GemvProblem single,
     __shared__ __attribute__((aligned(16))) int rs_lds[kStreamMaxProblems * 16];
 
     const Problems<kGrouped> ps{table, single, count};
-    const int64_t s_lo = total_steps * blockIdx.x / gridDim.x;
-    const int64_t s_hi = total_steps * (blockIdx.x + 1) / gridDim.x;
-    const int t_begin = first_tile_from_step(ps, s_lo, total_tiles);
-    const int t_end = first_tile_from_step(ps, s_hi, total_tiles);
+    const int G = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+    const int t_begin = first_tile_from_step(ps, share_start(total_steps, b, G, n_first), total_tiles);
+    const int t_end = first_tile_from_step(ps, share_start(total_steps, b + 1, G, n_first), total_tiles);
     if (t_begin >= t_end) return;                       // workgroup-uniform
     const int p_first = find_problem(ps, t_begin);
     const int p_last = find_problem(ps, t_end - 1);     // the host keeps the span within kStreamMaxProblems
@@ -953,17 +972,23 @@ hipError_t launch_persistent(const GemvProblem& single, const GemvProblem* table
                                                                stream);
 }
 
-// Workgroups of the streaming kernel resident at once on the current device.
-int stream_grid() {
+// CUs of the current device (0 on error).
+int device_cus() {
     static int cached[64] = {0};
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     if (cached[dev] == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cached[dev] = cus * BITNET_STREAM_PER_CU;
+        cached[dev] = cus;
     }
     return cached[dev];
 }
+
+// Workgroups of the streaming kernel resident at once on the current device.
+int stream_grid() { return device_cus() * BITNET_STREAM_PER_CU; }
+
+// Workgroups of a streaming grid that are the first on their CU.
+int stream_first(int grid) { return std::min(grid, device_cus()); }
 
 // Host copy of the kernel's first_tile_from_step.
 int64_t host_first_tile(const GemvProblem* t, int count, int64_t s, int64_t total_tiles) {
@@ -973,7 +998,7 @@ int64_t host_first_tile(const GemvProblem* t, int count, int64_t s, int64_t tota
         if (t[mid].step0 <= s) lo = mid;
         else hi = mid - 1;
     }
-    const int64_t k = (s - t[lo].step0 + t[lo].steps - 1) / t[lo].steps;
+    const int64_t k = (2 * (s - t[lo].step0) + t[lo].steps) / (2 * t[lo].steps);
     if (k >= t[lo].ntiles) return lo + 1 < count ? t[lo + 1].tile0 : total_tiles;
     return t[lo].tile0 + k;
 }
@@ -992,8 +1017,8 @@ template <bool kFused, bool kGrouped, bool XB, bool YB>
 hipError_t launch_stream_t(const GemvProblem& single, const GemvProblem* table, int count, int64_t total_tiles,
                            int64_t total_steps, int grid, size_t lds, hipStream_t stream) {
     auto kern = gemv_stream_kernel<kFused, kGrouped, XB, YB>;
-    kern<<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream>>>(single, table, count,
-                                                                           static_cast<int>(total_tiles), total_steps);
+    kern<<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream>>>(
+        single, table, count, static_cast<int>(total_tiles), total_steps, stream_first(grid));
     return hipGetLastError();
 }
 
@@ -1043,8 +1068,9 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
             return false;
     // the token rows of each workgroup's problems must fit the static array
     size_t need = 0;
+    const int n_first = stream_first(grid);
     for (int b = 0; b < grid; ++b) {
-        const int64_t lo = total_steps * b / grid, hi = total_steps * (b + 1) / grid;
+        const int64_t lo = share_start(total_steps, b, grid, n_first), hi = share_start(total_steps, b + 1, grid, n_first);
         const int64_t t0 = host_first_tile(host_table, count, lo, total_tiles);
         const int64_t t1 = host_first_tile(host_table, count, hi, total_tiles);
         if (t0 >= t1) continue;

@@ -557,6 +557,30 @@ def test_grouped_many_problems_per_workgroup(orc):
             check_y(y, ref["y"])
 
 
+@pytest.mark.parametrize("M", [1, 2])
+def test_grouped_few_tall_tiles(orc, M):
+    """Two groups with fewer 64-row tiles than CUs (16384-wide rows, so one
+    tile is a workgroup's whole share, and a 100 x 2560 + 64 x 4304 group),
+    each launched four times with the other in between: every launch of a
+    reused plan matches the oracle."""
+    items, refs = _group_case(orc, M, torch.bfloat16, torch.float32, [(192, 16384), (50, 16384)], 2100 + M)
+    other, other_refs = _group_case(orc, M, torch.float32, torch.bfloat16, [(100, 2560), (64, 4304)], 2200 + M)
+    g, g_other = tw.GroupedBitLinear(items), tw.GroupedBitLinear(other)
+    assert g.kernel == "stream" and g_other.kernel == "stream"
+    for rep in range(4):
+        for _, _, y in items + other:
+            y.fill_(float("nan"))
+        g()
+        if rep % 2:
+            g_other()
+        torch.cuda.synchronize()
+        for (_, _, y), ref in zip(items, refs):
+            check_y(y, ref["y"])
+        if rep % 2:
+            for (_, _, y), ref in zip(other, other_refs):
+                check_y(y, ref["y"])
+
+
 def test_grouped_plan_rejects_bad_items():
     x = torch.zeros((1, 64), dtype=torch.bfloat16, device=DEV)
     pw = tw.pack(torch.ones((8, 64), dtype=torch.bfloat16, device=DEV))
