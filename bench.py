@@ -176,8 +176,9 @@ def bench_norm(tw, wl, torch, steps, warmup):
 
 def bench_a16(tw, wl, torch, steps, warmup):
     """The W1.58A16 variant (BitVLA s5: bf16 activations, ternary weights) at M = 1:
-    the c2 30-layer stream as a HIP graph of 210 launches, and one large projection
-    (gate|up 13824 x 2560) alone; GB/s of packed weights."""
+    the c2 30-layer stream as one grouped streaming launch and as a HIP graph of
+    210 launches, and one large projection (gate|up 13824 x 2560) alone; GB/s of
+    packed weights."""
     items, nbytes = setup_decode(tw, wl, torch, 30)
 
     def calls():
@@ -190,7 +191,13 @@ def bench_a16(tw, wl, torch, steps, warmup):
         calls()
     ms = time_region(torch, g.replay, steps, warmup)
     out = dict(stream=dict(value=nbytes / (ms * 1e-3) / 1e9, unit="GB/s", ms_per_step=ms, launches_per_step=210))
-    del g, items
+    group = tw.GroupedBitLinear(items, a16=True)
+    msg = time_region(torch, group, steps, warmup)
+    gbps_g = nbytes / (msg * 1e-3) / 1e9
+    out["grouped"] = dict(value=gbps_g, unit="GB/s", ms_per_step=msg, kernel=group.kernel, launches_per_step=1,
+                          roofline=dict(bound="hbm", achieved=gbps_g, peak=HBM_PEAK_GBPS, unit="GB/s",
+                                        frac=gbps_g / HBM_PEAK_GBPS, traffic=None))
+    del g, group, items
     torch.cuda.empty_cache()
     W = wl.draw_weight((13824, 2560), seed=3, device="cuda")
     pw = tw.pack(W)

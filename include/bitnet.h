@@ -276,6 +276,21 @@ bitnet_status_t bitnet_group_plan_rmsnorm(hipStream_t stream, const bitnet_group
                                           void* table_dev, int64_t table_bytes, bitnet_group_plan_t* plan);
 
 /*
+ * W1.58A16 variant of bitnet_group_plan [BitVLA s5: 16-bit activations with
+ * the ternary weights]: items as for bitnet_group_plan with bf16 x (M 1..16,
+ * 16-byte aligned rows), launched by bitnet_bitlinear_grouped as one
+ * streaming launch that computes y_i = w_scale_i * (x_i . t_i) with the sum in
+ * fp32 on bf16 matrix cores, as bitnet_linear_a16 does per item (the fp32
+ * order differs; both stay within bitnet_linear_a16's bound).  Errors as for
+ * bitnet_group_plan, and UNSUPPORTED when one workgroup's share of the group
+ * needs more LDS than it has for the bf16 token rows (2 * M * Kp bytes per
+ * item it touches); then use bitnet_linear_a16 per item.
+ */
+bitnet_status_t bitnet_group_plan_a16(hipStream_t stream, const bitnet_group_item_t* items, int32_t count,
+                                      int64_t M, bitnet_dtype_t y_dtype, void* table_dev, int64_t table_bytes,
+                                      bitnet_group_plan_t* plan);
+
+/*
  * Run every item of a plan in one kernel launch on `stream`: each workgroup
  * quantises its item's tokens (ActQuant, same numerics as bitnet_act_quant)
  * and streams its share of that item's packed weight once.  Results are
@@ -284,10 +299,11 @@ bitnet_status_t bitnet_group_plan_rmsnorm(hipStream_t stream, const bitnet_group
  */
 bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_plan_t* plan);
 
-/* Name of the kernel a plan launches: "stream" (each workgroup streams an
- * equal share of all packed bytes through per-wave LDS rings; chosen when
- * every workgroup's token rows fit its LDS share) or "persistent" (the
- * fallback); "" for a handle not made by bitnet_group_plan.  The environment
+/* Name of the kernel a plan launches: "stream" (each workgroup streams a
+ * share of all packed bytes through per-wave LDS rings; chosen when every
+ * workgroup's token rows fit its LDS share), "persistent" (the fallback) or
+ * "stream-a16" (a bitnet_group_plan_a16 plan); "" for a handle not made by
+ * bitnet_group_plan*.  The environment
  * variable BITNET_GROUP_KERNEL=persistent, read by bitnet_group_plan, forces
  * the fallback (for comparisons; results are identical). */
 const char* bitnet_group_plan_kernel(const bitnet_group_plan_t* plan);

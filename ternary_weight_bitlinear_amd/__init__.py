@@ -288,13 +288,19 @@ class GroupedBitLinear:
     plan keeps pointers to them, so they must stay alive and in place.  Calling
     the object writes y_i = linear(ActQuant(x_i), WeightQuant(W_i)) for all i."""
 
-    def __init__(self, items, norms=None):
+    def __init__(self, items, norms=None, a16=False):
         """``norms``: None, or one entry per item, each None or (norm_w [K], up or None, eps):
-        the item's input is then RMSNorm(x or silu(x) * up, norm_w) before ActQuant."""
+        the item's input is then RMSNorm(x or silu(x) * up, norm_w) before ActQuant.
+        ``a16``: the W1.58A16 variant, y_i = w_scale_i * (x_i . t_i) with bf16 x_i kept
+        unquantised (as linear_a16 per item); no norms."""
         if not items:
             raise ValueError("need at least one item")
         if norms is not None and len(norms) != len(items):
             raise ValueError("norms needs one entry per item")
+        if a16 and norms is not None:
+            raise ValueError("the W1.58A16 group takes no input norms")
+        if a16 and any(x.dtype != torch.bfloat16 for x, _, _ in items):
+            raise ValueError("the W1.58A16 group takes bf16 activations")
         x0 = items[0][0]
         M = x0.shape[0]
         self._keep = list(items)
@@ -324,7 +330,11 @@ class GroupedBitLinear:
         self.plan = _lib.GroupPlan()
         self.device = x0.device
         with torch.cuda.device(x0.device):
-            if nrm is None:
+            if a16:
+                _lib.check(_lib.lib().bitnet_group_plan_a16(
+                    _stream(x0), ctypes.cast(arr, ctypes.c_void_p), len(items), M, _dtype(items[0][2]),
+                    self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
+            elif nrm is None:
                 _lib.check(_lib.lib().bitnet_group_plan(
                     _stream(x0), ctypes.cast(arr, ctypes.c_void_p), len(items), M, _dtype(x0),
                     _dtype(items[0][2]), self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
@@ -333,7 +343,7 @@ class GroupedBitLinear:
                     _stream(x0), ctypes.cast(arr, ctypes.c_void_p), ctypes.cast(nrm, ctypes.c_void_p), len(items),
                     M, _dtype(x0), _dtype(items[0][2]), self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
         self.bytes = sum(w.N * w.K // 4 for _, w, _ in items)
-        # which kernel the plan launches: "dynamic", "stream" or "persistent"
+        # which kernel the plan launches: "stream", "persistent" or "stream-a16"
         self.kernel = _lib.lib().bitnet_group_plan_kernel(ctypes.byref(self.plan)).decode()
 
     def __call__(self):

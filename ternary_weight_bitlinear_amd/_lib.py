@@ -38,6 +38,7 @@ SIGNATURES = {
     "bitnet_group_plan": (ctypes.c_int, [_vp, _vp, _i32, _i64, ctypes.c_int, ctypes.c_int, _vp, _i64, _vp]),
     "bitnet_group_plan_rmsnorm": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, ctypes.c_int, ctypes.c_int, _vp, _i64,
                                                  _vp]),
+    "bitnet_group_plan_a16": (ctypes.c_int, [_vp, _vp, _i32, _i64, ctypes.c_int, _vp, _i64, _vp]),
     "bitnet_bitlinear_grouped": (ctypes.c_int, [_vp, _vp]),
     "bitnet_group_plan_kernel": (ctypes.c_char_p, [_vp]),
     "bitnet_linear_a16": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _i64, _vp,

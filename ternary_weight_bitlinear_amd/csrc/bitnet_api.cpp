@@ -642,7 +642,7 @@ bitnet_status_t bitnet_load_packed(const char* path, int64_t* N, int64_t* K, int
 // Kernels of a grouped plan.  BITNET_GROUP_KERNEL=persistent, read when a
 // plan is made, skips the streaming kernel (for comparisons; results are
 // identical).
-enum { kGroupPersistent = 0, kGroupStream = 1 };
+enum { kGroupPersistent = 0, kGroupStream = 1, kGroupA16 = 2 };
 static bool persistent_forced() {
     const char* v = getenv("BITNET_GROUP_KERNEL");
     return v && strcmp(v, "persistent") == 0;
@@ -656,7 +656,8 @@ int64_t bitnet_group_table_bytes(int32_t count) {
 static bitnet_status_t group_plan_impl(hipStream_t stream, const bitnet_group_item_t* items,
                                        const bitnet_group_norm_t* norms, int32_t count, int64_t M,
                                        bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype, void* table_dev,
-                                       int64_t table_bytes, bitnet_group_plan_t* plan, const char* fn) {
+                                       int64_t table_bytes, bitnet_group_plan_t* plan, const char* fn,
+                                       bool a16 = false) {
     if (count <= 0 || !items || !plan || !table_dev)
         return fail(BITNET_ERR_INVALID_ARG, "%s: need count > 0, items, table_dev and plan", fn);
     if (!aligned(table_dev, 16) || table_bytes < bitnet_group_table_bytes(count))
@@ -711,7 +712,14 @@ static bitnet_status_t group_plan_impl(hipStream_t stream, const bitnet_group_it
     // fit its LDS share, else the persistent one.
     int kind = kGroupPersistent, grid = 0;
     size_t lds = bitnet::gemv_group_lds(M, max_kp);
-    if (!persistent_forced() && bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &grid, &lds)) {
+    if (a16) {
+        if (!bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &grid, &lds, 2))
+            return fail(BITNET_ERR_UNSUPPORTED,
+                        "%s: a workgroup's share of the group needs more LDS than it has for M=%lld bf16 token rows "
+                        "(use bitnet_linear_a16 per item)",
+                        fn, (long long)M);
+        kind = kGroupA16;
+    } else if (!persistent_forced() && bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &grid, &lds)) {
         kind = kGroupStream;
     } else {
         grid = 0;
@@ -740,6 +748,13 @@ bitnet_status_t bitnet_group_plan(hipStream_t stream, const bitnet_group_item_t*
                            "bitnet_group_plan");
 }
 
+bitnet_status_t bitnet_group_plan_a16(hipStream_t stream, const bitnet_group_item_t* items, int32_t count, int64_t M,
+                                      bitnet_dtype_t y_dtype, void* table_dev, int64_t table_bytes,
+                                      bitnet_group_plan_t* plan) {
+    return group_plan_impl(stream, items, nullptr, count, M, BITNET_BF16, y_dtype, table_dev, table_bytes, plan,
+                           "bitnet_group_plan_a16", true);
+}
+
 bitnet_status_t bitnet_group_plan_rmsnorm(hipStream_t stream, const bitnet_group_item_t* items,
                                           const bitnet_group_norm_t* norms, int32_t count, int64_t M,
                                           bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype, void* table_dev,
@@ -759,16 +774,20 @@ bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_
     const int grid = static_cast<int>(plan->opaque[6] >> 32);
     const bool x_bf16 = (plan->opaque[6] & 0xFF) == BITNET_BF16;
     const bool y_bf16 = ((plan->opaque[6] >> 8) & 0xFF) == BITNET_BF16;
-    hipError_t e = bitnet::launch_gemv_grouped(table, count, plan->opaque[4], plan->opaque[7],
-                                               static_cast<size_t>(plan->opaque[5]),
-                                               kind == kGroupStream ? grid : 0, x_bf16, y_bf16, stream);
+    hipError_t e = kind == kGroupA16
+                       ? bitnet::launch_gemv_a16_grouped(table, count, plan->opaque[4], plan->opaque[7], grid, y_bf16,
+                                                         stream)
+                       : bitnet::launch_gemv_grouped(table, count, plan->opaque[4], plan->opaque[7],
+                                                     static_cast<size_t>(plan->opaque[5]),
+                                                     kind == kGroupStream ? grid : 0, x_bf16, y_bf16, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }
 
 const char* bitnet_group_plan_kernel(const bitnet_group_plan_t* plan) {
     if (!plan || plan->opaque[0] != kPlanMagic) return "";
-    return ((plan->opaque[6] >> 16) & 0xFF) == kGroupStream ? "stream" : "persistent";
+    const int kind = static_cast<int>((plan->opaque[6] >> 16) & 0xFF);
+    return kind == kGroupStream ? "stream" : kind == kGroupA16 ? "stream-a16" : "persistent";
 }
 
 const char* bitnet_status_string(bitnet_status_t s) {

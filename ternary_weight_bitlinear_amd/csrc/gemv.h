@@ -45,10 +45,16 @@ hipError_t launch_gemv_fused(const GemvProblem& p, bool x_bf16, bool y_bf16, hip
 
 // Whether the streaming kernel (per-wave LDS ring of DMA weight loads) can
 // run this table of problems (host copy, tile0 / ntiles / steps / step0 set):
-// every workgroup's problems must fit its LDS share.  On success gives the
-// grid and the dynamic LDS bytes to launch with.
+// every workgroup's problems must fit its LDS share, with token rows of
+// token_bytes per element (1: int8 codes; 2: the bf16 rows of the W1.58A16
+// kernel).  On success gives the grid and the dynamic LDS bytes to launch with.
 bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_tiles, int64_t total_steps,
-                      int* grid, size_t* lds);
+                      int* grid, size_t* lds, int token_bytes = 1);
+
+// W1.58A16 grouped launch of the streaming kernel (bf16 x, no quantiser):
+// table_dev and the grid as for launch_gemv_grouped's streaming case.
+hipError_t launch_gemv_a16_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,
+                                   int64_t total_steps, int grid, bool y_bf16, hipStream_t stream);
 
 // Many independent problems in one launch (ActQuant fused); table_dev is a
 // device array of `count` descriptors with tile0 / ntiles / steps / step0 set.

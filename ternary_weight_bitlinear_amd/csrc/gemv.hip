@@ -921,6 +921,189 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     }
 }
 
+// ------------------------------------------------------ W1.58A16 streaming kernel
+//
+// The grouped W1.58A16 decode ("BitVLA -- 1.58-bit Vision-Language-Action on
+// Core AI", s5: 16-bit activations with the ternary weights): the streaming
+// kernel's work split, tiles and memory pipeline, with the bf16 token rows
+// copied into LDS as given (no quantiser) and each lane's 16 bytes of codes
+// (64 k of one row) expanded into the B operands of eight
+// v_mfma_f32_16x16x32_bf16.  Lane group g of a wave takes the 16-byte chunk
+// 4s + g of k step s, as in the int8 kernel; its A operands are the 64
+// consecutive bf16 of the token row at the same k (128 bytes of LDS), so the
+// k order inside an MFMA differs from the int8 kernel's but pairs the same
+// x[m][k] with t[n][k].  The fp32 sums are scaled by w_scale alone.
+
+// 64 consecutive bf16 of a token row (8 A operands of 8 k).
+__device__ __forceinline__ void lds_read128(const void* p, u32x4 (&a)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\tds_read_b128 %2, %8 offset:32\n\t"
+        "ds_read_b128 %3, %8 offset:48\n\tds_read_b128 %4, %8 offset:64\n\tds_read_b128 %5, %8 offset:80\n\t"
+        "ds_read_b128 %6, %8 offset:96\n\tds_read_b128 %7, %8 offset:112\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+        : "v"(lds_addr(p))
+        : "memory");
+}
+
+template <bool kGrouped, bool kOutBf16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITNET_STREAM_PER_CU)))
+void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ table, int count, int total_tiles,
+                            int64_t total_steps, int n_first) {
+    uint16_t* const x_lds = reinterpret_cast<uint16_t*>(g_stream_q);   // bf16 token rows of the problems
+
+    const Problems<kGrouped> ps{table, single, count};
+    const int G = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+    const int t_begin = first_tile_from_step(ps, share_start(total_steps, b, G, n_first), total_tiles);
+    const int t_end = first_tile_from_step(ps, share_start(total_steps, b + 1, G, n_first), total_tiles);
+    if (t_begin >= t_end) return;                       // workgroup-uniform
+    const int p_first = find_problem(ps, t_begin);
+    const int p_last = find_problem(ps, t_end - 1);     // the host keeps the span within kStreamMaxProblems
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int col = lane % 16;
+    const int grp = lane / 16;
+    int8_t* const ring = g_stream_ring + wave * 1024;   // slot j of this wave: ring + j * kThreads * 16
+
+    // producer: as in gemv_stream_kernel
+    int pp = p_first;
+    GemvProblem PP = ps.get(pp);
+    __amdgpu_buffer_rsrc_t rsrc = packed_rsrc(PP);
+    int tp = t_begin, sp = 0, steps_p = stream_steps(PP.Kp), chunks_p = PP.Kp / 64, slot_p = 0;
+    uint32_t rowoff = static_cast<uint32_t>(((tp - PP.tile0) * 64 + wave * 16 + col) * (PP.Kp / 4) + 16 * grp);
+    auto produce = [&]() {
+        const uint32_t off = tp < t_end && 4 * sp + grp < chunks_p ? rowoff + 64u * static_cast<uint32_t>(sp)
+                                                                   : kStreamOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(ring + slot_p * kThreads * 16), 16, off, 0, 0, 0);
+        slot_p = slot_p + 1 == kDepth ? 0 : slot_p + 1;
+        if (tp < t_end && ++sp == steps_p) {
+            sp = 0;
+            ++tp;
+            rowoff += static_cast<uint32_t>(64 * (PP.Kp / 4));
+            if (tp < t_end && tp == PP.tile0 + PP.ntiles) {
+                PP = ps.get(++pp);
+                rsrc = packed_rsrc(PP);
+                steps_p = stream_steps(PP.Kp);
+                chunks_p = PP.Kp / 64;
+                rowoff = static_cast<uint32_t>((wave * 16 + col) * (PP.Kp / 4) + 16 * grp);
+            }
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < kDepth - 2; ++i) produce();
+
+    // w_scale of the workgroup's rows (DMA behind the ring's first loads), then
+    // the token rows of its problems: x [M][K] bf16, zero padded to
+    // padded_q_row(Kp) elements so padded k steps multiply zeros
+    int x_elems = 0;
+    for (int pi = p_first; pi <= p_last; ++pi) {
+        const GemvProblem Pi = ps.get(pi);
+        x_elems += Pi.M * padded_q_row(Pi.Kp);
+    }
+    float* const ws_lds = reinterpret_cast<float*>(x_lds + x_elems);
+    {
+        for (int pi = p_first; pi <= p_last; ++pi) {
+            const GemvProblem Pi = ps.get(pi);
+            const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(Pi.w_scale), 0, Pi.N * static_cast<int>(sizeof(float)), kRsrcWord3);
+            const int t0 = max(t_begin, Pi.tile0), t1 = min(t_end, Pi.tile0 + Pi.ntiles);
+            for (int t = t0 + wave; t < t1; t += kWaves)   // rows past N read as zero
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ws_rsrc, (lds_ptr_t)(ws_lds + (t - t_begin) * 64), 4,
+                    static_cast<uint32_t>(((t - Pi.tile0) * 64 + lane) * sizeof(float)), 0, 0, 0);
+        }
+        int off = 0;
+        for (int pi = p_first; pi <= p_last; ++pi) {
+            const GemvProblem Pi = ps.get(pi);
+            const int ldq = padded_q_row(Pi.Kp);
+            const uint16_t* xg = static_cast<const uint16_t*>(Pi.x);
+            for (int i = threadIdx.x; i < Pi.M * (ldq / 8); i += kThreads) {
+                const int m = i / (ldq / 8), k = 8 * (i % (ldq / 8));
+                const u32x4 v = k < Pi.K ? gload<u32x4>(xg + static_cast<int64_t>(m) * Pi.ldx + k) : u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(x_lds + off + m * ldq + k) = v;
+            }
+            off += Pi.M * ldq;
+        }
+        wait_vm<0>();
+        __syncthreads();
+    }
+
+    // consumer
+    const int wg_rows = (t_end - t_begin) * 64;
+    float* const out_lds = ws_lds + wg_rows;           // [M][wg_rows] fp32 sums
+    int pc = p_first, tc = t_begin, sc = 0, slot_c = 0;
+    GemvProblem P = ps.get(pc);
+    int steps_c = stream_steps(P.Kp);
+    int xoff = 0;
+    const bool m_ok = col < P.M;                        // M is shared by the group
+    const uint16_t* xbase = x_lds + (m_ok ? col : 0) * padded_q_row(P.Kp) + 64 * grp;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    u32x4 a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = u32x4{0u, 0u, 0u, 0u};
+    while (true) {
+        produce();
+        produce();
+        wait_vm<kDepth - 2>();                          // both steps' ring loads have landed
+        u32x4 w[2];
+        lds_read_ring2(ring + slot_c * kThreads * 16 + 16 * lane, w[0], w[1]);
+        slot_c = slot_c + 2 == kDepth ? 0 : slot_c + 2;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (m_ok) lds_read128(xbase + 256 * (sc + i), a);
+            const uint32_t words[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[2 * j + h]),
+                                                                  __builtin_bit_cast(bf16x8, expand_bf16(words[j], h)),
+                                                                  acc, 0, 0, 0);
+        }
+        sc += 2;
+        if (sc < steps_c) continue;
+        // tile epilogue: lane holds C[m = 4*grp + r][row] of this wave's 16 rows
+        sc = 0;
+        {
+            const int row = (tc - t_begin) * 64 + wave * 16 + col;
+            const int32_t bits[4] = {__float_as_int(acc[0]), __float_as_int(acc[1]), __float_as_int(acc[2]),
+                                     __float_as_int(acc[3])};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * grp + r;
+                if (m < P.M) lds_write_i32(out_lds + m * wg_rows + row, bits[r]);
+            }
+        }
+        acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (++tc == t_end) break;
+        if (tc == P.tile0 + P.ntiles) {
+            xoff += P.M * padded_q_row(P.Kp);
+            P = ps.get(++pc);
+            steps_c = stream_steps(P.Kp);
+            xbase = x_lds + xoff + (m_ok ? col : 0) * padded_q_row(P.Kp) + 64 * grp;
+        }
+    }
+    wait_vm<0>();                                       // ring loads past the end land before the LDS is reused
+    __syncthreads();
+
+    for (int pi = p_first; pi <= p_last; ++pi) {
+        const GemvProblem Pi = ps.get(pi);
+        const int t0 = max(t_begin, Pi.tile0), t1 = min(t_end, Pi.tile0 + Pi.ntiles);
+        const int rows = (t1 - t0) * 64;
+        for (int i = threadIdx.x; i < Pi.M * rows; i += kThreads) {
+            const int m = i / rows, rr = i % rows;
+            const int n = (t0 - Pi.tile0) * 64 + rr;
+            if (n >= Pi.N) continue;
+            const int lrow = (t0 - t_begin) * 64 + rr;
+            const float v = out_lds[m * wg_rows + lrow] * ws_lds[lrow];
+            if constexpr (kOutBf16)
+                gstore<uint16_t>(static_cast<uint16_t*>(Pi.y) + m * Pi.ldy + n, f32_to_bf16(v));
+            else
+                gstore<float>(static_cast<float*>(Pi.y) + m * Pi.ldy + n, v);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 
 
@@ -1037,6 +1220,15 @@ hipError_t launch_stream(const GemvProblem& single, const GemvProblem* table, in
                                                            lds, stream);
 }
 
+template <bool kOutBf16>
+hipError_t launch_stream_a16_t(const GemvProblem* table, int count, int64_t total_tiles, int64_t total_steps,
+                               int grid, hipStream_t stream) {
+    GemvProblem none{};
+    gemv_stream_a16_kernel<true, kOutBf16><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
+        none, table, count, static_cast<int>(total_tiles), total_steps, stream_first(grid));
+    return hipGetLastError();
+}
+
 // A single problem laid out as a one-entry group.
 GemvProblem as_group_of_one(GemvProblem p, int64_t& tiles, int64_t& steps) {
     p.tile0 = 0;
@@ -1059,7 +1251,7 @@ int64_t gemv_group_steps(int64_t Kp) {          // batches of kBatch k steps per
 }
 
 bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_tiles, int64_t total_steps,
-                      int* grid_out, size_t* lds_out) {
+                      int* grid_out, size_t* lds_out, int token_bytes) {
     const int grid = static_cast<int>(std::min<int64_t>(stream_grid(), total_tiles));
     if (grid <= 0 || count <= 0) return false;
     // buffer offsets are 32-bit: every problem's padded rows must stay below 2 GiB
@@ -1079,7 +1271,7 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
         // w_scale and the M exact sums of each row
         size_t bytes = static_cast<size_t>(t1 - t0) * 64 * sizeof(float) * (1 + host_table[p0].M);
         for (int i = p0; i <= p1; ++i)
-            bytes += static_cast<size_t>(host_table[i].M) * padded_q_row(host_table[i].Kp);
+            bytes += static_cast<size_t>(host_table[i].M) * padded_q_row(host_table[i].Kp) * token_bytes;
         need = std::max(need, bytes);
     }
     if (need > static_cast<size_t>(kStreamQBytes)) return false;
@@ -1121,6 +1313,12 @@ hipError_t launch_gemv_fused(const GemvProblem& p, bool x_bf16, bool y_bf16, hip
                                               y_bf16, stream);
     }
     return launch_splitk<true>(p, static_cast<size_t>(p.M) * p.Kp, x_bf16, y_bf16, stream);
+}
+
+hipError_t launch_gemv_a16_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,
+                                   int64_t total_steps, int grid, bool y_bf16, hipStream_t stream) {
+    return y_bf16 ? launch_stream_a16_t<true>(table_dev, count, total_tiles, total_steps, grid, stream)
+                  : launch_stream_a16_t<false>(table_dev, count, total_tiles, total_steps, grid, stream);
 }
 
 hipError_t launch_gemv_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,

@@ -350,6 +350,73 @@ def test_linear_a16(orc, M, N, K, out):
     assert np.all(err <= tol), float((err / np.maximum(tol, 1e-300)).max())
 
 
+def _check_a16(orc, y, x, W):
+    """y against the oracle's fp64 value of w_scale * (x . t), within the bound
+    bitnet_linear_a16 states for an fp32 sum in the hardware's order."""
+    K = x.shape[1]
+    t, ws, _, _ = orc.weight_quant(bits(W))
+    ye, mag = orc.linear_a16(bits(x), t, ws)
+    tol = ws.astype(np.float64)[None, :] * (K / 32 + 64) * 2.0 ** -24 * mag
+    tol = tol + np.abs(ye) * (2.0 ** -8 if y.dtype == torch.bfloat16 else 2.0 ** -24)
+    err = np.abs(y.float().cpu().numpy().astype(np.float64) - ye)
+    assert np.all(err <= tol), float((err / np.maximum(tol, 1e-300)).max())
+
+
+@pytest.mark.parametrize("M,shapes,y_dtype", [
+    (1, "group", torch.float32), (1, "group", torch.bfloat16), (3, "group", torch.float32),
+    (4, "small", torch.bfloat16), (16, "tiny", torch.float32)])
+def test_grouped_a16(orc, M, shapes, y_dtype):
+    """The W1.58A16 group (bf16 x kept unquantised) in one streaming launch: ragged
+    N, K not a multiple of 128, one-tile problems; each launch of the reused plan
+    within the oracle bound."""
+    sh = {"group": GROUP_SHAPES, "small": [(640, 1024), (100, 512), (64, 256), (130, 1152)],
+          "tiny": [(100, 512), (64, 256), (33, 128)]}[shapes]
+    items, cases = [], []
+    for i, (N, K) in enumerate(sh):
+        x, W = wl.random_case(5300 + 17 * M + i, M, N, K, x_dist="normal_outliers")
+        pw = tw.pack(W.to(DEV))
+        items.append((x.to(DEV), pw, torch.full((M, N), float("nan"), device=DEV, dtype=y_dtype)))
+        cases.append((x, W))
+    group = tw.GroupedBitLinear(items, a16=True)
+    assert group.kernel == "stream-a16"
+    for rep in range(2):
+        for _, _, y in items:
+            y.fill_(float("nan"))
+        group()
+        torch.cuda.synchronize()
+        for (_, _, y), (x, W) in zip(items, cases):
+            _check_a16(orc, y, x, W)
+
+
+def test_grouped_a16_decoder_layers(orc):
+    """Two BitNet-2B-shaped decoder layers (14 projections) as one W1.58A16
+    launch: workgroup shares span several projections."""
+    shapes = [(2560, 2560), (640, 2560), (640, 2560), (2560, 2560), (6912, 2560), (6912, 2560), (2560, 6912)] * 2
+    items, cases = [], []
+    for i, (N, K) in enumerate(shapes):
+        x, W = wl.random_case(5500 + i, 1, N, K, x_dist="normal_outliers")
+        pw = tw.pack(W.to(DEV))
+        items.append((x.to(DEV), pw, torch.full((1, N), float("nan"), device=DEV)))
+        cases.append((x, W))
+    group = tw.GroupedBitLinear(items, a16=True)
+    group()
+    torch.cuda.synchronize()
+    for (_, _, y), (x, W) in zip(items, cases):
+        _check_a16(orc, y, x, W)
+
+
+def test_grouped_a16_rejects_what_does_not_fit():
+    """16 bf16 token rows of K = 6912 (221 KB) exceed a workgroup's LDS: the plan
+    says so; fp32 activations are refused before any plan is made."""
+    x = torch.zeros((16, 6912), dtype=torch.bfloat16, device=DEV)
+    pw = tw.pack(torch.ones((64, 6912), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(tw.BitnetError) as e:
+        tw.GroupedBitLinear([(x, pw, torch.empty((16, 64), device=DEV))], a16=True)
+    assert e.value.status == _lib.ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        tw.GroupedBitLinear([(x.float(), pw, torch.empty((16, 64), device=DEV))], a16=True)
+
+
 def test_linear_a16_rejects_fp32_activations():
     x = torch.zeros((1, 64), device=DEV)
     pw = tw.pack(torch.ones((8, 64), dtype=torch.bfloat16, device=DEV))
