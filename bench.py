@@ -98,7 +98,7 @@ def bench_decode(tw, wl, torch, steps, warmup, per_call: bool):
     group = tw.GroupedBitLinear(items)
     ms = time_region(torch, group, steps, warmup)     # one launch per step
     gbps = nbytes / (ms * 1e-3) / 1e9
-    src = kernel_source_hash("gemv.hip", "gemv.h", "device_common.h")
+    src = kernel_source_hash("gemv.hip", "gemv.h", "device_common.h", "codes_bf16.h")
     out = dict(value=gbps, ms_per_step=ms, bytes=nbytes, launches_per_step=1,
                roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s",
                              frac=gbps / HBM_PEAK_GBPS,

@@ -39,6 +39,7 @@
 // the ring's loads are counted by vmcnt alone and are waited for one at a time.
 #include <algorithm>
 
+#include "codes_bf16.h"
 #include "device_common.h"
 #include "gemv.h"
 #include "kernels.h"

@@ -18,6 +18,7 @@
 // read from global memory (L1/L2-resident: every workgroup reads the same
 // rows).  Token tiles beyond the first 16 re-read the packed rows, so this is
 // a decode-size kernel.
+#include "codes_bf16.h"
 #include "device_common.h"
 #include "kernels.h"
 
