@@ -194,9 +194,11 @@ def bench_a16(tw, wl, torch, steps, warmup):
     group = tw.GroupedBitLinear(items, a16=True)
     msg = time_region(torch, group, steps, warmup)
     gbps_g = nbytes / (msg * 1e-3) / 1e9
+    src = kernel_source_hash("gemv.hip", "gemv.h", "device_common.h", "codes_bf16.h")
     out["grouped"] = dict(value=gbps_g, unit="GB/s", ms_per_step=msg, kernel=group.kernel, launches_per_step=1,
                           roofline=dict(bound="hbm", achieved=gbps_g, peak=HBM_PEAK_GBPS, unit="GB/s",
-                                        frac=gbps_g / HBM_PEAK_GBPS, traffic=None))
+                                        frac=gbps_g / HBM_PEAK_GBPS,
+                                        traffic=traffic_from_profile("decode_a16_bitnet2b_30_layers_m1", src)))
     del g, group, items
     torch.cuda.empty_cache()
     W = wl.draw_weight((13824, 2560), seed=3, device="cuda")
