@@ -302,6 +302,111 @@ def bench_prefill(tw, wl, torch, steps, warmup, out_dtype):
                 timing="HIP graph replays: whole steps, and GEMM launches alone")
 
 
+def bench_configs(tw, wl, torch, steps, warmup):
+    """The other configurations, each timed on its own: the c1 2560 x 2560
+    decode cold (a ring of 320 distinct packed copies, 524 MB, more than twice
+    the MALL, as single calls replayed from a HIP graph and as one grouped
+    launch), the c2 stream at M = 2, 4, 8 (grouped), the c3 (SigLIP, M = 2048)
+    and c4 (embedder, M = 8192) prefill GEMMs per shape with bf16 output and
+    the c5 GEMMs with fp32 output, and ActQuant alone at the c5 inputs."""
+    steps = max(3, min(steps, 10))
+    out = {}
+    # c1 ring
+    w1 = wl.WORKLOADS["c1"]
+    p1 = w1.projections[0]
+    ring = []
+    for i in range(320):
+        pw = tw.pack(wl.weight_for(w1, 0, layer=i, device="cuda"))
+        x = wl.activation_for(w1, 0, layer=i, device="cuda")
+        ring.append((x, pw, torch.empty((1, p1.N), device="cuda")))
+    nb = len(ring) * p1.N * p1.K // 4
+    ws = (torch.empty((1, tw.padded_k(p1.K)), dtype=torch.int8, device="cuda"), torch.empty(1, device="cuda"),
+          torch.empty(1, dtype=torch.int32, device="cuda"))
+
+    def calls():
+        for x, pw, y in ring:
+            tw.bitlinear(x, pw, out=y, workspace=ws)
+    calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    ms = time_region(torch, g.replay, steps, warmup)
+    out["c1_ring_single_calls"] = dict(value=nb / (ms * 1e-3) / 1e9, unit="GB/s", us_per_call=ms * 1e3 / len(ring),
+                                       calls=len(ring), bytes=nb)
+    group = tw.GroupedBitLinear(ring)
+    msg = time_region(torch, group, steps, warmup)
+    out["c1_ring_grouped"] = dict(value=nb / (msg * 1e-3) / 1e9, unit="GB/s", ms_per_launch=msg, kernel=group.kernel)
+    del g, group, ring
+    torch.cuda.empty_cache()
+    # c2 at M = 2, 4, 8
+    items, nbytes = setup_decode(tw, wl, torch, 30)
+    res = {}
+    for M in (2, 4, 8):
+        its = [(wl.draw_activation((M, pw.K), seed=7000 + 10 * M + i, device="cuda"), pw,
+                torch.empty((M, pw.N), device="cuda")) for i, (_, pw, _) in enumerate(items)]
+        gm = tw.GroupedBitLinear(its)
+        msm = time_region(torch, gm, steps, warmup)
+        res[f"M{M}"] = dict(value=nbytes / (msm * 1e-3) / 1e9, unit="GB/s", ms_per_step=msm, kernel=gm.kernel)
+        del gm, its
+    out["c2_grouped_multi_token"] = res
+    del items
+    torch.cuda.empty_cache()
+    # prefill GEMMs per shape
+
+    def gemm_shapes(name, out_dtype):
+        w = wl.WORKLOADS[name]
+        rows, tot_ops, tot_ms = [], 0, 0.0
+        for i, p in enumerate(w.projections):
+            pw = tw.pack(wl.weight_for(w, i, device="cuda"), p.segments or None)
+            x = wl.activation_for(w, i, device="cuda")
+            q, a, r = tw.act_quant(x)
+            y = torch.empty((w.M, p.N), dtype=out_dtype, device="cuda")
+            gg = torch.cuda.CUDAGraph()
+            tw.linear(q, a, r, pw, out=y)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gg):
+                for _ in range(4):
+                    tw.linear(q, a, r, pw, out=y)
+            ms_l = time_region(torch, gg.replay, steps, 2) / 4
+            ops = 2 * w.M * p.N * p.K
+            tops = ops / (ms_l * 1e-3) / 1e12
+            rows.append(dict(shape=f"{p.name} {w.M}x{p.N}x{p.K}", us=ms_l * 1e3, tops=tops,
+                             frac_of_peak=tops / INT8_PEAK_TOPS))
+            tot_ops += ops
+            tot_ms += ms_l
+            del pw, x, q, a, r, y, gg
+        torch.cuda.empty_cache()
+        agg = tot_ops / (tot_ms * 1e-3) / 1e12
+        return dict(workload=w.name, out_dtype=str(out_dtype).replace("torch.", ""), tops=agg,
+                    frac_of_peak=agg / INT8_PEAK_TOPS, shapes=rows)
+    out["gemm_c3"] = gemm_shapes("c3", torch.bfloat16)
+    out["gemm_c4"] = gemm_shapes("c4", torch.bfloat16)
+    out["gemm_c5_f32_out"] = gemm_shapes("c5", torch.float32)
+    # ActQuant alone (HBM-bound: 2 B in + 1 B out per element, 8 B per token)
+    aq = {}
+    for K in (2560, 6912):
+        M = 4096
+        x = wl.draw_activation((M, K), seed=9000 + K, device="cuda")
+        q = torch.empty((M, tw.padded_k(K)), dtype=torch.int8, device="cuda")
+        a = torch.empty(M, dtype=torch.float32, device="cuda")
+        r = torch.empty(M, dtype=torch.int32, device="cuda")
+        L = tw._lib.lib()
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def run():
+            tw._lib.check(L.bitnet_act_quant(stream, x.data_ptr(), tw._lib.BF16, M, K, K, q.data_ptr(), a.data_ptr(),
+                                             r.data_ptr()))
+        ms_a = time_region(torch, run, steps * 5, warmup)
+        nb_a = 2 * M * K + M * tw.padded_k(K) + 8 * M
+        gbps = nb_a / (ms_a * 1e-3) / 1e9
+        aq[f"M{M}_K{K}"] = dict(us=ms_a * 1e3, value=gbps, unit="GB/s", frac_of_hbm_peak=gbps / HBM_PEAK_GBPS)
+        del x, q, a, r
+    out["act_quant"] = aq
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline_prefill(wl, torch, budget_s: float):
     """The oracle's ActQuant + int dot + epilogue on slices of 64 tokens of the
     prefill activations through all three projections, until budget_s of timed
@@ -341,6 +446,8 @@ def main() -> int:
     ap.add_argument("--no-per-call", action="store_true")
     ap.add_argument("--no-norm", action="store_true", help="skip the input-norm measurements")
     ap.add_argument("--no-a16", action="store_true", help="skip the W1.58A16 measurements")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations (c1 ring, c2 at M>1, c3/c4 GEMMs, ActQuant alone)")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first fill and copy a buffer of this many MiB three times: plain kernels of "
@@ -398,6 +505,8 @@ def main() -> int:
             line.update(value=g["value"], unit="TOPS", ms_per_step=g["ms_per_step"], roofline=g["roofline"],
                         config=g["config"])
             line["config"]["workload"] = wl.WORKLOADS["c5"].name
+    if args.only is None and not args.no_configs:
+        line["configs"] = bench_configs(tw, wl, torch, args.steps, args.warmup)
     print(json.dumps(line), flush=True)
     return 0
 
