@@ -41,6 +41,9 @@
 //    together on one XCD share both activation rows and code rows in its L2.
 //  * Kp is a multiple of 128 = BK, so there is no K tail; ragged M and N are
 //    handled by the buffer range and guarded stores.
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -342,6 +345,18 @@ int resident_slots(Kern kern, int threads, size_t lds, int (&cache)[64]) {
     return cache[dev];
 }
 
+// A third tile, 64x64 with 2 waves of 32x64, for shapes whose 128x128 tiles
+// would leave most resident slots empty (e.g. 2048 x 1152: 144 tiles for 768
+// slots): four times the tiles at a lower MFMA rate per tile.
+#ifndef BITNET_GEMM_TINY_FILL
+#define BITNET_GEMM_TINY_FILL 0.5
+#endif
+bool use_tiny(int64_t M, int64_t N, int slots_small) {
+    if (slots_small <= 0) return false;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    return static_cast<double>(tiles) < BITNET_GEMM_TINY_FILL * slots_small;
+}
+
 // Share of the launched rounds' resident slots that hold a tile.
 double round_fill(int64_t tiles, int slots) {
     if (slots <= 0) return 1.0;
@@ -349,7 +364,18 @@ double round_fill(int64_t tiles, int slots) {
     return static_cast<double>(tiles) / static_cast<double>(rounds * slots);
 }
 
-int g_slots_small[64], g_slots_wide[64];
+int g_slots_small[64], g_slots_wide[64], g_slots_tiny[64];
+
+// BITNET_GEMM_TILE=small|wide|tiny forces a tile (for comparisons; results are
+// identical), read at each launch.
+int forced_tile() {
+    const char* v = getenv("BITNET_GEMM_TILE");
+    if (!v) return -1;
+    if (strcmp(v, "small") == 0) return 0;
+    if (strcmp(v, "wide") == 0) return 1;
+    if (strcmp(v, "tiny") == 0) return 2;
+    return -1;
+}
 
 }  // namespace
 
@@ -370,7 +396,11 @@ hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_r
     const int64_t tiles_m = (M + 127) / 128;
     const double small = round_fill(tiles_m * ((N + 127) / 128), slots_small);
     const double wide = 1.07 * round_fill(tiles_m * ((N + 255) / 256), slots_wide);
-    if (wide > small)
+    const int forced = forced_tile();
+    if (forced == 2 || (forced < 0 && use_tiny(M, N, slots_small)))
+        return launch_tile<64, 64, 2, 1, BITNET_GEMM_PF, 4>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16,
+                                                            ldy, acc_debug, BITNET_GEMM_GM, stream);
+    if (forced == 1 || (forced < 0 && wide > small))
         return launch_tile<128, 256, 1, 4, BITNET_GEMM_PF, 2>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y,
                                                               y_bf16, ldy, acc_debug, BITNET_GEMM_GM, stream);
     return launch_tile<128, 128, 2, 2, BITNET_GEMM_PF, 3>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16,

@@ -453,6 +453,21 @@ def test_linear(orc, M, N, K, out):
     check_y(y, ref["y"])
 
 
+@pytest.mark.parametrize("tile", ["small", "wide", "tiny"])
+@pytest.mark.parametrize("M,N,K", [(17, 16, 16), (130, 257, 1152), (300, 200, 4304), (257, 129, 6912)])
+def test_linear_each_gemm_tile(orc, tile, M, N, K, monkeypatch):
+    """Every GEMM tile (128x128, 128x256 and 64x64, forced) gives the oracle's
+    exact sums and outputs on ragged M, N and padded K."""
+    monkeypatch.setenv("BITNET_GEMM_TILE", tile)
+    x, W = wl.random_case(M * 31 + N * 3 + K, M, N, K, x_dist="normal_outliers")
+    ref = orc.linear(bits(x), bits(W), out="bf16")
+    pw = tw.pack(W.to(DEV))
+    q, a, r = tw.act_quant(x.to(DEV))
+    y, acc = tw.linear(q, a, r, pw, out_dtype=torch.bfloat16, acc_debug=True)
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    check_y(y, ref["y"])
+
+
 @pytest.mark.parametrize("M", [1, 4, 16, 17, 64])
 def test_linear_segments_and_strided_output(orc, M):
     K, segs = 2560, (256, 64, 64)
