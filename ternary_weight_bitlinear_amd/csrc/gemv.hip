@@ -22,18 +22,18 @@
 //    absmax over K, then q into LDS) while its first weight loads are in
 //    flight, so ActQuant costs no extra launch and no HBM round trip of q.
 //
-// Two kernels:
+// Kernels:
 //  * split-K (small single calls): a workgroup owns 16 output rows and its 4
 //    waves split K; partial 16x16 tiles meet in LDS.  Most workgroups for a
 //    small matrix, which is what a latency-bound launch needs.
-//  * persistent (grouped launches and large single calls): about one
-//    workgroup per resident slot; workgroup w owns the 64-row tiles whose
-//    first k step falls in its equal share of all k steps, so every workgroup
-//    streams about the same number of bytes.  A ring of D prefetched 1 KB
-//    steps per wave runs across tile and problem boundaries: the producer walks
-//    the workgroup's (tile, step) sequence D steps ahead of the consumer, so
-//    loads stay in flight through epilogues and through the ActQuant prologue,
-//    which runs only when the consumer enters a new problem.
+//  * streaming (grouped launches and large single calls): two workgroups per
+//    CU, each owning the 64-row tiles of its share of all k steps; every wave
+//    streams its 16 rows through a private LDS ring filled by buffer-to-LDS
+//    loads, across tile and problem boundaries (see its section below).  A
+//    W1.58A16 version of it takes bf16 token rows on bf16 MFMA.
+//  * persistent (groups whose token rows do not fit the streaming kernel's
+//    LDS share): the same work split with double-buffered register batches,
+//    the ActQuant prologue running when the consumer enters a new problem.
 //
 // Every global access goes through gload / gstore (global address space), so
 // the ring's loads are counted by vmcnt alone and are waited for one at a time.
