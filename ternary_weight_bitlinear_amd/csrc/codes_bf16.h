@@ -13,23 +13,23 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr uint32_t kTableLo = 0x00800080u;
 constexpr uint32_t kTableHi = 0x003F00BFu;
 
-// Two bf16 values of t from the codes in bytes i0 and i1 of f (each 0..2):
-// a byte permute spreads them to [u0, u0, u1, u1], +4 on the odd bytes picks
-// the high-byte table, and a second permute looks both tables up.
-template <uint32_t kSpread>
-__device__ __forceinline__ uint32_t bf16_pair(uint32_t f) {
-    const uint32_t sel = __builtin_amdgcn_perm(f, f, kSpread) + 0x04000400u;
-    return __builtin_amdgcn_perm(kTableHi, kTableLo, sel);
+// Four bf16 values of t from the codes in the bytes of f (each 0..2), as two
+// dwords of two: with g = f + 4 in every byte, one byte permute of (g, f)
+// spreads two codes to [u0, u0 + 4, u1, u1 + 4] (the +4 picks the high-byte
+// table) and a second looks both tables up: 5 VALU ops per 4 codes.
+__device__ __forceinline__ u32x2 bf16_quad(uint32_t f) {
+    const uint32_t g = f + 0x04040404u;
+    return u32x2{__builtin_amdgcn_perm(kTableHi, kTableLo, __builtin_amdgcn_perm(g, f, 0x05010400u)),
+                 __builtin_amdgcn_perm(kTableHi, kTableLo, __builtin_amdgcn_perm(g, f, 0x07030602u))};
 }
 
 // B operand (8 bf16 of t, k ascending) from fields 2h and 2h+1 of a packed
 // word: field p holds k = 16j + 4p + b in byte b, so the two fields cover the
 // 8 consecutive k from 16j + 8h.
 __device__ __forceinline__ u32x4 expand_bf16(uint32_t w, int h) {
-    const uint32_t f0 = (w >> (4 * h)) & 0x03030303u;
-    const uint32_t f1 = (w >> (4 * h + 2)) & 0x03030303u;
-    return u32x4{bf16_pair<0x01010000u>(f0), bf16_pair<0x03030202u>(f0), bf16_pair<0x01010000u>(f1),
-                 bf16_pair<0x03030202u>(f1)};
+    const u32x2 a = bf16_quad((w >> (4 * h)) & 0x03030303u);
+    const u32x2 b = bf16_quad((w >> (4 * h + 2)) & 0x03030303u);
+    return u32x4{a.x, a.y, b.x, b.y};
 }
 
 }  // namespace bitnet
