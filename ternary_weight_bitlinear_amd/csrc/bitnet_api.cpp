@@ -650,7 +650,9 @@ static bool persistent_forced() {
 
 int64_t bitnet_group_table_bytes(int32_t count) {
     if (count <= 0) return -1;
-    return static_cast<int64_t>(count) * static_cast<int64_t>(sizeof(bitnet::GemvProblem));
+    // the problems, then the share bounds of a streaming launch
+    return static_cast<int64_t>(count) * static_cast<int64_t>(sizeof(bitnet::GemvProblem)) +
+           (bitnet::kMaxStreamGrid + 1) * static_cast<int64_t>(sizeof(int32_t));
 }
 
 static bitnet_status_t group_plan_impl(hipStream_t stream, const bitnet_group_item_t* items,
@@ -712,21 +714,29 @@ static bitnet_status_t group_plan_impl(hipStream_t stream, const bitnet_group_it
     // fit its LDS share, else the persistent one.
     int kind = kGroupPersistent, grid = 0;
     size_t lds = bitnet::gemv_group_lds(M, max_kp);
+    std::vector<int32_t> bounds;
     if (a16) {
-        if (!bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &grid, &lds, 2))
+        if (!bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &grid, &lds, 2, &bounds))
             return fail(BITNET_ERR_UNSUPPORTED,
                         "%s: a workgroup's share of the group needs more LDS than it has for M=%lld bf16 token rows "
                         "(use bitnet_linear_a16 per item)",
                         fn, (long long)M);
         kind = kGroupA16;
-    } else if (!persistent_forced() && bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &grid, &lds)) {
+    } else if (!persistent_forced() &&
+               bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &grid, &lds, 1, &bounds)) {
         kind = kGroupStream;
     } else {
         grid = 0;
         lds = bitnet::gemv_group_lds(M, max_kp);
+        bounds.clear();
     }
-    hipError_t e = hipMemcpyAsync(table_dev, table.data(), table.size() * sizeof(bitnet::GemvProblem),
-                                  hipMemcpyHostToDevice, stream);
+    // one upload: the problems, then (streaming kernels) the share bounds
+    std::vector<char> blob(table.size() * sizeof(bitnet::GemvProblem) + bounds.size() * sizeof(int32_t));
+    memcpy(blob.data(), table.data(), table.size() * sizeof(bitnet::GemvProblem));
+    if (!bounds.empty())
+        memcpy(blob.data() + table.size() * sizeof(bitnet::GemvProblem), bounds.data(),
+               bounds.size() * sizeof(int32_t));
+    hipError_t e = hipMemcpyAsync(table_dev, blob.data(), blob.size(), hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return hip_fail(e, "bitnet_group_plan: table upload");
     if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "bitnet_group_plan: sync");
     plan->opaque[0] = kPlanMagic;

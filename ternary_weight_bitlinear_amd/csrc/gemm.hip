@@ -384,24 +384,31 @@ hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_r
                        int64_t N, void* y, bool y_bf16, int64_t ldy, int32_t* acc_debug,
                        hipStream_t stream) {
     // Two tiles: 128x128 with 2x2 waves of 64x64 (3 workgroups per CU), and
-    // 128x256 with 1x4 waves of 128x64 (2 per CU), which halves the code
-    // expansion and the global bytes per MFMA and runs each tile ~7% faster.
+    // 128x256 with 2x2 waves of 64x128 (2 per CU), which has 40% fewer global
+    // bytes per MFMA and runs each tile ~7% faster (a 1x4 split of it, with
+    // half the expansion but a third more LDS reads per MFMA, measured 1-3%
+    // slower).
     // The grid runs in rounds of resident workgroups, so the choice weighs
     // that gain against the share of the last round left empty (e.g. N=3840:
     // 960 small tiles fill 1.25 rounds of 768, 480 wide tiles 0.94 of 512).
     const int slots_small = resident_slots(gemm_kernel<128, 128, 2, 2, BITNET_GEMM_PF, 3, true>, 256,
                                            lds_bytes<128, 128>(), g_slots_small);
-    const int slots_wide = resident_slots(gemm_kernel<128, 256, 1, 4, BITNET_GEMM_PF, 2, true>, 256,
+    const int slots_wide = resident_slots(gemm_kernel<128, 256, 2, 2, BITNET_GEMM_PF, 2, true>, 256,
                                           lds_bytes<128, 256>(), g_slots_wide);
     const int64_t tiles_m = (M + 127) / 128;
     const double small = round_fill(tiles_m * ((N + 127) / 128), slots_small);
-    const double wide = 1.07 * round_fill(tiles_m * ((N + 255) / 256), slots_wide);
+    const int64_t tiles_wide = tiles_m * ((N + 255) / 256);
+    const double wide = 1.07 * round_fill(tiles_wide, slots_wide);
+    // Measured on the prefill shapes: the wide tile wins only with K >= 2048
+    // (with 8-16 stages the per-tile prologue and epilogue favour three
+    // resident 128x128 tiles) and at least ~a full round of wide tiles.
+    const bool use_wide = wide > small && Kp >= 2048 && tiles_wide * 10 >= static_cast<int64_t>(slots_wide) * 9;
     const int forced = forced_tile();
     if (forced == 2 || (forced < 0 && use_tiny(M, N, slots_small)))
         return launch_tile<64, 64, 2, 1, BITNET_GEMM_PF, 4>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16,
                                                             ldy, acc_debug, BITNET_GEMM_GM, stream);
-    if (forced == 1 || (forced < 0 && wide > small))
-        return launch_tile<128, 256, 1, 4, BITNET_GEMM_PF, 2>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y,
+    if (forced == 1 || (forced < 0 && use_wide))
+        return launch_tile<128, 256, 2, 2, BITNET_GEMM_PF, 2>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y,
                                                               y_bf16, ldy, acc_debug, BITNET_GEMM_GM, stream);
     return launch_tile<128, 128, 2, 2, BITNET_GEMM_PF, 3>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16,
                                                           ldy, acc_debug, BITNET_GEMM_GM, stream);

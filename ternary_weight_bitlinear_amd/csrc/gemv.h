@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace bitnet {
 
 struct GemvProblem {
@@ -43,13 +45,20 @@ int64_t gemv_group_steps(int64_t Kp);
 // Fused ActQuant + decode linear for one problem; LDS holds M*Kp bytes.
 hipError_t launch_gemv_fused(const GemvProblem& p, bool x_bf16, bool y_bf16, hipStream_t stream);
 
+// Largest grid of a grouped streaming launch: the device table holds this
+// many + 1 share bounds after the problems.
+constexpr int kMaxStreamGrid = 4096;
+
 // Whether the streaming kernel (per-wave LDS ring of DMA weight loads) can
 // run this table of problems (host copy, tile0 / ntiles / steps / step0 set):
 // every workgroup's problems must fit its LDS share, with token rows of
 // token_bytes per element (1: int8 codes; 2: the bf16 rows of the W1.58A16
 // kernel).  On success gives the grid and the dynamic LDS bytes to launch with.
+// `bounds` (grouped launches) receives grid + 1 share bounds, to be uploaded
+// right after the problem table; without it the shares are k-step shares
+// snapped to tile starts (single problems).
 bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_tiles, int64_t total_steps,
-                      int* grid, size_t* lds, int token_bytes = 1);
+                      int* grid, size_t* lds, int token_bytes = 1, std::vector<int32_t>* bounds = nullptr);
 
 // W1.58A16 grouped launch of the streaming kernel (bf16 x, no quantiser):
 // table_dev and the grid as for launch_gemv_grouped's streaming case.

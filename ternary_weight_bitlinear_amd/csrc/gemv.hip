@@ -723,14 +723,31 @@ __host__ __device__ __forceinline__ int64_t share_start(int64_t total_steps, int
 // the token rows are zero padded that far, see padded_q_row).
 __device__ __forceinline__ int stream_steps(int Kp) { return ((Kp / 64 + 3) / 4 + 1) / 2 * 2; }
 
+// Tiles [t_begin, t_end) of this workgroup: for a grouped launch the host's
+// balanced share bounds (stored after the problem table), for a single
+// problem its k-step share snapped to the nearest tile start.
+template <bool kGrouped>
+__device__ __forceinline__ void stream_share(const Problems<kGrouped>& ps, const int32_t* bounds, int total_tiles,
+                                             int64_t total_steps, int n_first, int& t_begin, int& t_end) {
+    const int G = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+    if constexpr (kGrouped) {
+        t_begin = bounds[b];
+        t_end = bounds[b + 1];
+    } else {
+        t_begin = first_tile_from_step(ps, share_start(total_steps, b, G, n_first), total_tiles);
+        t_end = first_tile_from_step(ps, share_start(total_steps, b + 1, G, n_first), total_tiles);
+    }
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t packed_rsrc(const GemvProblem& p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.packed), 0, p.N * (p.Kp / 4), kRsrcWord3);
 }
 
 template <bool kFused, bool kGrouped, bool kXBf16, bool kOutBf16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITNET_STREAM_PER_CU)))
-void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ table, int count, int total_tiles,
-                        int64_t total_steps, int n_first) {
+void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ table,
+                        const int32_t* __restrict__ bounds, int count, int total_tiles, int64_t total_steps,
+                        int n_first) {
     int8_t* const q_lds = g_stream_q;                   // the workgroup's problems' token rows
     __shared__ float red_f[kWaves];
     __shared__ int red_i[kWaves];
@@ -739,9 +756,8 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     __shared__ __attribute__((aligned(16))) int rs_lds[kStreamMaxProblems * 16];
 
     const Problems<kGrouped> ps{table, single, count};
-    const int G = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
-    const int t_begin = first_tile_from_step(ps, share_start(total_steps, b, G, n_first), total_tiles);
-    const int t_end = first_tile_from_step(ps, share_start(total_steps, b + 1, G, n_first), total_tiles);
+    int t_begin, t_end;
+    stream_share(ps, bounds, total_tiles, total_steps, n_first, t_begin, t_end);
     if (t_begin >= t_end) return;                       // workgroup-uniform
     const int p_first = find_problem(ps, t_begin);
     const int p_last = find_problem(ps, t_end - 1);     // the host keeps the span within kStreamMaxProblems
@@ -948,14 +964,14 @@ __device__ __forceinline__ void lds_read128(const void* p, u32x4 (&a)[8]) {
 
 template <bool kGrouped, bool kOutBf16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITNET_STREAM_PER_CU)))
-void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ table, int count, int total_tiles,
-                            int64_t total_steps, int n_first) {
+void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ table,
+                            const int32_t* __restrict__ bounds, int count, int total_tiles, int64_t total_steps,
+                            int n_first) {
     uint16_t* const x_lds = reinterpret_cast<uint16_t*>(g_stream_q);   // bf16 token rows of the problems
 
     const Problems<kGrouped> ps{table, single, count};
-    const int G = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
-    const int t_begin = first_tile_from_step(ps, share_start(total_steps, b, G, n_first), total_tiles);
-    const int t_end = first_tile_from_step(ps, share_start(total_steps, b + 1, G, n_first), total_tiles);
+    int t_begin, t_end;
+    stream_share(ps, bounds, total_tiles, total_steps, n_first, t_begin, t_end);
     if (t_begin >= t_end) return;                       // workgroup-uniform
     const int p_first = find_problem(ps, t_begin);
     const int p_last = find_problem(ps, t_end - 1);     // the host keeps the span within kStreamMaxProblems
@@ -1197,12 +1213,88 @@ int host_find_problem(const GemvProblem* t, int count, int64_t tile) {
     return lo;
 }
 
+// A grouped launch's share bounds sit right after its problem table.
+const int32_t* stream_bounds_of(const GemvProblem* table, int count) {
+    return reinterpret_cast<const int32_t*>(table + count);
+}
+
+// Extra cost of each problem a workgroup touches beyond its first, in k-step
+// batches of a CU's second workgroup per token row: the problem's token rows
+// are quantised (or staged) into LDS before the loop, measured at ~2.5 us per
+// problem and token while such a workgroup streams ~1.3 batches per us.
+#ifndef BITNET_STREAM_PROBLEM_COST
+#define BITNET_STREAM_PROBLEM_COST 3
+#endif
+
+// Greedy share of one workgroup: the tiles from `i` on whose cost (k-step
+// batches over the slot's relative rate, plus the cost of every further
+// problem) stays within `cap` and whose token rows, w_scale and exact sums
+// fit the LDS array.  Returns the end tile.
+int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_tiles, double cap, double rate,
+                   int token_bytes) {
+    if (i >= total_tiles) return i;
+    int p = host_find_problem(t, count, i);
+    double cost = 0.0;
+    int64_t bytes = 0;
+    for (int np = 0; i < total_tiles && np < kStreamMaxProblems && p < count; ++np, ++p) {
+        const GemvProblem& P = t[p];
+        const double enter = np > 0 ? static_cast<double>(BITNET_STREAM_PROBLEM_COST) * P.M : 0.0;
+        const int64_t enter_bytes = static_cast<int64_t>(P.M) * padded_q_row(P.Kp) * token_bytes;
+        const double tile_cost = P.steps / rate;
+        const int64_t tile_bytes = 64 * static_cast<int64_t>(sizeof(float)) * (1 + P.M);
+        const int64_t left = P.tile0 + P.ntiles - i;
+        const double room = cap - cost - enter;
+        const int64_t lds_room = kStreamQBytes - bytes - enter_bytes;
+        if (room < tile_cost || lds_room < tile_bytes) break;
+        const int64_t k = std::min<int64_t>(left, std::min<int64_t>(static_cast<int64_t>(room / tile_cost),
+                                                                     lds_room / tile_bytes));
+        cost += enter + static_cast<double>(k) * tile_cost;
+        bytes += enter_bytes + k * tile_bytes;
+        i += k;
+        if (k < left) break;
+    }
+    return i;
+}
+
+// Share bounds of a grouped streaming launch (bounds[b] .. bounds[b + 1] are
+// workgroup b's tiles, whole tiles in table order) that minimise the largest
+// workgroup cost: a binary search on that cost, each candidate filled
+// greedily.  The first n_first workgroups (the first on their CU) stream
+// BITNET_STREAM_FIRST_WEIGHT percent as fast as the rest.  False if no cost
+// covers every tile within the LDS limits.
+bool stream_bounds(const GemvProblem* t, int count, int64_t total_tiles, int grid, int n_first, int token_bytes,
+                   std::vector<int32_t>& bounds) {
+    auto cover = [&](double cap, bool keep) {
+        int64_t i = 0;
+        for (int b = 0; b < grid; ++b) {
+            if (keep) bounds[b] = static_cast<int32_t>(i);
+            const double rate = b < n_first ? BITNET_STREAM_FIRST_WEIGHT / 100.0 : 1.0;
+            i = fill_share(t, count, i, total_tiles, cap, rate, token_bytes);
+        }
+        if (keep) bounds[grid] = static_cast<int32_t>(i);
+        return i >= total_tiles;
+    };
+    double all = 0.0;
+    for (int p = 0; p < count; ++p)
+        all += static_cast<double>(t[p].ntiles) * t[p].steps + static_cast<double>(BITNET_STREAM_PROBLEM_COST) * t[p].M;
+    double lo = 0.0, hi = all + 1.0;
+    if (!cover(hi, false)) return false;
+    for (int it = 0; it < 64 && hi - lo > 1e-3; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        if (cover(mid, false)) hi = mid;
+        else lo = mid;
+    }
+    bounds.assign(static_cast<size_t>(grid) + 1, 0);
+    return cover(hi, true);
+}
+
 template <bool kFused, bool kGrouped, bool XB, bool YB>
 hipError_t launch_stream_t(const GemvProblem& single, const GemvProblem* table, int count, int64_t total_tiles,
                            int64_t total_steps, int grid, size_t lds, hipStream_t stream) {
     auto kern = gemv_stream_kernel<kFused, kGrouped, XB, YB>;
+    const int32_t* bounds = kGrouped ? stream_bounds_of(table, count) : nullptr;
     kern<<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream>>>(
-        single, table, count, static_cast<int>(total_tiles), total_steps, stream_first(grid));
+        single, table, bounds, count, static_cast<int>(total_tiles), total_steps, stream_first(grid));
     return hipGetLastError();
 }
 
@@ -1226,7 +1318,8 @@ hipError_t launch_stream_a16_t(const GemvProblem* table, int count, int64_t tota
                                int grid, hipStream_t stream) {
     GemvProblem none{};
     gemv_stream_a16_kernel<true, kOutBf16><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
-        none, table, count, static_cast<int>(total_tiles), total_steps, stream_first(grid));
+        none, table, stream_bounds_of(table, count), count, static_cast<int>(total_tiles), total_steps,
+        stream_first(grid));
     return hipGetLastError();
 }
 
@@ -1252,20 +1345,31 @@ int64_t gemv_group_steps(int64_t Kp) {          // batches of kBatch k steps per
 }
 
 bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_tiles, int64_t total_steps,
-                      int* grid_out, size_t* lds_out, int token_bytes) {
-    const int grid = static_cast<int>(std::min<int64_t>(stream_grid(), total_tiles));
+                      int* grid_out, size_t* lds_out, int token_bytes, std::vector<int32_t>* bounds) {
+    const int grid = static_cast<int>(std::min<int64_t>(std::min(stream_grid(), kMaxStreamGrid), total_tiles));
     if (grid <= 0 || count <= 0) return false;
     // buffer offsets are 32-bit: every problem's padded rows must stay below 2 GiB
     for (int i = 0; i < count; ++i)
         if (static_cast<int64_t>(host_table[i].ntiles) * 64 * (host_table[i].Kp / 4) >= (int64_t(1) << 31))
             return false;
-    // the token rows of each workgroup's problems must fit the static array
-    size_t need = 0;
     const int n_first = stream_first(grid);
+    // grouped: balanced shares (built to fit; the loop below checks them)
+    if (bounds && !stream_bounds(host_table, count, total_tiles, grid, n_first, token_bytes, *bounds)) return false;
+    // the shares must tile [0, total_tiles) in order, and the token rows of
+    // each workgroup's problems must fit the static array
+    size_t need = 0;
+    int64_t covered = 0;
     for (int b = 0; b < grid; ++b) {
-        const int64_t lo = share_start(total_steps, b, grid, n_first), hi = share_start(total_steps, b + 1, grid, n_first);
-        const int64_t t0 = host_first_tile(host_table, count, lo, total_tiles);
-        const int64_t t1 = host_first_tile(host_table, count, hi, total_tiles);
+        int64_t t0, t1;
+        if (bounds) {
+            t0 = (*bounds)[b];
+            t1 = (*bounds)[b + 1];
+        } else {
+            t0 = host_first_tile(host_table, count, share_start(total_steps, b, grid, n_first), total_tiles);
+            t1 = host_first_tile(host_table, count, share_start(total_steps, b + 1, grid, n_first), total_tiles);
+        }
+        if (t0 != covered || t1 < t0 || t1 > total_tiles) return false;
+        covered = t1;
         if (t0 >= t1) continue;
         const int p0 = host_find_problem(host_table, count, t0), p1 = host_find_problem(host_table, count, t1 - 1);
         if (p1 - p0 + 1 > kStreamMaxProblems) return false;
@@ -1275,7 +1379,7 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
             bytes += static_cast<size_t>(host_table[i].M) * padded_q_row(host_table[i].Kp) * token_bytes;
         need = std::max(need, bytes);
     }
-    if (need > static_cast<size_t>(kStreamQBytes)) return false;
+    if (need > static_cast<size_t>(kStreamQBytes) || covered != total_tiles) return false;
     *grid_out = grid;
     *lds_out = 0;                                       // all of the kernel's LDS is static
     return true;

@@ -46,13 +46,14 @@ def test_sizes_and_strings():
 
 
 def test_group_table_and_plan_handle():
-    """The table holds one descriptor per item; a handle that bitnet_group_plan
-    did not fill names no kernel."""
+    """The table holds one descriptor per item plus a fixed block of share
+    bounds; a handle that bitnet_group_plan did not fill names no kernel."""
     L = _lib.lib()
     assert L.bitnet_group_table_bytes(0) == -1
-    one = L.bitnet_group_table_bytes(1)
-    assert one > 0 and one % 8 == 0
-    assert L.bitnet_group_table_bytes(210) == 210 * one
+    one, two = L.bitnet_group_table_bytes(1), L.bitnet_group_table_bytes(2)
+    per_item = two - one
+    assert per_item > 0 and per_item % 8 == 0 and one > per_item
+    assert L.bitnet_group_table_bytes(210) == one + 209 * per_item
     assert L.bitnet_group_plan_kernel(ctypes.byref(_lib.GroupPlan())) == b""
     assert L.bitnet_group_plan_kernel(None) == b""
 

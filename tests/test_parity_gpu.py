@@ -639,6 +639,35 @@ def test_grouped_many_problems_per_workgroup(orc):
             check_y(y, ref["y"])
 
 
+def test_grouped_lds_limited_shares(orc):
+    """Thirty decoder layers at M = 4: the token rows of the problems a share
+    spans fill the streaming kernel's LDS, so the planner cuts shares where
+    they would overflow.  Every output equals the single-call result, and the
+    k/v projections of the first and last layer match the oracle."""
+    M, gen = 4, torch.Generator(device="cpu").manual_seed(2400)
+    layer = [(2560, 2560), (640, 2560), (640, 2560), (2560, 2560), (6912, 2560), (6912, 2560), (2560, 6912)]
+    items, checks = [], []
+    for li in range(30):
+        for pi, (N, K) in enumerate(layer):
+            W = (torch.randn(N, K, generator=gen) * 0.02).to(torch.bfloat16)
+            x = torch.randn(M, K, generator=gen).to(torch.bfloat16)
+            pw = tw.pack(W.to(DEV))
+            items.append((x.to(DEV), pw, torch.full((M, N), float("nan"), device=DEV)))
+            if li in (0, 29) and pi in (1, 2):
+                checks.append((len(items) - 1, orc.linear(bits(x), bits(W))))
+    group = tw.GroupedBitLinear(items)
+    assert group.kernel == "stream"
+    for rep in range(2):
+        for _, _, y in items:
+            y.fill_(float("nan"))
+        group()
+        torch.cuda.synchronize()
+        for x, pw, y in items:
+            assert torch.equal(y, tw.bitlinear(x, pw))
+        for i, ref in checks:
+            check_y(items[i][2], ref["y"])
+
+
 @pytest.mark.parametrize("M", [1, 2])
 def test_grouped_few_tall_tiles(orc, M):
     """Two groups with fewer 64-row tiles than CUs (16384-wide rows, so one
