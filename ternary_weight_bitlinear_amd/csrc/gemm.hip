@@ -89,6 +89,67 @@ __device__ __forceinline__ void tile_of(const TileOrder& o, int& tm, int& tn) {
     tn = in_band / rows;
 }
 
+// Epilogue shared by both GEMM kernels: register 4rb + rr of lane l in
+// acc[j][i] holds output row m = i*32 + l%32, column n = j*32 + 8rb + 4(l/32)
+// + rr of the wave's tile; the stored codes are t + 1, so the exact sum of
+// q*t is the register minus q_rowsum[m].
+template <int BM, int BN, int WM, int WN, int TM, int TN, bool kOutBf16>
+__device__ __forceinline__ void gemm_epilogue(const v16i (&acc)[TN][TM], const float* as_s, const int32_t* rs_s,
+                                              const float* ws_s, int m0, int n0, int wm, int wn, int r32, int g,
+                                              int M, int N, void* __restrict__ y, int64_t ldy,
+                                              int32_t* __restrict__ acc_debug, int vec_store) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int ml = wm * WM + i * 32 + r32;
+        const int m = m0 + ml;
+        const float as = as_s[ml];
+        const int32_t rs = rs_s[ml];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int nl = wn * WN + j * 32 + 8 * rb + 4 * g;
+                const int n = n0 + nl;
+                const f32x4 ws4 = *reinterpret_cast<const f32x4*>(&ws_s[nl]);
+                int32_t e[4];
+                f32x4 v;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    e[rr] = acc[j][i][4 * rb + rr] - rs;
+                    v[rr] = static_cast<float>(e[rr]) * (as * ws4[rr]);
+                }
+                if (m >= M) continue;
+                const int64_t off = static_cast<int64_t>(m) * ldy + n;
+                if (vec_store && n + 3 < N) {
+                    if constexpr (kOutBf16) {
+                        bf16x4 h;
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) h[rr] = static_cast<__bf16>(v[rr]);   // v_cvt_pk_bf16_f32: RNE
+                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(y) + off) = h;
+                    } else {
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + off) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        if (n + rr >= N) break;
+                        if constexpr (kOutBf16)
+                            static_cast<__bf16*>(y)[off + rr] = static_cast<__bf16>(v[rr]);
+                        else
+                            static_cast<float*>(y)[off + rr] = v[rr];
+                    }
+                }
+                if (acc_debug) {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        if (n + rr < N) acc_debug[static_cast<int64_t>(m) * N + n + rr] = e[rr];
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int WGM, int WGN, int PF, int kWaves, bool kOutBf16>
 __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(kWaves))) void gemm_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ a_scale,
@@ -240,58 +301,285 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
         }
     }
 
-    // epilogue: register 4rb + rr of lane l holds output row m = i*32 + l%32,
-    // column n = j*32 + 8rb + 4(l/32) + rr of the wave's tile
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    gemm_epilogue<BM, BN, WM, WN, TM, TN, kOutBf16>(acc, as_s, rs_s, ws_s, m0, n0, wm, wn, r32, g, M, N, y, ldy,
+                                                   acc_debug, vec_store);
+}
+
+// ------------------------------------------------------------ LDS-DMA variant
+//
+// Same tiles, operand roles and epilogue as gemm_kernel, with a different
+// memory pipeline:
+//  * Global data goes straight to LDS with buffer_load_dwordx4 ... lds (the
+//    memory unit writes LDS; no staging registers, no ds_write), into a ring
+//    of NS stage buffers.  One such load of a wave fills 1 KB of LDS, lane l at
+//    byte 16*l, so the LDS layout is set by choosing which 16 global bytes each
+//    lane fetches: rows are unpadded (128 B of activations, 32 B of codes per
+//    stage) and the 16-byte chunks of a row are XOR-swizzled so that the
+//    16-byte fragment reads of 16 consecutive rows hit distinct bank groups.
+//      activations: chunk c of row r at 16 * (c ^ sa(r)), sa(r) = (r&7) ^ ((r>>3)&1)
+//      codes:       chunk c of row n at 16 * (c ^ sb(n)), sb(n) = ((n>>2) ^ (n>>3)) & 1
+//    Both depend on the row's low 4 bits only, which are the lane's own in
+//    every fragment read.
+//  * Pipeline per stage k, four 32-k steps: each step issues the next step's
+//    activation fragments (step 3: the next stage's code words and first
+//    fragments) from asm, then runs its MFMAs interleaved with the next
+//    step's code expansion (scheduling groups of one MFMA and up to four VALU
+//    ops), then waits for the reads.  Before step 3 the wave waits for its
+//    own loads of stage k+1 and one barrier makes every wave's loads visible
+//    (and tells that stage k's buffer has been read by all); the loads of
+//    stage k+NS then go into that buffer.  One barrier per stage; loads run
+//    NS stages ahead.
+//  * LDS reads are issued from asm: the compiler would otherwise order every
+//    LDS read after all LDS DMA loads in flight.  The issuing asm names the
+//    destination registers as outputs and a later waiting asm names them as
+//    in-out operands, with scheduling barriers on both sides of the step's
+//    MFMAs, so no use of the data precedes the wait and the reads' latency
+//    hides behind the MFMAs.  The MFMAs are compiler builtins, so the
+//    compiler's hazard handling covers them.
+//  * Tail stages past the end are fetched from an offset outside the buffer
+//    range, so every stage issues the same loads and the wait counts are
+//    compile-time constants; those loads write zeros into buffers nobody
+//    reads, and the wave drains them before the epilogue.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int kVm>
+__device__ __forceinline__ void wait_vm() {     // s_waitcnt vmcnt(kVm), other counters untouched
+    static_assert(kVm >= 0 && kVm < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16 bytes per lane from buffer offset off to LDS at dst + 16 * lane (dst
+// wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+__host__ __device__ constexpr int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__host__ __device__ constexpr int swz_b(int n) { return ((n >> 2) ^ (n >> 3)) & 1; }
+
+template <int BM, int BN>
+constexpr int dma_stage_bytes() {
+    return BM * BK + BN * (BK / 4);
+}
+
+// Split LDS reads: the issuing asm names the destination registers as
+// outputs, the waiting asm names them again as in-out operands, so the
+// compiler keeps them live and places no use of them before the wait.
+__device__ __forceinline__ void lds_issue_a(v4i (&na)[2], uint32_t ad) {
+    asm volatile("ds_read_b128 %[n0], %[ad]\n\tds_read_b128 %[n1], %[ad] offset:4096"
+                 : [n0] "=&v"(na[0]), [n1] "=&v"(na[1])
+                 : [ad] "v"(ad)
+                 : "memory");
+}
+__device__ __forceinline__ void lds_wait_a(v4i (&na)[2]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(na[0]), "+v"(na[1]) : : "memory");
+}
+__device__ __forceinline__ void lds_issue_head(v4i (&na)[2], u32x4 (&nw)[4], uint32_t ad, uint32_t bd) {
+    asm volatile(
+        "ds_read_b128 %[w0], %[bd]\n\tds_read_b128 %[w1], %[bd] offset:1024\n\t"
+        "ds_read_b128 %[w2], %[bd] offset:2048\n\tds_read_b128 %[w3], %[bd] offset:3072\n\t"
+        "ds_read_b128 %[n0], %[ad]\n\tds_read_b128 %[n1], %[ad] offset:4096"
+        : [n0] "=&v"(na[0]), [n1] "=&v"(na[1]), [w0] "=&v"(nw[0]), [w1] "=&v"(nw[1]), [w2] "=&v"(nw[2]),
+          [w3] "=&v"(nw[3])
+        : [ad] "v"(ad), [bd] "v"(bd)
+        : "memory");
+}
+__device__ __forceinline__ void lds_wait_head(v4i (&na)[2], u32x4 (&nw)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(na[0]), "+v"(na[1]), "+v"(nw[0]), "+v"(nw[1]), "+v"(nw[2]), "+v"(nw[3])
+                 :
+                 : "memory");
+}
+__device__ __forceinline__ void lds_issue_head(v4i (&na)[2], u32x4 (&nw)[2], uint32_t ad, uint32_t bd) {
+    asm volatile(
+        "ds_read_b128 %[w0], %[bd]\n\tds_read_b128 %[w1], %[bd] offset:1024\n\t"
+        "ds_read_b128 %[n0], %[ad]\n\tds_read_b128 %[n1], %[ad] offset:4096"
+        : [n0] "=&v"(na[0]), [n1] "=&v"(na[1]), [w0] "=&v"(nw[0]), [w1] "=&v"(nw[1])
+        : [ad] "v"(ad), [bd] "v"(bd)
+        : "memory");
+}
+__device__ __forceinline__ void lds_wait_head(v4i (&na)[2], u32x4 (&nw)[2]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(na[0]), "+v"(na[1]), "+v"(nw[0]), "+v"(nw[1]) : : "memory");
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int kWaves, bool kOutBf16>
+__global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(kWaves))) void gemm_dma_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ a_scale,
+    const int32_t* __restrict__ q_rowsum, int M, int Kp,
+    const uint8_t* __restrict__ packed, const float* __restrict__ w_scale, int N,
+    void* __restrict__ y, int64_t ldy, int32_t* __restrict__ acc_debug, TileOrder order, int vec_store) {
+    constexpr int kNW = WGM * WGN;
+    constexpr int kThreads = kNW * 64;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int SA = BM * BK, SB = BN * (BK / 4), STAGE = SA + SB;
+    constexpr int A_DMA = SA / 1024 / kNW, B_DMA = SB / 1024 / kNW, D = A_DMA + B_DMA;
+    static_assert(TM == 2 && (TN == 2 || TN == 4), "wave tile 64 x 64 or 64 x 128");
+    static_assert(SA % (1024 * kNW) == 0 && SB % (1024 * kNW) == 0 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
+    static_assert(NS >= 2 && (NS - 1) * D < 64, "stage ring");
+
+    extern __shared__ __attribute__((aligned(16))) int8_t lds[];   // [NS][activations SA | codes SB]
+    __shared__ __attribute__((aligned(16))) float as_s[BM];
+    __shared__ __attribute__((aligned(16))) int32_t rs_s[BM];
+    __shared__ __attribute__((aligned(16))) float ws_s[BN];
+
+    int tm, tn;
+    tile_of(order, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid % 64;
+    const int wave = tid / 64;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int r32 = lane % 32;
+    const int g = lane / 32;
+    const int brow_bytes = Kp / 4;
+    const int stages = Kp / BK;
+
+    const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(q + static_cast<int64_t>(m0) * Kp), 0, a_rows * Kp, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(packed + static_cast<int64_t>(n0) * brow_bytes), 0, b_rows * brow_bytes, kRsrcWord3);
+
+    // Global offsets (stage 0) of the lane's 16 bytes in each of its loads.
+    uint32_t a_off[A_DMA], b_off[B_DMA];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int ml = wm * WM + i * 32 + r32;
-        const int m = m0 + ml;
-        const float as = as_s[ml];
-        const int32_t rs = rs_s[ml];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int nl = wn * WN + j * 32 + 8 * rb + 4 * g;
-                const int n = n0 + nl;
-                const f32x4 ws4 = *reinterpret_cast<const f32x4*>(&ws_s[nl]);
-                int32_t e[4];
-                f32x4 v;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    e[rr] = acc[j][i][4 * rb + rr] - rs;
-                    v[rr] = static_cast<float>(e[rr]) * (as * ws4[rr]);
-                }
-                if (m >= M) continue;
-                const int64_t off = static_cast<int64_t>(m) * ldy + n;
-                if (vec_store && n + 3 < N) {
-                    if constexpr (kOutBf16) {
-                        bf16x4 h;
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) h[rr] = static_cast<__bf16>(v[rr]);   // v_cvt_pk_bf16_f32: RNE
-                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(y) + off) = h;
-                    } else {
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + off) = v;
-                    }
-                } else {
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        if (n + rr >= N) break;
-                        if constexpr (kOutBf16)
-                            static_cast<__bf16*>(y)[off + rr] = static_cast<__bf16>(v[rr]);
-                        else
-                            static_cast<float*>(y)[off + rr] = v[rr];
-                    }
-                }
-                if (acc_debug) {
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        if (n + rr < N) acc_debug[static_cast<int64_t>(m) * N + n + rr] = e[rr];
-                }
-            }
-        }
+    for (int i = 0; i < A_DMA; ++i) {
+        const int r = (i * kNW + wave) * 8 + lane / 8;           // 8 rows of 128 B per load
+        a_off[i] = static_cast<uint32_t>(r * Kp + 16 * ((lane % 8) ^ swz_a(r)));
     }
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) {
+        const int n = (i * kNW + wave) * 32 + lane / 2;          // 32 rows of 32 B per load
+        b_off[i] = static_cast<uint32_t>(n * brow_bytes + 16 * ((lane % 2) ^ swz_b(n)));
+    }
+    auto issue = [&](int ks, int buf) {                           // stage ks -> buffer buf (= ks % NS)
+        const bool in = ks < stages;
+        const uint32_t ka = in ? static_cast<uint32_t>(ks * BK) : kOutOfRange;
+        const uint32_t kb = in ? static_cast<uint32_t>(ks * (BK / 4)) : kOutOfRange;
+        int8_t* base = lds + buf * STAGE + wave * 1024;
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i)
+            dma16(a_rsrc, base + i * kNW * 1024, a_off[i] + ka);
+#pragma unroll
+        for (int i = 0; i < B_DMA; ++i)
+            dma16(b_rsrc, base + SA + i * kNW * 1024, b_off[i] + kb);
+    };
+
+    // LDS byte addresses of the lane's fragment reads in buffer 0: activation
+    // row wm*WM + r32 (+32 rows at +4096), k chunk 4g + s; code row wn*WN + r32
+    // (+32 rows per code tile at +1024), chunk g.
+    const uint32_t lds0 = lds_offset(lds);
+    uint32_t a_rd[4];
+    {
+        const int r = wm * WM + r32;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a_rd[s] = lds0 + r * BK + 16 * ((4 * g + s) ^ swz_a(r));
+    }
+    const int bn = wn * WN + r32;
+    const uint32_t b_rd = lds0 + SA + bn * (BK / 4) + 16 * (g ^ swz_b(bn));
+
+    for (int i = tid; i < BM; i += kThreads) {
+        const int m = m0 + i;
+        as_s[i] = m < M ? a_scale[m] : 0.0f;
+        rs_s[i] = m < M ? q_rowsum[m] : 0;
+    }
+    for (int i = tid; i < BN; i += kThreads) ws_s[i] = n0 + i < N ? w_scale[n0 + i] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) issue(u, u);
+    wait_vm<(NS - 1) * D>();
+    __syncthreads();
+
+    v16i acc[TN][TM];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
+
+    v4i a[2], na[2];
+    u32x4 bw[TN];
+    lds_issue_head(a, bw, a_rd[0], b_rd);
+    lds_wait_head(a, bw);
+    int cur = 0;                                                  // buffer of stage k
+    v4i b[TN], bx[TN];                                            // this and the next step's codes
+    u32x4 nbw[TN];
+    for (int k = 0; k < stages; ++k) {
+        const int nxt = cur + 1 == NS ? 0 : cur + 1;
+        const uint32_t co = static_cast<uint32_t>(cur * STAGE), no = static_cast<uint32_t>(nxt * STAGE);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = expand_word(bw[j][0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s == 3) {
+                // every wave: own loads of stage k+1 landed, stage k's buffer read
+                wait_vm<(NS - 2) * D>();
+                __builtin_amdgcn_s_barrier();
+                issue(k + NS, cur);
+                lds_issue_head(na, nbw, a_rd[0] + no, b_rd + no);
+            } else {
+                lds_issue_a(na, a_rd[s + 1] + co);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (s < 3) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) bx[j] = expand_word(bw[j][s + 1]);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[j][i] = mfma32(b[j], a[i], acc[j][i]);
+#pragma unroll
+            for (int t = 0; t < TM * TN; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // up to four VALU
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (s == 3) {
+                lds_wait_head(na, nbw);
+            } else {
+                lds_wait_a(na);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) b[j] = bx[j];
+            }
+            a[0] = na[0];
+            a[1] = na[1];
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bw[j] = nbw[j];
+        cur = nxt;
+    }
+    // the loads past the last stage must land before the workgroup's LDS is released
+    wait_vm<0>();
+
+    gemm_epilogue<BM, BN, WM, WN, TM, TN, kOutBf16>(acc, as_s, rs_s, ws_s, m0, n0, wm, wn, r32, g, M, N, y, ldy,
+                                                   acc_debug, vec_store);
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int kWaves>
+hipError_t launch_tile_dma(const int8_t* q, const float* a_scale, const int32_t* q_rowsum, int64_t M, int64_t Kp,
+                           const uint8_t* packed, const float* w_scale, int64_t N, void* y, bool y_bf16,
+                           int64_t ldy, int32_t* acc_debug, int group_m, hipStream_t stream) {
+    TileOrder order;
+    order.tiles_m = static_cast<int>((M + BM - 1) / BM);
+    order.tiles_n = static_cast<int>((N + BN - 1) / BN);
+    order.group_m = group_m > 0 ? group_m : order.tiles_m;
+    constexpr size_t lds = static_cast<size_t>(NS) * dma_stage_bytes<BM, BN>();
+    const dim3 grid(static_cast<unsigned>(order.tiles_m) * order.tiles_n), block(WGM * WGN * 64);
+    auto kern = y_bf16 ? gemm_dma_kernel<BM, BN, WGM, WGN, NS, kWaves, true>
+                       : gemm_dma_kernel<BM, BN, WGM, WGN, NS, kWaves, false>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    const int vec_store = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+    kern<<<grid, block, lds, stream>>>(q, a_scale, q_rowsum, (int)M, (int)Kp, packed, w_scale, (int)N, y, ldy,
+                                       acc_debug, order, vec_store);
+    return hipGetLastError();
 }
 
 template <int BM, int BN, int WGM, int WGN, int PF, int kWaves>
@@ -377,6 +665,22 @@ int forced_tile() {
     return -1;
 }
 
+// BITNET_GEMM_KERNEL=regs selects the register-staged kernel for the 128x128
+// and 128x256 tiles instead of the LDS-DMA one (for comparisons; results are
+// identical), read at each launch.
+bool use_regs_kernel() {
+    const char* v = getenv("BITNET_GEMM_KERNEL");
+    return v && strcmp(v, "regs") == 0;
+}
+
+#ifndef BITNET_GEMM_NS_WIDE
+#define BITNET_GEMM_NS_WIDE 3
+#endif
+#ifndef BITNET_GEMM_NS_SMALL
+#define BITNET_GEMM_NS_SMALL 2
+#endif
+int g_dslots_small[64], g_dslots_wide[64];
+
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_rowsum,
@@ -385,16 +689,21 @@ hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_r
                        hipStream_t stream) {
     // Two tiles: 128x128 with 2x2 waves of 64x64 (3 workgroups per CU), and
     // 128x256 with 2x2 waves of 64x128 (2 per CU), which has 40% fewer global
-    // bytes per MFMA and runs each tile ~7% faster (a 1x4 split of it, with
-    // half the expansion but a third more LDS reads per MFMA, measured 1-3%
-    // slower).
+    // bytes per MFMA and runs each tile faster.
     // The grid runs in rounds of resident workgroups, so the choice weighs
     // that gain against the share of the last round left empty (e.g. N=3840:
     // 960 small tiles fill 1.25 rounds of 768, 480 wide tiles 0.94 of 512).
-    const int slots_small = resident_slots(gemm_kernel<128, 128, 2, 2, BITNET_GEMM_PF, 3, true>, 256,
-                                           lds_bytes<128, 128>(), g_slots_small);
-    const int slots_wide = resident_slots(gemm_kernel<128, 256, 2, 2, BITNET_GEMM_PF, 2, true>, 256,
-                                          lds_bytes<128, 256>(), g_slots_wide);
+    const bool regs = use_regs_kernel();
+    const int slots_small =
+        regs ? resident_slots(gemm_kernel<128, 128, 2, 2, BITNET_GEMM_PF, 3, true>, 256, lds_bytes<128, 128>(),
+                              g_slots_small)
+             : resident_slots(gemm_dma_kernel<128, 128, 2, 2, BITNET_GEMM_NS_SMALL, 3, true>, 256,
+                              BITNET_GEMM_NS_SMALL * dma_stage_bytes<128, 128>(), g_dslots_small);
+    const int slots_wide =
+        regs ? resident_slots(gemm_kernel<128, 256, 2, 2, BITNET_GEMM_PF, 2, true>, 256, lds_bytes<128, 256>(),
+                              g_slots_wide)
+             : resident_slots(gemm_dma_kernel<128, 256, 2, 2, BITNET_GEMM_NS_WIDE, 2, true>, 256,
+                              BITNET_GEMM_NS_WIDE * dma_stage_bytes<128, 256>(), g_dslots_wide);
     const int64_t tiles_m = (M + 127) / 128;
     const double small = round_fill(tiles_m * ((N + 127) / 128), slots_small);
     const int64_t tiles_wide = tiles_m * ((N + 255) / 256);
@@ -408,10 +717,16 @@ hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_r
         return launch_tile<64, 64, 2, 1, BITNET_GEMM_PF, 4>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16,
                                                             ldy, acc_debug, BITNET_GEMM_GM, stream);
     if (forced == 1 || (forced < 0 && use_wide))
-        return launch_tile<128, 256, 2, 2, BITNET_GEMM_PF, 2>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y,
-                                                              y_bf16, ldy, acc_debug, BITNET_GEMM_GM, stream);
-    return launch_tile<128, 128, 2, 2, BITNET_GEMM_PF, 3>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16,
-                                                          ldy, acc_debug, BITNET_GEMM_GM, stream);
+        return regs ? launch_tile<128, 256, 2, 2, BITNET_GEMM_PF, 2>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N,
+                                                                     y, y_bf16, ldy, acc_debug, BITNET_GEMM_GM, stream)
+                    : launch_tile_dma<128, 256, 2, 2, BITNET_GEMM_NS_WIDE, 2>(q, a_scale, q_rowsum, M, Kp, packed,
+                                                                            w_scale, N, y, y_bf16, ldy, acc_debug,
+                                                                            BITNET_GEMM_GM, stream);
+    return regs ? launch_tile<128, 128, 2, 2, BITNET_GEMM_PF, 3>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y,
+                                                                 y_bf16, ldy, acc_debug, BITNET_GEMM_GM, stream)
+                : launch_tile_dma<128, 128, 2, 2, BITNET_GEMM_NS_SMALL, 3>(q, a_scale, q_rowsum, M, Kp, packed,
+                                                                         w_scale, N, y, y_bf16, ldy, acc_debug,
+                                                                         BITNET_GEMM_GM, stream);
 }
 
 }  // namespace bitnet

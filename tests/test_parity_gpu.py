@@ -453,12 +453,18 @@ def test_linear(orc, M, N, K, out):
     check_y(y, ref["y"])
 
 
+@pytest.mark.parametrize("kernel", ["dma", "regs"])
 @pytest.mark.parametrize("tile", ["small", "wide", "tiny"])
-@pytest.mark.parametrize("M,N,K", [(17, 16, 16), (130, 257, 1152), (300, 200, 4304), (257, 129, 6912)])
-def test_linear_each_gemm_tile(orc, tile, M, N, K, monkeypatch):
-    """Every GEMM tile (128x128, 128x256 and 64x64, forced) gives the oracle's
-    exact sums and outputs on ragged M, N and padded K."""
+@pytest.mark.parametrize("M,N,K", [(17, 16, 16), (130, 257, 1152), (300, 200, 4304), (257, 129, 6912),
+                                   (384, 512, 2560), (520, 1100, 2560)])
+def test_linear_each_gemm_tile(orc, kernel, tile, M, N, K, monkeypatch):
+    """Every GEMM tile (128x128, 128x256 and 64x64, forced) of both kernels
+    (LDS-DMA and register-staged loads) gives the oracle's exact sums and
+    outputs on ragged M, N and padded K."""
+    if kernel == "regs" and tile == "tiny":
+        pytest.skip("the 64x64 tile has one kernel")
     monkeypatch.setenv("BITNET_GEMM_TILE", tile)
+    monkeypatch.setenv("BITNET_GEMM_KERNEL", kernel)
     x, W = wl.random_case(M * 31 + N * 3 + K, M, N, K, x_dist="normal_outliers")
     ref = orc.linear(bits(x), bits(W), out="bf16")
     pw = tw.pack(W.to(DEV))
