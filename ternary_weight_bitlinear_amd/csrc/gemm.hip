@@ -18,11 +18,15 @@
 //  * Workgroup tile BM x BN, k stage BK = 128, double-buffered in LDS; waves
 //    in a WGM x WGN grid, each owning (BM/WGM) x (BN/WGN) as 32x32 tiles held
 //    in accumulation registers.
-//  * Global loads run PF stages ahead of the MFMAs through PF register sets,
-//    so a load has PF stages of matrix work to land in; a stage is written to
-//    the free LDS buffer one stage before it is used.  The loads are buffer
-//    loads: rows past M or N and stages past the end lie outside the buffer's
-//    range and read as zero, so every load is issued unconditionally and the
+//  * Two kernels share tiles, operand roles and epilogue.  gemm_dma_kernel
+//    (the default for the 128x128 and 128x256 tiles; its own comment block
+//    below) fetches stages straight into an LDS ring.  gemm_kernel (the 64x64
+//    tile, and the others under BITNET_GEMM_KERNEL=regs) runs global loads PF
+//    stages ahead of the MFMAs through PF register sets, so a load has PF
+//    stages of matrix work to land in; a stage is written to the free LDS
+//    buffer one stage before it is used.  In both the loads are buffer loads:
+//    rows past M or N and stages past the end lie outside the buffer's range
+//    and read as zero, so every load is issued unconditionally and the
 //    compiler can keep exact wait counts.
 //  * Codes stay packed in LDS (a quarter of an int8 tile).  In one stage lane
 //    group g takes the contiguous k range [64g, 64g + 64) of the stage, so its
@@ -33,8 +37,9 @@
 //    k order.
 //  * Stored codes are u = t + 1 in {0,1,2}; the epilogue subtracts q_rowsum[m]
 //    (the padded tail has q = 0) to get the exact sum of q*t.
-//  * LDS rows are padded (A: 144 B, B: 48 B) so that the 16-byte reads of 16
-//    consecutive rows fall in distinct bank groups.
+//  * gemm_kernel pads LDS rows (A: 144 B, B: 48 B) so that the 16-byte reads
+//    of 16 consecutive rows fall in distinct bank groups; gemm_dma_kernel
+//    swizzles 16-byte chunks instead.
 //  * Tile order: workgroup b runs on XCD b % 8, so ids are remapped to give
 //    each XCD a contiguous range of the tile sequence, and the sequence walks
 //    bands of GM tile rows column by column, so the workgroups that run
@@ -342,6 +347,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
 //    reads, and the wave drains them before the epilogue.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// VALU ops placed after each MFMA of a step (the next step's code expansion).
+#ifndef BITNET_GEMM_VALU_GROUP
+#define BITNET_GEMM_VALU_GROUP 4
+#endif
+
 template <int kVm>
 __device__ __forceinline__ void wait_vm() {     // s_waitcnt vmcnt(kVm), other counters untouched
     static_assert(kVm >= 0 && kVm < 64, "vmcnt range");
@@ -537,7 +547,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int t = 0; t < TM * TN; ++t) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // up to four VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, BITNET_GEMM_VALU_GROUP, 0);   // then VALU ops
             }
             __builtin_amdgcn_sched_barrier(0);
             if (s == 3) {
