@@ -83,6 +83,22 @@
  *       rounding per addition, k ascending) -- the reference value that a
  *       kernel summing in fp32, in its own order, is held to within a bound.
  *
+ * Per-block weight scales [BitVLA s2: the sibling matvec kernel it grew from
+ * keeps one scale per 256-weight block where BitNet keeps one per tensor,
+ * i.e. a scale matrix of N x K/256 instead of N x 1]:
+ *   R15 Blocks run along k within a row: block b of row n holds
+ *       k = 256b .. min(256b + 256, K) - 1, nb = ceil(K / 256) blocks per
+ *       row, the last one partial when 256 does not divide K.  Its scale is
+ *       the absmean of its own weights, R2 restricted to the block: fp64 sum
+ *       of |W| over its k ascending, one fp64 division by the number of
+ *       weights in the block, rounding to fp32.  Codes follow R1, R3, R7 with
+ *       the block's s = 1/mean.  Scales are stored block-major,
+ *       block_scale[b][n].
+ *   R16 y[m][n] = a_scale[m] * sum_b acc_b[m][n] * block_scale[b][n] with the
+ *       exact int32 block sums acc_b = sum_{k in block b} q*t, evaluated in
+ *       fp32 in this order: total = 0; for b ascending,
+ *       total = total + (float)acc_b * block_scale[b][n]; y = total * a_scale.
+ *
  * Everything here is a direct loop over the definition.  No blocking, no
  * fusion, no intrinsics.
  */
@@ -545,4 +561,76 @@ int orc_max_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* ------------------------------------------------ per-block weight scales */
+
+/* Blocks of 256 weights per row (R15); -1 for a bad K. */
+int64_t orc_block_count(int64_t K)
+{
+    if (K <= 0 || K % 16 != 0)
+        return -1;
+    return (K + 255) / 256;
+}
+
+/*
+ * WeightQuant with one scale per 256-weight block of a row (R15): codes
+ * t [N][K] and block_scale [nb][N].  Returns 0, -1 for a bad K, -2 if a
+ * weight is not finite.
+ */
+int orc_weight_quant_blocked(const void* W, int dtype, int64_t N, int64_t K, int64_t ldw,
+                             int8_t* t, float* block_scale)
+{
+    int64_t nb = orc_block_count(K);
+    if (nb < 0)
+        return -1;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            if (!isfinite(load_elem(W, dtype, n * ldw + k)))
+                return -2;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < nb; ++b) {
+            int64_t k0 = 256 * b, k1 = (k0 + 256 < K) ? k0 + 256 : K;
+            double sum = 0.0;
+            for (int64_t k = k0; k < k1; ++k)
+                sum += fabs((double)load_elem(W, dtype, n * ldw + k));
+            float mean = (float)(sum / (double)(k1 - k0));
+            float s = 1.0f / mean;
+            block_scale[b * N + n] = mean;
+            for (int64_t k = k0; k < k1; ++k)
+                t[n * K + k] = orc_ternary(load_elem(W, dtype, n * ldw + k), s);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Linear with block scales (R16): y [M][N] fp32 from q [M][Kp] (ActQuant
+ * output), a_scale [M], codes t [N][K] and block_scale [nb][N].  acc_blocks
+ * [M][nb][N] (or NULL) receives the exact block sums.  Returns -1 for a bad K.
+ */
+int orc_linear_blocked(const int8_t* q, const float* a_scale, int64_t M, int64_t K, const int8_t* t,
+                       const float* block_scale, int64_t N, float* y, int32_t* acc_blocks)
+{
+    int64_t Kp = orc_padded_k(K), nb = orc_block_count(K);
+    if (Kp < 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float total = 0.0f;
+            for (int64_t b = 0; b < nb; ++b) {
+                int64_t k0 = 256 * b, k1 = (k0 + 256 < K) ? k0 + 256 : K;
+                int64_t s = 0;
+                for (int64_t k = k0; k < k1; ++k)
+                    s += (int64_t)t[n * K + k] * (int64_t)q[m * Kp + k];
+                if (acc_blocks)
+                    acc_blocks[(m * nb + b) * N + n] = (int32_t)s;
+                float term = (float)s * block_scale[b * N + n];
+                total = total + term;
+            }
+            y[m * N + n] = total * a_scale[m];
+        }
+    }
+    return 0;
 }

@@ -88,6 +88,11 @@ class Oracle:
         lib.orc_epilogue.argtypes = [vp, i64, i64, vp, vp, ctypes.c_int, vp, i64]
         lib.orc_epilogue.restype = None
         lib.orc_max_threads.argtypes, lib.orc_max_threads.restype = [], ctypes.c_int
+        lib.orc_block_count.argtypes, lib.orc_block_count.restype = [i64], i64
+        lib.orc_weight_quant_blocked.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp]
+        lib.orc_weight_quant_blocked.restype = ctypes.c_int
+        lib.orc_linear_blocked.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp]
+        lib.orc_linear_blocked.restype = ctypes.c_int
         self.lib = lib
 
     # ----------------------------------------------------------- scalars
@@ -283,6 +288,52 @@ class Oracle:
         y = self.epilogue(acc, a_scale, w_scale, out)
         return dict(t=t, packed=packed, w_scale=w_scale, seg_mean=seg_mean, zero_count=zeros,
                     q=q, a_scale=a_scale, q_rowsum=rowsum, acc=acc, y=y)
+
+    # ------------------------------------------- per-block weight scales
+    def block_count(self, K: int) -> int:
+        return int(self.lib.orc_block_count(K))
+
+    def weight_quant_blocked(self, W: np.ndarray):
+        """Codes t [N, K] and block_scale [nb, N]: one absmean scale per 256
+        weights of a row (reading R15 of the C file)."""
+        W = np.ascontiguousarray(W)
+        N, K = W.shape
+        nb = self.block_count(K)
+        if nb < 0:
+            raise ValueError("K must be a positive multiple of 16")
+        t = np.empty((N, K), dtype=np.int8)
+        bs = np.empty((nb, N), dtype=np.float32)
+        rc = self.lib.orc_weight_quant_blocked(_ptr(W), _dtype_code(W), N, K, K, _ptr(t), _ptr(bs))
+        if rc == -2:
+            raise FloatingPointError("non-finite weight")
+        return t, bs
+
+    def linear_blocked_q(self, q: np.ndarray, a_scale: np.ndarray, t: np.ndarray, block_scale: np.ndarray):
+        """fp32 y [M, N] and exact block sums [M, nb, N] from quantised
+        operands (reading R16 of the C file)."""
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        a_scale = np.ascontiguousarray(a_scale, dtype=np.float32)
+        t = np.ascontiguousarray(t, dtype=np.int8)
+        block_scale = np.ascontiguousarray(block_scale, dtype=np.float32)
+        M, (N, K) = q.shape[0], t.shape
+        if q.shape[1] != self.padded_k(K) or block_scale.shape != (self.block_count(K), N):
+            raise ValueError("q must be [M, Kp] and block_scale [nb, N]")
+        y = np.empty((M, N), dtype=np.float32)
+        accb = np.empty((M, block_scale.shape[0], N), dtype=np.int32)
+        self.lib.orc_linear_blocked(_ptr(q), _ptr(a_scale), M, K, _ptr(t), _ptr(block_scale), N, _ptr(y),
+                                    _ptr(accb))
+        return y, accb
+
+    def linear_blocked(self, x: np.ndarray, W: np.ndarray, out: str = "f32") -> dict:
+        """y = linear(ActQuant(x), blocked WeightQuant(W)) and its intermediates."""
+        t, bs = self.weight_quant_blocked(W)
+        packed = self.pack(t)
+        q, a_scale, rowsum = self.act_quant(x)
+        y, accb = self.linear_blocked_q(q, a_scale, t, bs)
+        if out == "bf16":
+            y = self.bf16_from_f32(y)
+        return dict(t=t, packed=packed, block_scale=bs, q=q, a_scale=a_scale, q_rowsum=rowsum,
+                    acc_blocks=accb, y=y)
 
     def max_threads(self) -> int:
         return int(self.lib.orc_max_threads())

@@ -513,6 +513,102 @@ def pin_i2s_roundtrip_and_blocks(orc):
     assert d.size == 1 and d[0] // 32 == 200 // 128
 
 
+# ------------------------------------------- per-block weight scales (R15, R16)
+
+def _blocked_fp32_bound(acc_blocks, bs, a_scale):
+    """Exact value a_scale * sum_b acc_b * bs_b (fp64 of exact products) and a
+    bound on the sequential fp32 evaluation: every product and partial sum
+    rounds once (2**-24 relative each), then one product with a_scale."""
+    M, nb, N = acc_blocks.shape
+    terms = acc_blocks.astype(np.float64) * bs.astype(np.float64)[None, :, :]
+    exact = terms.sum(axis=1) * a_scale.astype(np.float64)[:, None]
+    mag = np.abs(terms).sum(axis=1) * a_scale.astype(np.float64)[:, None]
+    return exact, (nb + 2) * 2.0 ** -24 * mag + 1e-30
+
+
+def pin_blocked_closed_form(orc):
+    """Blocks of constant magnitude c[n][b] with a sign pattern and 10% zeros:
+    each block's absmean is c * nonzeros / count (the last block of K = 1152
+    holds 128 weights), every nonzero weight maps to its sign, and y equals
+    a_scale * sum_b c-scaled integer block sums within the fp32 bound."""
+    rng = np.random.default_rng(71)
+    N, K = 6, 1152
+    nb = orc.block_count(K)
+    assert nb == 5
+    sigma = rng.choice(np.array([-1, 1], dtype=np.int8), size=(N, K))
+    sigma[rng.random((N, K)) < 0.1] = 0
+    c = (2.0 ** rng.integers(-9, -3, size=(N, nb))) * rng.choice([1.0, 1.5, 1.25], size=(N, nb))
+    W32 = np.zeros((N, K), dtype=np.float32)
+    for b in range(nb):
+        W32[:, 256 * b:256 * b + 256] = c[:, b:b + 1] * sigma[:, 256 * b:256 * b + 256]
+    W = f32_to_bf16_bits(W32)
+    t, bs = orc.weight_quant_blocked(W)
+    assert np.array_equal(t, sigma)
+    for n in range(N):
+        for b in range(nb):
+            blk = sigma[n, 256 * b:256 * b + 256]
+            assert bs[b, n] == np.float32(c[n, b] * np.count_nonzero(blk) / blk.size)
+    x = rng_bf16(rng, (3, K))
+    q, a_scale, _ = orc.act_quant(x)
+    y, accb = orc.linear_blocked_q(q, a_scale, t, bs)
+    want = np.stack([(q[:, 256 * b:min(256 * b + 256, K)].astype(np.int64)
+                      @ sigma[:, 256 * b:min(256 * b + 256, K)].astype(np.int64).T) for b in range(nb)], axis=1)
+    assert np.array_equal(accb, want)
+    exact, bound = _blocked_fp32_bound(want, bs, a_scale)
+    assert np.all(np.abs(y.astype(np.float64) - exact) <= bound)
+
+
+def pin_blocked_reduces_to_tensor(orc):
+    """When every block has the tensor's absmean (W = mu * sign), the block codes
+    and scales are the per-tensor ones and the block sums add up to the
+    per-tensor integer dot exactly."""
+    rng = np.random.default_rng(73)
+    N, K = 5, 2560
+    sign = rng.choice(np.array([-1, 1], dtype=np.int8), size=(N, K))
+    W = f32_to_bf16_bits((np.float32(0.046875) * sign).astype(np.float32))
+    t_b, bs = orc.weight_quant_blocked(W)
+    t, w_scale, _, _ = orc.weight_quant(W)
+    assert np.array_equal(t_b, t) and np.all(bs == w_scale[None, :])
+    x = rng_bf16(rng, (4, K))
+    q, a_scale, _ = orc.act_quant(x)
+    y_b, accb = orc.linear_blocked_q(q, a_scale, t_b, bs)
+    acc = orc.int_dot(q, t)
+    assert np.array_equal(accb.astype(np.int64).sum(axis=1), acc.astype(np.int64))
+    y = orc.epilogue(acc, a_scale, w_scale)
+    assert np.allclose(y_b, y, rtol=4e-6, atol=0)
+
+
+def pin_blocked_random_codes_and_float(orc):
+    """Random weights with a different spread in every row: codes are the sign
+    where |W| >= 1.5 * block mean and 0 where |W| <= 0.5 * block mean (away from
+    the two rounding boundaries); y is within the fp32 bound of the exact
+    a_scale * sum_k q * t * block_scale (K = 400: blocks of 256 and 144)."""
+    rng = np.random.default_rng(79)
+    N, K = 7, 400
+    W32 = (rng.standard_normal((N, K)) * (0.01 * (1 + np.arange(N)))[:, None]).astype(np.float32)
+    W = rng_bf16_from(W32)
+    Wf = bf16_bits_to_f32(W).astype(np.float64)
+    t, bs = orc.weight_quant_blocked(W)
+    assert set(np.unique(t)) <= {-1, 0, 1}
+    for b in range(orc.block_count(K)):
+        sl = slice(256 * b, min(256 * b + 256, K))
+        mean = np.abs(Wf[:, sl]).mean(axis=1)
+        assert np.allclose(bs[b], mean, rtol=2 ** -23)
+        ratio = np.abs(Wf[:, sl]) / mean[:, None]
+        tb = t[:, sl]
+        big, small = ratio >= 1.5 * (1 + 1e-6), ratio <= 0.5 * (1 - 1e-6)
+        assert np.array_equal(tb[big], np.sign(Wf[:, sl])[big].astype(np.int8))
+        assert np.all(tb[small] == 0)
+    x = rng_bf16(rng, (3, K))
+    q, a_scale, _ = orc.act_quant(x)
+    y, accb = orc.linear_blocked_q(q, a_scale, t, bs)
+    exact, bound = _blocked_fp32_bound(accb, bs, a_scale)
+    qt = np.stack([q[:, 256 * b:min(256 * b + 256, K)].astype(np.int64)
+                   @ t[:, 256 * b:min(256 * b + 256, K)].astype(np.int64).T for b in range(2)], axis=1)
+    assert np.array_equal(accb, qt)
+    assert np.all(np.abs(y.astype(np.float64) - exact) <= bound)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

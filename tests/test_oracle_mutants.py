@@ -16,6 +16,17 @@ from oracle import oracle as orc_mod
 HERE = Path(__file__).resolve().parent
 
 MUTANTS = [
+    ("block mean divides by 256 in a partial block",
+     "float mean = (float)(sum / (double)(k1 - k0));", "float mean = (float)(sum / 256.0);"),
+    ("block scales stored row-major", "block_scale[b * N + n] = mean;", "block_scale[n * nb + b] = mean;"),
+    ("blocked sum drops the last block",
+     "for (int64_t b = 0; b < nb; ++b) {\n                int64_t k0",
+     "for (int64_t b = 0; b < nb - 1; ++b) {\n                int64_t k0"),
+    ("blocked output omits a_scale", "y[m * N + n] = total * a_scale[m];", "y[m * N + n] = total;"),
+    ("block codes use the tensor's first block scale",
+     "float s = 1.0f / mean;\n            block_scale[b * N + n] = mean;",
+     "float s = 1.0f / (float)(fabs((double)load_elem(W, dtype, n * ldw + 0)) + 1e-30);\n"
+     "            block_scale[b * N + n] = mean;"),
     ("weight rounding half away from zero",
      "float r = round_half_even(p);", "float r = roundf(p);"),
     ("activation rounding half away from zero",
