@@ -325,6 +325,40 @@ bitnet_status_t bitnet_linear_a16(hipStream_t stream, const void* x, bitnet_dtyp
                                   void* y, bitnet_dtype_t y_dtype, int64_t ldy);
 
 /*
+ * Per-block weight scales [BitVLA s2: the sibling matvec kernel keeps one
+ * scale per 256-weight block, a scale matrix of N x K/256, where BitNet keeps
+ * one per tensor].  Block b of row n holds k = 256b .. min(256b + 256, K) - 1;
+ * a row has bitnet_block_count(K) = ceil(K/256) blocks, the last one partial
+ * when 256 does not divide K.
+ *
+ * bitnet_pack_weights_blocked (device memory, synchronous on `stream`):
+ *   W [N, K] bf16 or fp32 (row stride ldw), packed [N][Kp/4] in layout v1
+ *   (16-byte aligned), block_scale [nb][N] fp32, block-major.  Per block:
+ *   mean = fp32(fp64 sum of |W| over the block, k ascending, / the block's
+ *   weight count), s = 1/mean (fp32), t = clamp(rne(W*s), -1, 1); a zero
+ *   block has scale 0 and codes 0.  K <= 8192.
+ * bitnet_linear_blocked_forward (asynchronous on `stream`): q, a_scale from
+ *   bitnet_act_quant ([M][Kp], 16-byte aligned), y fp32 or bf16 [M, N] (ldy):
+ *   y[m][n] = a_scale[m] * sum_b acc_b * block_scale[b][n] with the exact
+ *   int32 block sums acc_b = sum_{k in block b} q*t, evaluated in fp32 as
+ *   total = 0; for b ascending: total = total + (float)acc_b * block_scale;
+ *   y = total * a_scale (bf16 y: that value rounded to nearest even).  One
+ *   int8-MFMA GEMM for every M (not tuned for decode sizes).
+ * Errors: INVALID_ARG (sizes, NULL or misaligned pointers, ld < K or N, bad
+ * dtype); UNSUPPORTED for K > 8192; NONFINITE for a non-finite weight; HIP.
+ */
+int64_t bitnet_block_count(int64_t K);   /* ceil(K/256); -1 for a bad K */
+
+bitnet_status_t bitnet_pack_weights_blocked(hipStream_t stream, const void* W, bitnet_dtype_t w_dtype,
+                                            int64_t N, int64_t K, int64_t ldw,
+                                            uint8_t* packed, float* block_scale);
+
+bitnet_status_t bitnet_linear_blocked_forward(hipStream_t stream, const int8_t* q, const float* a_scale,
+                                              int64_t M, int64_t K, const uint8_t* packed,
+                                              const float* block_scale, int64_t N,
+                                              void* y, bitnet_dtype_t y_dtype, int64_t ldy);
+
+/*
  * I2_S interchange [Guide s3.3 "I2_S Ternary Packing"], for weights
  * converted by bitnet.cpp's tooling.  An I2_S buffer of one [N, K] tensor is
  * N*K/4 code bytes followed by one fp32 scale s = 1/mean|W| (little-endian),

@@ -219,6 +219,44 @@ def linear(q: torch.Tensor, a_scale: torch.Tensor, q_rowsum: torch.Tensor, w: Pa
     return (y, acc) if acc_debug else y
 
 
+@dataclass
+class BlockPackedWeight:
+    packed: torch.Tensor       # uint8 [N, Kp/4], layout v1
+    block_scale: torch.Tensor  # float32 [ceil(K/256), N], block-major
+    N: int
+    K: int
+
+
+def pack_blocked(W: torch.Tensor) -> BlockPackedWeight:
+    """WeightQuant with one absmean scale per 256 weights of a row (device W)."""
+    ldw = _rows(W, "W")
+    N, K = W.shape
+    nb = int(_lib.lib().bitnet_block_count(K))
+    if nb < 0:
+        raise ValueError(f"K={K} must be a positive multiple of 16")
+    packed = torch.empty((N, padded_k(K) // 4), dtype=torch.uint8, device=W.device)
+    block_scale = torch.empty((nb, N), dtype=torch.float32, device=W.device)
+    with torch.cuda.device(W.device):
+        _lib.check(_lib.lib().bitnet_pack_weights_blocked(_stream(W), W.data_ptr(), _dtype(W), N, K, ldw,
+                                                          packed.data_ptr(), block_scale.data_ptr()))
+    return BlockPackedWeight(packed, block_scale, N, K)
+
+
+def linear_blocked(q: torch.Tensor, a_scale: torch.Tensor, w: BlockPackedWeight, out_dtype=torch.float32,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """y [M, N] = a_scale[m] * sum_b acc_b * block_scale[b][n] (fp32, blocks in order)."""
+    M = q.shape[0]
+    if q.shape[1] != padded_k(w.K):
+        raise ValueError("q must be [M, Kp] for the packed weight's K")
+    y = out if out is not None else torch.empty((M, w.N), dtype=out_dtype, device=q.device)
+    ldy = _rows(y, "y")
+    with torch.cuda.device(q.device):
+        _lib.check(_lib.lib().bitnet_linear_blocked_forward(
+            _stream(q), q.data_ptr(), a_scale.data_ptr(), M, w.K, w.packed.data_ptr(), w.block_scale.data_ptr(),
+            w.N, y.data_ptr(), _dtype(y), ldy))
+    return y
+
+
 def bitlinear(x: torch.Tensor, w: PackedWeight, out_dtype=torch.float32, out: torch.Tensor | None = None,
               workspace=None):
     """y = linear(ActQuant(x), WeightQuant(W)) from activations x [M, K].

@@ -48,6 +48,10 @@ SIGNATURES = {
     "bitnet_i2s_export": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp]),
     "bitnet_save_packed": (ctypes.c_int, [ctypes.c_char_p, _vp, _vp, _i64, _i64, _vp, _vp, _i32]),
     "bitnet_load_packed": (ctypes.c_int, [ctypes.c_char_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "bitnet_block_count": (_i64, [_i64]),
+    "bitnet_pack_weights_blocked": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp]),
+    "bitnet_linear_blocked_forward": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp,
+                                                     ctypes.c_int, _i64]),
     "bitnet_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bitnet_last_error": (ctypes.c_char_p, []),
 }

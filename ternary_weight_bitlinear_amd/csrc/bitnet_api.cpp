@@ -27,6 +27,7 @@ namespace {
 
 constexpr int64_t kMaxK = 1 << 20;
 constexpr int64_t kMaxMN = 0x7FFFFFFF;
+constexpr int64_t kBlockedMaxK = 8192;   // block scales of a 128-column tile staged in LDS
 constexpr int64_t kGemvMaxM = 16;
 constexpr int64_t kFusedLdsBytes = 32768;     // single call: M * Kp bytes of q in LDS
 constexpr int64_t kGroupLdsBytes = 65536;     // grouped launch: M * max Kp
@@ -322,6 +323,63 @@ bitnet_status_t bitnet_rmsnorm_act_quant(hipStream_t stream, const void* x, cons
     hipError_t e = bitnet::launch_norm_act_quant(x, up, x_dtype == BITNET_BF16, M, K, ldx, norm_w,
                                                  norm_dtype == BITNET_BF16, eps, q, a_scale, q_rowsum,
                                                  padded_k(K), stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+int64_t bitnet_block_count(int64_t K) {
+    return padded_k(K) < 0 ? -1 : (K + 255) / 256;
+}
+
+bitnet_status_t bitnet_pack_weights_blocked(hipStream_t stream, const void* W, bitnet_dtype_t w_dtype, int64_t N,
+                                            int64_t K, int64_t ldw, uint8_t* packed, float* block_scale) {
+    const char* fn = "bitnet_pack_weights_blocked";
+    bitnet_status_t s = check_dims(fn, 1, N, K);
+    if (s != BITNET_OK) return s;
+    if (K > kBlockedMaxK) return fail(BITNET_ERR_UNSUPPORTED, "%s: K=%lld > %lld", fn, (long long)K, (long long)kBlockedMaxK);
+    if (!W || !packed || !block_scale) return fail(BITNET_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (!valid_dtype(w_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad W dtype %d", fn, (int)w_dtype);
+    if (ldw < K) return fail(BITNET_ERR_INVALID_ARG, "%s: ldw=%lld < K=%lld", fn, (long long)ldw, (long long)K);
+    if (!aligned(W, w_dtype == BITNET_F32 ? 4 : 2) || !aligned(packed, 16) || !aligned(block_scale, 4))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned pointer (packed must be 16-byte aligned)", fn);
+    DeviceTemps temps;
+    temps.stream = stream;
+    hipError_t e = hipMallocAsync(&temps.p, sizeof(unsigned int), stream);
+    if (e != hipSuccess) {
+        temps.p = nullptr;
+        return hip_fail(e, "bitnet_pack_weights_blocked: temporary allocation");
+    }
+    auto* d_status = static_cast<unsigned int*>(temps.p);
+    if ((e = hipMemsetAsync(d_status, 0, sizeof(unsigned int), stream)) != hipSuccess)
+        return hip_fail(e, "bitnet_pack_weights_blocked: status clear");
+    e = bitnet::launch_pack_blocked(W, w_dtype == BITNET_BF16, N, K, ldw, padded_k(K), d_status, packed, block_scale,
+                                    stream);
+    if (e != hipSuccess) return hip_fail(e, "bitnet_pack_weights_blocked: launch");
+    unsigned int status = 0;
+    if ((e = hipMemcpyAsync(&status, d_status, sizeof status, hipMemcpyDeviceToHost, stream)) != hipSuccess)
+        return hip_fail(e, "bitnet_pack_weights_blocked: read-back");
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "bitnet_pack_weights_blocked: sync");
+    if (status & 1u) return fail(BITNET_ERR_NONFINITE, "bitnet_pack_weights_blocked: a weight is not finite");
+    return ok();
+}
+
+bitnet_status_t bitnet_linear_blocked_forward(hipStream_t stream, const int8_t* q, const float* a_scale, int64_t M,
+                                              int64_t K, const uint8_t* packed, const float* block_scale, int64_t N,
+                                              void* y, bitnet_dtype_t y_dtype, int64_t ldy) {
+    const char* fn = "bitnet_linear_blocked_forward";
+    bitnet_status_t s = check_dims(fn, M, N, K);
+    if (s != BITNET_OK) return s;
+    if (K > kBlockedMaxK) return fail(BITNET_ERR_UNSUPPORTED, "%s: K=%lld > %lld", fn, (long long)K, (long long)kBlockedMaxK);
+    if (!q || !a_scale || !packed || !block_scale || !y)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (!valid_dtype(y_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad y dtype %d", fn, (int)y_dtype);
+    if (ldy < N) return fail(BITNET_ERR_INVALID_ARG, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+    if (!aligned(q, 16) || !aligned(packed, 16))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: q and packed must be 16-byte aligned", fn);
+    if (!aligned(y, y_dtype == BITNET_F32 ? 4 : 2) || !aligned(a_scale, 4) || !aligned(block_scale, 4))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned y or scale pointer", fn);
+    hipError_t e = bitnet::launch_gemm_blocked(q, a_scale, M, K, padded_k(K), packed, block_scale, N, y,
+                                               y_dtype == BITNET_BF16, ldy, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }

@@ -416,12 +416,87 @@ __device__ __forceinline__ void lds_wait_head(v4i (&na)[2], u32x4 (&nw)[2]) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(na[0]), "+v"(na[1]), "+v"(nw[0]), "+v"(nw[1]) : : "memory");
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int kWaves, bool kOutBf16>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Signed MFMA operand of one packed word: byte 4p+b is t = u - 1 of element
+// 16j+4p+b, looked up from the stored code u in {0,1,2} with one byte
+// permute per 4 codes (table bytes 0xFF, 0x00, 0x01).
+__device__ __forceinline__ v4i expand_word_signed(uint32_t w) {
+    constexpr uint32_t kSigned = 0x000100FFu;
+    v4i r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        r[p] = static_cast<int>(__builtin_amdgcn_perm(0u, kSigned, (w >> (2 * p)) & 0x03030303u));
+    return r;
+}
+
+// One 16-byte LDS read with its completion wait in the same asm block (see the
+// LDS-read note above: a compiler-visible read would wait for the DMA loads).
+__device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_offset(p)) : "memory");
+    return v;
+}
+
+// Epilogue of the block-scaled kernel: y = facc * a_scale[m] (fp32), with
+// the register-to-output mapping of gemm_epilogue.
+template <int BM, int BN, int WM, int WN, int TM, int TN, bool kOutBf16>
+__device__ __forceinline__ void gemm_epilogue_blocked(const f32x16 (&facc)[TN][TM], const float* as_s, int m0,
+                                                      int n0, int wm, int wn, int r32, int g, int M, int N,
+                                                      void* __restrict__ y, int64_t ldy, int vec_store) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int ml = wm * WM + i * 32 + r32;
+        const int m = m0 + ml;
+        if (m >= M) continue;
+        const float as = as_s[ml];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int n = n0 + wn * WN + j * 32 + 8 * rb + 4 * g;
+                f32x4 v;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) v[rr] = facc[j][i][4 * rb + rr] * as;
+                const int64_t off = static_cast<int64_t>(m) * ldy + n;
+                if (vec_store && n + 3 < N) {
+                    if constexpr (kOutBf16) {
+                        bf16x4 h;
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) h[rr] = static_cast<__bf16>(v[rr]);
+                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(y) + off) = h;
+                    } else {
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + off) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        if (n + rr >= N) break;
+                        if constexpr (kOutBf16)
+                            static_cast<__bf16*>(y)[off + rr] = static_cast<__bf16>(v[rr]);
+                        else
+                            static_cast<float*>(y)[off + rr] = v[rr];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// kBlocked: weights with one scale per 256-k block of a row.  The codes are
+// expanded to signed t (one byte permute per 4 codes), every 256 k (two
+// stages, or the last stage) the exact int32 block sums are scaled by the
+// block's scale and added to fp32 accumulators in block order, and the
+// epilogue multiplies by a_scale; block_scale [nb][N] is staged in LDS after
+// the ring and read from asm like the ring.
+template <int BM, int BN, int WGM, int WGN, int NS, int kWaves, bool kOutBf16, bool kBlocked = false>
 __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(kWaves))) void gemm_dma_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ a_scale,
     const int32_t* __restrict__ q_rowsum, int M, int Kp,
     const uint8_t* __restrict__ packed, const float* __restrict__ w_scale, int N,
-    void* __restrict__ y, int64_t ldy, int32_t* __restrict__ acc_debug, TileOrder order, int vec_store) {
+    void* __restrict__ y, int64_t ldy, int32_t* __restrict__ acc_debug, TileOrder order, int vec_store,
+    const float* __restrict__ block_scale, int nb) {
     constexpr int kNW = WGM * WGN;
     constexpr int kThreads = kNW * 64;
     constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -496,9 +571,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
     for (int i = tid; i < BM; i += kThreads) {
         const int m = m0 + i;
         as_s[i] = m < M ? a_scale[m] : 0.0f;
-        rs_s[i] = m < M ? q_rowsum[m] : 0;
+        if constexpr (!kBlocked) rs_s[i] = m < M ? q_rowsum[m] : 0;   // kBlocked: q_rowsum not passed
     }
-    for (int i = tid; i < BN; i += kThreads) ws_s[i] = n0 + i < N ? w_scale[n0 + i] : 0.0f;
+    float* const bs_lds = reinterpret_cast<float*>(lds + NS * STAGE);   // kBlocked: [nb][BN]
+    if constexpr (kBlocked) {
+        for (int i = tid; i < nb * BN; i += kThreads) {
+            const int b = i / BN, n = n0 + i % BN;
+            bs_lds[i] = n < N ? block_scale[static_cast<int64_t>(b) * N + n] : 0.0f;
+        }
+    } else {
+        for (int i = tid; i < BN; i += kThreads) ws_s[i] = n0 + i < N ? w_scale[n0 + i] : 0.0f;
+    }
 #pragma unroll
     for (int u = 0; u < NS; ++u) issue(u, u);
     wait_vm<(NS - 1) * D>();
@@ -512,6 +595,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
 
+    f32x16 facc[TN][TM];                                          // kBlocked: scaled block sums
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) facc[j][i][r] = 0.0f;
     v4i a[2], na[2];
     u32x4 bw[TN];
     lds_issue_head(a, bw, a_rd[0], b_rd);
@@ -523,7 +613,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
         const int nxt = cur + 1 == NS ? 0 : cur + 1;
         const uint32_t co = static_cast<uint32_t>(cur * STAGE), no = static_cast<uint32_t>(nxt * STAGE);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = expand_word(bw[j][0]);
+        for (int j = 0; j < TN; ++j) b[j] = kBlocked ? expand_word_signed(bw[j][0]) : expand_word(bw[j][0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             if (s == 3) {
@@ -538,7 +628,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
             __builtin_amdgcn_sched_barrier(0);
             if (s < 3) {
 #pragma unroll
-                for (int j = 0; j < TN; ++j) bx[j] = expand_word(bw[j][s + 1]);
+                for (int j = 0; j < TN; ++j)
+                    bx[j] = kBlocked ? expand_word_signed(bw[j][s + 1]) : expand_word(bw[j][s + 1]);
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -562,13 +653,35 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) bw[j] = nbw[j];
+        if constexpr (kBlocked) {
+            if ((k & 1) || k + 1 == stages) {             // block k/2 complete
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb) {
+                        const u32x4 w4 = lds_read_b128(bs_lds + (k >> 1) * BN + wn * WN + j * 32 + 8 * rb + 4 * g);
+#pragma unroll
+                        for (int i = 0; i < TM; ++i)
+#pragma unroll
+                            for (int rr = 0; rr < 4; ++rr) {
+                                const float term = static_cast<float>(acc[j][i][4 * rb + rr]) * __uint_as_float(w4[rr]);
+                                facc[j][i][4 * rb + rr] = facc[j][i][4 * rb + rr] + term;
+                                acc[j][i][4 * rb + rr] = 0;
+                            }
+                    }
+            }
+        }
         cur = nxt;
     }
     // the loads past the last stage must land before the workgroup's LDS is released
     wait_vm<0>();
 
-    gemm_epilogue<BM, BN, WM, WN, TM, TN, kOutBf16>(acc, as_s, rs_s, ws_s, m0, n0, wm, wn, r32, g, M, N, y, ldy,
-                                                   acc_debug, vec_store);
+    if constexpr (kBlocked)
+        gemm_epilogue_blocked<BM, BN, WM, WN, TM, TN, kOutBf16>(facc, as_s, m0, n0, wm, wn, r32, g, M, N, y, ldy,
+                                                               vec_store);
+    else
+        gemm_epilogue<BM, BN, WM, WN, TM, TN, kOutBf16>(acc, as_s, rs_s, ws_s, m0, n0, wm, wn, r32, g, M, N, y, ldy,
+                                                       acc_debug, vec_store);
 }
 
 template <int BM, int BN, int WGM, int WGN, int NS, int kWaves>
@@ -588,7 +701,7 @@ hipError_t launch_tile_dma(const int8_t* q, const float* a_scale, const int32_t*
     if (e != hipSuccess) return e;
     const int vec_store = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
     kern<<<grid, block, lds, stream>>>(q, a_scale, q_rowsum, (int)M, (int)Kp, packed, w_scale, (int)N, y, ldy,
-                                       acc_debug, order, vec_store);
+                                       acc_debug, order, vec_store, nullptr, 0);
     return hipGetLastError();
 }
 
@@ -737,6 +850,30 @@ hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_r
                 : launch_tile_dma<128, 128, 2, 2, BITNET_GEMM_NS_SMALL, 3>(q, a_scale, q_rowsum, M, Kp, packed,
                                                                          w_scale, N, y, y_bf16, ldy, acc_debug,
                                                                          BITNET_GEMM_GM, stream);
+}
+
+hipError_t launch_gemm_blocked(const int8_t* q, const float* a_scale, int64_t M, int64_t K, int64_t Kp,
+                               const uint8_t* packed, const float* block_scale, int64_t N, void* y, bool y_bf16,
+                               int64_t ldy, hipStream_t stream) {
+    // 128x128 tiles (2x2 waves of 64x64): the fp32 block accumulators double
+    // the accumulator registers, which leaves two workgroups per CU.
+    constexpr int BM = 128, BN = 128, NS = 2;
+    const int nb = static_cast<int>((K + 255) / 256);
+    TileOrder order;
+    order.tiles_m = static_cast<int>((M + BM - 1) / BM);
+    order.tiles_n = static_cast<int>((N + BN - 1) / BN);
+    order.group_m = BITNET_GEMM_GM;
+    const size_t lds = static_cast<size_t>(NS) * dma_stage_bytes<BM, BN>() + static_cast<size_t>(nb) * BN * sizeof(float);
+    auto kern = y_bf16 ? gemm_dma_kernel<BM, BN, 2, 2, NS, 2, true, true>
+                       : gemm_dma_kernel<BM, BN, 2, 2, NS, 2, false, true>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    const int vec_store = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+    const dim3 grid(static_cast<unsigned>(order.tiles_m) * order.tiles_n), block(256);
+    kern<<<grid, block, lds, stream>>>(q, a_scale, nullptr, (int)M, (int)Kp, packed, nullptr, (int)N, y, ldy,
+                                       nullptr, order, vec_store, block_scale, nb);
+    return hipGetLastError();
 }
 
 }  // namespace bitnet

@@ -40,6 +40,18 @@ hipError_t launch_pack(const void* W, bool w_bf16, int64_t N, int64_t K, int64_t
                        unsigned int* status_dev, uint8_t* packed, float* w_scale,
                        hipStream_t stream);
 
+// WeightQuant with one scale per 256-weight block of a row: packed [N][Kp/4]
+// (layout v1) and block_scale [ceil(K/256)][N]; status bit 0: a weight is not
+// finite.
+hipError_t launch_pack_blocked(const void* W, bool w_bf16, int64_t N, int64_t K, int64_t ldw, int64_t Kp,
+                               unsigned int* status_dev, uint8_t* packed, float* block_scale, hipStream_t stream);
+
+// Linear with per-block weight scales, any M: y = a_scale * sum_b (float)acc_b
+// * block_scale[b][n] in block order (int8 MFMA GEMM, 128x128 tiles); K <= 8192.
+hipError_t launch_gemm_blocked(const int8_t* q, const float* a_scale, int64_t M, int64_t K, int64_t Kp,
+                               const uint8_t* packed, const float* block_scale, int64_t N, void* y, bool y_bf16,
+                               int64_t ldy, hipStream_t stream);
+
 // W1.58A16: y = w_scale * (x_bf16 . t), fp32 accumulation on bf16 MFMA; x rows
 // 16-byte aligned (ldx * 2 % 16 == 0).
 hipError_t launch_gemv_a16(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, int64_t Kp, const uint8_t* packed,

@@ -19,6 +19,13 @@
 //     this is exactly clamp(rne(W*s), -1, 1) (rne(0.5) = 0), and a NaN product
 //     gives 0.  Zero codes are counted per segment (wave sum, one atomic).
 // Packing runs once per weight, offline; it is not on the timed path.
+//
+// Per-block scales ("BitVLA -- 1.58-bit Vision-Language-Action on Core AI",
+// s2: the sibling matvec kernel keeps one scale per 256-weight block instead
+// of one per tensor): pack_blocked_kernel, one thread per (row, block of 256
+// k), adds |W| over the block's k in fp64 in k order, divides once by the
+// block's weight count, rounds to fp32, and writes the block's code words
+// (padding positions k >= K hold code 1) and its scale, block-major.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -130,6 +137,44 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ W, int6
     }
 }
 
+
+// One thread per (row n, block b): block b of row n covers k = 256b ..
+// min(256b + 256, K) - 1 and the packed words 16b .. 16b + 15 that lie below
+// Kp / 16.  block_scale is [nb][N].
+template <typename T>
+__global__ __launch_bounds__(256) void pack_blocked_kernel(const T* __restrict__ W, int64_t N, int64_t K,
+                                                           int64_t ldw, int64_t Kp, int64_t nb,
+                                                           uint32_t* __restrict__ packed_words,
+                                                           float* __restrict__ block_scale,
+                                                           unsigned int* __restrict__ status) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= N * nb) return;
+    const int64_t n = idx / nb, b = idx % nb;
+    const int64_t k0 = 256 * b, k1 = k0 + 256 < K ? k0 + 256 : K;
+    const T* wr = W + n * ldw;
+    double sum = 0.0;
+    for (int64_t k = k0; k < k1; ++k) sum += fabs(static_cast<double>(ld<T>(wr + k)));
+    if (!isfinite(sum)) atomicOr(status, 1u);
+    const float mean = static_cast<float>(sum / static_cast<double>(k1 - k0));
+    const float s = 1.0f / mean;
+    block_scale[b * N + n] = mean;
+    const int64_t words_per_row = Kp / 16;
+    for (int64_t j = 16 * b; j < 16 * b + 16 && j < words_per_row; ++j) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t k = 16 * j + e;
+            uint32_t u = 1u;                          // padding: weight 0
+            if (k < K) {
+                const float p = ld<T>(wr + k) * s;
+                u = static_cast<uint32_t>((p > 0.5f) - (p < -0.5f) + 1);
+            }
+            word |= u << (8 * (e % 4) + 2 * (e / 4));  // element 16j + 4*(e/4) + e%4
+        }
+        packed_words[n * words_per_row + j] = word;
+    }
+}
+
 template <typename T>
 hipError_t launch_t(const T* W, int64_t N, int64_t K, int64_t ldw, int64_t Kp,
                     const int64_t* seg_start, int n_segs, double* row_sum, float* seg_mean,
@@ -160,6 +205,21 @@ hipError_t launch_pack(const void* W, bool w_bf16, int64_t N, int64_t K, int64_t
                         seg_mean_dev, seg_zero_dev, status_dev, packed, w_scale, stream);
     return launch_t(static_cast<const float*>(W), N, K, ldw, Kp, seg_start_dev, n_segs, row_sum,
                     seg_mean_dev, seg_zero_dev, status_dev, packed, w_scale, stream);
+}
+
+hipError_t launch_pack_blocked(const void* W, bool w_bf16, int64_t N, int64_t K, int64_t ldw, int64_t Kp,
+                               unsigned int* status_dev, uint8_t* packed, float* block_scale, hipStream_t stream) {
+    const int64_t nb = (K + 255) / 256;
+    const unsigned grid = static_cast<unsigned>((N * nb + 255) / 256);
+    if (w_bf16)
+        pack_blocked_kernel<uint16_t><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(W), N, K, ldw, Kp, nb,
+                                                                reinterpret_cast<uint32_t*>(packed), block_scale,
+                                                                status_dev);
+    else
+        pack_blocked_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(W), N, K, ldw, Kp, nb,
+                                                             reinterpret_cast<uint32_t*>(packed), block_scale,
+                                                             status_dev);
+    return hipGetLastError();
 }
 
 }  // namespace bitnet

@@ -63,6 +63,18 @@ def _status_and_error(fn, *args):
     return st, _lib.lib().bitnet_last_error().decode()
 
 
+def test_blocked_sizes_and_limits():
+    L = _lib.lib()
+    assert [L.bitnet_block_count(k) for k in (16, 256, 272, 1152, 6912, 8192)] == [1, 1, 2, 5, 27, 32]
+    assert L.bitnet_block_count(0) == -1 and L.bitnet_block_count(24) == -1
+    buf = (ctypes.c_uint8 * 256)()
+    p16 = (ctypes.addressof(buf) + 15) // 16 * 16
+    assert L.bitnet_linear_blocked_forward(None, p16, p16, 1, 8208, p16, p16, 4, p16, _lib.F32, 4) == \
+        _lib.ERR_UNSUPPORTED
+    assert b"8192" in L.bitnet_last_error()
+    assert L.bitnet_pack_weights_blocked(None, p16, _lib.BF16, 4, 8208, 8208, p16, p16) == _lib.ERR_UNSUPPORTED
+
+
 def test_argument_errors_launch_nothing():
     """Every call here fails validation on the host, so no HIP call is made."""
     L = _lib.lib()
@@ -71,6 +83,15 @@ def test_argument_errors_launch_nothing():
     p16 = (p + 15) // 16 * 16
     cases = [
         (L.bitnet_act_quant, (None, p16, _lib.BF16, 1, 15, 16, p16, p16, p16), "K=15"),
+        (L.bitnet_pack_weights_blocked, (None, p16, _lib.BF16, 4, 24, 24, p16, p16), "K=24"),
+        (L.bitnet_pack_weights_blocked, (None, p16, _lib.BF16, 4, 16, 8, p16, p16), "ldw"),
+        (L.bitnet_pack_weights_blocked, (None, p16, _lib.BF16, 4, 16, 16, p16 + 4, p16), "aligned"),
+        (L.bitnet_pack_weights_blocked, (None, p16, _lib.BF16, 4, 16, 16, p16, None), "NULL"),
+        (L.bitnet_pack_weights_blocked, (None, p16, 5, 4, 16, 16, p16, p16), "dtype"),
+        (L.bitnet_linear_blocked_forward, (None, p16, p16, 1, 16, p16, p16, 4, p16, _lib.F32, 3), "ldy"),
+        (L.bitnet_linear_blocked_forward, (None, p16 + 8, p16, 1, 16, p16, p16, 4, p16, _lib.F32, 4), "aligned"),
+        (L.bitnet_linear_blocked_forward, (None, p16, p16, 0, 16, p16, p16, 4, p16, _lib.F32, 4), "M=0"),
+        (L.bitnet_linear_blocked_forward, (None, p16, None, 1, 16, p16, p16, 4, p16, _lib.F32, 4), "NULL"),
         (L.bitnet_act_quant, (None, p16, _lib.BF16, 0, 16, 16, p16, p16, p16), "M=0"),
         (L.bitnet_act_quant, (None, p16, _lib.BF16, 1, 16, 8, p16, p16, p16), "ldx"),
         (L.bitnet_act_quant, (None, None, _lib.BF16, 1, 16, 16, p16, p16, p16), "NULL"),
