@@ -403,6 +403,35 @@ def bench_configs(tw, wl, torch, steps, warmup):
         aq[f"M{M}_K{K}"] = dict(us=ms_a * 1e3, value=gbps, unit="GB/s", frac_of_hbm_peak=gbps / HBM_PEAK_GBPS)
         del x, q, a, r
     out["act_quant"] = aq
+    # per-256-block weight scales: the c5 GEMMs with block-scaled weights (bf16 out),
+    # and one 2560 x 2560 projection at M = 1
+    w5 = wl.WORKLOADS["c5"]
+    rows, tot_ops, tot_ms = [], 0, 0.0
+    for i, p in enumerate(w5.projections):
+        pb = tw.pack_blocked(wl.weight_for(w5, i, device="cuda"))
+        q, a, _ = tw.act_quant(wl.activation_for(w5, i, device="cuda"))
+        y = torch.empty((w5.M, p.N), dtype=torch.bfloat16, device="cuda")
+        gg = torch.cuda.CUDAGraph()
+        tw.linear_blocked(q, a, pb, out=y)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gg):
+            for _ in range(4):
+                tw.linear_blocked(q, a, pb, out=y)
+        ms_l = time_region(torch, gg.replay, steps, 2) / 4
+        ops = 2 * w5.M * p.N * p.K
+        rows.append(dict(shape=f"{p.name} {w5.M}x{p.N}x{p.K}", us=ms_l * 1e3, tops=ops / (ms_l * 1e-3) / 1e12))
+        tot_ops += ops
+        tot_ms += ms_l
+        del pb, q, a, y, gg
+    agg = tot_ops / (tot_ms * 1e-3) / 1e12
+    pb = tw.pack_blocked(wl.draw_weight((2560, 2560), seed=9100, device="cuda"))
+    q, a, _ = tw.act_quant(wl.draw_activation((1, 2560), seed=9101, device="cuda"))
+    y = torch.empty((1, 2560), dtype=torch.float32, device="cuda")
+    ms_1 = time_region(torch, lambda: tw.linear_blocked(q, a, pb, out=y), steps * 5, warmup)
+    out["block_scaled"] = dict(gemm_c5=dict(tops=agg, frac_of_peak=agg / INT8_PEAK_TOPS, shapes=rows),
+                               m1_2560x2560=dict(us=ms_1 * 1e3, value=2560 * 2560 / 4 / (ms_1 * 1e-3) / 1e9,
+                                                 unit="GB/s", note="warm, single call; the kernel is the GEMM"))
+    del pb, q, a, y
     torch.cuda.empty_cache()
     return out
 
