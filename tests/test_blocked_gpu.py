@@ -88,3 +88,23 @@ def test_blocked_rejects_non_finite():
     with pytest.raises(RuntimeError):
         tw.pack_blocked(W)
     assert b"finite" in _lib.lib().bitnet_last_error()
+
+
+@pytest.mark.parametrize("proj", [0, 1, 2])
+def test_blocked_full_size_sampled(orc, proj):
+    """The benchmarked shapes (BitNet-b1.58-2B prefill, M = 4096: gate|up,
+    down, q|k|v) with block-scaled weights, in the launch the bench times; 48
+    sampled tokens checked against the oracle (tokens are independent, so the
+    oracle runs on those tokens only)."""
+    w5 = wl.WORKLOADS["c5"]
+    p = w5.projections[proj]
+    W = wl.weight_for(w5, proj, device=DEV)
+    x = wl.activation_for(w5, proj, device=DEV)
+    pb = tw.pack_blocked(W)
+    q, a, _ = tw.act_quant(x)
+    y = tw.linear_blocked(q, a, pb, out_dtype=torch.bfloat16)
+    rows = np.random.default_rng(proj).choice(w5.M, size=48, replace=False)
+    ref = orc.linear_blocked(bits(x[rows]), bits(W), out="bf16")
+    assert np.array_equal(pb.packed.cpu().numpy(), ref["packed"])
+    assert np.array_equal(pb.block_scale.cpu().numpy().view(np.uint32), ref["block_scale"].view(np.uint32))
+    assert np.array_equal(bits(y)[rows], ref["y"])
