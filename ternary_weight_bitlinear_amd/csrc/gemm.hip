@@ -484,7 +484,9 @@ __device__ __forceinline__ void gemm_epilogue_blocked(const f32x16 (&facc)[TN][T
     }
 }
 
-// kBlocked: weights with one scale per 256-k block of a row.  The codes are
+// kBlocked: weights with one scale per 256-k block of a row ("BitVLA --
+// 1.58-bit Vision-Language-Action on Core AI", s2: the sibling matvec
+// kernel's per-256-block scales, against BitNet's one per tensor).  The codes are
 // expanded to signed t (one byte permute per 4 codes), every 256 k (two
 // stages, or the last stage) the exact int32 block sums are scaled by the
 // block's scale and added to fp32 accumulators in block order, and the
