@@ -24,12 +24,15 @@
  *                -1 -> 0, 0 -> 1, +1 -> 2.
  *   Tails        [BitVLA s2]: K must be a multiple of 16; N is arbitrary.
  *
- * Readings taken where the pages leave a step open (each one is also listed
- * with its reasons in the design notes of the repository):
+ * Readings taken where the pages leave a step open.  The numbers are the
+ * same as in the design notes of the repository, which give the reasons;
+ * R10 concerns the tests, not this file.
  *   R1  "round" is round-half-to-even, for weights and activations.
  *   R2  mean|W| is an fp64 sum of |W| over k ascending within a row, then
  *       over the tensor's rows ascending, one fp64 division by rows*K, then
- *       rounding to fp32.
+ *       rounding to fp32.  (For bf16 weights of the workloads' magnitudes
+ *       every partial sum is exact in fp64, so this is the correctly rounded
+ *       fp32 value of the exact mean.)
  *   R3  s = 1/mean is an fp32 division; the code uses the fp32 product W*s.
  *   R4  ActQuant uses one fp32 factor sa = 127/amax, then the fp32 product
  *       x*sa; a_scale = amax/127 (fp32 division).
@@ -40,45 +43,47 @@
  *       mean rounded to 0) the code is 0.
  *   R8  Epilogue: f = a_scale[m] * w_scale[n] in fp32, then y = (float)acc * f
  *       in fp32; a bf16 output is y rounded to nearest-even.
- *   R9  Storage layout ("layout v1", this library's own, not I2_S):
+ *   R9  The activation clamp is [-128, 127] as written; it never binds, since
+ *       the largest element maps to exactly +-127.
+ *   R11 K must be a multiple of 16; rows are padded to Kp (R12) with weight-0
+ *       codes; N is arbitrary, with no padding rows.
+ *   R12 Storage layout ("layout v1", this library's own, not I2_S):
  *       Kp = K rounded up to a multiple of 128; row n occupies Kp/4 bytes;
  *       element k of a row is in byte 4*(k/16) + (k%4), bits
  *       2*((k%16)/4) .. +1; positions k >= K hold code 1 (weight 0).
- *
  *
  * The step before the path [Guide s3.1 "Background"; s3.1 key parameters,
  * rms_norm_eps]: every projection normalises its input first,
  * y = ActQuant(RMSNorm(x, g)) with a per-projection weight g [K] and eps; for
  * the down projection the input is the gated product silu(gate) * up [Guide
  * s2, model table: SiLU activation].
- *   R10 RMSNorm(x, g)_k = x_k * g_k * r with r = 1/sqrt(mean_k(x_k^2) + eps)
+ *   R13 RMSNorm(x, g)_k = x_k * g_k * r with r = 1/sqrt(mean_k(x_k^2) + eps)
  *       (the plain reading; no rounding of the normalised vector to bf16).
  *       r > 0 is one factor for the whole token, and ActQuant's codes do not
  *       change when a token is scaled by a positive factor, so the codes are
  *       taken from z = x*g (fp32 products, R4 on z) and r enters a_scale
  *       only: a_scale = amax(z) * r / 127, evaluated in fp64 with the sum of
  *       squares in fp64 (k ascending) and rounded once to fp32.
- *   R11 silu(a) * u = a / (1 + e) * u in fp32, with e = exp(-a) by the
- *       fp32 steps of orc_exp_f32 below (Cody-Waite reduction by ln 2 and a
- *       degree-7 Taylor polynomial), so that both implementations reach the
- *       same bits; the fp32 result is the input of R10.
+ *   R14 silu(a) * u is the definition a / (1 + exp(-a)) * u evaluated in
+ *       fp64 (the C library's exp) and rounded once to fp32; that fp32 value
+ *       is the input of R13.
  *
  * The I2_S interchange format [Guide s3.3 "I2_S Ternary Packing"]: the
  * tensor's values, flattened row-major, form blocks of 128; a block is 32
  * bytes; byte = (c0 << 6) | (c1 << 4) | (c2 << 2) | c3 with the stored codes
  * -1 -> 0, 0 -> 1, +1 -> 2; the fp32 scale 1/mean|W| follows the codes.
- *   R12 Which four values of a block share a byte is not stated.  Reading
+ *   R15 Which four values of a block share a byte is not stated.  Reading
  *       "strided" (the default): byte j of a block holds values j, j+32,
  *       j+64, j+96 as c0..c3 -- a block size only matters to a layout of
  *       this kind.  Reading "consecutive": byte j holds values 4j..4j+3.
  *       Both are provided.
- *   R13 The appended float is the quantisation scale s = 1/mean|W| as the
+ *   R16 The appended float is the quantisation scale s = 1/mean|W| as the
  *       page names it; the dequantisation factor is 1/s.
  *
  * The W1.58A16 variant [BitVLA s5 "On-device gotchas": where the in-graph
  * 8-bit activation quantiser stalled the GPU, the path kept the activations
  * in 16-bit and quantised only the weights]:
- *   R14 y[m][n] = w_scale[n] * sum_k x[m][k] * t[n][k] with the activations
+ *   R17 y[m][n] = w_scale[n] * sum_k x[m][k] * t[n][k] with the activations
  *       as given; the oracle evaluates it in fp64 (each product exact, one
  *       rounding per addition, k ascending) -- the reference value that a
  *       kernel summing in fp32, in its own order, is held to within a bound.
@@ -86,7 +91,7 @@
  * Per-block weight scales [BitVLA s2: the sibling matvec kernel it grew from
  * keeps one scale per 256-weight block where BitNet keeps one per tensor,
  * i.e. a scale matrix of N x K/256 instead of N x 1]:
- *   R15 Blocks run along k within a row: block b of row n holds
+ *   R18 Blocks run along k within a row: block b of row n holds
  *       k = 256b .. min(256b + 256, K) - 1, nb = ceil(K / 256) blocks per
  *       row, the last one partial when 256 does not divide K.  Its scale is
  *       the absmean of its own weights, R2 restricted to the block: fp64 sum
@@ -94,7 +99,7 @@
  *       weights in the block, rounding to fp32.  Codes follow R1, R3, R7 with
  *       the block's s = 1/mean.  Scales are stored block-major,
  *       block_scale[b][n].
- *   R16 y[m][n] = a_scale[m] * sum_b acc_b[m][n] * block_scale[b][n] with the
+ *   R19 y[m][n] = a_scale[m] * sum_b acc_b[m][n] * block_scale[b][n] with the
  *       exact int32 block sums acc_b = sum_{k in block b} q*t, evaluated in
  *       fp32 in this order: total = 0; for b ascending,
  *       total = total + (float)acc_b * block_scale[b][n]; y = total * a_scale.
@@ -245,7 +250,7 @@ int orc_weight_quant(const void* W, int dtype, int64_t N, int64_t K, int64_t ldw
 
 /* ------------------------------------------------------------- layout v1 */
 
-/* Byte index and bit offset of element k inside a row (R9). */
+/* Byte index and bit offset of element k inside a row (R12). */
 static int64_t v1_byte(int64_t k) { return 4 * (k / 16) + (k % 4); }
 static int v1_shift(int64_t k) { return (int)(2 * ((k % 16) / 4)); }
 
@@ -286,13 +291,13 @@ int64_t orc_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* t)
 
 /* ----------------------------------------------------------------- I2_S */
 
-/* Byte index inside a block and shift of value v (0..127) of the block (R12). */
+/* Byte index inside a block and shift of value v (0..127) of the block (R15). */
 static int64_t i2s_byte(int64_t v, int consecutive) { return consecutive ? v / 4 : v % 32; }
 static int i2s_shift(int64_t v, int consecutive) { return consecutive ? 6 - 2 * (int)(v % 4) : 6 - 2 * (int)(v / 32); }
 
 /*
  * Codes t [N, K] (-1, 0, +1) and the scale s = 1/mean|W| as an I2_S buffer:
- * N*K/4 code bytes, then s as 4 little-endian bytes (R12, R13).  N*K must be
+ * N*K/4 code bytes, then s as 4 little-endian bytes (R15, R16).  N*K must be
  * a multiple of 128.  Returns -1 otherwise.
  */
 int orc_i2s_pack(const int8_t* t, int64_t N, int64_t K, float s, int consecutive, uint8_t* out)
@@ -332,7 +337,7 @@ int64_t orc_i2s_unpack(const uint8_t* in, int64_t N, int64_t K, int consecutive,
 /*
  * Per-token ActQuant of x [M, K] (row stride ldx, fp32 or bf16).
  * q [M][Kp]: int8 codes, columns K..Kp-1 set to 0.  a_scale [M] = amax/127.
- * q_rowsum [M] = sum of q over the row.  (R1, R4, R5.)
+ * q_rowsum [M] = sum of q over the row.  (R1, R4, R5, R9.)
  */
 int orc_act_quant(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
                   int8_t* q, float* a_scale, int32_t* q_rowsum)
@@ -375,7 +380,7 @@ int orc_act_quant(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
 /* ------------------------------------------------- RMSNorm -> ActQuant */
 
 /*
- * q, a_scale and q_rowsum of ActQuant(RMSNorm(x, g)) for M tokens of K (R10):
+ * q, a_scale and q_rowsum of ActQuant(RMSNorm(x, g)) for M tokens of K (R13):
  * codes of z = x*g exactly as orc_act_quant, a_scale = amax(z) * r / 127 with
  * r = 1/sqrt(sum_k x_k^2 / K + eps) in fp64.  x and g are bf16 or fp32; g has
  * K entries.  Returns -1 for a bad K.
@@ -422,48 +427,22 @@ int orc_rms_act_quant(const void* x, int x_dtype, const void* g, int g_dtype, in
     return 0;
 }
 
-/*
- * exp(t) in fp32 (R11): above 88 the result is +inf and below -88 it is 0;
- * otherwise n = rint(t * log2(e)), the reduced argument
- * r = (t - n * ln2_hi) - n * ln2_lo (ln2_hi has 15 significant bits, so
- * n * ln2_hi is exact for the |n| <= 127 used here), the Taylor polynomial of
- * exp to degree 7 at r (|r| <= ln2/2: truncation below 2^-27 relative) in
- * Horner form, and a scaling by 2^n.  Every step is one IEEE fp32 operation.
- */
-float orc_exp_f32(float t)
-{
-    if (t > 88.0f)
-        return INFINITY;
-    if (t < -88.0f)
-        return 0.0f;
-    float n = nearbyintf(t * 1.44269502f);
-    float r = (t - n * 0.693145752f) - n * 1.42860677e-06f;
-    float p = 1.0f / 5040.0f;
-    p = p * r + 1.0f / 720.0f;
-    p = p * r + 1.0f / 120.0f;
-    p = p * r + 1.0f / 24.0f;
-    p = p * r + 1.0f / 6.0f;
-    p = p * r + 0.5f;
-    p = p * r + 1.0f;
-    p = p * r + 1.0f;
-    return ldexpf(p, (int)n);
-}
-
-/* h = silu(gate) * up per element (R11), fp32 out [M][K] (row stride K). */
+/* h = silu(gate) * up per element (R14): the definition in fp64, one
+ * rounding to fp32; out [M][K] (row stride K). */
 void orc_swiglu(const void* gate, const void* up, int dtype, int64_t M, int64_t K, int64_t ld, float* h)
 {
     for (int64_t m = 0; m < M; ++m)
         for (int64_t k = 0; k < K; ++k) {
-            float a = load_elem(gate, dtype, m * ld + k);
-            float u = load_elem(up, dtype, m * ld + k);
-            h[m * K + k] = a / (1.0f + orc_exp_f32(-a)) * u;
+            double a = (double)load_elem(gate, dtype, m * ld + k);
+            double u = (double)load_elem(up, dtype, m * ld + k);
+            h[m * K + k] = (float)(a / (1.0 + exp(-a)) * u);
         }
 }
 
 /* ------------------------------------------------------------- W1.58A16 */
 
 /*
- * y [M][N] fp64 = w_scale[n] * sum_{k<K} x[m][k] * t[n][k] (R14); also the
+ * y [M][N] fp64 = w_scale[n] * sum_{k<K} x[m][k] * t[n][k] (R17); also the
  * magnitude sum_k |x[m][k] * t[n][k]| into mag [M][N] (for error bounds).
  * x is bf16 or fp32 with row stride ldx; t has row stride K.
  */
@@ -565,7 +544,7 @@ int orc_max_threads(void)
 
 /* ------------------------------------------------ per-block weight scales */
 
-/* Blocks of 256 weights per row (R15); -1 for a bad K. */
+/* Blocks of 256 weights per row (R18); -1 for a bad K. */
 int64_t orc_block_count(int64_t K)
 {
     if (K <= 0 || K % 16 != 0)
@@ -574,7 +553,7 @@ int64_t orc_block_count(int64_t K)
 }
 
 /*
- * WeightQuant with one scale per 256-weight block of a row (R15): codes
+ * WeightQuant with one scale per 256-weight block of a row (R18): codes
  * t [N][K] and block_scale [nb][N].  Returns 0, -1 for a bad K, -2 if a
  * weight is not finite.
  */
@@ -605,7 +584,7 @@ int orc_weight_quant_blocked(const void* W, int dtype, int64_t N, int64_t K, int
 }
 
 /*
- * Linear with block scales (R16): y [M][N] fp32 from q [M][Kp] (ActQuant
+ * Linear with block scales (R19): y [M][N] fp32 from q [M][Kp] (ActQuant
  * output), a_scale [M], codes t [N][K] and block_scale [nb][N].  acc_blocks
  * [M][nb][N] (or NULL) receives the exact block sums.  Returns -1 for a bad K.
  */

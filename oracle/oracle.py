@@ -75,7 +75,6 @@ class Oracle:
         lib.orc_act_quant.restype = ctypes.c_int
         lib.orc_rms_act_quant.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, i64, i64, f32, vp, vp, vp]
         lib.orc_rms_act_quant.restype = ctypes.c_int
-        lib.orc_exp_f32.argtypes, lib.orc_exp_f32.restype = [f32], f32
         lib.orc_swiglu.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp]
         lib.orc_swiglu.restype = None
         lib.orc_linear_a16.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, vp, vp, vp]
@@ -208,12 +207,9 @@ class Oracle:
                                    _ptr(q), _ptr(a_scale), _ptr(rowsum))
         return q, a_scale, rowsum
 
-    def exp_f32(self, t: float) -> np.float32:
-        """The fp32 exp the gated input uses (Cody-Waite reduction, degree-7 Taylor)."""
-        return np.float32(self.lib.orc_exp_f32(float(t)))
-
     def swiglu(self, gate: np.ndarray, up: np.ndarray) -> np.ndarray:
-        """silu(gate) * up, fp32 [M, K] (gate and up of one dtype and shape)."""
+        """silu(gate) * up, fp32 [M, K]: the definition in fp64, rounded once
+        (reading R14 of the C file); gate and up of one dtype and shape."""
         gate = np.ascontiguousarray(gate)
         up = np.ascontiguousarray(up)
         if gate.shape != up.shape or gate.dtype != up.dtype:
@@ -295,7 +291,7 @@ class Oracle:
 
     def weight_quant_blocked(self, W: np.ndarray):
         """Codes t [N, K] and block_scale [nb, N]: one absmean scale per 256
-        weights of a row (reading R15 of the C file)."""
+        weights of a row (reading R18 of the C file)."""
         W = np.ascontiguousarray(W)
         N, K = W.shape
         nb = self.block_count(K)
@@ -310,7 +306,7 @@ class Oracle:
 
     def linear_blocked_q(self, q: np.ndarray, a_scale: np.ndarray, t: np.ndarray, block_scale: np.ndarray):
         """fp32 y [M, N] and exact block sums [M, nb, N] from quantised
-        operands (reading R16 of the C file)."""
+        operands (reading R19 of the C file)."""
         q = np.ascontiguousarray(q, dtype=np.int8)
         a_scale = np.ascontiguousarray(a_scale, dtype=np.float32)
         t = np.ascontiguousarray(t, dtype=np.int8)

@@ -45,6 +45,63 @@ def _rows(t: torch.Tensor, name: str) -> int:
     return t.stride(0)
 
 
+def _vector(t, n: int, dtype, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.dim() != 1 or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape [{n}]")
+
+
+def _quantised(q, a_scale, q_rowsum, K: int) -> int:
+    """Check ActQuant outputs for a weight of K columns; returns M."""
+    Kp = padded_k(K)
+    if (not isinstance(q, torch.Tensor) or q.dtype != torch.int8 or q.dim() != 2 or q.shape[1] != Kp
+            or not q.is_contiguous()):
+        raise ValueError(f"q must be a contiguous int8 tensor of shape [M, {Kp}] (Kp of the weight's K={K})")
+    M = q.shape[0]
+    if M < 1:
+        raise ValueError("q must hold at least one token")
+    _vector(a_scale, M, torch.float32, "a_scale")
+    if q_rowsum is not None:
+        _vector(q_rowsum, M, torch.int32, "q_rowsum")
+    return M
+
+
+def _weight(w) -> None:
+    Kp = padded_k(w.K)
+    if Kp < 0 or w.N < 1:
+        raise ValueError(f"packed weight has a bad shape N={w.N}, K={w.K}")
+    if (w.packed.dtype != torch.uint8 or tuple(w.packed.shape) != (w.N, Kp // 4)
+            or not w.packed.is_contiguous()):
+        raise ValueError(f"packed must be a contiguous uint8 tensor of shape [{w.N}, {Kp // 4}]")
+    scale = getattr(w, "w_scale", None)
+    if scale is not None:
+        _vector(scale, w.N, torch.float32, "w_scale")
+    else:
+        nb = -(-w.K // 256)
+        if (w.block_scale.dtype != torch.float32 or tuple(w.block_scale.shape) != (nb, w.N)
+                or not w.block_scale.is_contiguous()):
+            raise ValueError(f"block_scale must be a contiguous float32 tensor of shape [{nb}, {w.N}]")
+
+
+def _output(y, M: int, N: int) -> int:
+    """Check an output tensor [M, N] (fp32 or bf16, unit column stride); returns its row stride."""
+    if not isinstance(y, torch.Tensor) or y.dim() != 2 or tuple(y.shape) != (M, N):
+        raise ValueError(f"out must be a tensor of shape [{M}, {N}]")
+    if y.dtype not in _DT:
+        raise TypeError(f"out must be float32 or bfloat16, not {y.dtype}")
+    return _rows(y, "out")
+
+
+def _on_device(device, **tensors) -> None:
+    """Every tensor must be a CUDA tensor on ``device``."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def padded_k(K: int) -> int:
     """Kp = K rounded up to a multiple of 128 (-1 if K is not a positive multiple of 16)."""
     return int(_lib.lib().bitnet_padded_k(K))
@@ -170,6 +227,7 @@ def act_quant(x: torch.Tensor):
     Kp = padded_k(K)
     if Kp < 0:
         raise ValueError(f"K={K} must be a positive multiple of 16")
+    _on_device(x.device, x=x)
     q = torch.empty((M, Kp), dtype=torch.int8, device=x.device)
     a_scale = torch.empty(M, dtype=torch.float32, device=x.device)
     rowsum = torch.empty(M, dtype=torch.int32, device=x.device)
@@ -191,6 +249,7 @@ def rmsnorm_act_quant(x: torch.Tensor, norm_w: torch.Tensor, eps: float = 1e-6, 
         raise ValueError("norm_w must be a contiguous [K] tensor")
     if up is not None and (up.shape != x.shape or up.dtype != x.dtype or _rows(up, "up") != ldx):
         raise ValueError("up must match x in shape, dtype and row stride")
+    _on_device(x.device, x=x, norm_w=norm_w, up=up)
     q = torch.empty((M, Kp), dtype=torch.int8, device=x.device)
     a_scale = torch.empty(M, dtype=torch.float32, device=x.device)
     rowsum = torch.empty(M, dtype=torch.int32, device=x.device)
@@ -205,11 +264,11 @@ def linear(q: torch.Tensor, a_scale: torch.Tensor, q_rowsum: torch.Tensor, w: Pa
            out_dtype=torch.float32, out: torch.Tensor | None = None, acc_debug: bool = False):
     """y [M, N] = (acc) * (a_scale[m] * w_scale[n]) with acc the exact int32 sum of q*t.
     Returns y, or (y, acc) when acc_debug is set."""
-    M = q.shape[0]
-    if q.shape[1] != padded_k(w.K):
-        raise ValueError("q must be [M, Kp] for the packed weight's K")
+    M = _quantised(q, a_scale, q_rowsum, w.K)
+    _weight(w)
     y = out if out is not None else torch.empty((M, w.N), dtype=out_dtype, device=q.device)
-    ldy = _rows(y, "y")
+    ldy = _output(y, M, w.N)
+    _on_device(q.device, q=q, a_scale=a_scale, q_rowsum=q_rowsum, packed=w.packed, w_scale=w.w_scale, out=y)
     acc = torch.empty((M, w.N), dtype=torch.int32, device=q.device) if acc_debug else None
     with torch.cuda.device(q.device):
         _lib.check(_lib.lib().bitnet_linear_forward(
@@ -245,11 +304,11 @@ def pack_blocked(W: torch.Tensor) -> BlockPackedWeight:
 def linear_blocked(q: torch.Tensor, a_scale: torch.Tensor, w: BlockPackedWeight, out_dtype=torch.float32,
                    out: torch.Tensor | None = None) -> torch.Tensor:
     """y [M, N] = a_scale[m] * sum_b acc_b * block_scale[b][n] (fp32, blocks in order)."""
-    M = q.shape[0]
-    if q.shape[1] != padded_k(w.K):
-        raise ValueError("q must be [M, Kp] for the packed weight's K")
+    M = _quantised(q, a_scale, None, w.K)
+    _weight(w)
     y = out if out is not None else torch.empty((M, w.N), dtype=out_dtype, device=q.device)
-    ldy = _rows(y, "y")
+    ldy = _output(y, M, w.N)
+    _on_device(q.device, q=q, a_scale=a_scale, packed=w.packed, block_scale=w.block_scale, out=y)
     with torch.cuda.device(q.device):
         _lib.check(_lib.lib().bitnet_linear_blocked_forward(
             _stream(q), q.data_ptr(), a_scale.data_ptr(), M, w.K, w.packed.data_ptr(), w.block_scale.data_ptr(),
@@ -265,13 +324,17 @@ def bitlinear(x: torch.Tensor, w: PackedWeight, out_dtype=torch.float32, out: to
     M, K = x.shape
     if K != w.K:
         raise ValueError("x and the packed weight disagree on K")
+    _weight(w)
     if workspace is None:
         workspace = (torch.empty((M, padded_k(K)), dtype=torch.int8, device=x.device),
                      torch.empty(M, dtype=torch.float32, device=x.device),
                      torch.empty(M, dtype=torch.int32, device=x.device))
     q, a_scale, rowsum = workspace
+    if _quantised(q, a_scale, rowsum, K) != M:
+        raise ValueError("workspace must hold M tokens")
     y = out if out is not None else torch.empty((M, w.N), dtype=out_dtype, device=x.device)
-    ldy = _rows(y, "y")
+    ldy = _output(y, M, w.N)
+    _on_device(x.device, x=x, q=q, a_scale=a_scale, q_rowsum=rowsum, packed=w.packed, w_scale=w.w_scale, out=y)
     with torch.cuda.device(x.device):
         _lib.check(_lib.lib().bitnet_bitlinear_forward(
             _stream(x), x.data_ptr(), _dtype(x), M, K, ldx, w.packed.data_ptr(), w.w_scale.data_ptr(),
@@ -285,10 +348,13 @@ def linear_a16(x: torch.Tensor, w: PackedWeight, out_dtype=torch.float32, out: t
     M, K = x.shape
     if K != w.K:
         raise ValueError("x and the packed weight disagree on K")
+    _weight(w)
     y = out if out is not None else torch.empty((M, w.N), dtype=out_dtype, device=x.device)
+    ldy = _output(y, M, w.N)
+    _on_device(x.device, x=x, packed=w.packed, w_scale=w.w_scale, out=y)
     with torch.cuda.device(x.device):
         _lib.check(_lib.lib().bitnet_linear_a16(_stream(x), x.data_ptr(), _dtype(x), M, K, ldx, w.packed.data_ptr(),
-                                                w.w_scale.data_ptr(), w.N, y.data_ptr(), _dtype(y), _rows(y, "y")))
+                                                w.w_scale.data_ptr(), w.N, y.data_ptr(), _dtype(y), ldy))
     return y
 
 
@@ -304,13 +370,18 @@ def rmsnorm_bitlinear(x: torch.Tensor, norm_w: torch.Tensor, w: PackedWeight, ep
         raise ValueError("norm_w must be a contiguous [K] tensor")
     if up is not None and (up.shape != x.shape or up.dtype != x.dtype or _rows(up, "up") != ldx):
         raise ValueError("up must match x in shape, dtype and row stride")
+    _weight(w)
     if workspace is None:
         workspace = (torch.empty((M, padded_k(K)), dtype=torch.int8, device=x.device),
                      torch.empty(M, dtype=torch.float32, device=x.device),
                      torch.empty(M, dtype=torch.int32, device=x.device))
     q, a_scale, rowsum = workspace
+    if _quantised(q, a_scale, rowsum, K) != M:
+        raise ValueError("workspace must hold M tokens")
     y = out if out is not None else torch.empty((M, w.N), dtype=out_dtype, device=x.device)
-    ldy = _rows(y, "y")
+    ldy = _output(y, M, w.N)
+    _on_device(x.device, x=x, up=up, norm_w=norm_w, q=q, a_scale=a_scale, q_rowsum=rowsum, packed=w.packed,
+               w_scale=w.w_scale, out=y)
     with torch.cuda.device(x.device):
         _lib.check(_lib.lib().bitnet_rmsnorm_bitlinear_forward(
             _stream(x), x.data_ptr(), up.data_ptr() if up is not None else None, _dtype(x), M, K, ldx,
@@ -346,6 +417,11 @@ class GroupedBitLinear:
         for i, (x, w, y) in enumerate(items):
             if x.shape != (M, w.K) or y.shape != (M, w.N):
                 raise ValueError(f"item {i}: shapes do not match")
+            if x.dtype != x0.dtype or y.dtype != items[0][2].dtype:
+                raise ValueError(f"item {i}: every x must share one dtype, and every y another")
+            _weight(w)
+            _output(y, M, w.N)
+            _on_device(x0.device, x=x, packed=w.packed, w_scale=w.w_scale, out=y)
             arr[i] = _lib.GroupItem(x.data_ptr(), _rows(x, "x"), w.packed.data_ptr(), w.w_scale.data_ptr(),
                                     y.data_ptr(), _rows(y, "y"), w.N, w.K)
         nrm = None
@@ -360,6 +436,7 @@ class GroupedBitLinear:
                     raise ValueError(f"item {i}: norm_w must be a contiguous [K] tensor")
                 if up is not None and (up.shape != x.shape or up.dtype != x.dtype or _rows(up, "up") != _rows(x, "x")):
                     raise ValueError(f"item {i}: up must match x in shape, dtype and row stride")
+                _on_device(x0.device, norm_w=g, up=up)
                 nrm[i] = _lib.GroupNorm(up.data_ptr() if up is not None else None, g.data_ptr(), _dtype(g),
                                         float(eps))
                 self._keep.append((g, up))

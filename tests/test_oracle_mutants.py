@@ -93,14 +93,22 @@ MUTANTS = [
      "a_scale[m] = (float)((double)amax * r / 127.0);", "a_scale[m] = (float)((double)amax / 127.0);"),
     ("RMSNorm squares the weighted value",
      "squares += (double)xv * (double)xv;", "squares += (double)z * (double)z;"),
-    ("silu sign flipped", "h[m * K + k] = a / (1.0f + orc_exp_f32(-a)) * u;",
-     "h[m * K + k] = a / (1.0f + orc_exp_f32(a)) * u;"),
-    ("gated product drops up", "h[m * K + k] = a / (1.0f + orc_exp_f32(-a)) * u;",
-     "h[m * K + k] = a / (1.0f + orc_exp_f32(-a));"),
-    ("exp drops the low part of ln 2", "float r = (t - n * 0.693145752f) - n * 1.42860677e-06f;",
-     "float r = t - n * 0.693145752f;"),
-    ("exp polynomial one degree short", "    p = p * r + 1.0f / 24.0f;\n", "    p = 1.0f / 24.0f;\n"),
-    ("exp scaled by 2^(n+1)", "return ldexpf(p, (int)n);", "return ldexpf(p, (int)n + 1);"),
+    ("silu sign flipped", "(float)(a / (1.0 + exp(-a)) * u)", "(float)(a / (1.0 + exp(a)) * u)"),
+    ("gated product drops up", "(float)(a / (1.0 + exp(-a)) * u)", "(float)(a / (1.0 + exp(-a)))"),
+    ("silu divides by 1 - exp", "(float)(a / (1.0 + exp(-a)) * u)", "(float)(a / (2.0 - exp(-a)) * u)"),
+    ("silu evaluated in fp32", "h[m * K + k] = (float)(a / (1.0 + exp(-a)) * u);",
+     "h[m * K + k] = (float)a / (1.0f + expf(-(float)a)) * (float)u;"),
+    ("row sum of |W| in fp32",
+     "double s = 0.0;\n    for (int64_t k = 0; k < K; ++k)\n        s += fabs((double)load_elem(W, dtype, n * ldw + k));",
+     "float s = 0.0f;\n    for (int64_t k = 0; k < K; ++k)\n        s += fabsf(load_elem(W, dtype, n * ldw + k));"),
+    ("segment total in fp32", "double total = 0.0;\n    for (int64_t n = row0;", "float total = 0.0f;\n    for (int64_t n = row0;"),
+    ("block sum of |W| in fp32", "double sum = 0.0;\n            for (int64_t k = k0;",
+     "float sum = 0.0f;\n            for (int64_t k = k0;"),
+    ("block terms added in reverse order",
+     "for (int64_t b = 0; b < nb; ++b) {\n                int64_t k0",
+     "for (int64_t b = nb - 1; b >= 0; --b) {\n                int64_t k0"),
+    ("block terms accumulated in fp64", "float total = 0.0f;\n            for (int64_t b = 0;",
+     "double total = 0.0;\n            for (int64_t b = 0;"),
     ("A16 product transposed",
      "double p = (double)load_elem(x, dtype, m * ldx + k) * (double)t[n * K + k];",
      "double p = (double)load_elem(x, dtype, m * ldx + k) * (double)t[(k % N) * K + (n % K)];"),
@@ -131,7 +139,7 @@ def _run_mutant(args):
 def test_every_planted_mistake_is_caught(tmp_path):
     src = orc_mod.SOURCE.read_text()
     jobs = [(i, m, src, tmp_path) for i, m in enumerate(MUTANTS)]
-    with ThreadPoolExecutor(max_workers=4) as pool:
+    with ThreadPoolExecutor(max_workers=6) as pool:
         results = list(pool.map(_run_mutant, jobs))
     missed = [name for name, caught in results if not caught]
     assert not missed, f"pins missed: {missed}"

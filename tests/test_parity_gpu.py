@@ -146,6 +146,55 @@ def check_y_tol(y_dev: torch.Tensor, y_orc: np.ndarray, rel_tol: float = 1e-5):
     assert np.all((rel <= rel_tol) | (y == y_orc)), float(rel.max())
 
 
+# The kernels evaluate silu(gate) * up with their own fp32 steps (an exp built
+# from a Cody-Waite reduction and a degree-7 polynomial: within 4 fp32 ulps of
+# the true silu(a) * u); the oracle evaluates the definition in fp64 and rounds
+# once.  Policy for the gated input:
+#   * a code may differ by one only where the oracle's value before rounding,
+#     v = fp32(h * g) * fp32(127 / amax) (exact product), lies within GATE_WINDOW
+#     of a .5 tie.  GATE_WINDOW: h differs by <= 4.5 * 2^-23 relative, then z,
+#     amax, sa and v add one rounding each (<= 13 * 2^-23 relative in all), and
+#     |v| <= 127, so |dv| <= 127 * 13 * 2^-23 < 2e-4;
+#   * every other code is equal, and q_rowsum is the sum of the kernel's codes;
+#   * a_scale is within 1e-5 relative (it moves by ~1e-6 at most);
+#   * y is within 1e-5 relative plus one a_scale * w_scale step per code of the
+#     token inside the window (|t| <= 1, so each such code moves acc by <= 1).
+GATE_WINDOW = 2e-4
+
+
+def gated_reference(orc, gate_np, up_np, g_np, eps):
+    """Oracle q, a_scale, q_rowsum for RMSNorm(silu(gate) * up) and the window mask."""
+    h = orc.swiglu(gate_np, up_np)
+    qo, ao, ro = orc.rms_act_quant(h, g_np, eps)
+    gv = g_np if g_np.dtype == np.float32 else (g_np.astype(np.uint32) << 16).view(np.float32)
+    z = (h * gv[None, :]).astype(np.float32)
+    amax = np.abs(z).max(axis=1)
+    sa = np.where(amax > 0, np.float32(127) / np.where(amax > 0, amax, np.float32(1)), np.float32(0))
+    v = z.astype(np.float64) * sa.astype(np.float64)[:, None]
+    window = np.abs(np.abs(v - np.trunc(v)) - 0.5) <= GATE_WINDOW
+    win = np.zeros_like(qo, dtype=bool)
+    win[:, :h.shape[1]] = window
+    return qo, ao, ro, win
+
+
+def check_gated_codes(q_dev, a_dev, r_dev, qo, ao, ro, win):
+    q = q_dev.cpu().numpy()
+    d = q.astype(np.int32) - qo.astype(np.int32)
+    assert np.all(d[~win] == 0), int(np.count_nonzero(d[~win]))
+    assert np.all(np.abs(d[win]) <= 1)
+    assert np.array_equal(r_dev.cpu().numpy(), q.astype(np.int64).sum(axis=1).astype(np.int32))
+    _check_scale(a_dev, ao)
+
+
+def check_y_gated(y_dev, y_orc, a_o, ws_o, win):
+    """y against the oracle under the gated-input policy (see GATE_WINDOW)."""
+    y = y_dev.float().cpu().numpy().astype(np.float64)
+    steps = win.sum(axis=1).astype(np.float64)[:, None] * (a_o.astype(np.float64)[:, None] *
+                                                            ws_o.astype(np.float64)[None, :])
+    err = np.abs(y - y_orc.astype(np.float64))
+    assert np.all(err <= 1e-5 * np.abs(y_orc.astype(np.float64)) + steps * (1 + 1e-5)), float(err.max())
+
+
 @pytest.mark.parametrize("M,K,dist", [
     (1, 16, "normal"), (1, 2560, "normal_outliers"), (3, 1152, "normal"), (17, 4304, "student_t_channels"),
     (5, 6912, "normal"), (2, 20480, "normal"), (64, 1024, "normal_outliers"),
@@ -172,7 +221,8 @@ def test_rmsnorm_act_quant(orc, M, K, dist, x_dtype, g_dtype):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_gated_rmsnorm_act_quant(orc, M, K, dtype):
     """The down projection's input: silu(gate) * up, then RMSNorm and ActQuant;
-    gate and up are strided views of one [M, 2K] buffer (the fused gate|up output)."""
+    gate and up are strided views of one [M, 2K] buffer (the fused gate|up output).
+    Held to the oracle's fp64 silu under the gated-input policy (GATE_WINDOW)."""
     gu = (wl.draw_activation((M, 2 * K), seed=K + M, dist="normal").float() * 3).to(dtype)
     g = _norm_weight(K, K + 7, torch.bfloat16)
     gud = gu.to(DEV)
@@ -181,10 +231,8 @@ def test_gated_rmsnorm_act_quant(orc, M, K, dtype):
         go, uo = bits(gu[:, :K].contiguous()), bits(gu[:, K:].contiguous())
     else:
         go, uo = gu[:, :K].contiguous().numpy(), gu[:, K:].contiguous().numpy()
-    qo, ao, ro = orc.swiglu_rms_act_quant(go, uo, bits(g), 1e-6)
-    assert np.array_equal(q.cpu().numpy(), qo)
-    assert np.array_equal(r.cpu().numpy(), ro)
-    _check_scale(a, ao)
+    qo, ao, ro, win = gated_reference(orc, go, uo, bits(g), 1e-6)
+    check_gated_codes(q, a, r, qo, ao, ro, win)
 
 
 def test_rmsnorm_strided_unaligned_and_eps_zero(orc):
@@ -225,7 +273,7 @@ def test_rmsnorm_then_linear(orc):
 def test_rmsnorm_bitlinear(orc, M, N, K, gated):
     """Input norm fused into the decode kernels' token prologue (or a separate
     launch for larger M) against the oracle: codes and sums bit-exact, a_scale
-    and y within 1e-5 relative."""
+    and y within 1e-5 relative; gated inputs under the GATE_WINDOW policy."""
     x, W = wl.random_case(3100 + M * 7 + N, M, N, K, x_dist="normal_outliers")
     g = _norm_weight(K, K + 11, torch.bfloat16)
     pw = tw.pack(W.to(DEV))
@@ -234,15 +282,20 @@ def test_rmsnorm_bitlinear(orc, M, N, K, gated):
     ws = (torch.empty((M, tw.padded_k(K)), dtype=torch.int8, device=DEV),
           torch.empty(M, dtype=torch.float32, device=DEV), torch.empty(M, dtype=torch.int32, device=DEV))
     y = tw.rmsnorm_bitlinear(xd, g.to(DEV), pw, 1e-6, up=up, workspace=ws)
+    t, wsc, _, _ = orc.weight_quant(bits(W))
     if gated:
-        qo, ao, ro = orc.swiglu_rms_act_quant(bits(x), bits(up), bits(g), 1e-6)
+        qo, ao, ro, win = gated_reference(orc, bits(x), bits(up), bits(g), 1e-6)
+        check_gated_codes(ws[0], ws[1], ws[2], qo, ao, ro, win)
+        # y is the epilogue of the kernel's own codes, and within the policy of the oracle's
+        qk, ak = ws[0].cpu().numpy(), ws[1].cpu().numpy()
+        assert np.array_equal(f32bits(y.cpu().numpy()), f32bits(orc.epilogue(orc.int_dot(qk, t), ak, wsc)))
+        check_y_gated(y, orc.epilogue(orc.int_dot(qo, t), ao, wsc), ao, wsc, win)
     else:
         qo, ao, ro = orc.rms_act_quant(bits(x), bits(g), 1e-6)
-    assert np.array_equal(ws[0].cpu().numpy(), qo)
-    assert np.array_equal(ws[2].cpu().numpy(), ro)
-    _check_scale(ws[1], ao)
-    t, wsc, _, _ = orc.weight_quant(bits(W))
-    check_y_tol(y, orc.epilogue(orc.int_dot(qo, t), ao, wsc))
+        assert np.array_equal(ws[0].cpu().numpy(), qo)
+        assert np.array_equal(ws[2].cpu().numpy(), ro)
+        _check_scale(ws[1], ao)
+        check_y_tol(y, orc.epilogue(orc.int_dot(qo, t), ao, wsc))
 
 
 @pytest.mark.parametrize("kernel", ["stream", "persistent"])
@@ -271,10 +324,11 @@ def test_grouped_rmsnorm(orc, kernel, monkeypatch):
             norms.append((g.to(DEV), up, 1e-6))
             go = bits(g) if g.dtype == torch.bfloat16 else g.numpy()
             if kind == "gated":
-                qo, ao, _ = orc.swiglu_rms_act_quant(bits(x), bits(up), go, 1e-6)
-            else:
-                qo, ao, _ = orc.rms_act_quant(bits(x), go, 1e-6)
-        refs.append(orc.epilogue(orc.int_dot(qo, t), ao, wsc))
+                qo, ao, _, win = gated_reference(orc, bits(x), bits(up), go, 1e-6)
+                refs.append((orc.epilogue(orc.int_dot(qo, t), ao, wsc), ao, wsc, win))
+                continue
+            qo, ao, _ = orc.rms_act_quant(bits(x), go, 1e-6)
+        refs.append((orc.epilogue(orc.int_dot(qo, t), ao, wsc), None, None, None))
     group = tw.GroupedBitLinear(items, norms)
     assert group.kernel == kernel
     for rep in range(2):
@@ -282,8 +336,11 @@ def test_grouped_rmsnorm(orc, kernel, monkeypatch):
             y.fill_(float("nan"))
         group()
         torch.cuda.synchronize()
-        for (_, _, y), ref in zip(items, refs):
-            check_y_tol(y, ref)
+        for (_, _, y), (ref, ao, wsc, win) in zip(items, refs):
+            if win is None:
+                check_y_tol(y, ref)
+            else:
+                check_y_gated(y, ref, ao, wsc, win)
 
 
 # ------------------------------------------------------------------- I2_S
