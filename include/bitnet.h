@@ -123,6 +123,28 @@ bitnet_status_t bitnet_pack_weights(bitnet_mem_t where, hipStream_t stream,
                                     float* seg_mean, int64_t* zero_count);
 
 /*
+ * bitnet_pack_weights for device memory, for callers that cannot allocate
+ * device memory (code that must not call hipMalloc: serving loops, harnesses
+ * that forbid it).  Same arguments, results and errors as
+ * bitnet_pack_weights(BITNET_MEM_DEVICE, ...), but its temporaries (the fp64
+ * row sums and the per-segment fields) live in a fixed device array of the
+ * library, about 1 MiB, held on each GPU the library runs on until the
+ * process ends.  It allocates nothing and is synchronous on `stream` like the
+ * device pack.  Limits: N <= BITNET_PACK_STATIC_MAX_ROWS and at most
+ * BITNET_PACK_STATIC_MAX_SEGS segments; larger requests return
+ * BITNET_ERR_UNSUPPORTED before any launch.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (from several host threads or
+ * streams) race and must be serialised by the caller.
+ */
+#define BITNET_PACK_STATIC_MAX_ROWS 131072
+#define BITNET_PACK_STATIC_MAX_SEGS 64
+bitnet_status_t bitnet_pack_weights_static(hipStream_t stream, const void* W, bitnet_dtype_t w_dtype,
+                                           int64_t N, int64_t K, int64_t ldw,
+                                           const int64_t* seg_rows, int32_t n_segs,
+                                           uint8_t* packed, float* w_scale,
+                                           float* seg_mean, int64_t* zero_count);
+
+/*
  * ActQuant, per token [BitVLA s1; Guide s2].  Device memory throughout.
  *
  * x        [M, K] activations, row stride ldx >= K, dtype x_dtype (BF16 or

@@ -24,6 +24,8 @@ SIGNATURES = {
     "bitnet_packed_bytes": (_i64, [_i64, _i64]),
     "bitnet_pack_weights": (ctypes.c_int, [ctypes.c_int, _vp, _vp, ctypes.c_int, _i64, _i64, _i64,
                                            _vp, _i32, _vp, _vp, _vp, _vp]),
+    "bitnet_pack_weights_static": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
+                                                  _vp, _vp]),
     "bitnet_act_quant": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp, _vp, _vp]),
     "bitnet_rmsnorm_act_quant": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp,
                                                 ctypes.c_int, ctypes.c_float, _vp, _vp, _vp]),

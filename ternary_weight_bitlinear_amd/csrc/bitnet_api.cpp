@@ -32,6 +32,9 @@ constexpr int64_t kGemvMaxM = 16;
 constexpr int64_t kFusedLdsBytes = 32768;     // single call: M * Kp bytes of q in LDS
 constexpr int64_t kGroupLdsBytes = 65536;     // grouped launch: M * max Kp
 constexpr int64_t kPlanMagic = 0x62746E6770ll;   // "btngp"
+static_assert(bitnet::kPackStaticMaxRows == BITNET_PACK_STATIC_MAX_ROWS &&
+                  bitnet::kPackStaticMaxSegs == BITNET_PACK_STATIC_MAX_SEGS,
+              "limits of the allocation-free pack");
 
 thread_local std::string g_last_error;
 
@@ -148,38 +151,34 @@ struct DeviceTemps {
     }
 };
 
-bitnet_status_t device_pack(hipStream_t stream, const void* W, bitnet_dtype_t dt, int64_t N, int64_t K,
-                            int64_t ldw, const std::vector<int64_t>& seg_start, uint8_t* packed,
-                            float* w_scale, float* seg_mean, int64_t* zero_count) {
+// Device pack with its temporaries (pack_temp_layout(N, n_segs).bytes) at
+// `temps`: upload the segment table, launch, read back the status, the means
+// and the zero counts, and wait.
+bitnet_status_t device_pack_into(hipStream_t stream, void* temps, const void* W, bitnet_dtype_t dt, int64_t N,
+                                 int64_t K, int64_t ldw, const std::vector<int64_t>& seg_start, uint8_t* packed,
+                                 float* w_scale, float* seg_mean, int64_t* zero_count, const char* fn) {
     const int64_t Kp = padded_k(K);
     const int n_segs = static_cast<int>(seg_start.size()) - 1;
-    // one block of temporaries: row_sum | seg_start | seg_mean | seg_zero | status
-    const size_t off_start = static_cast<size_t>(N) * sizeof(double);
-    const size_t off_mean = off_start + (n_segs + 1) * sizeof(int64_t);
-    const size_t off_zero = (off_mean + n_segs * sizeof(float) + 7) / 8 * 8;
-    const size_t off_status = off_zero + n_segs * sizeof(unsigned long long);
-    const size_t bytes = off_status + sizeof(unsigned int);
-    DeviceTemps temps;
-    temps.stream = stream;
-    hipError_t e = hipMallocAsync(&temps.p, bytes, stream);
-    if (e != hipSuccess) {
-        temps.p = nullptr;
-        return hip_fail(e, "bitnet_pack_weights: temporary allocation");
-    }
-    char* base = static_cast<char*>(temps.p);
+    const bitnet::PackTemps lay = bitnet::pack_temp_layout(N, n_segs);
+    char* base = static_cast<char*>(temps);
     auto* d_row_sum = reinterpret_cast<double*>(base);
-    auto* d_start = reinterpret_cast<int64_t*>(base + off_start);
-    auto* d_mean = reinterpret_cast<float*>(base + off_mean);
-    auto* d_zero = reinterpret_cast<unsigned long long*>(base + off_zero);
-    auto* d_status = reinterpret_cast<unsigned int*>(base + off_status);
+    auto* d_start = reinterpret_cast<int64_t*>(base + lay.off_start);
+    auto* d_mean = reinterpret_cast<float*>(base + lay.off_mean);
+    auto* d_zero = reinterpret_cast<unsigned long long*>(base + lay.off_zero);
+    auto* d_status = reinterpret_cast<unsigned int*>(base + lay.off_status);
+    hipError_t e;
+    char what[96];
     if ((e = hipMemcpyAsync(d_start, seg_start.data(), (n_segs + 1) * sizeof(int64_t), hipMemcpyHostToDevice,
-                            stream)) != hipSuccess)
-        return hip_fail(e, "bitnet_pack_weights: segment table upload");
-    if ((e = hipMemsetAsync(d_status, 0, sizeof(unsigned int), stream)) != hipSuccess)
-        return hip_fail(e, "bitnet_pack_weights: status clear");
+                            stream)) != hipSuccess) {
+        snprintf(what, sizeof what, "%s: segment table upload", fn);
+        return hip_fail(e, what);
+    }
     e = bitnet::launch_pack(W, dt == BITNET_BF16, N, K, ldw, Kp, d_start, n_segs, d_row_sum, d_mean, d_zero,
                             d_status, packed, w_scale, stream);
-    if (e != hipSuccess) return hip_fail(e, "bitnet_pack_weights: launch");
+    if (e != hipSuccess) {
+        snprintf(what, sizeof what, "%s: launch", fn);
+        return hip_fail(e, what);
+    }
     unsigned int status = 0;
     std::vector<float> means(static_cast<size_t>(n_segs));
     std::vector<unsigned long long> zeros(static_cast<size_t>(n_segs));
@@ -187,15 +186,35 @@ bitnet_status_t device_pack(hipStream_t stream, const void* W, bitnet_dtype_t dt
         (e = hipMemcpyAsync(means.data(), d_mean, n_segs * sizeof(float), hipMemcpyDeviceToHost, stream)) !=
             hipSuccess ||
         (e = hipMemcpyAsync(zeros.data(), d_zero, n_segs * sizeof(unsigned long long), hipMemcpyDeviceToHost,
-                            stream)) != hipSuccess)
-        return hip_fail(e, "bitnet_pack_weights: read-back");
-    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "bitnet_pack_weights: sync");
-    if (status & 1u) return fail(BITNET_ERR_NONFINITE, "bitnet_pack_weights: a weight is not finite");
+                            stream)) != hipSuccess) {
+        snprintf(what, sizeof what, "%s: read-back", fn);
+        return hip_fail(e, what);
+    }
+    if ((e = hipStreamSynchronize(stream)) != hipSuccess) {
+        snprintf(what, sizeof what, "%s: sync", fn);
+        return hip_fail(e, what);
+    }
+    if (status & 1u) return fail(BITNET_ERR_NONFINITE, "%s: a weight is not finite", fn);
     for (int s = 0; s < n_segs; ++s) {
         if (seg_mean) seg_mean[s] = means[static_cast<size_t>(s)];
         if (zero_count) zero_count[s] = static_cast<int64_t>(zeros[static_cast<size_t>(s)]);
     }
     return ok();
+}
+
+bitnet_status_t device_pack(hipStream_t stream, const void* W, bitnet_dtype_t dt, int64_t N, int64_t K,
+                            int64_t ldw, const std::vector<int64_t>& seg_start, uint8_t* packed,
+                            float* w_scale, float* seg_mean, int64_t* zero_count) {
+    const int n_segs = static_cast<int>(seg_start.size()) - 1;
+    DeviceTemps temps;
+    temps.stream = stream;
+    hipError_t e = hipMallocAsync(&temps.p, bitnet::pack_temp_layout(N, n_segs).bytes, stream);
+    if (e != hipSuccess) {
+        temps.p = nullptr;
+        return hip_fail(e, "bitnet_pack_weights: temporary allocation");
+    }
+    return device_pack_into(stream, temps.p, W, dt, N, K, ldw, seg_start, packed, w_scale, seg_mean, zero_count,
+                            "bitnet_pack_weights");
 }
 
 bitnet_status_t check_linear(const int8_t* q, const float* a_scale, const int32_t* q_rowsum, int64_t M,
@@ -256,14 +275,11 @@ int64_t bitnet_packed_bytes(int64_t N, int64_t K) {
     return N * (Kp / 4);
 }
 
-bitnet_status_t bitnet_pack_weights(bitnet_mem_t where, hipStream_t stream, const void* W, bitnet_dtype_t w_dtype,
-                                    int64_t N, int64_t K, int64_t ldw, const int64_t* seg_rows, int32_t n_segs,
-                                    uint8_t* packed, float* w_scale, float* seg_mean, int64_t* zero_count) {
-    const char* fn = "bitnet_pack_weights";
+static bitnet_status_t check_pack(const char* fn, const void* W, bitnet_dtype_t w_dtype, int64_t N, int64_t K,
+                                  int64_t ldw, const int64_t* seg_rows, int32_t n_segs, const uint8_t* packed,
+                                  const float* w_scale, std::vector<int64_t>& seg_start) {
     bitnet_status_t s = check_dims(fn, 1, N, K);
     if (s != BITNET_OK) return s;
-    if (where != BITNET_MEM_HOST && where != BITNET_MEM_DEVICE)
-        return fail(BITNET_ERR_INVALID_ARG, "%s: bad memory kind %d", fn, (int)where);
     if (!W || !packed || !w_scale) return fail(BITNET_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
     if (!valid_dtype(w_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad W dtype %d", fn, (int)w_dtype);
     if (ldw < K) return fail(BITNET_ERR_INVALID_ARG, "%s: ldw=%lld < K=%lld", fn, (long long)ldw, (long long)K);
@@ -271,7 +287,7 @@ bitnet_status_t bitnet_pack_weights(bitnet_mem_t where, hipStream_t stream, cons
         return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned pointer (packed must be 16-byte aligned)", fn);
     if (n_segs < 0 || (n_segs > 0 && !seg_rows))
         return fail(BITNET_ERR_INVALID_ARG, "%s: bad segment table", fn);
-    std::vector<int64_t> seg_start{0};
+    seg_start.assign(1, 0);
     if (n_segs == 0 || !seg_rows) {
         seg_start.push_back(N);
     } else {
@@ -284,8 +300,43 @@ bitnet_status_t bitnet_pack_weights(bitnet_mem_t where, hipStream_t stream, cons
         if (seg_start.back() != N || static_cast<int32_t>(seg_start.size()) != n_segs + 1)
             return fail(BITNET_ERR_INVALID_ARG, "%s: segment rows do not add up to N=%lld", fn, (long long)N);
     }
+    return BITNET_OK;
+}
+
+bitnet_status_t bitnet_pack_weights(bitnet_mem_t where, hipStream_t stream, const void* W, bitnet_dtype_t w_dtype,
+                                    int64_t N, int64_t K, int64_t ldw, const int64_t* seg_rows, int32_t n_segs,
+                                    uint8_t* packed, float* w_scale, float* seg_mean, int64_t* zero_count) {
+    const char* fn = "bitnet_pack_weights";
+    if (where != BITNET_MEM_HOST && where != BITNET_MEM_DEVICE)
+        return fail(BITNET_ERR_INVALID_ARG, "%s: bad memory kind %d", fn, (int)where);
+    std::vector<int64_t> seg_start;
+    bitnet_status_t s = check_pack(fn, W, w_dtype, N, K, ldw, seg_rows, n_segs, packed, w_scale, seg_start);
+    if (s != BITNET_OK) return s;
     if (where == BITNET_MEM_HOST) return host_pack(W, w_dtype, N, K, ldw, seg_start, packed, w_scale, seg_mean, zero_count);
     return device_pack(stream, W, w_dtype, N, K, ldw, seg_start, packed, w_scale, seg_mean, zero_count);
+}
+
+bitnet_status_t bitnet_pack_weights_static(hipStream_t stream, const void* W, bitnet_dtype_t w_dtype, int64_t N,
+                                           int64_t K, int64_t ldw, const int64_t* seg_rows, int32_t n_segs,
+                                           uint8_t* packed, float* w_scale, float* seg_mean, int64_t* zero_count) {
+    const char* fn = "bitnet_pack_weights_static";
+    std::vector<int64_t> seg_start;
+    bitnet_status_t s = check_pack(fn, W, w_dtype, N, K, ldw, seg_rows, n_segs, packed, w_scale, seg_start);
+    if (s != BITNET_OK) return s;
+    const int64_t segs = static_cast<int64_t>(seg_start.size()) - 1;
+    if (N > BITNET_PACK_STATIC_MAX_ROWS || segs > BITNET_PACK_STATIC_MAX_SEGS)
+        return fail(BITNET_ERR_UNSUPPORTED,
+                    "%s: N=%lld rows and %lld segments exceed the fixed temporaries (at most %d rows, %d segments); "
+                    "use bitnet_pack_weights",
+                    fn, (long long)N, (long long)segs, BITNET_PACK_STATIC_MAX_ROWS, BITNET_PACK_STATIC_MAX_SEGS);
+    void* temps = nullptr;
+    size_t bytes = 0;
+    hipError_t e = bitnet::pack_scratch(&temps, &bytes);
+    if (e != hipSuccess) return hip_fail(e, "bitnet_pack_weights_static: scratch address");
+    if (bitnet::pack_temp_layout(N, segs).bytes > bytes)
+        return fail(BITNET_ERR_UNSUPPORTED, "%s: temporaries exceed the fixed array", fn);
+    return device_pack_into(stream, temps, W, w_dtype, N, K, ldw, seg_start, packed, w_scale, seg_mean, zero_count,
+                            fn);
 }
 
 bitnet_status_t bitnet_act_quant(hipStream_t stream, const void* x, bitnet_dtype_t x_dtype, int64_t M, int64_t K,

@@ -31,9 +31,35 @@ hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_r
                        int64_t N, void* y, bool y_bf16, int64_t ldy, int32_t* acc_debug,
                        hipStream_t stream);
 
+// Temporaries of one device pack, carved from one buffer: row_sum [N] f64,
+// seg_start [n_segs + 1] i64, seg_mean [n_segs] f32 (padded to 8 bytes),
+// seg_zero [n_segs] u64, status u32.
+struct PackTemps {
+    size_t off_start, off_mean, off_zero, off_status, bytes;
+};
+constexpr PackTemps pack_temp_layout(int64_t N, int64_t n_segs) {
+    PackTemps t{};
+    t.off_start = static_cast<size_t>(N) * sizeof(double);
+    t.off_mean = t.off_start + static_cast<size_t>(n_segs + 1) * sizeof(int64_t);
+    t.off_zero = (t.off_mean + static_cast<size_t>(n_segs) * sizeof(float) + 7) / 8 * 8;
+    t.off_status = t.off_zero + static_cast<size_t>(n_segs) * sizeof(unsigned long long);
+    t.bytes = t.off_status + sizeof(unsigned int);
+    return t;
+}
+
+// Limits of the allocation-free device pack, whose temporaries live in a
+// fixed device array of the library (one per GPU, held until the process ends).
+constexpr int64_t kPackStaticMaxRows = 131072;
+constexpr int64_t kPackStaticMaxSegs = 64;
+
+// Device address of that array on the current device (looked up once per
+// device with hipGetSymbolAddress); its size in bytes in *bytes.
+hipError_t pack_scratch(void** ptr, size_t* bytes);
+
 // Device WeightQuant + pack.  seg_start_dev [n_segs + 1] holds the first row of
 // every segment and N at the end.  Temporaries: row_sum [N] doubles,
-// seg_mean_dev / seg_zero_dev [n_segs], status_dev (bit 0: non-finite weight).
+// seg_mean_dev / seg_zero_dev [n_segs], status_dev (bit 0: non-finite weight;
+// cleared by the launch itself, seg_zero_dev too).
 hipError_t launch_pack(const void* W, bool w_bf16, int64_t N, int64_t K, int64_t ldw,
                        int64_t Kp, const int64_t* seg_start_dev, int32_t n_segs,
                        double* row_sum, float* seg_mean_dev, unsigned long long* seg_zero_dev,

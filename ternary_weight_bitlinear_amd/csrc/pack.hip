@@ -26,11 +26,28 @@
 // k), adds |W| over the block's k in fp64 in k order, divides once by the
 // block's weight count, rounds to fp32, and writes the block's code words
 // (padding positions k >= K hold code 1) and its scale, block-major.
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace bitnet {
+
+// The allocation-free pack keeps its temporaries here: row sums of up to
+// kPackStaticMaxRows rows and the fields of up to kPackStaticMaxSegs segments
+// (about 1 MiB per GPU).  In host code this name is a stand-in for the symbol,
+// not a device address: host code uses the address from pack_scratch() only.
+constexpr size_t kPackScratchBytes =
+    (pack_temp_layout(kPackStaticMaxRows, kPackStaticMaxSegs).bytes + 255) / 256 * 256;
+static __device__ __align__(256) unsigned char scratch[kPackScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ void clear_status_kernel(unsigned int* status) { *status = 0u; }
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p);
@@ -180,8 +197,11 @@ hipError_t launch_t(const T* W, int64_t N, int64_t K, int64_t ldw, int64_t Kp,
                     const int64_t* seg_start, int n_segs, double* row_sum, float* seg_mean,
                     unsigned long long* seg_zero, unsigned int* status, uint8_t* packed,
                     float* w_scale, hipStream_t stream) {
-    row_sum_kernel<T><<<static_cast<unsigned>((N + kRowTile - 1) / kRowTile), 256, 0, stream>>>(W, N, K, ldw, row_sum);
+    clear_status_kernel<<<1, 1, 0, stream>>>(status);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    row_sum_kernel<T><<<static_cast<unsigned>((N + kRowTile - 1) / kRowTile), 256, 0, stream>>>(W, N, K, ldw, row_sum);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     finalize_kernel<<<static_cast<unsigned>((n_segs + 63) / 64), 64, 0, stream>>>(row_sum, seg_start, n_segs, K,
                                                                                 seg_mean, seg_zero, status);
@@ -194,6 +214,23 @@ hipError_t launch_t(const T* W, int64_t N, int64_t K, int64_t ldw, int64_t Kp,
 }
 
 }  // namespace
+
+hipError_t pack_scratch(void** ptr, size_t* bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {                 // once per device, with that device current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    *bytes = kPackScratchBytes;
+    return hipSuccess;
+}
 
 hipError_t launch_pack(const void* W, bool w_bf16, int64_t N, int64_t K, int64_t ldw,
                        int64_t Kp, const int64_t* seg_start_dev, int32_t n_segs,

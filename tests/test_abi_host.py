@@ -123,11 +123,32 @@ def test_argument_errors_launch_nothing():
         (L.bitnet_pack_weights, (9, None, p16, _lib.BF16, 4, 16, 16, None, 0, p16, p16, None, None), "memory"),
         (L.bitnet_pack_weights, (_lib.MEM_DEVICE, None, p16, _lib.BF16, 4, 24, 24, None, 0, p16, p16, None,
                                  None), "K=24"),
+        (L.bitnet_pack_weights_static, (None, p16, _lib.BF16, 4, 24, 24, None, 0, p16, p16, None, None), "K=24"),
+        (L.bitnet_pack_weights_static, (None, p16, _lib.BF16, 4, 16, 8, None, 0, p16, p16, None, None), "ldw"),
+        (L.bitnet_pack_weights_static, (None, p16, _lib.BF16, 4, 16, 16, None, 0, p16 + 4, p16, None, None),
+         "aligned"),
+        (L.bitnet_pack_weights_static, (None, p16, _lib.BF16, 4, 16, 16, (ctypes.c_int64 * 2)(2, 1), 2, p16, p16,
+                                        None, None), "segment"),
     ]
     for fn, args, needle in cases:
         st, msg = _status_and_error(fn, *args)
         assert st == _lib.ERR_INVALID_ARG, (fn.__name__, needle, st, msg)
         assert needle in msg, (needle, msg)
+
+
+def test_static_pack_limits():
+    """The allocation-free pack refuses, before any launch, what its fixed
+    temporaries cannot hold."""
+    L = _lib.lib()
+    buf = (ctypes.c_uint8 * 4096)()
+    p16 = (ctypes.addressof(buf) + 15) // 16 * 16
+    big = _lib.lib().bitnet_pack_weights_static
+    st, msg = _status_and_error(big, None, p16, _lib.BF16, 131073, 16, 16, None, 0, p16, p16, None, None)
+    assert st == _lib.ERR_UNSUPPORTED and "131072" in msg, msg
+    segs = (ctypes.c_int64 * 65)(*([1] * 65))
+    st, msg = _status_and_error(L.bitnet_pack_weights_static, None, p16, _lib.BF16, 65, 16, 16, segs, 65, p16, p16,
+                                None, None)
+    assert st == _lib.ERR_UNSUPPORTED and "segments" in msg, msg
 
 
 def _bits(t: torch.Tensor) -> np.ndarray:
