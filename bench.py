@@ -93,13 +93,64 @@ def time_region(torch, fn, steps: int, warmup: int):
     return start.elapsed_time(end) / steps      # ms per step
 
 
+def time_each(torch, fn, n: int, warmup: int = 2):
+    """Device time of each of n calls of fn (HIP events around every call on the
+    current stream): a list of ms, for per-dispatch median and min."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def dispatch_stats(times_ms):
+    xs = sorted(times_ms)
+    return dict(n=len(xs), median_us=xs[len(xs) // 2] * 1e3, min_us=xs[0] * 1e3, max_us=xs[-1] * 1e3)
+
+
+def cpu_model() -> str:
+    try:
+        for ln in Path("/proc/cpuinfo").read_text().splitlines():
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def applicable_roofline(M: int, N: int, K: int, out_bytes: int, seconds: float) -> dict:
+    """The shape's bound: the larger of its MFMA time (2MNK at the int8 peak) and
+    its HBM time (M*Kp + N*K/4 + M*N*out_bytes at the HBM peak)."""
+    Kp = (K + 127) // 128 * 128
+    ops = 2 * M * N * K
+    nbytes = M * Kp + N * K // 4 + M * N * out_bytes
+    t_mfma = ops / (INT8_PEAK_TOPS * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
+    return dict(bound="mfma" if t_mfma >= t_hbm else "hbm", frac_of_mfma_peak=t_mfma / seconds,
+                frac_of_applicable=max(t_mfma, t_hbm) / seconds, algorithmic_bytes=nbytes)
+
+
+def zero_fraction(pws) -> float:
+    """Zero codes over all weights of the packed tensors (the packer's counts)."""
+    zeros = sum(int(pw.zero_count.sum()) for pw in pws)
+    total = sum(pw.N * pw.K for pw in pws)
+    return zeros / total
+
+
 def bench_decode(tw, wl, torch, steps, warmup, per_call: bool):
     items, nbytes = setup_decode(tw, wl, torch, 30)
     group = tw.GroupedBitLinear(items)
     ms = time_region(torch, group, steps, warmup)     # one launch per step
     gbps = nbytes / (ms * 1e-3) / 1e9
+    per = dispatch_stats(time_each(torch, group, max(steps, 20)))
     src = kernel_source_hash("gemv.hip", "gemv.h", "device_common.h", "codes_bf16.h")
-    out = dict(value=gbps, ms_per_step=ms, bytes=nbytes, launches_per_step=1,
+    out = dict(value=gbps, ms_per_step=ms, bytes=nbytes, launches_per_step=1, per_dispatch=per,
+               zero_code_fraction=zero_fraction([pw for _, pw, _ in items]),
                roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s",
                              frac=gbps / HBM_PEAK_GBPS,
                              traffic=traffic_from_profile("decode_gemv_bitnet2b_30_layers_m1", src)))
@@ -216,11 +267,20 @@ def bench_a16(tw, wl, torch, steps, warmup):
 
 def cpu_baseline_decode(wl, torch, budget_s: float, max_layers: int = 3):
     """The oracle's ActQuant + int dot + epilogue over the first layers' projections
-    (weights quantised once, untimed), cycled until budget_s of timed work."""
+    (weights quantised once, untimed), cycled until budget_s of timed work, on all
+    the host's threads and again on one."""
+    res = _cpu_decode(wl, torch, budget_s / 2, max_layers, None)
+    one = _cpu_decode(wl, torch, budget_s / 2, max_layers, 1)
+    res["one_thread"] = dict(value=one["value"], unit=one["unit"], cores=1, sample=one["sample"])
+    res["cpu_model"] = cpu_model()
+    return res
+
+
+def _cpu_decode(wl, torch, budget_s: float, max_layers: int, nthreads):
     from oracle.oracle import Oracle
     orc = Oracle()
     w = wl.WORKLOADS["c2"]
-    threads = orc.max_threads()
+    threads = nthreads or orc.max_threads()
     prepared = []
     for layer in range(max_layers):
         for i, p in enumerate(w.projections):
@@ -287,6 +347,12 @@ def bench_prefill(tw, wl, torch, steps, warmup, out_dtype):
             gemms()
     ms = time_region(torch, g_step.replay, steps, warmup)
     gemm_ms = time_region(torch, g_gemm.replay, max(steps // 2, 3), 2) / (reps * len(projs))
+    per_shape = {}
+    for p, pw, x, q, a, r, y in projs:
+        t_each = time_each(torch, lambda: tw.linear(q, a, r, pw, out=y), max(steps, 20))
+        st = dispatch_stats(t_each)
+        st["tops_at_median"] = 2 * w.M * p.N * p.K / (st["median_us"] * 1e-6) / 1e12
+        per_shape[f"{p.name} {w.M}x{p.N}x{p.K}"] = st
     ops_per_launch = ops / len(projs)
     achieved = ops_per_launch / (gemm_ms * 1e-3) / 1e12
     tops = ops / (ms * 1e-3) / 1e12
@@ -298,17 +364,21 @@ def bench_prefill(tw, wl, torch, steps, warmup, out_dtype):
                 roofline=dict(bound="mfma", achieved=achieved, peak=INT8_PEAK_TOPS, unit="TOPS",
                               frac=achieved / INT8_PEAK_TOPS,
                               traffic=traffic_from_profile("prefill_gemm_bitnet2b_m4096", src)),
-                gemm_ms_per_launch=gemm_ms, launches_per_step=2 * len(projs),
-                timing="HIP graph replays: whole steps, and GEMM launches alone")
+                gemm_ms_per_launch=gemm_ms, launches_per_step=2 * len(projs), per_dispatch=per_shape,
+                zero_code_fraction=zero_fraction([pw for _, pw, *_ in projs]),
+                timing="HIP graph replays: whole steps, and GEMM launches alone; per_dispatch: HIP events "
+                       "around single launches")
 
 
 def bench_configs(tw, wl, torch, steps, warmup):
     """The other configurations, each timed on its own: the c1 2560 x 2560
     decode cold (a ring of 320 distinct packed copies, 524 MB, more than twice
     the MALL, as single calls replayed from a HIP graph and as one grouped
-    launch), the c2 stream at M = 2, 4, 8 (grouped), the c3 (SigLIP, M = 2048)
-    and c4 (embedder, M = 8192) prefill GEMMs per shape with bf16 output and
-    the c5 GEMMs with fp32 output, and ActQuant alone at the c5 inputs."""
+    launch) and warm as one call repeated on cached weights, the c2 stream at
+    M = 2, 4, 8 (grouped), the c3 (SigLIP, M = 2048), c4 (embedder, M = 8192)
+    and c5 prefill GEMMs per shape with bf16 and fp32 output (each against the
+    MFMA peak and its applicable roofline), with each workload's zero-code
+    fraction, and ActQuant alone at the c5 inputs."""
     steps = max(3, min(steps, 10))
     out = {}
     # c1 ring
@@ -337,6 +407,11 @@ def bench_configs(tw, wl, torch, steps, warmup):
     group = tw.GroupedBitLinear(ring)
     msg = time_region(torch, group, steps, warmup)
     out["c1_ring_grouped"] = dict(value=nb / (msg * 1e-3) / 1e9, unit="GB/s", ms_per_launch=msg, kernel=group.kernel)
+    x0, pw0, y0 = ring[0]
+    warm = dispatch_stats(time_each(torch, lambda: tw.bitlinear(x0, pw0, out=y0, workspace=ws), 200, warmup=20))
+    out["c1_warm_single_call"] = dict(warm, note="one 2560 x 2560 BitLinear called repeatedly on the same "
+                                            "weights (in cache): per-call device time, HIP events",
+                                      zero_code_fraction=zero_fraction([pw0]))
     del g, group, ring
     torch.cuda.empty_cache()
     # c2 at M = 2, 4, 8
@@ -354,35 +429,45 @@ def bench_configs(tw, wl, torch, steps, warmup):
     torch.cuda.empty_cache()
     # prefill GEMMs per shape
 
-    def gemm_shapes(name, out_dtype):
+    def gemm_shapes(name, out_dtypes):
+        """Every projection of a prefill workload with each output dtype: int8 TOPS,
+        % of the MFMA peak and % of the shape's applicable min(MFMA, HBM) roofline."""
         w = wl.WORKLOADS[name]
-        rows, tot_ops, tot_ms = [], 0, 0.0
+        res = dict(workload=w.name)
+        pws = []
         for i, p in enumerate(w.projections):
-            pw = tw.pack(wl.weight_for(w, i, device="cuda"), p.segments or None)
-            x = wl.activation_for(w, i, device="cuda")
-            q, a, r = tw.act_quant(x)
-            y = torch.empty((w.M, p.N), dtype=out_dtype, device="cuda")
-            gg = torch.cuda.CUDAGraph()
-            tw.linear(q, a, r, pw, out=y)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(gg):
-                for _ in range(4):
-                    tw.linear(q, a, r, pw, out=y)
-            ms_l = time_region(torch, gg.replay, steps, 2) / 4
-            ops = 2 * w.M * p.N * p.K
-            tops = ops / (ms_l * 1e-3) / 1e12
-            rows.append(dict(shape=f"{p.name} {w.M}x{p.N}x{p.K}", us=ms_l * 1e3, tops=tops,
-                             frac_of_peak=tops / INT8_PEAK_TOPS))
-            tot_ops += ops
-            tot_ms += ms_l
-            del pw, x, q, a, r, y, gg
+            pws.append(tw.pack(wl.weight_for(w, i, device="cuda"), p.segments or None))
+        res["zero_code_fraction"] = zero_fraction(pws)
+        for out_dtype in out_dtypes:
+            rows, tot_ops, tot_ms, tot_bound = [], 0, 0.0, 0.0
+            for i, p in enumerate(w.projections):
+                pw = pws[i]
+                q, a, r = tw.act_quant(wl.activation_for(w, i, device="cuda"))
+                y = torch.empty((w.M, p.N), dtype=out_dtype, device="cuda")
+                gg = torch.cuda.CUDAGraph()
+                tw.linear(q, a, r, pw, out=y)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(gg):
+                    for _ in range(4):
+                        tw.linear(q, a, r, pw, out=y)
+                ms_l = time_region(torch, gg.replay, steps, 2) / 4
+                ops = 2 * w.M * p.N * p.K
+                tops = ops / (ms_l * 1e-3) / 1e12
+                roof = applicable_roofline(w.M, p.N, p.K, y.element_size(), ms_l * 1e-3)
+                rows.append(dict(shape=f"{p.name} {w.M}x{p.N}x{p.K}", us=ms_l * 1e3, tops=tops, **roof))
+                tot_ops += ops
+                tot_ms += ms_l
+                tot_bound += roof["frac_of_applicable"] * ms_l
+                del q, a, r, y, gg
+            agg = tot_ops / (tot_ms * 1e-3) / 1e12
+            res[str(out_dtype).replace("torch.", "")] = dict(
+                tops=agg, frac_of_mfma_peak=agg / INT8_PEAK_TOPS, frac_of_applicable=tot_bound / tot_ms, shapes=rows)
+        del pws
         torch.cuda.empty_cache()
-        agg = tot_ops / (tot_ms * 1e-3) / 1e12
-        return dict(workload=w.name, out_dtype=str(out_dtype).replace("torch.", ""), tops=agg,
-                    frac_of_peak=agg / INT8_PEAK_TOPS, shapes=rows)
-    out["gemm_c3"] = gemm_shapes("c3", torch.bfloat16)
-    out["gemm_c4"] = gemm_shapes("c4", torch.bfloat16)
-    out["gemm_c5_f32_out"] = gemm_shapes("c5", torch.float32)
+        return res
+    out["gemm_c3"] = gemm_shapes("c3", (torch.bfloat16, torch.float32))
+    out["gemm_c4"] = gemm_shapes("c4", (torch.bfloat16, torch.float32))
+    out["gemm_c5"] = gemm_shapes("c5", (torch.bfloat16, torch.float32))
     # ActQuant alone (HBM-bound: 2 B in + 1 B out per element, 8 B per token)
     aq = {}
     for K in (2560, 6912):
@@ -439,11 +524,20 @@ def bench_configs(tw, wl, torch, steps, warmup):
 def cpu_baseline_prefill(wl, torch, budget_s: float):
     """The oracle's ActQuant + int dot + epilogue on slices of 64 tokens of the
     prefill activations through all three projections, until budget_s of timed
-    work or all 4096 tokens (weights quantised once, untimed)."""
+    work or all 4096 tokens (weights quantised once, untimed), on all the host's
+    threads and again on one."""
+    res = _cpu_prefill(wl, torch, budget_s / 2, None)
+    one = _cpu_prefill(wl, torch, budget_s / 2, 1)
+    res["one_thread"] = dict(value=one["value"], unit=one["unit"], cores=1, sample=one["sample"])
+    res["cpu_model"] = cpu_model()
+    return res
+
+
+def _cpu_prefill(wl, torch, budget_s: float, nthreads):
     from oracle.oracle import Oracle
     orc = Oracle()
     w = wl.WORKLOADS["c5"]
-    threads = orc.max_threads()
+    threads = nthreads or orc.max_threads()
     prepared = []
     for i, p in enumerate(w.projections):
         W = wl.weight_for(w, i, device="cuda").cpu()
@@ -470,7 +564,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget per CPU-baseline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="budget per CPU-baseline leg (half on all host threads, half on one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-call", action="store_true")
     ap.add_argument("--no-norm", action="store_true", help="skip the input-norm measurements")

@@ -79,9 +79,22 @@ typedef enum {
     BITNET_ERR_NONFINITE = 4     /* a weight given to the packer is inf or NaN     */
 } bitnet_status_t;
 
-typedef enum { BITNET_F32 = 0, BITNET_BF16 = 1 } bitnet_dtype_t;
+/* The last two enumerators of each input enum give it the range of int32, so
+ * that a caller's out-of-range value is a checked argument error rather than
+ * undefined behaviour in the library (they are not valid arguments). */
+typedef enum {
+    BITNET_F32 = 0,
+    BITNET_BF16 = 1,
+    BITNET_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+    BITNET_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
+} bitnet_dtype_t;
 
-typedef enum { BITNET_MEM_HOST = 0, BITNET_MEM_DEVICE = 1 } bitnet_mem_t;
+typedef enum {
+    BITNET_MEM_HOST = 0,
+    BITNET_MEM_DEVICE = 1,
+    BITNET_MEM_RANGE_MIN_ = -0x7FFFFFFF - 1,
+    BITNET_MEM_RANGE_MAX_ = 0x7FFFFFFF
+} bitnet_mem_t;
 
 /* ABI version of the loaded library (BITNET_ABI_VERSION). */
 int32_t bitnet_abi_version(void);
@@ -394,7 +407,12 @@ bitnet_status_t bitnet_linear_blocked_forward(hipStream_t stream, const int8_t* 
  *                           layout of this kind, so this is the default);
  *   BITNET_I2S_CONSECUTIVE  byte j holds values 4j, 4j+1, 4j+2, 4j+3.
  */
-typedef enum { BITNET_I2S_STRIDED = 0, BITNET_I2S_CONSECUTIVE = 1 } bitnet_i2s_order_t;
+typedef enum {
+    BITNET_I2S_STRIDED = 0,
+    BITNET_I2S_CONSECUTIVE = 1,
+    BITNET_I2S_RANGE_MIN_ = -0x7FFFFFFF - 1,
+    BITNET_I2S_RANGE_MAX_ = 0x7FFFFFFF
+} bitnet_i2s_order_t;
 
 /* Bytes of the I2_S buffer of an [N, K] tensor; -1 unless K % 16 == 0 and
  * N*K % 128 == 0. */
@@ -426,9 +444,10 @@ bitnet_status_t bitnet_i2s_export(bitnet_mem_t where, hipStream_t stream, const 
  * offline conversion [Guide s3.3]) is done once.  Host memory, synchronous.
  * Format (little-endian): a 64-byte header -- magic "BTNLV1\0\0", u32
  * version (1), u32 header size (64), i64 N, K, Kp, i32 segment count, u32
- * layout (1 = layout v1), u64 FNV-1a-64 of every byte after the header, u64
- * reserved (0) -- then packed [N][Kp/4], w_scale [N] fp32, the segments' row
- * counts (i64) and means (fp32).
+ * layout (1 = layout v1), u64 FNV-1a-64 of the 48 header bytes before it and
+ * then of every byte after the header, u64 reserved (0) -- then packed
+ * [N][Kp/4], w_scale [N] fp32, the segments' row counts (i64) and means
+ * (fp32).
  * bitnet_load_packed with packed == NULL only reads the header into N, K and
  * n_segs (to size the buffers); otherwise it fills all four arrays and checks
  * the checksum.  Errors: INVALID_ARG (I/O, bad or inconsistent file,

@@ -144,6 +144,13 @@ uint16_t orc_f32_to_bf16(float f)
                                         /* it yields the next binade or inf  */
 }
 
+/* The same rounding for n values. */
+void orc_f32_to_bf16_array(const float* f, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_f32_to_bf16(f[i]);
+}
+
 static float load_elem(const void* base, int dtype, int64_t idx)
 {
     if (dtype == ORC_BF16)

@@ -35,6 +35,21 @@ def build(source: Path = SOURCE, out: Path = LIBRARY) -> Path:
     return out
 
 
+SANITIZED = HERE / "liboracle_san.so"
+
+
+def build_sanitized(out: Path = SANITIZED) -> Path:
+    """The oracle built with AddressSanitizer and UndefinedBehaviorSanitizer by
+    the ROCm clang, to run under that compiler's ASan runtime (CPU tests only)."""
+    clang = "/opt/rocm/llvm/bin/clang"
+    flags = [f for f in CFLAGS if f not in ("-O2", "-fopenmp")] + [
+        "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+    tmp = Path(str(out) + f".tmp{os.getpid()}")
+    subprocess.run([clang, *flags, str(SOURCE), "-o", str(tmp), "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def _ptr(a: np.ndarray):
     return ctypes.c_void_p(a.ctypes.data)
 
@@ -51,6 +66,8 @@ class Oracle:
     """Handle on one compiled oracle shared object."""
 
     def __init__(self, path: Path | str | None = None):
+        if path is None and os.environ.get("BITNET_ORACLE_LIBRARY"):
+            path = os.environ["BITNET_ORACLE_LIBRARY"]     # e.g. the sanitized build
         path = Path(path) if path is not None else LIBRARY
         if path == LIBRARY and (not path.exists() or path.stat().st_mtime < SOURCE.stat().st_mtime):
             build(out=path)
@@ -59,6 +76,7 @@ class Oracle:
         i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
         lib.orc_bf16_to_f32.argtypes, lib.orc_bf16_to_f32.restype = [ctypes.c_uint16], f32
         lib.orc_f32_to_bf16.argtypes, lib.orc_f32_to_bf16.restype = [f32], ctypes.c_uint16
+        lib.orc_f32_to_bf16_array.argtypes, lib.orc_f32_to_bf16_array.restype = [vp, i64, vp], None
         lib.orc_padded_k.argtypes, lib.orc_padded_k.restype = [i64], i64
         lib.orc_row_abs_sum.argtypes, lib.orc_row_abs_sum.restype = [vp, ctypes.c_int, i64, i64, i64], ctypes.c_double
         lib.orc_segment_mean.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64]
@@ -99,12 +117,10 @@ class Oracle:
         return int(self.lib.orc_padded_k(K))
 
     def bf16_from_f32(self, v: np.ndarray) -> np.ndarray:
-        """fp32 -> bf16 bit patterns, round to nearest even (element loop)."""
+        """fp32 -> bf16 bit patterns, round to nearest even (the C element loop)."""
         v = np.ascontiguousarray(v, dtype=np.float32)
         out = np.empty(v.shape, dtype=np.uint16)
-        flat_in, flat_out = v.reshape(-1), out.reshape(-1)
-        for i in range(flat_in.size):
-            flat_out[i] = self.lib.orc_f32_to_bf16(float(flat_in[i]))
+        self.lib.orc_f32_to_bf16_array(_ptr(v), v.size, _ptr(out))
         return out
 
     def ternary(self, w: float, s: float) -> int:

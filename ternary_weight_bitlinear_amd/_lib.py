@@ -9,7 +9,11 @@ from __future__ import annotations
 import ctypes
 from pathlib import Path
 
-LIBRARY = Path(__file__).resolve().parent / "libbitnet_hip.so"
+import os
+
+# BITNET_LIBRARY may name another build of the same library (the tests use it
+# for the sanitized host build); by default the in-tree build is loaded.
+LIBRARY = Path(os.environ.get("BITNET_LIBRARY") or Path(__file__).resolve().parent / "libbitnet_hip.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NONFINITE = range(5)
 F32, BF16 = 0, 1

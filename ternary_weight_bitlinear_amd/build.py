@@ -65,6 +65,50 @@ def build(verbose: bool = False) -> Path:
     return LIBRARY
 
 
+SANITIZED = BUILD / "sanitize" / "libbitnet_hip_san.so"
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(verbose: bool = False) -> Path:
+    """A copy of the library whose host code (argument checks, host packer, host
+    I2_S paths, packed-weight files, plans) is built with AddressSanitizer and
+    UndefinedBehaviorSanitizer; device code as in build().  For CPU tests only:
+    load it with the compiler's ASan runtime preloaded."""
+    build(verbose=verbose)
+    out_dir = SANITIZED.parent
+    out_dir.mkdir(parents=True, exist_ok=True)
+    obj = out_dir / "bitnet_api.o"
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"] + SANITIZE_FLAGS
+    res = subprocess.run([hipcc(), "-x", "hip", *flags, "-c", str(CSRC / "bitnet_api.cpp"), "-o", str(obj)],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on bitnet_api.cpp (sanitized):\n{res.stderr}")
+    objs = [obj] + [BUILD / (Path(src).stem + ".o") for src in SOURCES if src != "bitnet_api.cpp"]
+    tmp = SANITIZED.with_suffix(f".so.tmp{os.getpid()}")
+    res = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed (sanitized):\n{res.stderr}")
+    os.replace(tmp, SANITIZED)
+    if verbose:
+        print(f"built {SANITIZED}")
+    return SANITIZED
+
+
+def asan_runtime() -> Path:
+    """The ASan runtime of the compiler that built the sanitized library."""
+    root = Path(hipcc()).resolve().parent.parent
+    for base in (root / "llvm" / "lib" / "clang", root / "lib" / "llvm" / "lib" / "clang", Path("/opt/rocm/llvm/lib/clang")):
+        found = sorted(base.glob("*/lib/linux/libclang_rt.asan-x86_64.so"))
+        if found:
+            return found[-1]
+    raise FileNotFoundError("libclang_rt.asan-x86_64.so not found")
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "sanitized":
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -13,6 +13,7 @@
 #include "../../include/bitnet.h"
 
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -651,10 +652,12 @@ struct FileHeader {                 // little-endian, 64 bytes
     int64_t N, K, Kp;
     int32_t n_segs;
     uint32_t layout;                // 1: layout v1
-    uint64_t payload_fnv1a;         // FNV-1a 64 over every byte after the header
-    uint64_t reserved;
+    uint64_t fnv1a;                 // FNV-1a 64 over header bytes 0..47, then every byte after the header
+    uint64_t reserved;              // 0
 };
 static_assert(sizeof(FileHeader) == kFileHeaderBytes, "file header layout");
+constexpr size_t kHashedHeaderBytes = offsetof(FileHeader, fnv1a);
+static_assert(kHashedHeaderBytes == 48, "the checksum covers the header fields before it");
 
 uint64_t fnv1a(uint64_t h, const void* p, size_t n) {
     const auto* b = static_cast<const unsigned char*>(p);
@@ -691,12 +694,12 @@ bitnet_status_t bitnet_save_packed(const char* path, const uint8_t* packed, cons
     h.version = kFileVersion;
     h.header_bytes = kFileHeaderBytes;
     h.N = N; h.K = K; h.Kp = Kp; h.n_segs = n_segs; h.layout = 1;
-    uint64_t c = 0xcbf29ce484222325ull;
+    uint64_t c = fnv1a(0xcbf29ce484222325ull, &h, kHashedHeaderBytes);
     c = fnv1a(c, packed, nb_packed);
     c = fnv1a(c, w_scale, nb_scale);
     c = fnv1a(c, seg_rows, static_cast<size_t>(n_segs) * 8);
     c = fnv1a(c, seg_mean, static_cast<size_t>(n_segs) * 4);
-    h.payload_fnv1a = c;
+    h.fnv1a = c;
     File f;
     f.f = fopen(path, "wb");
     if (!f.f) return fail(BITNET_ERR_INVALID_ARG, "%s: cannot open %s for writing", fn, path);
@@ -726,7 +729,8 @@ bitnet_status_t bitnet_load_packed(const char* path, int64_t* N, int64_t* K, int
     if (h.version != kFileVersion || h.header_bytes != kFileHeaderBytes || h.layout != 1)
         return fail(BITNET_ERR_UNSUPPORTED, "%s: file version %u, layout %u not supported (this library: %u, 1)", fn,
                     h.version, h.layout, kFileVersion);
-    if (check_dims(fn, 1, h.N, h.K) != BITNET_OK || h.Kp != padded_k(h.K) || h.n_segs <= 0 || h.n_segs > h.N)
+    if (check_dims(fn, 1, h.N, h.K) != BITNET_OK || h.Kp != padded_k(h.K) || h.n_segs <= 0 || h.n_segs > h.N ||
+        h.reserved != 0)
         return fail(BITNET_ERR_INVALID_ARG, "%s: %s has an inconsistent header", fn, path);
     *N = h.N;
     *K = h.K;
@@ -739,12 +743,12 @@ bitnet_status_t bitnet_load_packed(const char* path, int64_t* N, int64_t* K, int
     if (fread(packed, 1, nb_packed, f.f) != nb_packed || fread(w_scale, 1, nb_scale, f.f) != nb_scale ||
         fread(seg_rows, 8, ns, f.f) != ns || fread(seg_mean, 4, ns, f.f) != ns)
         return fail(BITNET_ERR_INVALID_ARG, "%s: %s is truncated", fn, path);
-    uint64_t c = 0xcbf29ce484222325ull;
+    uint64_t c = fnv1a(0xcbf29ce484222325ull, &h, kHashedHeaderBytes);
     c = fnv1a(c, packed, nb_packed);
     c = fnv1a(c, w_scale, nb_scale);
     c = fnv1a(c, seg_rows, ns * 8);
     c = fnv1a(c, seg_mean, ns * 4);
-    if (c != h.payload_fnv1a) return fail(BITNET_ERR_INVALID_ARG, "%s: %s fails its checksum", fn, path);
+    if (c != h.fnv1a) return fail(BITNET_ERR_INVALID_ARG, "%s: %s fails its checksum", fn, path);
     return ok();
 }
 

@@ -484,6 +484,88 @@ __device__ __forceinline__ void gemm_epilogue_blocked(const f32x16 (&facc)[TN][T
     }
 }
 
+// Bytes of one wave's staging region in gemm_epilogue_lds: the rows of one
+// pass (all TM*32 rows for bf16, 32 rows per pass for fp32) at a row pitch of
+// WN elements plus 8 bytes, so that the 8- or 16-byte writes of the 32 rows a
+// fragment spans spread over the LDS banks.
+template <int WN, int TM, bool kOutBf16>
+constexpr int epi_pitch() { return WN * (kOutBf16 ? 2 : 4) + 8; }
+template <int WN, int TM, bool kOutBf16>
+constexpr int epi_wave_bytes() { return (kOutBf16 ? TM * 32 : 32) * epi_pitch<WN, TM, kOutBf16>(); }
+
+// Epilogue through LDS (the stage ring is free by then): each wave writes its
+// WM x WN outputs, y = (float)(acc - q_rowsum) * (a_scale * w_scale) rounded
+// to the output type, into its own LDS region in the fragment layout, then
+// reads them back as 16-byte row segments and stores whole rows, 16 bytes per
+// lane.  A store instruction then covers 2-8 full rows instead of 16 bytes of
+// 32 rows, a quarter of the cache lines per output byte.  The values and
+// their roundings are those of gemm_epilogue.  Needs 16-byte aligned y rows
+// (ldy * size % 16 == 0 and y 16-byte aligned).
+//
+// value(i, j, rb, ml, nl) returns the four fp32 outputs a lane holds in
+// registers 4rb..4rb+3 of fragment (j, i): rows ml, columns nl..nl+3 of the
+// workgroup tile.
+template <int WM, int WN, int TM, int TN, bool kOutBf16, typename Value>
+__device__ __forceinline__ void gemm_epilogue_lds(Value value, int8_t* region, int m0, int n0, int wm, int wn,
+                                                  int lane, int M, int N, void* __restrict__ y, int64_t ldy) {
+    constexpr int ESZ = kOutBf16 ? 2 : 4;
+    constexpr int PITCH = epi_pitch<WN, TM, kOutBf16>();
+    constexpr int PASS_TM = kOutBf16 ? TM : 1;             // 32-row fragments per pass
+    constexpr int LANES_PER_ROW = WN * ESZ / 16;
+    constexpr int ROWS_PER_READ = 64 / LANES_PER_ROW;
+    static_assert(64 % LANES_PER_ROW == 0 && (PASS_TM * 32) % ROWS_PER_READ == 0, "epilogue shape");
+    const int r32 = lane % 32, g = lane / 32;
+#pragma unroll
+    for (int pass = 0; pass < TM / PASS_TM; ++pass) {
+#pragma unroll
+        for (int ii = 0; ii < PASS_TM; ++ii) {
+            const int i = pass * PASS_TM + ii;
+            const int ml = wm * WM + i * 32 + r32;
+            int8_t* row = region + (ii * 32 + r32) * PITCH;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const int nl = j * 32 + 8 * rb + 4 * g;          // column inside the wave tile
+                    const f32x4 v = value(i, j, rb, ml, wn * WN + nl);
+                    if constexpr (kOutBf16) {
+                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                        bf16x4 h;
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) h[rr] = static_cast<__bf16>(v[rr]);   // RNE
+                        *reinterpret_cast<bf16x4*>(row + nl * ESZ) = h;
+                    } else {
+                        *reinterpret_cast<f32x4*>(row + nl * ESZ) = v;
+                    }
+                }
+            }
+        }
+        // the wave's own LDS writes are visible to its own reads after they complete
+#pragma unroll
+        for (int r0 = 0; r0 < PASS_TM * 32; r0 += ROWS_PER_READ) {
+            const int rl = r0 + lane / LANES_PER_ROW;                 // row inside the pass
+            const int cb = (lane % LANES_PER_ROW) * 16;               // byte inside the row
+            const u32x4 v = *reinterpret_cast<const u32x4*>(region + rl * PITCH + cb);
+            const int m = m0 + wm * WM + pass * PASS_TM * 32 + rl;
+            const int n = n0 + wn * WN + cb / ESZ;
+            if (m >= M) continue;
+            char* dst = static_cast<char*>(y) + (static_cast<int64_t>(m) * ldy + n) * ESZ;
+            if (n + 16 / ESZ <= N) {
+                *reinterpret_cast<u32x4*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16 / ESZ; ++e) {
+                    if (n + e >= N) break;
+                    if constexpr (kOutBf16)
+                        reinterpret_cast<uint16_t*>(dst)[e] = static_cast<uint16_t>(v[e / 2] >> (16 * (e % 2)));
+                    else
+                        reinterpret_cast<uint32_t*>(dst)[e] = v[e];
+                }
+            }
+        }
+    }
+}
+
 // kBlocked: weights with one scale per 256-k block of a row ("BitVLA --
 // 1.58-bit Vision-Language-Action on Core AI", s2: the sibling matvec
 // kernel's per-256-block scales, against BitNet's one per tensor).  The codes are
@@ -678,12 +760,46 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
     // the loads past the last stage must land before the workgroup's LDS is released
     wait_vm<0>();
 
-    if constexpr (kBlocked)
+    static_assert(kNW * epi_wave_bytes<WN, TM, kOutBf16>() <= NS * STAGE, "epilogue staging fits the ring");
+    int8_t* const region = lds + wave * epi_wave_bytes<WN, TM, kOutBf16>();
+    if (kBlocked && vec_store == 2) {
+        __syncthreads();          // every wave has read the ring for the last time
+        gemm_epilogue_lds<WM, WN, TM, TN, kOutBf16>(
+            [&](int i, int j, int rb, int ml, int) {
+                const float as = as_s[ml];
+                f32x4 v;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) v[rr] = facc[j][i][4 * rb + rr] * as;
+                return v;
+            },
+            region, m0, n0, wm, wn, lane, M, N, y, ldy);
+    } else if (kBlocked) {
         gemm_epilogue_blocked<BM, BN, WM, WN, TM, TN, kOutBf16>(facc, as_s, m0, n0, wm, wn, r32, g, M, N, y, ldy,
                                                                vec_store);
-    else
+    } else if (vec_store == 2 && !acc_debug) {
+        __syncthreads();          // every wave has read the ring for the last time
+        gemm_epilogue_lds<WM, WN, TM, TN, kOutBf16>(
+            [&](int i, int j, int rb, int ml, int nl) {
+                const float as = as_s[ml];
+                const int32_t rs = rs_s[ml];
+                const f32x4 ws4 = *reinterpret_cast<const f32x4*>(&ws_s[nl]);
+                f32x4 v;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) v[rr] = static_cast<float>(acc[j][i][4 * rb + rr] - rs) * (as * ws4[rr]);
+                return v;
+            },
+            region, m0, n0, wm, wn, lane, M, N, y, ldy);
+    } else {
         gemm_epilogue<BM, BN, WM, WN, TM, TN, kOutBf16>(acc, as_s, rs_s, ws_s, m0, n0, wm, wn, r32, g, M, N, y, ldy,
                                                        acc_debug, vec_store);
+    }
+}
+
+// BITNET_GEMM_EPILOGUE=direct keeps the register-to-global epilogue in the
+// LDS-DMA kernel (for comparisons; results are identical), read at each launch.
+bool epilogue_direct() {
+    const char* v = getenv("BITNET_GEMM_EPILOGUE");
+    return v && strcmp(v, "direct") == 0;
 }
 
 template <int BM, int BN, int WGM, int WGN, int NS, int kWaves>
@@ -701,7 +817,9 @@ hipError_t launch_tile_dma(const int8_t* q, const float* a_scale, const int32_t*
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    const int vec_store = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+    // 1: 4-element vector stores; 2: 16-byte rows, so the LDS-staged epilogue
+    const bool rows16 = (ldy * (y_bf16 ? 2 : 4)) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
+    const int vec_store = rows16 && !epilogue_direct() ? 2 : (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
     kern<<<grid, block, lds, stream>>>(q, a_scale, q_rowsum, (int)M, (int)Kp, packed, w_scale, (int)N, y, ldy,
                                        acc_debug, order, vec_store, nullptr, 0);
     return hipGetLastError();
@@ -871,7 +989,8 @@ hipError_t launch_gemm_blocked(const int8_t* q, const float* a_scale, int64_t M,
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    const int vec_store = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+    const bool rows16 = (ldy * (y_bf16 ? 2 : 4)) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0;
+    const int vec_store = rows16 && !epilogue_direct() ? 2 : (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
     const dim3 grid(static_cast<unsigned>(order.tiles_m) * order.tiles_n), block(256);
     kern<<<grid, block, lds, stream>>>(q, a_scale, nullptr, (int)M, (int)Kp, packed, nullptr, (int)N, y, ldy,
                                        nullptr, order, vec_store, block_scale, nb);

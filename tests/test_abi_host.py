@@ -286,3 +286,91 @@ def test_packed_file_roundtrip_and_damage(tmp_path):
         tw.load_packed(tmp_path / "m.btnl")
     with pytest.raises(ValueError):
         tw.save_packed(f, pw)                          # two segments need two row counts
+
+
+def _load_raw(path, limit_bytes=1 << 26):
+    """bitnet_load_packed through the C ABI with buffers sized exactly from the
+    header query (so an over-read or over-write shows under AddressSanitizer)."""
+    L = _lib.lib()
+    N, K, ns = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    st = L.bitnet_load_packed(str(path).encode(), ctypes.byref(N), ctypes.byref(K), ctypes.byref(ns),
+                              None, None, None, None)
+    if st != _lib.OK:
+        return st
+    N, K, ns = N.value, K.value, ns.value
+    kp = L.bitnet_padded_k(K)
+    assert N > 0 and kp > 0 and 0 < ns <= N
+    if N * kp // 4 + N * 4 > limit_bytes:
+        return "too large to load"
+    packed = np.empty(N * kp // 4, dtype=np.uint8)
+    w_scale = np.empty(N, dtype=np.float32)
+    segs = np.empty(ns, dtype=np.int64)
+    means = np.empty(ns, dtype=np.float32)
+    d = ctypes.c_int64()
+    return L.bitnet_load_packed(str(path).encode(), ctypes.byref(d), ctypes.byref(ctypes.c_int64()),
+                                ctypes.byref(ctypes.c_int32()), packed.ctypes.data, w_scale.ctypes.data,
+                                segs.ctypes.data, means.ctypes.data)
+
+
+def test_packed_file_fuzz(tmp_path):
+    """Damaged files: every header byte flipped, extreme header fields,
+    truncations at many lengths and random payload damage.  The loader must
+    return a status (OK only for an undamaged file) and never read or write out
+    of bounds."""
+    import struct
+    W = wl.draw_weight((24, 160), seed=21)
+    pw = tw.pack(W, (8, 16))
+    f = tmp_path / "w.btnl"
+    tw.save_packed(f, pw, (8, 16))
+    raw = f.read_bytes()
+    assert _load_raw(f) == _lib.OK
+    rng = np.random.default_rng(5)
+    cases = []
+    for pos in range(64):                                   # every header byte, two flips each
+        for bit in rng.choice(8, size=2, replace=False):
+            b = bytearray(raw)
+            b[pos] ^= 1 << int(bit)
+            cases.append(bytes(b))
+    for off, fmt, val in ((16, "<q", 1 << 40), (16, "<q", -5), (24, "<q", 1 << 30), (24, "<q", 17),
+                          (32, "<q", 1 << 20), (40, "<i", 1 << 30), (40, "<i", -1), (40, "<i", 0),
+                          (24, "<q", 0), (16, "<q", 0)):
+        b = bytearray(raw)
+        struct.pack_into(fmt, b, off, val)
+        cases.append(bytes(b))
+    for n in sorted(set(rng.integers(0, len(raw), size=40).tolist()) | {0, 1, 63, 64, len(raw) - 1}):
+        cases.append(raw[:n])
+    for _ in range(20):
+        b = bytearray(raw)
+        for p in rng.integers(64, len(raw), size=3):
+            b[int(p)] = int(rng.integers(0, 256))
+        cases.append(bytes(b))
+    for _ in range(10):
+        cases.append(rng.integers(0, 256, size=int(rng.integers(1, 400)), dtype=np.uint8).tobytes())
+    for i, data in enumerate(cases):
+        g = tmp_path / f"c{i}.btnl"
+        g.write_bytes(data)
+        st = _load_raw(g)
+        assert st in (_lib.OK, _lib.ERR_INVALID_ARG, _lib.ERR_UNSUPPORTED, "too large to load"), (i, st)
+        if data != raw:
+            assert st != _lib.OK, f"case {i}: a damaged file loaded"
+
+
+def test_host_i2s_import_fuzz():
+    """Random I2_S buffers into the host importer: every field value 3 is an
+    error, other bytes import, nothing out of bounds."""
+    L = _lib.lib()
+    rng = np.random.default_rng(6)
+    for N, K in ((4, 32), (2, 64), (3, 128)):
+        nbytes = L.bitnet_i2s_bytes(N, K)
+        kp = L.bitnet_padded_k(K)
+        for _ in range(30):
+            buf = rng.integers(0, 256, size=nbytes, dtype=np.uint8)
+            buf[-4:] = np.frombuffer(np.float32(rng.uniform(-2, 8)).tobytes(), dtype=np.uint8)
+            packed = np.empty(N * kp // 4, dtype=np.uint8)
+            ws = np.empty(N, dtype=np.float32)
+            st = L.bitnet_i2s_import(_lib.MEM_HOST, None, buf.ctypes.data, N, K, int(rng.integers(0, 2)),
+                                     packed.ctypes.data, ws.ctypes.data)
+            fields = np.stack([(buf[:-4] >> s) & 3 for s in (0, 2, 4, 6)])
+            scale = np.frombuffer(buf[-4:].tobytes(), dtype=np.float32)[0]
+            ok = not (fields == 3).any() and scale > 0
+            assert (st == _lib.OK) == ok, (st, ok)

@@ -502,33 +502,78 @@ def test_linear(orc, M, N, K, out):
     ref = orc.linear(bits(x), bits(W), out=out)
     pw = tw.pack(W.to(DEV))
     q, a, r = tw.act_quant(x.to(DEV))
-    y, acc = tw.linear(q, a, r, pw, out_dtype=torch.float32 if out == "f32" else torch.bfloat16,
-                       acc_debug=True)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    check_y(tw.linear(q, a, r, pw, out_dtype=dt), ref["y"])          # the launch the benchmark times
+    y, acc = tw.linear(q, a, r, pw, out_dtype=dt, acc_debug=True)    # and with the exact sums written out
     assert np.array_equal(pw.packed.cpu().numpy(), ref["packed"])
     assert np.array_equal(q.cpu().numpy(), ref["q"])
     assert np.array_equal(acc.cpu().numpy(), ref["acc"])
     check_y(y, ref["y"])
 
 
-@pytest.mark.parametrize("kernel", ["dma", "regs"])
-@pytest.mark.parametrize("tile", ["small", "wide", "tiny"])
+_TILE_REFS = {}
+
+
+def _tile_case(orc, M, N, K):
+    """Inputs and oracle results of one GEMM tile case, computed once per shape."""
+    if (M, N, K) not in _TILE_REFS:
+        x, W = wl.random_case(M * 31 + N * 3 + K, M, N, K, x_dist="normal_outliers")
+        ref = orc.linear(bits(x), bits(W), out="f32")
+        ref["y_bf16"] = orc.epilogue(ref["acc"], ref["a_scale"], ref["w_scale"], "bf16")
+        _TILE_REFS[(M, N, K)] = (x, W, ref)
+    return _TILE_REFS[(M, N, K)]
+
+
 @pytest.mark.parametrize("M,N,K", [(17, 16, 16), (130, 257, 1152), (300, 200, 4304), (257, 129, 6912),
                                    (384, 512, 2560), (520, 1100, 2560)])
-def test_linear_each_gemm_tile(orc, kernel, tile, M, N, K, monkeypatch):
+@pytest.mark.parametrize("kernel", ["dma", "regs"])
+@pytest.mark.parametrize("tile", ["small", "wide", "tiny"])
+@pytest.mark.parametrize("epilogue", ["lds", "direct"])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_linear_each_gemm_tile(orc, kernel, tile, epilogue, out, M, N, K, monkeypatch):
     """Every GEMM tile (128x128, 128x256 and 64x64, forced) of both kernels
-    (LDS-DMA and register-staged loads) gives the oracle's exact sums and
-    outputs on ragged M, N and padded K."""
+    (LDS-DMA and register-staged loads), with the LDS-staged and the direct
+    epilogue of the LDS-DMA kernel, gives the oracle's exact sums and outputs
+    on ragged M, N and padded K, bf16 and fp32."""
+    if (kernel == "regs" or tile == "tiny") and epilogue == "lds":
+        pytest.skip("the LDS-staged epilogue belongs to the LDS-DMA kernel")
     if kernel == "regs" and tile == "tiny":
         pytest.skip("the 64x64 tile has one kernel")
     monkeypatch.setenv("BITNET_GEMM_TILE", tile)
     monkeypatch.setenv("BITNET_GEMM_KERNEL", kernel)
-    x, W = wl.random_case(M * 31 + N * 3 + K, M, N, K, x_dist="normal_outliers")
-    ref = orc.linear(bits(x), bits(W), out="bf16")
+    if epilogue == "direct":
+        monkeypatch.setenv("BITNET_GEMM_EPILOGUE", "direct")
+    else:
+        monkeypatch.delenv("BITNET_GEMM_EPILOGUE", raising=False)
+    x, W, ref = _tile_case(orc, M, N, K)
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    want = ref["y_bf16"] if out == "bf16" else ref["y"]
     pw = tw.pack(W.to(DEV))
     q, a, r = tw.act_quant(x.to(DEV))
-    y, acc = tw.linear(q, a, r, pw, out_dtype=torch.bfloat16, acc_debug=True)
+    check_y(tw.linear(q, a, r, pw, out_dtype=dt), want)
+    y, acc = tw.linear(q, a, r, pw, out_dtype=dt, acc_debug=True)
     assert np.array_equal(acc.cpu().numpy(), ref["acc"])
-    check_y(y, ref["y"])
+    check_y(y, want)
+
+
+@pytest.mark.parametrize("pad", [0, 3, 4, 8])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("tile", ["small", "wide"])
+def test_gemm_output_strides(orc, pad, out, tile, monkeypatch):
+    """GEMM outputs into a NaN-filled buffer with a row stride of N + pad: rows
+    aligned to 16 bytes take the LDS-staged epilogue, the others the direct one;
+    nothing is written past column N."""
+    monkeypatch.setenv("BITNET_GEMM_TILE", tile)
+    M, N, K = 200, 300, 1152
+    x, W, ref = _tile_case(orc, M, N, K)
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    pw = tw.pack(W.to(DEV))
+    q, a, r = tw.act_quant(x.to(DEV))
+    ybuf = torch.full((M, N + pad + 8), float("nan"), device=DEV, dtype=dt)
+    y = ybuf.view(-1)[: M * (N + pad)].view(M, N + pad)[:, :N]
+    tw.linear(q, a, r, pw, out=y)
+    check_y(y, ref["y_bf16"] if out == "bf16" else ref["y"])
+    assert torch.isnan(ybuf.view(-1)[: M * (N + pad)].view(M, N + pad)[:, N:].float()).all()
 
 
 @pytest.mark.parametrize("M", [1, 4, 16, 17, 64])
