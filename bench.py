@@ -515,8 +515,28 @@ def bench_configs(tw, wl, torch, steps, warmup):
     ms_1 = time_region(torch, lambda: tw.linear_blocked(q, a, pb, out=y), steps * 5, warmup)
     out["block_scaled"] = dict(gemm_c5=dict(tops=agg, frac_of_peak=agg / INT8_PEAK_TOPS, shapes=rows),
                                m1_2560x2560=dict(us=ms_1 * 1e3, value=2560 * 2560 / 4 / (ms_1 * 1e-3) / 1e9,
-                                                 unit="GB/s", note="warm, single call; the kernel is the GEMM"))
+                                                 unit="GB/s", note="warm, single call on the streaming kernel"))
     del pb, q, a, y
+    torch.cuda.empty_cache()
+    # the c2 decode stream with block-scaled weights, one grouped launch (ActQuant fused)
+    w2 = wl.WORKLOADS["c2"]
+    items, nb_codes, nb_scales = [], 0, 0
+    for layer in range(w2.layers):
+        for i, p in enumerate(w2.projections):
+            items.append((wl.activation_for(w2, i, layer=layer, device="cuda"),
+                          tw.pack_blocked(wl.weight_for(w2, i, layer=layer, device="cuda")),
+                          torch.empty((1, p.N), device="cuda")))
+            nb_codes += p.N * p.K // 4
+            nb_scales += (p.K + 255) // 256 * p.N * 4
+    group = tw.GroupedBitLinear(items)
+    ms_g = time_region(torch, group, steps, warmup)
+    gbps = nb_codes / (ms_g * 1e-3) / 1e9
+    out["block_scaled"]["c2_grouped_m1"] = dict(
+        value=gbps, unit="GB/s", ms_per_step=ms_g, kernel=group.kernel, packed_bytes=nb_codes, scale_bytes=nb_scales,
+        with_scales_gbps=(nb_codes + nb_scales) / (ms_g * 1e-3) / 1e9, frac_of_hbm_peak=gbps / HBM_PEAK_GBPS,
+        per_dispatch=dispatch_stats(time_each(torch, group, 20)),
+        note="packed-code GB/s (N*K/4 per projection); with_scales counts the fp32 block scales too")
+    del group, items
     torch.cuda.empty_cache()
     return out
 

@@ -326,6 +326,19 @@ bitnet_status_t bitnet_group_plan_a16(hipStream_t stream, const bitnet_group_ite
                                       bitnet_group_plan_t* plan);
 
 /*
+ * Grouped decode with per-256-block weight scales [BitVLA s2]: items as for
+ * bitnet_group_plan, except that each item's w_scale points to its
+ * block_scale [ceil(K/256)][N] from bitnet_pack_weights_blocked (K <= 8192);
+ * the launch quantises each item's tokens (as bitnet_act_quant) and computes
+ * bitnet_linear_blocked_forward's y for every item, with the same bits.
+ * Errors as for bitnet_group_plan; UNSUPPORTED for K > 8192 or when a
+ * workgroup's token rows do not fit its LDS share.
+ */
+bitnet_status_t bitnet_group_plan_blocked(hipStream_t stream, const bitnet_group_item_t* items, int32_t count,
+                                          int64_t M, bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype,
+                                          void* table_dev, int64_t table_bytes, bitnet_group_plan_t* plan);
+
+/*
  * Run every item of a plan in one kernel launch on `stream`: each workgroup
  * quantises its item's tokens (ActQuant, same numerics as bitnet_act_quant)
  * and streams its share of that item's packed weight once.  Results are
@@ -337,7 +350,8 @@ bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_
 /* Name of the kernel a plan launches: "stream" (each workgroup streams a
  * share of all packed bytes through per-wave LDS rings; chosen when every
  * workgroup's token rows fit its LDS share), "persistent" (the fallback) or
- * "stream-a16" (a bitnet_group_plan_a16 plan); "" for a handle not made by
+ * "stream-a16" (a bitnet_group_plan_a16 plan), "stream-blocked" (a
+ * bitnet_group_plan_blocked plan); "" for a handle not made by
  * bitnet_group_plan*.  The environment
  * variable BITNET_GROUP_KERNEL=persistent, read by bitnet_group_plan, forces
  * the fallback (for comparisons; results are identical). */
@@ -377,8 +391,9 @@ bitnet_status_t bitnet_linear_a16(hipStream_t stream, const void* x, bitnet_dtyp
  *   y[m][n] = a_scale[m] * sum_b acc_b * block_scale[b][n] with the exact
  *   int32 block sums acc_b = sum_{k in block b} q*t, evaluated in fp32 as
  *   total = 0; for b ascending: total = total + (float)acc_b * block_scale;
- *   y = total * a_scale (bf16 y: that value rounded to nearest even).  One
- *   int8-MFMA GEMM for every M (not tuned for decode sizes).
+ *   y = total * a_scale (bf16 y: that value rounded to nearest even).
+ *   M <= 16 runs the streaming decode kernel (one pass over codes and scales),
+ *   larger M an int8-MFMA GEMM; both give identical bits.
  * Errors: INVALID_ARG (sizes, NULL or misaligned pointers, ld < K or N, bad
  * dtype); UNSUPPORTED for K > 8192; NONFINITE for a non-finite weight; HIP.
  */

@@ -395,7 +395,9 @@ class GroupedBitLinear:
 
     ``items`` is a list of (x [M, K], PackedWeight, y [M, N]) device tensors; the
     plan keeps pointers to them, so they must stay alive and in place.  Calling
-    the object writes y_i = linear(ActQuant(x_i), WeightQuant(W_i)) for all i."""
+    the object writes y_i = linear(ActQuant(x_i), WeightQuant(W_i)) for all i.
+    With BlockPackedWeight items (per-256-block scales) every y_i is
+    linear_blocked's result for that item."""
 
     def __init__(self, items, norms=None, a16=False):
         """``norms``: None, or one entry per item, each None or (norm_w [K], up or None, eps):
@@ -410,6 +412,11 @@ class GroupedBitLinear:
             raise ValueError("the W1.58A16 group takes no input norms")
         if a16 and any(x.dtype != torch.bfloat16 for x, _, _ in items):
             raise ValueError("the W1.58A16 group takes bf16 activations")
+        blocked = isinstance(items[0][1], BlockPackedWeight)
+        if any(isinstance(w, BlockPackedWeight) != blocked for _, w, _ in items):
+            raise ValueError("a group takes either per-tensor or per-256-block scaled weights, not both")
+        if blocked and (a16 or norms is not None):
+            raise ValueError("the block-scaled group takes neither input norms nor 16-bit activations")
         x0 = items[0][0]
         M = x0.shape[0]
         self._keep = list(items)
@@ -421,8 +428,9 @@ class GroupedBitLinear:
                 raise ValueError(f"item {i}: every x must share one dtype, and every y another")
             _weight(w)
             _output(y, M, w.N)
-            _on_device(x0.device, x=x, packed=w.packed, w_scale=w.w_scale, out=y)
-            arr[i] = _lib.GroupItem(x.data_ptr(), _rows(x, "x"), w.packed.data_ptr(), w.w_scale.data_ptr(),
+            scale = w.block_scale if blocked else w.w_scale
+            _on_device(x0.device, x=x, packed=w.packed, w_scale=scale, out=y)
+            arr[i] = _lib.GroupItem(x.data_ptr(), _rows(x, "x"), w.packed.data_ptr(), scale.data_ptr(),
                                     y.data_ptr(), _rows(y, "y"), w.N, w.K)
         nrm = None
         if norms is not None:
@@ -445,7 +453,11 @@ class GroupedBitLinear:
         self.plan = _lib.GroupPlan()
         self.device = x0.device
         with torch.cuda.device(x0.device):
-            if a16:
+            if blocked:
+                _lib.check(_lib.lib().bitnet_group_plan_blocked(
+                    _stream(x0), ctypes.cast(arr, ctypes.c_void_p), len(items), M, _dtype(x0),
+                    _dtype(items[0][2]), self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
+            elif a16:
                 _lib.check(_lib.lib().bitnet_group_plan_a16(
                     _stream(x0), ctypes.cast(arr, ctypes.c_void_p), len(items), M, _dtype(items[0][2]),
                     self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
@@ -458,7 +470,7 @@ class GroupedBitLinear:
                     _stream(x0), ctypes.cast(arr, ctypes.c_void_p), ctypes.cast(nrm, ctypes.c_void_p), len(items),
                     M, _dtype(x0), _dtype(items[0][2]), self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
         self.bytes = sum(w.N * w.K // 4 for _, w, _ in items)
-        # which kernel the plan launches: "stream", "persistent" or "stream-a16"
+        # which kernel the plan launches: "stream", "persistent", "stream-a16" or "stream-blocked"
         self.kernel = _lib.lib().bitnet_group_plan_kernel(ctypes.byref(self.plan)).decode()
 
     def __call__(self):

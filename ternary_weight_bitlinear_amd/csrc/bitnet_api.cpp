@@ -430,8 +430,18 @@ bitnet_status_t bitnet_linear_blocked_forward(hipStream_t stream, const int8_t* 
         return fail(BITNET_ERR_INVALID_ARG, "%s: q and packed must be 16-byte aligned", fn);
     if (!aligned(y, y_dtype == BITNET_F32 ? 4 : 2) || !aligned(a_scale, 4) || !aligned(block_scale, 4))
         return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned y or scale pointer", fn);
-    hipError_t e = bitnet::launch_gemm_blocked(q, a_scale, M, K, padded_k(K), packed, block_scale, N, y,
-                                               y_dtype == BITNET_BF16, ldy, stream);
+    hipError_t e = hipErrorInvalidValue;
+    if (M <= kGemvMaxM) {
+        // decode sizes: the streaming kernel, one pass over codes and scales
+        bitnet::GemvProblem p{};
+        p.q = q; p.a_scale = a_scale; p.packed = packed; p.w_scale = block_scale;
+        p.y = y; p.ldy = ldy;
+        p.M = (int)M; p.N = (int)N; p.K = (int)K; p.Kp = (int)padded_k(K);
+        e = bitnet::launch_gemv_blocked(p, y_dtype == BITNET_BF16, stream);
+    }
+    if (e == hipErrorInvalidValue)          // larger M, or token rows beyond the streaming kernel's LDS
+        e = bitnet::launch_gemm_blocked(q, a_scale, M, K, padded_k(K), packed, block_scale, N, y,
+                                        y_dtype == BITNET_BF16, ldy, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }
@@ -755,7 +765,8 @@ bitnet_status_t bitnet_load_packed(const char* path, int64_t* N, int64_t* K, int
 // Kernels of a grouped plan.  BITNET_GROUP_KERNEL=persistent, read when a
 // plan is made, skips the streaming kernel (for comparisons; results are
 // identical).
-enum { kGroupPersistent = 0, kGroupStream = 1, kGroupA16 = 2 };
+enum { kGroupPersistent = 0, kGroupStream = 1, kGroupA16 = 2, kGroupBlocked = 3 };
+enum GroupMode { kModeA8 = 0, kModeA16 = 1, kModeBlocked = 2 };
 static bool persistent_forced() {
     const char* v = getenv("BITNET_GROUP_KERNEL");
     return v && strcmp(v, "persistent") == 0;
@@ -772,7 +783,8 @@ static bitnet_status_t group_plan_impl(hipStream_t stream, const bitnet_group_it
                                        const bitnet_group_norm_t* norms, int32_t count, int64_t M,
                                        bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype, void* table_dev,
                                        int64_t table_bytes, bitnet_group_plan_t* plan, const char* fn,
-                                       bool a16 = false) {
+                                       GroupMode mode = kModeA8) {
+    const bool a16 = mode == kModeA16;
     if (count <= 0 || !items || !plan || !table_dev)
         return fail(BITNET_ERR_INVALID_ARG, "%s: need count > 0, items, table_dev and plan", fn);
     if (!aligned(table_dev, 16) || table_bytes < bitnet_group_table_bytes(count))
@@ -796,6 +808,8 @@ static bitnet_status_t group_plan_impl(hipStream_t stream, const bitnet_group_it
             !aligned(it.w_scale, 4) || !aligned(it.y, y_dtype == BITNET_F32 ? 4 : 2))
             return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned pointer or x row stride", where);
         const int64_t Kp = padded_k(it.K);
+        if (mode == kModeBlocked && it.K > kBlockedMaxK)
+            return fail(BITNET_ERR_UNSUPPORTED, "%s: K=%lld > %lld", where, (long long)it.K, (long long)kBlockedMaxK);
         if (static_cast<int64_t>(bitnet::gemv_group_lds(M, Kp)) > kGroupLdsBytes)
             return fail(BITNET_ERR_UNSUPPORTED, "%s: M tokens of K=%lld need more than %lld bytes of LDS", where,
                         (long long)it.K, (long long)kGroupLdsBytes);
@@ -828,7 +842,13 @@ static bitnet_status_t group_plan_impl(hipStream_t stream, const bitnet_group_it
     int kind = kGroupPersistent, grid = 0;
     size_t lds = bitnet::gemv_group_lds(M, max_kp);
     std::vector<int32_t> bounds;
-    if (a16) {
+    if (mode == kModeBlocked) {
+        if (!bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &grid, &lds, 1, &bounds, true))
+            return fail(BITNET_ERR_UNSUPPORTED,
+                        "%s: a workgroup's share of the group needs more LDS than it has for M=%lld token rows", fn,
+                        (long long)M);
+        kind = kGroupBlocked;
+    } else if (a16) {
         if (!bitnet::gemv_stream_plan(table.data(), count, tiles, steps, &grid, &lds, 2, &bounds))
             return fail(BITNET_ERR_UNSUPPORTED,
                         "%s: a workgroup's share of the group needs more LDS than it has for M=%lld bf16 token rows "
@@ -875,7 +895,14 @@ bitnet_status_t bitnet_group_plan_a16(hipStream_t stream, const bitnet_group_ite
                                       bitnet_dtype_t y_dtype, void* table_dev, int64_t table_bytes,
                                       bitnet_group_plan_t* plan) {
     return group_plan_impl(stream, items, nullptr, count, M, BITNET_BF16, y_dtype, table_dev, table_bytes, plan,
-                           "bitnet_group_plan_a16", true);
+                           "bitnet_group_plan_a16", kModeA16);
+}
+
+bitnet_status_t bitnet_group_plan_blocked(hipStream_t stream, const bitnet_group_item_t* items, int32_t count,
+                                          int64_t M, bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype, void* table_dev,
+                                          int64_t table_bytes, bitnet_group_plan_t* plan) {
+    return group_plan_impl(stream, items, nullptr, count, M, x_dtype, y_dtype, table_dev, table_bytes, plan,
+                           "bitnet_group_plan_blocked", kModeBlocked);
 }
 
 bitnet_status_t bitnet_group_plan_rmsnorm(hipStream_t stream, const bitnet_group_item_t* items,
@@ -897,12 +924,16 @@ bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_
     const int grid = static_cast<int>(plan->opaque[6] >> 32);
     const bool x_bf16 = (plan->opaque[6] & 0xFF) == BITNET_BF16;
     const bool y_bf16 = ((plan->opaque[6] >> 8) & 0xFF) == BITNET_BF16;
-    hipError_t e = kind == kGroupA16
-                       ? bitnet::launch_gemv_a16_grouped(table, count, plan->opaque[4], plan->opaque[7], grid, y_bf16,
-                                                         stream)
-                       : bitnet::launch_gemv_grouped(table, count, plan->opaque[4], plan->opaque[7],
-                                                     static_cast<size_t>(plan->opaque[5]),
-                                                     kind == kGroupStream ? grid : 0, x_bf16, y_bf16, stream);
+    hipError_t e;
+    if (kind == kGroupA16)
+        e = bitnet::launch_gemv_a16_grouped(table, count, plan->opaque[4], plan->opaque[7], grid, y_bf16, stream);
+    else if (kind == kGroupBlocked)
+        e = bitnet::launch_gemv_blocked_grouped(table, count, plan->opaque[4], plan->opaque[7], grid, x_bf16, y_bf16,
+                                                stream);
+    else
+        e = bitnet::launch_gemv_grouped(table, count, plan->opaque[4], plan->opaque[7],
+                                        static_cast<size_t>(plan->opaque[5]), kind == kGroupStream ? grid : 0, x_bf16,
+                                        y_bf16, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }
@@ -910,7 +941,10 @@ bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_
 const char* bitnet_group_plan_kernel(const bitnet_group_plan_t* plan) {
     if (!plan || plan->opaque[0] != kPlanMagic) return "";
     const int kind = static_cast<int>((plan->opaque[6] >> 16) & 0xFF);
-    return kind == kGroupStream ? "stream" : kind == kGroupA16 ? "stream-a16" : "persistent";
+    return kind == kGroupStream    ? "stream"
+           : kind == kGroupA16     ? "stream-a16"
+           : kind == kGroupBlocked ? "stream-blocked"
+                                   : "persistent";
 }
 
 const char* bitnet_status_string(bitnet_status_t s) {

@@ -71,8 +71,10 @@ __device__ __forceinline__ v4i expand_word(uint32_t w) {
     return r;
 }
 
-// exp(t) in fp32 by fixed IEEE steps, so that the gated input silu(a) * u of
-// the down projection has the same bits on every implementation of them:
+// exp(t) in fp32 by fixed IEEE steps (Cody and Waite's argument reduction
+// with a Taylor polynomial), used for the gated input silu(a) * u of the down
+// projection, where it stays within 2 fp32 ulps of exp and silu(a) * u within
+// 4 ulps of the exact value, independent of any math library:
 // +inf above 88 and 0 below -88; else n = rint(t * log2 e), reduced argument
 // r = (t - n * ln2_hi) - n * ln2_lo with a 15-bit ln2_hi (n * ln2_hi exact),
 // the degree-7 Taylor polynomial of exp at r in Horner form (|r| <= ln2/2),

@@ -57,8 +57,21 @@ constexpr int kMaxStreamGrid = 4096;
 // `bounds` (grouped launches) receives grid + 1 share bounds, to be uploaded
 // right after the problem table; without it the shares are k-step shares
 // snapped to tile starts (single problems).
+// `blocked`: the per-256-block scale version of the kernel, which keeps less
+// LDS for token rows.
 bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_tiles, int64_t total_steps,
-                      int* grid, size_t* lds, int token_bytes = 1, std::vector<int32_t>* bounds = nullptr);
+                      int* grid, size_t* lds, int token_bytes = 1, std::vector<int32_t>* bounds = nullptr,
+                      bool blocked = false);
+
+// Per-256-block weight scales (w_scale holds block_scale [ceil(K/256)][N]):
+// one problem on quantised tokens (q, a_scale; M <= 16) through the streaming
+// kernel; hipErrorInvalidValue if its token rows do not fit.
+hipError_t launch_gemv_blocked(const GemvProblem& p, bool y_bf16, hipStream_t stream);
+
+// Grouped block-scaled launch (ActQuant fused), table and grid from
+// gemv_stream_plan(..., blocked = true).
+hipError_t launch_gemv_blocked_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,
+                                       int64_t total_steps, int grid, bool x_bf16, bool y_bf16, hipStream_t stream);
 
 // W1.58A16 grouped launch of the streaming kernel (bf16 x, no quantiser):
 // table_dev and the grid as for launch_gemv_grouped's streaming case.

@@ -245,7 +245,7 @@ __device__ void quantise_tokens(const GemvProblem& p, int8_t* q_lds, float* as_l
 // Unfused persistent path: copy the problem's quantised rows q [M][Kp] from
 // global memory into the permuted, zero-padded LDS layout, with a_scale and
 // q_rowsum into as_lds / rs_lds.
-__device__ void stage_tokens(const GemvProblem& p, int8_t* q_lds, float* as_lds, int* rs_lds) {
+__device__ void stage_tokens(const GemvProblem& p, int8_t* q_lds, float* as_lds, int* rs_lds, bool rowsum = true) {
     const int ldq = padded_q_row(p.Kp);
     __syncthreads();   // every wave is done with the previous problem's rows and scales
     for (int i = threadIdx.x; i < p.M * (ldq / 8); i += kThreads) {
@@ -258,7 +258,7 @@ __device__ void stage_tokens(const GemvProblem& p, int8_t* q_lds, float* as_lds,
     }
     if (threadIdx.x < p.M) {
         as_lds[threadIdx.x] = gload<float>(p.a_scale + threadIdx.x);
-        rs_lds[threadIdx.x] = gload<int32_t>(p.q_rowsum + threadIdx.x);
+        rs_lds[threadIdx.x] = rowsum ? gload<int32_t>(p.q_rowsum + threadIdx.x) : 0;
     }
     __syncthreads();
 }
@@ -611,6 +611,114 @@ __global__ __launch_bounds__(kThreads) void gemv_persistent_kernel(GemvProblem s
     }
 }
 
+// ActQuant of up to kQuantBatch single-token problems at once (M = 1, bf16
+// x, no input norm, K <= 8192): every problem's token is loaded into registers
+// before any reduction, and the absmax and row-sum reductions of all of them
+// share one barrier each, so a workgroup that touches several problems pays
+// one memory latency and two barriers instead of that per problem.  Results
+// are bit-identical to quantise_tokens (same fp32 operations per element).
+constexpr int kQuantBatch = 4;
+constexpr int kQuantVecs = 4;                   // 8-element vectors per thread and problem: K <= 8192
+
+template <typename PS>
+__device__ bool quantise_batch_ok(const PS& ps, int p0, int p1) {
+    for (int pi = p0; pi <= p1; ++pi) {
+        const GemvProblem P = ps.get(pi);
+        if (P.M != 1 || P.norm_w != nullptr || P.K > 8 * kThreads * kQuantVecs) return false;
+    }
+    return true;
+}
+
+template <typename PS>
+__device__ void quantise_batch(const PS& ps, int p0, int np, int8_t* q_lds, float* as_lds, int* rs_lds,
+                               float* red_f, int* red_i, int t_begin) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    u32x4 raw[kQuantBatch][kQuantVecs];
+#pragma unroll
+    for (int j = 0; j < kQuantBatch; ++j) {
+        const GemvProblem P = ps.get(p0 + (j < np ? j : 0));
+        const int nvec = j < np ? P.K / 8 : 0;
+#pragma unroll
+        for (int i = 0; i < kQuantVecs; ++i) {
+            const int vi = tid + i * kThreads;
+            raw[j][i] = vi < nvec ? gload<u32x4>(static_cast<const char*>(P.x) + 16 * vi) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kQuantBatch; ++j) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kQuantVecs; ++i) {
+            const u32x4 w = raw[j][i];
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_lo(w.x)), fabsf(bf16_hi(w.x))),
+                                     fmaxf(fabsf(bf16_lo(w.y)), fabsf(bf16_hi(w.y)))));
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_lo(w.z)), fabsf(bf16_hi(w.z))),
+                                     fmaxf(fabsf(bf16_lo(w.w)), fabsf(bf16_hi(w.w)))));
+        }
+        amax = wave_max(amax);
+        if (lane == 0) red_f[wave * kQuantBatch + j] = amax;
+    }
+    __syncthreads();
+    int off = 0;
+    int sums[kQuantBatch];
+#pragma unroll
+    for (int j = 0; j < kQuantBatch; ++j) {
+        sums[j] = 0;
+        if (j >= np) continue;
+        const GemvProblem P = ps.get(p0 + j);
+        const float amax = fmaxf(fmaxf(red_f[j], red_f[kQuantBatch + j]),
+                                 fmaxf(red_f[2 * kQuantBatch + j], red_f[3 * kQuantBatch + j]));
+        const float sa = (amax == 0.0f) ? 0.0f : 127.0f / amax;
+        const int ldq = padded_q_row(P.Kp), nvec = P.K / 8;
+        int8_t* qrow = q_lds + off;
+        const bool store = P.q_out != nullptr && t_begin <= P.tile0;
+#pragma unroll
+        for (int i = 0; i < kQuantVecs; ++i) {
+            const int vi = tid + i * kThreads;
+            if (vi >= ldq / 8) continue;
+            uint32_t lo = 0, hi = 0;
+            if (vi < nvec) {
+                const u32x4 w = raw[j][i];
+                const float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                                    bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int c = static_cast<int>(fminf(fmaxf(rne(v[e] * sa), -128.0f), 127.0f));
+                    sums[j] += c;
+                    const uint32_t byte = static_cast<uint32_t>(c) & 0xFFu;
+                    if (e < 4) lo |= byte << (8 * e);
+                    else hi |= byte << (8 * (e - 4));
+                }
+            }
+            *reinterpret_cast<uint32_t*>(qrow + perm_pos(8 * vi)) = lo;
+            *reinterpret_cast<uint32_t*>(qrow + perm_pos(8 * vi + 4)) = hi;
+            if (store && vi < P.Kp / 8) gstore<u32x2>(P.q_out + 8 * vi, u32x2{lo, hi});
+        }
+        off += ldq;
+    }
+#pragma unroll
+    for (int j = 0; j < kQuantBatch; ++j) {
+        const int total = wave_sum(sums[j]);
+        if (lane == 0) red_i[wave * kQuantBatch + j] = total;
+    }
+    __syncthreads();
+    if (tid < np) {
+        const GemvProblem P = ps.get(p0 + tid);
+        const float amax = fmaxf(fmaxf(red_f[tid], red_f[kQuantBatch + tid]),
+                                 fmaxf(red_f[2 * kQuantBatch + tid], red_f[3 * kQuantBatch + tid]));
+        const int total = red_i[tid] + red_i[kQuantBatch + tid] + red_i[2 * kQuantBatch + tid] +
+                          red_i[3 * kQuantBatch + tid];
+        const float as = amax == 0.0f ? 0.0f : amax / 127.0f;
+        as_lds[16 * tid] = as;
+        rs_lds[16 * tid] = total;
+        if (P.q_out != nullptr && t_begin <= P.tile0) {
+            gstore<float>(P.a_scale_out, as);
+            gstore<int32_t>(P.rowsum_out, total);
+        }
+    }
+    __syncthreads();                    // red_f / red_i are reused by the next batch
+}
+
 // ---------------------------------------------------------------- streaming kernel
 //
 // Same work split, tiles and MFMA arithmetic as the persistent kernel, with a
@@ -646,12 +754,19 @@ __shared__ __attribute__((aligned(1024))) int8_t g_stream_ring[kDepth * kThreads
 
 // Token rows of the workgroup's problems, then the w_scale of its rows: a
 // static array sized to the workgroup's LDS share.
-constexpr int kStreamStaticOther = 2 * 4 * kStreamMaxProblems * 16 + 2 * 4 * kWaves + 8 * kWaves;
+constexpr int kStreamStaticOther = 2 * 4 * kStreamMaxProblems * 16 + 2 * 4 * kWaves + 8 * kWaves + 2 * 4 * kWaves * 4;
 constexpr int kStreamQBytes = (160 * 1024 / BITNET_STREAM_PER_CU - kDepth * kThreads * 16 - kStreamStaticOther - 256) / 256 * 256;
 static_assert(kStreamQBytes >= 8192, "streaming kernel: too little LDS left for token rows");
 static_assert(kThreads * 16 == 4096 && kDepth % 2 == 0, "ring slot stride and pairs of steps");
 static_assert(kBatch % 2 == 0, "token rows must be zero padded to whole pairs of k steps");
 __shared__ __attribute__((aligned(16))) int8_t g_stream_q[kStreamQBytes];
+
+// Per-256-block weight scales ride the ring too: per step each lane DMAs the
+// 4-byte scale of its row into a second ring (kThreads floats per slot), so
+// the block-scaled kernel keeps kDepth KB less for token rows.
+constexpr int kStreamQBytesBlocked = kStreamQBytes - kDepth * kThreads * 4;
+__shared__ __attribute__((aligned(1024))) float g_stream_bs_ring[kDepth * kThreads];
+__shared__ __attribute__((aligned(16))) int8_t g_stream_q_blocked[kStreamQBytesBlocked];
 
 template <int kVm>
 __device__ __forceinline__ void wait_vm() {     // s_waitcnt vmcnt(kVm), other counters untouched
@@ -743,15 +858,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t packed_rsrc(const GemvProblem&
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.packed), 0, p.N * (p.Kp / 4), kRsrcWord3);
 }
 
-template <bool kFused, bool kGrouped, bool kXBf16, bool kOutBf16>
+// Block scales [nb][N] of a block-scaled problem (held in w_scale).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_scale_rsrc(const GemvProblem& p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.w_scale), 0,
+                                             (p.K + 255) / 256 * p.N * static_cast<int>(sizeof(float)), kRsrcWord3);
+}
+
+//
+// kBlocked: weights with one scale per 256-weight block of a row ("BitVLA --
+// 1.58-bit Vision-Language-Action on Core AI", s2: the sibling matvec kernel's
+// per-256-block scales); the problem's w_scale points to block_scale [nb][N].
+// A k step is exactly one block.  Per step the unscaled fields of the codes u
+// give sum q*u and an all-ones B operand gives sum q over the same k, so their
+// difference is the exact int32 block sum of q*t; it is scaled by the block's
+// scale (DMA'd with the codes) and added to fp32 totals in block order, and
+// the outputs are y = total * a_scale.
+template <bool kFused, bool kGrouped, bool kXBf16, bool kOutBf16, bool kBlocked = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITNET_STREAM_PER_CU)))
 void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ table,
                         const int32_t* __restrict__ bounds, int count, int total_tiles, int64_t total_steps,
                         int n_first) {
-    int8_t* const q_lds = g_stream_q;                   // the workgroup's problems' token rows
+    int8_t* const q_lds = kBlocked ? g_stream_q_blocked : g_stream_q;   // the problems' token rows
     __shared__ float red_f[kWaves];
     __shared__ int red_i[kWaves];
     __shared__ double red_d[kWaves];
+    __shared__ float red_fb[kWaves * kQuantBatch];
+    __shared__ int red_ib[kWaves * kQuantBatch];
     __shared__ __attribute__((aligned(16))) float as_lds[kStreamMaxProblems * 16];
     __shared__ __attribute__((aligned(16))) int rs_lds[kStreamMaxProblems * 16];
 
@@ -774,25 +906,42 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     __amdgpu_buffer_rsrc_t rsrc = packed_rsrc(PP);
     int tp = t_begin, sp = 0, steps_p = stream_steps(PP.Kp), chunks_p = PP.Kp / 64, slot_p = 0;
     uint32_t rowoff = static_cast<uint32_t>(((tp - PP.tile0) * 64 + wave * 16 + col) * (PP.Kp / 4) + 16 * grp);
+    // kBlocked: the lane's row and the buffer of the problem's block scales
+    int row_p = (tp - PP.tile0) * 64 + wave * 16 + col, nb_p = (PP.K + 255) / 256;
+    __amdgpu_buffer_rsrc_t bs_rsrc = kBlocked ? block_scale_rsrc(PP) : rsrc;
+    float* const bs_ring = g_stream_bs_ring + wave * kWave;   // slot j of this wave: bs_ring + j * kThreads
     auto produce = [&]() {
         // chunks past the row (padding steps) read nothing
         const uint32_t off = tp < t_end && 4 * sp + grp < chunks_p ? rowoff + 64u * static_cast<uint32_t>(sp)
                                                                    : kStreamOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(ring + slot_p * kThreads * 16), 16, off, 0, 0, 0);
+        if constexpr (kBlocked) {
+            // block sp of the lane's row (zero past the last block and past N)
+            const uint32_t soff = tp < t_end && sp < nb_p && row_p < PP.N
+                                      ? static_cast<uint32_t>((sp * PP.N + row_p) * 4)
+                                      : kStreamOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lds_ptr_t)(bs_ring + slot_p * kThreads), 4, soff, 0,
+                                                     0, 0);
+        }
         slot_p = slot_p + 1 == kDepth ? 0 : slot_p + 1;
         if (tp < t_end && ++sp == steps_p) {
             sp = 0;
             ++tp;
             rowoff += static_cast<uint32_t>(64 * (PP.Kp / 4));
+            row_p += 64;
             if (tp < t_end && tp == PP.tile0 + PP.ntiles) {
                 PP = ps.get(++pp);
                 rsrc = packed_rsrc(PP);
+                if constexpr (kBlocked) bs_rsrc = block_scale_rsrc(PP);
                 steps_p = stream_steps(PP.Kp);
                 chunks_p = PP.Kp / 64;
                 rowoff = static_cast<uint32_t>((wave * 16 + col) * (PP.Kp / 4) + 16 * grp);
+                row_p = wave * 16 + col;
+                nb_p = (PP.K + 255) / 256;
             }
         }
     };
+    constexpr int kDmaPerStep = kBlocked ? 2 : 1;
     // The ring holds kDepth steps: before the pass over steps (k, k+1) the
     // producer has issued up to step k + kDepth - 3, and the pass issues
     // k + kDepth - 2 and k + kDepth - 1 into the slots of k - 2 and k - 1,
@@ -811,7 +960,7 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
             q_bytes += Pi.M * padded_q_row(Pi.Kp);
         }
         int8_t* ws_lds = q_lds + q_bytes;
-        for (int pi = p_first; pi <= p_last; ++pi) {
+        for (int pi = p_first; pi <= p_last && !kBlocked; ++pi) {
             const GemvProblem Pi = ps.get(pi);
             const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<float*>(Pi.w_scale), 0, Pi.N * static_cast<int>(sizeof(float)), kRsrcWord3);
@@ -822,15 +971,25 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
                     static_cast<uint32_t>(((t - Pi.tile0) * 64 + lane) * sizeof(float)), 0, 0, 0);
         }
         int off = 0;
-        for (int pi = p_first; pi <= p_last; ++pi) {
-            const GemvProblem Pi = ps.get(pi);
-            const int j = pi - p_first;
-            if constexpr (kFused)
-                quantise_tokens<kXBf16, 2, true>(Pi, q_lds + off, as_lds + 16 * j, rs_lds + 16 * j, red_f, red_i, red_d,
-                                                 Pi.q_out != nullptr && t_begin <= Pi.tile0);
-            else
-                stage_tokens(Pi, q_lds + off, as_lds + 16 * j, rs_lds + 16 * j);
-            off += Pi.M * padded_q_row(Pi.Kp);
+        if (kFused && kXBf16 && quantise_batch_ok(ps, p_first, p_last)) {
+            // single tokens without a norm: up to kQuantBatch problems per pass
+            for (int pi = p_first; pi <= p_last; pi += kQuantBatch) {
+                const int np = min(kQuantBatch, p_last - pi + 1);
+                quantise_batch(ps, pi, np, q_lds + off, as_lds + 16 * (pi - p_first), rs_lds + 16 * (pi - p_first),
+                               red_fb, red_ib, t_begin);
+                for (int j = 0; j < np; ++j) off += padded_q_row(ps.get(pi + j).Kp);
+            }
+        } else {
+            for (int pi = p_first; pi <= p_last; ++pi) {
+                const GemvProblem Pi = ps.get(pi);
+                const int j = pi - p_first;
+                if constexpr (kFused)
+                    quantise_tokens<kXBf16, 2, true>(Pi, q_lds + off, as_lds + 16 * j, rs_lds + 16 * j, red_f, red_i,
+                                                     red_d, Pi.q_out != nullptr && t_begin <= Pi.tile0);
+                else
+                    stage_tokens(Pi, q_lds + off, as_lds + 16 * j, rs_lds + 16 * j, !kBlocked);
+                off += Pi.M * padded_q_row(Pi.Kp);
+            }
         }
         // Every wave's DMAs so far (ring and w_scale) have landed once its own
         // vmcnt drains (long done where the wave had token loads, since loads
@@ -859,6 +1018,8 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     v4i acc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[f] = v4i{0, 0, 0, 0};
+    float total[4] = {0.0f, 0.0f, 0.0f, 0.0f};           // kBlocked: fp32 sums of scaled block sums
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
     v4i a[2][4];                                        // zero where the lane has no token
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -869,13 +1030,33 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     while (true) {
         produce();
         produce();
-        wait_vm<kDepth - 2>();                          // both steps' ring loads have landed
+        wait_vm<kDmaPerStep * (kDepth - 2)>();          // both steps' ring loads have landed
         u32x4 w[2];
         lds_read_ring2(ring + slot_c * kThreads * 16 + 16 * lane, w[0], w[1]);
+        float bsc[2] = {0.0f, 0.0f};
+        if constexpr (kBlocked) {
+            bsc[0] = lds_read_f32(bs_ring + slot_c * kThreads + lane);
+            bsc[1] = lds_read_f32(bs_ring + (slot_c + 1) * kThreads + lane);
+        }
         slot_c = slot_c + 2 == kDepth ? 0 : slot_c + 2;
         if (m_ok) lds_read_a2(abase + 256 * sc, a);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 2 && kBlocked; ++i) {
+            const u32x4 v = w[i];
+            v4i su = {0, 0, 0, 0}, sq = {0, 0, 0, 0};
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const v4i bf = {int((v.x >> (2 * f)) & 0x03030303u), int((v.y >> (2 * f)) & 0x03030303u),
+                                int((v.z >> (2 * f)) & 0x03030303u), int((v.w >> (2 * f)) & 0x03030303u)};
+                su = mfma16(a[i][f], bf, su);          // sum q * u over the block
+                sq = mfma16(a[i][f], ones, sq);        // sum q over the block
+            }
+            // block order, fp32: total = total + (float)(exact block sum) * scale
+#pragma unroll
+            for (int r = 0; r < 4; ++r) total[r] = total[r] + static_cast<float>(su[r] - sq[r]) * bsc[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 2 && !kBlocked; ++i) {
             const u32x4 v = w[i];
             const v4i b0 = {int(v.x & 0x03030303u), int(v.y & 0x03030303u), int(v.z & 0x03030303u),
                             int(v.w & 0x03030303u)};
@@ -902,13 +1083,19 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
             for (int r = 0; r < 4; ++r) {
                 const int m = 4 * grp + r;
                 if (m < P.M) {
-                    const int32_t sum_qu = acc[0][r] + (acc[1][r] >> 2) + (acc[2][r] >> 4) + (acc[3][r] >> 5);
-                    lds_write_i32(out_lds + m * wg_rows + row, sum_qu - static_cast<int32_t>(rs4[r]));
+                    if constexpr (kBlocked) {
+                        lds_write_i32(out_lds + m * wg_rows + row, __float_as_int(total[r]));
+                    } else {
+                        const int32_t sum_qu = acc[0][r] + (acc[1][r] >> 2) + (acc[2][r] >> 4) + (acc[3][r] >> 5);
+                        lds_write_i32(out_lds + m * wg_rows + row, sum_qu - static_cast<int32_t>(rs4[r]));
+                    }
                 }
             }
         }
 #pragma unroll
         for (int f = 0; f < 4; ++f) acc[f] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) total[r] = 0.0f;
         if (++tc == t_end) break;
         if (tc == P.tile0 + P.ntiles) {
             qoff += P.M * padded_q_row(P.Kp);
@@ -933,7 +1120,15 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
             const int n = (t0 - Pi.tile0) * 64 + rr;
             if (n >= Pi.N) continue;
             const int lrow = (t0 - t_begin) * 64 + rr;
-            store_output<kOutBf16>(Pi, m, n, out_lds[m * wg_rows + lrow], as_lds[16 * j + m], ws_lds[lrow]);
+            if constexpr (kBlocked) {
+                const float v = __int_as_float(out_lds[m * wg_rows + lrow]) * as_lds[16 * j + m];
+                if constexpr (kOutBf16)
+                    gstore<uint16_t>(static_cast<uint16_t*>(Pi.y) + m * Pi.ldy + n, f32_to_bf16(v));
+                else
+                    gstore<float>(static_cast<float*>(Pi.y) + m * Pi.ldy + n, v);
+            } else {
+                store_output<kOutBf16>(Pi, m, n, out_lds[m * wg_rows + lrow], as_lds[16 * j + m], ws_lds[lrow]);
+            }
         }
     }
 }
@@ -1231,7 +1426,7 @@ const int32_t* stream_bounds_of(const GemvProblem* table, int count) {
 // problem) stays within `cap` and whose token rows, w_scale and exact sums
 // fit the LDS array.  Returns the end tile.
 int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_tiles, double cap, double rate,
-                   int token_bytes) {
+                   int token_bytes, int64_t q_limit) {
     if (i >= total_tiles) return i;
     int p = host_find_problem(t, count, i);
     double cost = 0.0;
@@ -1244,7 +1439,7 @@ int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_til
         const int64_t tile_bytes = 64 * static_cast<int64_t>(sizeof(float)) * (1 + P.M);
         const int64_t left = P.tile0 + P.ntiles - i;
         const double room = cap - cost - enter;
-        const int64_t lds_room = kStreamQBytes - bytes - enter_bytes;
+        const int64_t lds_room = q_limit - bytes - enter_bytes;
         if (room < tile_cost || lds_room < tile_bytes) break;
         const int64_t k = std::min<int64_t>(left, std::min<int64_t>(static_cast<int64_t>(room / tile_cost),
                                                                      lds_room / tile_bytes));
@@ -1263,13 +1458,13 @@ int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_til
 // BITNET_STREAM_FIRST_WEIGHT percent as fast as the rest.  False if no cost
 // covers every tile within the LDS limits.
 bool stream_bounds(const GemvProblem* t, int count, int64_t total_tiles, int grid, int n_first, int token_bytes,
-                   std::vector<int32_t>& bounds) {
+                   int64_t q_limit, std::vector<int32_t>& bounds) {
     auto cover = [&](double cap, bool keep) {
         int64_t i = 0;
         for (int b = 0; b < grid; ++b) {
             if (keep) bounds[b] = static_cast<int32_t>(i);
             const double rate = b < n_first ? BITNET_STREAM_FIRST_WEIGHT / 100.0 : 1.0;
-            i = fill_share(t, count, i, total_tiles, cap, rate, token_bytes);
+            i = fill_share(t, count, i, total_tiles, cap, rate, token_bytes, q_limit);
         }
         if (keep) bounds[grid] = static_cast<int32_t>(i);
         return i >= total_tiles;
@@ -1288,10 +1483,10 @@ bool stream_bounds(const GemvProblem* t, int count, int64_t total_tiles, int gri
     return cover(hi, true);
 }
 
-template <bool kFused, bool kGrouped, bool XB, bool YB>
+template <bool kFused, bool kGrouped, bool XB, bool YB, bool kBlocked = false>
 hipError_t launch_stream_t(const GemvProblem& single, const GemvProblem* table, int count, int64_t total_tiles,
                            int64_t total_steps, int grid, size_t lds, hipStream_t stream) {
-    auto kern = gemv_stream_kernel<kFused, kGrouped, XB, YB>;
+    auto kern = gemv_stream_kernel<kFused, kGrouped, XB, YB, kBlocked>;
     const int32_t* bounds = kGrouped ? stream_bounds_of(table, count) : nullptr;
     kern<<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds, stream>>>(
         single, table, bounds, count, static_cast<int>(total_tiles), total_steps, stream_first(grid));
@@ -1345,7 +1540,8 @@ int64_t gemv_group_steps(int64_t Kp) {          // batches of kBatch k steps per
 }
 
 bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_tiles, int64_t total_steps,
-                      int* grid_out, size_t* lds_out, int token_bytes, std::vector<int32_t>* bounds) {
+                      int* grid_out, size_t* lds_out, int token_bytes, std::vector<int32_t>* bounds, bool blocked) {
+    const int64_t q_limit = blocked ? kStreamQBytesBlocked : kStreamQBytes;
     const int grid = static_cast<int>(std::min<int64_t>(std::min(stream_grid(), kMaxStreamGrid), total_tiles));
     if (grid <= 0 || count <= 0) return false;
     // buffer offsets are 32-bit: every problem's padded rows must stay below 2 GiB
@@ -1354,7 +1550,8 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
             return false;
     const int n_first = stream_first(grid);
     // grouped: balanced shares (built to fit; the loop below checks them)
-    if (bounds && !stream_bounds(host_table, count, total_tiles, grid, n_first, token_bytes, *bounds)) return false;
+    if (bounds && !stream_bounds(host_table, count, total_tiles, grid, n_first, token_bytes, q_limit, *bounds))
+        return false;
     // the shares must tile [0, total_tiles) in order, and the token rows of
     // each workgroup's problems must fit the static array
     size_t need = 0;
@@ -1379,7 +1576,7 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
             bytes += static_cast<size_t>(host_table[i].M) * padded_q_row(host_table[i].Kp) * token_bytes;
         need = std::max(need, bytes);
     }
-    if (need > static_cast<size_t>(kStreamQBytes) || covered != total_tiles) return false;
+    if (need > static_cast<size_t>(q_limit) || covered != total_tiles) return false;
     *grid_out = grid;
     *lds_out = 0;                                       // all of the kernel's LDS is static
     return true;
@@ -1418,6 +1615,30 @@ hipError_t launch_gemv_fused(const GemvProblem& p, bool x_bf16, bool y_bf16, hip
                                               y_bf16, stream);
     }
     return launch_splitk<true>(p, static_cast<size_t>(p.M) * p.Kp, x_bf16, y_bf16, stream);
+}
+
+hipError_t launch_gemv_blocked(const GemvProblem& p, bool y_bf16, hipStream_t stream) {
+    int64_t tiles = 0, steps = 0;
+    const GemvProblem g = as_group_of_one(p, tiles, steps);
+    int grid = 0;
+    size_t lds = 0;
+    if (!gemv_stream_plan(&g, 1, tiles, steps, &grid, &lds, 1, nullptr, true)) return hipErrorInvalidValue;
+    return y_bf16 ? launch_stream_t<false, false, true, true, true>(g, nullptr, 1, tiles, steps, grid, lds, stream)
+                  : launch_stream_t<false, false, true, false, true>(g, nullptr, 1, tiles, steps, grid, lds, stream);
+}
+
+hipError_t launch_gemv_blocked_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,
+                                       int64_t total_steps, int grid, bool x_bf16, bool y_bf16, hipStream_t stream) {
+    GemvProblem none{};
+    if (x_bf16)
+        return y_bf16 ? launch_stream_t<true, true, true, true, true>(none, table_dev, count, total_tiles, total_steps,
+                                                                      grid, 0, stream)
+                      : launch_stream_t<true, true, true, false, true>(none, table_dev, count, total_tiles,
+                                                                       total_steps, grid, 0, stream);
+    return y_bf16 ? launch_stream_t<true, true, false, true, true>(none, table_dev, count, total_tiles, total_steps,
+                                                                   grid, 0, stream)
+                  : launch_stream_t<true, true, false, false, true>(none, table_dev, count, total_tiles, total_steps,
+                                                                    grid, 0, stream);
 }
 
 hipError_t launch_gemv_a16_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,

@@ -107,3 +107,73 @@ def test_blocked_full_size(orc, proj):
     assert np.array_equal(pb.packed.cpu().numpy(), ref["packed"])
     assert np.array_equal(pb.block_scale.cpu().numpy().view(np.uint32), ref["block_scale"].view(np.uint32))
     assert np.array_equal(bits(y), ref["y"])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 2560, 2560), (1, 640, 6912), (1, 13824, 2560), (2, 257, 400), (3, 130, 8192),
+                                   (16, 100, 2048), (1, 33, 16), (4, 2560, 6912)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_blocked_decode(orc, M, N, K, out):
+    """Decode sizes (M <= 16) of the block-scaled linear run on the streaming
+    kernel: bit-exact against the oracle, incl. a partial last block (K = 400),
+    27 blocks (K = 6912), the largest K (8192), ragged N and N < 64."""
+    x, W = blocked_case(M * 17 + N + K, M, N, K, zero_blocks=(K > 512))
+    ref = orc.linear_blocked(bits(x), bits(W), out=out)
+    pw = tw.pack_blocked(W.to(DEV))
+    q, a, _ = tw.act_quant(x.to(DEV))
+    ybuf = torch.full((M, N + 8), float("nan"), device=DEV,
+                      dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    y = tw.linear_blocked(q, a, pw, out=ybuf[:, :N])
+    assert np.array_equal(bits(y).view(np.uint32 if out == "f32" else np.uint16),
+                          ref["y"].view(np.uint32) if out == "f32" else ref["y"])
+    assert torch.isnan(ybuf[:, N:].float()).all()
+
+
+@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_blocked_grouped(orc, M, out):
+    """A decoder layer's projections (and a few ragged ones) with block-scaled
+    weights in one grouped launch, tokens quantised in the launch; every output
+    bit-exact against the oracle, on two launches of the same plan."""
+    shapes = [(2560, 2560), (640, 2560), (640, 2560), (2560, 2560), (6912, 2560), (6912, 2560), (2560, 6912),
+              (130, 1152), (33, 400)]
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    items, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        x, W = blocked_case(700 + i, M, N, K, zero_blocks=(i % 3 == 0 and K > 512))
+        refs.append(orc.linear_blocked(bits(x), bits(W), out=out)["y"])
+        items.append((x.to(DEV), tw.pack_blocked(W.to(DEV)), torch.full((M, N), float("nan"), device=DEV, dtype=dt)))
+    group = tw.GroupedBitLinear(items)
+    assert group.kernel == "stream-blocked"
+    for rep in range(2):
+        for _, _, y in items:
+            y.fill_(float("nan"))
+        group()
+        torch.cuda.synchronize()
+        for j, ((_, _, y), ref) in enumerate(zip(items, refs)):
+            got = bits(y)
+            assert np.array_equal(got.view(np.uint32) if out == "f32" else got,
+                                  ref.view(np.uint32) if out == "f32" else ref), (rep, j)
+
+
+def test_blocked_grouped_decode_30_layers(orc):
+    """The BitNet-b1.58-2B-shaped decode stream (30 layers x 7 projections,
+    M = 1) with per-256-block weight scales in one grouped launch, every output
+    against the oracle."""
+    from concurrent.futures import ThreadPoolExecutor
+    w = wl.WORKLOADS["c2"]
+    items, host = [], []
+    for layer in range(w.layers):
+        for i, p in enumerate(w.projections):
+            W = wl.weight_for(w, i, layer=layer, device=DEV)
+            x = wl.activation_for(w, i, layer=layer, device=DEV)
+            items.append((x, tw.pack_blocked(W), torch.full((1, p.N), float("nan"), device=DEV)))
+            host.append((bits(W), bits(x)))
+            del W
+    group = tw.GroupedBitLinear(items)
+    print(f"[case] blocked c2 grouped 210 items, kernel {group.kernel}", flush=True)
+    group()
+    torch.cuda.synchronize()
+    with ThreadPoolExecutor(max_workers=16) as pool:
+        refs = list(pool.map(lambda hw: orc.linear_blocked(hw[1], hw[0])["y"], host))
+    for j, ((_, _, y), ref) in enumerate(zip(items, refs)):
+        assert np.array_equal(bits(y).view(np.uint32), ref.view(np.uint32)), j
