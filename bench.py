@@ -250,7 +250,13 @@ def bench_a16(tw, wl, torch, steps, warmup):
                           roofline=dict(bound="hbm", achieved=gbps_g, peak=HBM_PEAK_GBPS, unit="GB/s",
                                         frac=gbps_g / HBM_PEAK_GBPS,
                                         traffic=traffic_from_profile("decode_a16_bitnet2b_30_layers_m1", src)))
-    del g, group, items
+    # the same group with fp16 activations (fp16 matrix cores)
+    items16 = [(x.to(torch.float16), pw, y) for x, pw, y in items]
+    group16 = tw.GroupedBitLinear(items16, a16=True)
+    ms16 = time_region(torch, group16, steps, warmup)
+    out["grouped_fp16"] = dict(value=nbytes / (ms16 * 1e-3) / 1e9, unit="GB/s", ms_per_step=ms16,
+                               kernel=group16.kernel, launches_per_step=1, activations="float16")
+    del g, group, group16, items, items16
     torch.cuda.empty_cache()
     W = wl.draw_weight((13824, 2560), seed=3, device="cuda")
     pw = tw.pack(W)

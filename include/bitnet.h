@@ -85,6 +85,7 @@ typedef enum {
 typedef enum {
     BITNET_F32 = 0,
     BITNET_BF16 = 1,
+    BITNET_F16 = 2,              /* IEEE binary16: W1.58A16 activations only */
     BITNET_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
     BITNET_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
 } bitnet_dtype_t;
@@ -325,6 +326,12 @@ bitnet_status_t bitnet_group_plan_a16(hipStream_t stream, const bitnet_group_ite
                                       int64_t M, bitnet_dtype_t y_dtype, void* table_dev, int64_t table_bytes,
                                       bitnet_group_plan_t* plan);
 
+/* bitnet_group_plan_a16 with fp16 activations x (fp16 matrix cores; the same
+ * bound as bitnet_linear_a16). */
+bitnet_status_t bitnet_group_plan_a16_fp16(hipStream_t stream, const bitnet_group_item_t* items, int32_t count,
+                                           int64_t M, bitnet_dtype_t y_dtype, void* table_dev, int64_t table_bytes,
+                                           bitnet_group_plan_t* plan);
+
 /*
  * Grouped decode with per-256-block weight scales [BitVLA s2]: items as for
  * bitnet_group_plan, except that each item's w_scale points to its
@@ -362,11 +369,13 @@ const char* bitnet_group_plan_kernel(const bitnet_group_plan_t* plan);
  * stalled the GPU, activations stayed in 16 bits]:
  * y[m][n] = w_scale[n] * sum_k x[m][k] * t[n][k], x bf16 [M, K] (row stride
  * ldx, rows 16-byte aligned), packed / w_scale as for bitnet_linear_forward,
- * y fp32 or bf16 [M, N] (ldy).  The sum runs in fp32 on the matrix cores in
- * the hardware's order: |y - exact| <= w_scale[n] * (K/32 + 64) * 2^-24 *
- * sum_k |x[m][k] * t[n][k]| (+ the bf16 rounding for bf16 y).  A decode-size
- * kernel: every 16 tokens re-read the packed weight.  Errors: UNSUPPORTED for
- * a non-bf16 x; INVALID_ARG as bitnet_linear_forward; HIP.
+ * y fp32 or bf16 [M, N] (ldy).  x may also be fp16 (x_dtype BITNET_F16; the
+ * path kept 16-bit activations, and both 16-bit formats widen exactly); the
+ * sum then runs on fp16 matrix cores.  The sum runs in fp32 on the matrix
+ * cores in the hardware's order: |y - exact| <= w_scale[n] * (K/32 + 64) *
+ * 2^-24 * sum_k |x[m][k] * t[n][k]| (+ the bf16 rounding for bf16 y).  A
+ * decode-size kernel: every 16 tokens re-read the packed weight.  Errors:
+ * UNSUPPORTED for fp32 x; INVALID_ARG as bitnet_linear_forward; HIP.
  */
 bitnet_status_t bitnet_linear_a16(hipStream_t stream, const void* x, bitnet_dtype_t x_dtype,
                                   int64_t M, int64_t K, int64_t ldx,

@@ -84,7 +84,8 @@
  * 8-bit activation quantiser stalled the GPU, the path kept the activations
  * in 16-bit and quantised only the weights]:
  *   R17 y[m][n] = w_scale[n] * sum_k x[m][k] * t[n][k] with the activations
- *       as given; the oracle evaluates it in fp64 (each product exact, one
+ *       as given (bf16 or fp16, the two 16-bit formats the path may keep;
+ *       both widen to fp32 exactly); the oracle evaluates it in fp64 (each product exact, one
  *       rounding per addition, k ascending) -- the reference value that a
  *       kernel summing in fp32, in its own order, is held to within a bound.
  *
@@ -114,7 +115,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2 };
 
 /* ---------------------------------------------------------------- scalars */
 
@@ -125,6 +126,22 @@ float orc_bf16_to_f32(uint16_t h)
     float f;
     memcpy(&f, &bits, sizeof f);
     return f;
+}
+
+/* IEEE binary16 -> fp32, exact: 1 sign bit, 5 exponent bits (bias 15), 10
+ * fraction bits; exponent 0 holds zero and the subnormals f * 2^-24,
+ * exponent 31 infinities (f = 0) and NaNs. */
+float orc_f16_to_f32(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 0x1F, f = h & 0x3FF;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(1024 + f), e - 25);
+    return sign ? -v : v;
 }
 
 /* fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN. */
@@ -155,6 +172,8 @@ static float load_elem(const void* base, int dtype, int64_t idx)
 {
     if (dtype == ORC_BF16)
         return orc_bf16_to_f32(((const uint16_t*)base)[idx]);
+    if (dtype == ORC_F16)
+        return orc_f16_to_f32(((const uint16_t*)base)[idx]);
     return ((const float*)base)[idx];
 }
 

@@ -22,7 +22,7 @@ HERE = Path(__file__).resolve().parent
 SOURCE = HERE / "bitnet_oracle.c"
 LIBRARY = HERE / "liboracle.so"
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
           "-shared", "-fopenmp", "-Wall", "-Wextra"]
 
@@ -59,7 +59,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.float32:
         return F32
-    raise TypeError(f"oracle inputs are bf16 bit patterns (uint16) or float32, not {a.dtype}")
+    if a.dtype == np.float16:
+        return F16                      # passed as its bit patterns; widened by orc_f16_to_f32
+    raise TypeError(f"oracle inputs are bf16 bit patterns (uint16), float16 or float32, not {a.dtype}")
 
 
 class Oracle:
@@ -75,6 +77,7 @@ class Oracle:
         lib = ctypes.CDLL(str(path))
         i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
         lib.orc_bf16_to_f32.argtypes, lib.orc_bf16_to_f32.restype = [ctypes.c_uint16], f32
+        lib.orc_f16_to_f32.argtypes, lib.orc_f16_to_f32.restype = [ctypes.c_uint16], f32
         lib.orc_f32_to_bf16.argtypes, lib.orc_f32_to_bf16.restype = [f32], ctypes.c_uint16
         lib.orc_f32_to_bf16_array.argtypes, lib.orc_f32_to_bf16_array.restype = [vp, i64, vp], None
         lib.orc_padded_k.argtypes, lib.orc_padded_k.restype = [i64], i64

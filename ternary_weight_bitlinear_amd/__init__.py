@@ -23,6 +23,7 @@ __all__ = ["BitnetError", "PackedWeight", "padded_k", "packed_bytes", "pack", "a
            "linear", "bitlinear", "GroupedBitLinear", "library_path"]
 
 _DT = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+_DT_A16 = {torch.bfloat16: _lib.BF16, torch.float16: _lib.F16}     # W1.58A16 activations
 
 
 def library_path() -> str:
@@ -343,7 +344,7 @@ def bitlinear(x: torch.Tensor, w: PackedWeight, out_dtype=torch.float32, out: to
 
 
 def linear_a16(x: torch.Tensor, w: PackedWeight, out_dtype=torch.float32, out: torch.Tensor | None = None):
-    """W1.58A16: y = w_scale * (x . t) with bf16 activations x [M, K] kept unquantised."""
+    """W1.58A16: y = w_scale * (x . t) with bf16 or fp16 activations x [M, K] kept unquantised."""
     ldx = _rows(x, "x")
     M, K = x.shape
     if K != w.K:
@@ -353,7 +354,8 @@ def linear_a16(x: torch.Tensor, w: PackedWeight, out_dtype=torch.float32, out: t
     ldy = _output(y, M, w.N)
     _on_device(x.device, x=x, packed=w.packed, w_scale=w.w_scale, out=y)
     with torch.cuda.device(x.device):
-        _lib.check(_lib.lib().bitnet_linear_a16(_stream(x), x.data_ptr(), _dtype(x), M, K, ldx, w.packed.data_ptr(),
+        _lib.check(_lib.lib().bitnet_linear_a16(_stream(x), x.data_ptr(), _DT_A16.get(x.dtype, _lib.F32), M, K, ldx,
+                                                w.packed.data_ptr(),
                                                 w.w_scale.data_ptr(), w.N, y.data_ptr(), _dtype(y), ldy))
     return y
 
@@ -410,8 +412,8 @@ class GroupedBitLinear:
             raise ValueError("norms needs one entry per item")
         if a16 and norms is not None:
             raise ValueError("the W1.58A16 group takes no input norms")
-        if a16 and any(x.dtype != torch.bfloat16 for x, _, _ in items):
-            raise ValueError("the W1.58A16 group takes bf16 activations")
+        if a16 and any(x.dtype not in _DT_A16 or x.dtype != items[0][0].dtype for x, _, _ in items):
+            raise ValueError("the W1.58A16 group takes bf16 or fp16 activations, one dtype for all items")
         blocked = isinstance(items[0][1], BlockPackedWeight)
         if any(isinstance(w, BlockPackedWeight) != blocked for _, w, _ in items):
             raise ValueError("a group takes either per-tensor or per-256-block scaled weights, not both")
@@ -458,7 +460,9 @@ class GroupedBitLinear:
                     _stream(x0), ctypes.cast(arr, ctypes.c_void_p), len(items), M, _dtype(x0),
                     _dtype(items[0][2]), self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
             elif a16:
-                _lib.check(_lib.lib().bitnet_group_plan_a16(
+                plan_fn = (_lib.lib().bitnet_group_plan_a16_fp16 if x0.dtype == torch.float16
+                           else _lib.lib().bitnet_group_plan_a16)
+                _lib.check(plan_fn(
                     _stream(x0), ctypes.cast(arr, ctypes.c_void_p), len(items), M, _dtype(items[0][2]),
                     self.table.data_ptr(), nbytes, ctypes.byref(self.plan)))
             elif nrm is None:

@@ -16,7 +16,7 @@ import os
 LIBRARY = Path(os.environ.get("BITNET_LIBRARY") or Path(__file__).resolve().parent / "libbitnet_hip.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NONFINITE = range(5)
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 MEM_HOST, MEM_DEVICE = 0, 1
 I2S_STRIDED, I2S_CONSECUTIVE = 0, 1
 
@@ -45,6 +45,7 @@ SIGNATURES = {
     "bitnet_group_plan_rmsnorm": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, ctypes.c_int, ctypes.c_int, _vp, _i64,
                                                  _vp]),
     "bitnet_group_plan_a16": (ctypes.c_int, [_vp, _vp, _i32, _i64, ctypes.c_int, _vp, _i64, _vp]),
+    "bitnet_group_plan_a16_fp16": (ctypes.c_int, [_vp, _vp, _i32, _i64, ctypes.c_int, _vp, _i64, _vp]),
     "bitnet_group_plan_blocked": (ctypes.c_int, [_vp, _vp, _i32, _i64, ctypes.c_int, ctypes.c_int, _vp, _i64,
                                                  _vp]),
     "bitnet_bitlinear_grouped": (ctypes.c_int, [_vp, _vp]),

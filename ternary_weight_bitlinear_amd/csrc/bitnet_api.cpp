@@ -520,15 +520,16 @@ bitnet_status_t bitnet_linear_a16(hipStream_t stream, const void* x, bitnet_dtyp
     bitnet_status_t s = check_dims(fn, M, N, K);
     if (s != BITNET_OK) return s;
     if (!x || !packed || !w_scale || !y) return fail(BITNET_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
-    if (x_dtype != BITNET_BF16)
-        return fail(BITNET_ERR_UNSUPPORTED, "%s: W1.58A16 takes bf16 activations (x_dtype %d)", fn, (int)x_dtype);
+    if (x_dtype != BITNET_BF16 && x_dtype != BITNET_F16)
+        return fail(BITNET_ERR_UNSUPPORTED, "%s: W1.58A16 takes bf16 or fp16 activations (x_dtype %d)", fn,
+                    (int)x_dtype);
     if (!valid_dtype(y_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad y dtype %d", fn, (int)y_dtype);
     if (ldx < K || ldy < N) return fail(BITNET_ERR_INVALID_ARG, "%s: ldx < K or ldy < N", fn);
     if (!aligned(x, 16) || (ldx * 2) % 16 != 0 || !aligned(packed, 16) || !aligned(w_scale, 4) ||
         !aligned(y, y_dtype == BITNET_F32 ? 4 : 2))
         return fail(BITNET_ERR_INVALID_ARG, "%s: misaligned pointer (x rows and packed must be 16-byte aligned)", fn);
     hipError_t e = bitnet::launch_gemv_a16(static_cast<const uint16_t*>(x), ldx, M, K, padded_k(K), packed, w_scale,
-                                           N, y, y_dtype == BITNET_BF16, ldy, stream);
+                                           N, y, y_dtype == BITNET_BF16, ldy, stream, x_dtype == BITNET_F16);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }
@@ -791,8 +792,9 @@ static bitnet_status_t group_plan_impl(hipStream_t stream, const bitnet_group_it
         return fail(BITNET_ERR_INVALID_ARG, "%s: table_dev must be 16-byte aligned and hold %lld bytes", fn,
                     (long long)bitnet_group_table_bytes(count));
     if (M <= 0 || M > kGemvMaxM) return fail(BITNET_ERR_INVALID_ARG, "%s: M=%lld must be in 1..16", fn, (long long)M);
-    if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return fail(BITNET_ERR_INVALID_ARG, "%s: bad dtype", fn);
-    const int64_t esize = x_dtype == BITNET_BF16 ? 2 : 4;
+    if (!(valid_dtype(x_dtype) || (a16 && x_dtype == BITNET_F16)) || !valid_dtype(y_dtype))
+        return fail(BITNET_ERR_INVALID_ARG, "%s: bad dtype", fn);
+    const int64_t esize = x_dtype == BITNET_F32 ? 4 : 2;
     std::vector<bitnet::GemvProblem> table(static_cast<size_t>(count));
     int64_t tiles = 0, steps = 0, max_kp = 0;
     for (int32_t i = 0; i < count; ++i) {
@@ -898,6 +900,13 @@ bitnet_status_t bitnet_group_plan_a16(hipStream_t stream, const bitnet_group_ite
                            "bitnet_group_plan_a16", kModeA16);
 }
 
+bitnet_status_t bitnet_group_plan_a16_fp16(hipStream_t stream, const bitnet_group_item_t* items, int32_t count,
+                                           int64_t M, bitnet_dtype_t y_dtype, void* table_dev, int64_t table_bytes,
+                                           bitnet_group_plan_t* plan) {
+    return group_plan_impl(stream, items, nullptr, count, M, BITNET_F16, y_dtype, table_dev, table_bytes, plan,
+                           "bitnet_group_plan_a16_fp16", kModeA16);
+}
+
 bitnet_status_t bitnet_group_plan_blocked(hipStream_t stream, const bitnet_group_item_t* items, int32_t count,
                                           int64_t M, bitnet_dtype_t x_dtype, bitnet_dtype_t y_dtype, void* table_dev,
                                           int64_t table_bytes, bitnet_group_plan_t* plan) {
@@ -926,7 +935,8 @@ bitnet_status_t bitnet_bitlinear_grouped(hipStream_t stream, const bitnet_group_
     const bool y_bf16 = ((plan->opaque[6] >> 8) & 0xFF) == BITNET_BF16;
     hipError_t e;
     if (kind == kGroupA16)
-        e = bitnet::launch_gemv_a16_grouped(table, count, plan->opaque[4], plan->opaque[7], grid, y_bf16, stream);
+        e = bitnet::launch_gemv_a16_grouped(table, count, plan->opaque[4], plan->opaque[7], grid, y_bf16, stream,
+                                            (plan->opaque[6] & 0xFF) == BITNET_F16);
     else if (kind == kGroupBlocked)
         e = bitnet::launch_gemv_blocked_grouped(table, count, plan->opaque[4], plan->opaque[7], grid, x_bf16, y_bf16,
                                                 stream);

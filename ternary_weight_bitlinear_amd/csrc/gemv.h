@@ -73,10 +73,11 @@ hipError_t launch_gemv_blocked(const GemvProblem& p, bool y_bf16, hipStream_t st
 hipError_t launch_gemv_blocked_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,
                                        int64_t total_steps, int grid, bool x_bf16, bool y_bf16, hipStream_t stream);
 
-// W1.58A16 grouped launch of the streaming kernel (bf16 x, no quantiser):
+// W1.58A16 grouped launch of the streaming kernel (bf16 or fp16 x, no quantiser):
 // table_dev and the grid as for launch_gemv_grouped's streaming case.
 hipError_t launch_gemv_a16_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,
-                                   int64_t total_steps, int grid, bool y_bf16, hipStream_t stream);
+                                   int64_t total_steps, int grid, bool y_bf16, hipStream_t stream,
+                                   bool x_f16 = false);
 
 // Many independent problems in one launch (ActQuant fused); table_dev is a
 // device array of `count` descriptors with tile0 / ntiles / steps / step0 set.

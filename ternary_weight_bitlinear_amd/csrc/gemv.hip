@@ -1137,10 +1137,10 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
 //
 // The grouped W1.58A16 decode ("BitVLA -- 1.58-bit Vision-Language-Action on
 // Core AI", s5: 16-bit activations with the ternary weights): the streaming
-// kernel's work split, tiles and memory pipeline, with the bf16 token rows
-// copied into LDS as given (no quantiser) and each lane's 16 bytes of codes
-// (64 k of one row) expanded into the B operands of eight
-// v_mfma_f32_16x16x32_bf16.  Lane group g of a wave takes the 16-byte chunk
+// kernel's work split, tiles and memory pipeline, with the bf16 (or, kF16,
+// fp16) token rows copied into LDS as given (no quantiser) and each lane's 16
+// bytes of codes (64 k of one row) expanded into the B operands of eight
+// v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x32_f16).  Lane group g of a wave takes the 16-byte chunk
 // 4s + g of k step s, as in the int8 kernel; its A operands are the 64
 // consecutive bf16 of the token row at the same k (128 bytes of LDS), so the
 // k order inside an MFMA differs from the int8 kernel's but pairs the same
@@ -1157,7 +1157,7 @@ __device__ __forceinline__ void lds_read128(const void* p, u32x4 (&a)[8]) {
         : "memory");
 }
 
-template <bool kGrouped, bool kOutBf16>
+template <bool kGrouped, bool kOutBf16, bool kF16 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITNET_STREAM_PER_CU)))
 void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ table,
                             const int32_t* __restrict__ bounds, int count, int total_tiles, int64_t total_steps,
@@ -1267,10 +1267,16 @@ void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ 
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[2 * j + h]),
-                                                                  __builtin_bit_cast(bf16x8, expand_bf16(words[j], h)),
-                                                                  acc, 0, 0, 0);
+                for (int h = 0; h < 2; ++h) {
+                    if constexpr (kF16)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[2 * j + h]),
+                                                                     __builtin_bit_cast(f16x8, expand_f16(words[j], h)),
+                                                                     acc, 0, 0, 0);
+                    else
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, a[2 * j + h]), __builtin_bit_cast(bf16x8, expand_bf16(words[j], h)),
+                            acc, 0, 0, 0);
+                }
         }
         sc += 2;
         if (sc < steps_c) continue;
@@ -1508,11 +1514,11 @@ hipError_t launch_stream(const GemvProblem& single, const GemvProblem* table, in
                                                            lds, stream);
 }
 
-template <bool kOutBf16>
+template <bool kOutBf16, bool kF16>
 hipError_t launch_stream_a16_t(const GemvProblem* table, int count, int64_t total_tiles, int64_t total_steps,
                                int grid, hipStream_t stream) {
     GemvProblem none{};
-    gemv_stream_a16_kernel<true, kOutBf16><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
+    gemv_stream_a16_kernel<true, kOutBf16, kF16><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream>>>(
         none, table, stream_bounds_of(table, count), count, static_cast<int>(total_tiles), total_steps,
         stream_first(grid));
     return hipGetLastError();
@@ -1642,9 +1648,12 @@ hipError_t launch_gemv_blocked_grouped(const GemvProblem* table_dev, int count, 
 }
 
 hipError_t launch_gemv_a16_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,
-                                   int64_t total_steps, int grid, bool y_bf16, hipStream_t stream) {
-    return y_bf16 ? launch_stream_a16_t<true>(table_dev, count, total_tiles, total_steps, grid, stream)
-                  : launch_stream_a16_t<false>(table_dev, count, total_tiles, total_steps, grid, stream);
+                                   int64_t total_steps, int grid, bool y_bf16, hipStream_t stream, bool x_f16) {
+    if (x_f16)
+        return y_bf16 ? launch_stream_a16_t<true, true>(table_dev, count, total_tiles, total_steps, grid, stream)
+                      : launch_stream_a16_t<false, true>(table_dev, count, total_tiles, total_steps, grid, stream);
+    return y_bf16 ? launch_stream_a16_t<true, false>(table_dev, count, total_tiles, total_steps, grid, stream)
+                  : launch_stream_a16_t<false, false>(table_dev, count, total_tiles, total_steps, grid, stream);
 }
 
 hipError_t launch_gemv_grouped(const GemvProblem* table_dev, int count, int64_t total_tiles,

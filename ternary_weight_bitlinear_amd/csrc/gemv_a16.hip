@@ -1,4 +1,4 @@
-// gemv_a16.hip -- the W1.58A16 variant: bf16 activations x ternary weights.
+// gemv_a16.hip -- the W1.58A16 variant: bf16 or fp16 activations x ternary weights.
 //
 // "BitVLA -- 1.58-bit Vision-Language-Action on Core AI", s5 (On-device
 // gotchas): where the in-graph 8-bit activation quantiser stalled the GPU,
@@ -29,7 +29,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kUnroll = 4;
 
-template <bool kOutBf16>
+// kF16: fp16 activations (v_mfma_f32_16x16x32_f16, codes expanded to fp16).
+template <bool kOutBf16, bool kF16 = false>
 __global__ __launch_bounds__(kThreads) void gemv_a16_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                             int K, int Kp, const uint8_t* __restrict__ packed,
                                                             const float* __restrict__ w_scale, int N, void* y,
@@ -68,9 +69,14 @@ __global__ __launch_bounds__(kThreads) void gemv_a16_kernel(const uint16_t* __re
                 for (int h = 0; h < 2; ++h) {
                     const int k = 64 * c + 16 * j + 8 * h;       // 8 consecutive k; K % 8 == 0
                     const u32x4 a = (m_ok && c < chunks && k < K) ? gload<u32x4>(xrow + k) : zero;
-                    const u32x4 b = expand_bf16(bw[u][j], h);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+                    if constexpr (kF16)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                                     __builtin_bit_cast(f16x8, expand_f16(bw[u][j], h)),
+                                                                     acc, 0, 0, 0);
+                    else
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                      __builtin_bit_cast(bf16x8, expand_bf16(bw[u][j], h)),
+                                                                      acc, 0, 0, 0);
                 }
             }
         }
@@ -96,14 +102,12 @@ __global__ __launch_bounds__(kThreads) void gemv_a16_kernel(const uint16_t* __re
 }  // namespace
 
 hipError_t launch_gemv_a16(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, int64_t Kp, const uint8_t* packed,
-                           const float* w_scale, int64_t N, void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
+                           const float* w_scale, int64_t N, void* y, bool y_bf16, int64_t ldy, hipStream_t stream,
+                           bool x_f16) {
     const dim3 grid(static_cast<unsigned>((N + 15) / 16), static_cast<unsigned>((M + 15) / 16)), block(kThreads);
-    if (y_bf16)
-        gemv_a16_kernel<true><<<grid, block, 0, stream>>>(x, ldx, (int)M, (int)K, (int)Kp, packed, w_scale, (int)N, y,
-                                                          ldy);
-    else
-        gemv_a16_kernel<false><<<grid, block, 0, stream>>>(x, ldx, (int)M, (int)K, (int)Kp, packed, w_scale, (int)N,
-                                                           y, ldy);
+    auto kern = x_f16 ? (y_bf16 ? gemv_a16_kernel<true, true> : gemv_a16_kernel<false, true>)
+                      : (y_bf16 ? gemv_a16_kernel<true, false> : gemv_a16_kernel<false, false>);
+    kern<<<grid, block, 0, stream>>>(x, ldx, (int)M, (int)K, (int)Kp, packed, w_scale, (int)N, y, ldy);
     return hipGetLastError();
 }
 

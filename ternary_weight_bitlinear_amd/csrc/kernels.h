@@ -80,8 +80,10 @@ hipError_t launch_gemm_blocked(const int8_t* q, const float* a_scale, int64_t M,
 
 // W1.58A16: y = w_scale * (x_bf16 . t), fp32 accumulation on bf16 MFMA; x rows
 // 16-byte aligned (ldx * 2 % 16 == 0).
+// x_f16: fp16 activations (fp16 matrix cores) instead of bf16.
 hipError_t launch_gemv_a16(const uint16_t* x, int64_t ldx, int64_t M, int64_t K, int64_t Kp, const uint8_t* packed,
-                           const float* w_scale, int64_t N, void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
+                           const float* w_scale, int64_t N, void* y, bool y_bf16, int64_t ldy, hipStream_t stream,
+                           bool x_f16 = false);
 
 // I2_S <-> layout v1 (status bits: 1 a field holds 3, 2 a scale is not
 // positive, 4 rows differ in scale on export).  The grid covers every output

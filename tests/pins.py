@@ -102,6 +102,26 @@ def pin_bf16_conversions(orc):
     assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F) != 0
 
 
+def pin_f16_widening(orc):
+    """IEEE binary16 -> fp32 against numpy's float16 (a library routine): every
+    one of the 65536 bit patterns, incl. subnormals, zeros of both signs,
+    infinities and NaNs; and fp16 activations through the W1.58A16 reference
+    equal the same values given as fp32."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = np.array([orc.lib.orc_f16_to_f32(int(b)) for b in allbits], dtype=np.float32)
+    ref = allbits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    rng = np.random.default_rng(61)
+    x16 = (rng.standard_normal((2, 48)) * 3).astype(np.float16)
+    t = rng.integers(-1, 2, size=(5, 48)).astype(np.int8)
+    ws = rng.random(5).astype(np.float32)
+    y16, m16 = orc.linear_a16(x16, t, ws)
+    y32, m32 = orc.linear_a16(x16.astype(np.float32), t, ws)
+    assert np.array_equal(y16, y32) and np.array_equal(m16, m32)
+
+
 def pin_weight_ties_golden(orc):
     g = read_golden("weight_ties.txt")
     N, K = int(g["N"][0][0]), int(g["K"][0][0])

@@ -109,6 +109,9 @@ MUTANTS = [
      "for (int64_t b = nb - 1; b >= 0; --b) {\n                int64_t k0"),
     ("block terms accumulated in fp64", "float total = 0.0f;\n            for (int64_t b = 0;",
      "double total = 0.0;\n            for (int64_t b = 0;"),
+    ("fp16 exponent bias off by one", "v = ldexpf((float)(1024 + f), e - 25);",
+     "v = ldexpf((float)(1024 + f), e - 24);"),
+    ("fp16 subnormals flushed to zero", "v = ldexpf((float)f, -24);", "v = 0.0f * (float)f;"),
     ("A16 product transposed",
      "double p = (double)load_elem(x, dtype, m * ldx + k) * (double)t[n * K + k];",
      "double p = (double)load_elem(x, dtype, m * ldx + k) * (double)t[(k % N) * K + (n % K)];"),

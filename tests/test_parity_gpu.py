@@ -387,16 +387,18 @@ def test_i2s_device_rejects_bad_fields():
 @pytest.mark.parametrize("M,N,K", [(1, 640, 2560), (3, 257, 1152), (16, 100, 2048), (1, 2560, 6912),
                                    (20, 130, 1152), (1, 1, 16), (2, 4352, 4304)])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
-def test_linear_a16(orc, M, N, K, out):
-    """bf16 activations x ternary weights against the oracle's fp64 value, within the
-    bound the header states for an fp32 sum in the hardware's order."""
+@pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float16])
+def test_linear_a16(orc, M, N, K, out, xdt):
+    """bf16 or fp16 activations x ternary weights against the oracle's fp64 value,
+    within the bound the header states for an fp32 sum in the hardware's order."""
     x, W = wl.random_case(5100 + M * 3 + N, M, N, K, x_dist="normal_outliers")
+    x = x.to(xdt)
     pw = tw.pack(W.to(DEV))
-    base = torch.zeros((M, K + 8), dtype=torch.bfloat16, device=DEV)
+    base = torch.zeros((M, K + 8), dtype=xdt, device=DEV)
     base[:, :K] = x.to(DEV)
     y = tw.linear_a16(base[:, :K], pw, out_dtype=out)          # ldx = K + 8: strided rows
     t, ws, _, _ = orc.weight_quant(bits(W))
-    ye, mag = orc.linear_a16(bits(x), t, ws)
+    ye, mag = orc.linear_a16(a16_bits(x), t, ws)
     tol = ws.astype(np.float64)[None, :] * (K / 32 + 64) * 2.0 ** -24 * mag
     got = y.float().cpu().numpy().astype(np.float64)
     if out == torch.bfloat16:
@@ -407,12 +409,18 @@ def test_linear_a16(orc, M, N, K, out):
     assert np.all(err <= tol), float((err / np.maximum(tol, 1e-300)).max())
 
 
+def a16_bits(x: torch.Tensor) -> np.ndarray:
+    """Activations for the oracle's W1.58A16 reference: bf16 bit patterns, or float16."""
+    x = x.detach().cpu().contiguous()
+    return x.numpy() if x.dtype == torch.float16 else bits(x)
+
+
 def _check_a16(orc, y, x, W):
     """y against the oracle's fp64 value of w_scale * (x . t), within the bound
     bitnet_linear_a16 states for an fp32 sum in the hardware's order."""
     K = x.shape[1]
     t, ws, _, _ = orc.weight_quant(bits(W))
-    ye, mag = orc.linear_a16(bits(x), t, ws)
+    ye, mag = orc.linear_a16(a16_bits(x), t, ws)
     tol = ws.astype(np.float64)[None, :] * (K / 32 + 64) * 2.0 ** -24 * mag
     tol = tol + np.abs(ye) * (2.0 ** -8 if y.dtype == torch.bfloat16 else 2.0 ** -24)
     err = np.abs(y.float().cpu().numpy().astype(np.float64) - ye)
@@ -422,15 +430,17 @@ def _check_a16(orc, y, x, W):
 @pytest.mark.parametrize("M,shapes,y_dtype", [
     (1, "group", torch.float32), (1, "group", torch.bfloat16), (3, "group", torch.float32),
     (4, "small", torch.bfloat16), (16, "tiny", torch.float32)])
-def test_grouped_a16(orc, M, shapes, y_dtype):
-    """The W1.58A16 group (bf16 x kept unquantised) in one streaming launch: ragged
-    N, K not a multiple of 128, one-tile problems; each launch of the reused plan
-    within the oracle bound."""
+@pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float16])
+def test_grouped_a16(orc, M, shapes, y_dtype, xdt):
+    """The W1.58A16 group (bf16 or fp16 x kept unquantised) in one streaming launch:
+    ragged N, K not a multiple of 128, one-tile problems; each launch of the
+    reused plan within the oracle bound."""
     sh = {"group": GROUP_SHAPES, "small": [(640, 1024), (100, 512), (64, 256), (130, 1152)],
           "tiny": [(100, 512), (64, 256), (33, 128)]}[shapes]
     items, cases = [], []
     for i, (N, K) in enumerate(sh):
         x, W = wl.random_case(5300 + 17 * M + i, M, N, K, x_dist="normal_outliers")
+        x = x.to(xdt)
         pw = tw.pack(W.to(DEV))
         items.append((x.to(DEV), pw, torch.full((M, N), float("nan"), device=DEV, dtype=y_dtype)))
         cases.append((x, W))
