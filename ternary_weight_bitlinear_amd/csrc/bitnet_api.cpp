@@ -775,9 +775,11 @@ static bool persistent_forced() {
 
 int64_t bitnet_group_table_bytes(int32_t count) {
     if (count <= 0) return -1;
-    // the problems, then the share bounds of a streaming launch
+    // the problems, then a streaming launch's share bounds (grid + 1) and
+    // per-workgroup records (4 each)
     return static_cast<int64_t>(count) * static_cast<int64_t>(sizeof(bitnet::GemvProblem)) +
-           (bitnet::kMaxStreamGrid + 1) * static_cast<int64_t>(sizeof(int32_t));
+           (bitnet::kMaxStreamGrid + 1 + 4 * static_cast<int64_t>(bitnet::kMaxStreamGrid)) *
+               static_cast<int64_t>(sizeof(int32_t));
 }
 
 static bitnet_status_t group_plan_impl(hipStream_t stream, const bitnet_group_item_t* items,

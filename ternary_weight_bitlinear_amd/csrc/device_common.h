@@ -99,16 +99,37 @@ __device__ __forceinline__ float exp_f32_fixed(float t) {
 // silu(a) * u = a / (1 + exp(-a)) * u, fp32.
 __device__ __forceinline__ float silu_mul(float a, float u) { return a / (1.0f + exp_f32_fixed(-a)) * u; }
 
+// Wave reductions without LDS traffic: DPP moves within each 16-lane row
+// (lane ^ 1, lane ^ 2, the other quad of the half row, the other half of the
+// row), after which every lane of a row holds the row's result, then the four
+// rows' results read out with v_readlane.  Max and integer sum do not depend
+// on the order of combination; the result is wave-uniform.
+template <int kCtrl>
+__device__ __forceinline__ int dpp_move(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i within each half row
+constexpr int kDppMirror = 0x140;       // lane i <-> 15 - i within each row
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    v = fmaxf(v, __int_as_float(dpp_move<kDppXor1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_move<kDppXor2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_move<kDppHalfMirror>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_move<kDppMirror>(__float_as_int(v))));
+    const int b = __float_as_int(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp_move<kDppXor1>(v);
+    v += dpp_move<kDppXor2>(v);
+    v += dpp_move<kDppHalfMirror>(v);
+    v += dpp_move<kDppMirror>(v);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
 // 16x16x64 int8 MFMA (gfx950): C[i][j] += sum_k A[i][k] B[k][j]; lane l holds

@@ -38,6 +38,7 @@
 // Every global access goes through gload / gstore (global address space), so
 // the ring's loads are counted by vmcnt alone and are waited for one at a time.
 #include <algorithm>
+#include <type_traits>
 
 #include "codes_bf16.h"
 #include "device_common.h"
@@ -49,6 +50,44 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kRsrcWord3 = 0x00020000;          // raw 32-bit buffer access on gfx9-family parts
+
+// Workgroup barrier for data written to LDS by ds_write: waits for this
+// wave's LDS operations only.  __syncthreads() would also wait for every
+// LDS-bound DMA still in flight (its release fence covers them); callers use
+// this one where no other wave reads DMA'd data after the barrier.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// LDS accesses in inline asm.  Once LDS-bound DMAs are in flight, the
+// compiler makes every plain LDS access it cannot prove disjoint from their
+// targets wait for all of them; these do not (the kernels order them against
+// the DMAs themselves, by vmcnt waits and barriers).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+__device__ __forceinline__ u32x4 lds_read16(const void* p) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p)) : "memory");
+    return v;
+}
+__device__ __forceinline__ float lds_read_f32(const void* p) {
+    float v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p)) : "memory");
+    return v;
+}
+__device__ __forceinline__ void lds_write_i32(void* p, int32_t v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+// Four 32-bit words 16 bytes apart (one per wave of a [wave][4] array).
+__device__ __forceinline__ u32x4 lds_read_4x16(const void* p) {
+    u32x4 v;
+    asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:16\n\tds_read_b32 %2, %4 offset:32\n\t"
+                 "ds_read_b32 %3, %4 offset:48\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v.x), "=&v"(v.y), "=&v"(v.z), "=&v"(v.w)
+                 : "v"(lds_addr(p))
+                 : "memory");
+    return v;
+}
 
 // Tuning knobs (build-time): rows and batch size of the persistent kernel, its
 // resident workgroups per CU, and the packed size from which a single call
@@ -613,42 +652,56 @@ __global__ __launch_bounds__(kThreads) void gemv_persistent_kernel(GemvProblem s
 
 // ActQuant of up to kQuantBatch single-token problems at once (M = 1, bf16
 // x, no input norm, K <= 8192): every problem's token is loaded into registers
-// before any reduction, and the absmax and row-sum reductions of all of them
-// share one barrier each, so a workgroup that touches several problems pays
-// one memory latency and two barriers instead of that per problem.  Results
-// are bit-identical to quantise_tokens (same fp32 operations per element).
+// before any reduction (quantise_batch_load, which the streaming kernel issues
+// ahead of its first weight DMAs so that the tokens return first), and the
+// absmax and row-sum reductions of all of them share one barrier each, so a
+// workgroup that touches several problems pays one memory latency and two
+// barriers instead of that per problem.  Results are bit-identical to
+// quantise_tokens (same fp32 operations per element).
 constexpr int kQuantBatch = 4;
-constexpr int kQuantVecs = 4;                   // 8-element vectors per thread and problem: K <= 8192
+constexpr int kQuantVecs = 4;                   // 8-element vectors per thread and problem
+constexpr int kQuantBatchMaxK = 8 * kThreads * kQuantVecs;
 
-template <typename PS>
-__device__ bool quantise_batch_ok(const PS& ps, int p0, int p1) {
-    for (int pi = p0; pi <= p1; ++pi) {
-        const GemvProblem P = ps.get(pi);
-        if (P.M != 1 || P.norm_w != nullptr || P.K > 8 * kThreads * kQuantVecs) return false;
-    }
-    return true;
+// Host and device test of one problem for the batched quantiser.
+__host__ __device__ inline bool quantise_batch_fits(const GemvProblem& P) {
+    return P.M == 1 && P.norm_w == nullptr && P.K <= kQuantBatchMaxK;
 }
 
 template <typename PS>
-__device__ void quantise_batch(const PS& ps, int p0, int np, int8_t* q_lds, float* as_lds, int* rs_lds,
-                               float* red_f, int* red_i, int t_begin) {
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    u32x4 raw[kQuantBatch][kQuantVecs];
+__device__ __forceinline__ void quantise_batch_load(const PS& ps, int p0, int np,
+                                                    u32x4 (&raw)[kQuantBatch][kQuantVecs]) {
+    // Buffer loads over the row's K bf16 (an empty range past the batch) read
+    // zeros beyond it.  The loads are unconditional: straight-line code lets
+    // the compiler count exactly how many later memory operations a wait for
+    // them may leave in flight.
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < kQuantBatch; ++j) {
         const GemvProblem P = ps.get(p0 + (j < np ? j : 0));
-        const int nvec = j < np ? P.K / 8 : 0;
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(P.x), 0, j < np ? 2 * P.K : 0, kRsrcWord3);
 #pragma unroll
-        for (int i = 0; i < kQuantVecs; ++i) {
-            const int vi = tid + i * kThreads;
-            raw[j][i] = vi < nvec ? gload<u32x4>(static_cast<const char*>(P.x) + 16 * vi) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < kQuantVecs; ++i)
+            raw[j][i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + i * kThreads), 0, 0);
     }
+}
+
+// The rest of the batch from the loaded tokens; ends with a barrier, after
+// which q, a_scale and the row sums are visible to the workgroup.
+template <typename PS>
+__device__ __forceinline__ void quantise_batch(const PS& ps, int p0, int np,
+                                               const u32x4 (&raw)[kQuantBatch][kQuantVecs], int8_t* q_lds,
+                                               float* as_lds, int* rs_lds, float* red_f, int* red_i, int t_begin) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    static_assert(kQuantBatch == 4 && kWaves == 4, "lds_read_4x16 reads one word per wave, 16 bytes apart");
 #pragma unroll
     for (int j = 0; j < kQuantBatch; ++j) {
+        if (j >= np) break;
+        const int nvec = ps.get(p0 + j).K / 8;
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < kQuantVecs; ++i) {
+            if (i * kThreads >= nvec) break;
             const u32x4 w = raw[j][i];
             amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_lo(w.x)), fabsf(bf16_hi(w.x))),
                                      fmaxf(fabsf(bf16_lo(w.y)), fabsf(bf16_hi(w.y)))));
@@ -656,9 +709,16 @@ __device__ void quantise_batch(const PS& ps, int p0, int np, int8_t* q_lds, floa
                                      fmaxf(fabsf(bf16_lo(w.w)), fabsf(bf16_hi(w.w)))));
         }
         amax = wave_max(amax);
-        if (lane == 0) red_f[wave * kQuantBatch + j] = amax;
+        if (lane == 0) lds_write_i32(red_f + wave * kQuantBatch + j, __float_as_int(amax));
     }
-    __syncthreads();
+    // Every token register is read here, before the barrier, so the waits for
+    // the loads all fall in the caller's straight-line code (where they count
+    // exactly the loads ahead of the weight DMAs); later reads need none.
+#pragma unroll
+    for (int j = 0; j < kQuantBatch; ++j)
+#pragma unroll
+        for (int i = 0; i < kQuantVecs; ++i) asm volatile("" : : "v"(raw[j][i]));
+    barrier_lds();
     int off = 0;
     int sums[kQuantBatch];
 #pragma unroll
@@ -666,8 +726,9 @@ __device__ void quantise_batch(const PS& ps, int p0, int np, int8_t* q_lds, floa
         sums[j] = 0;
         if (j >= np) continue;
         const GemvProblem P = ps.get(p0 + j);
-        const float amax = fmaxf(fmaxf(red_f[j], red_f[kQuantBatch + j]),
-                                 fmaxf(red_f[2 * kQuantBatch + j], red_f[3 * kQuantBatch + j]));
+        const u32x4 wm = lds_read_4x16(red_f + j);            // the waves' maxima
+        const float amax = fmaxf(fmaxf(__uint_as_float(wm.x), __uint_as_float(wm.y)),
+                                 fmaxf(__uint_as_float(wm.z), __uint_as_float(wm.w)));
         const float sa = (amax == 0.0f) ? 0.0f : 127.0f / amax;
         const int ldq = padded_q_row(P.Kp), nvec = P.K / 8;
         int8_t* qrow = q_lds + off;
@@ -690,33 +751,42 @@ __device__ void quantise_batch(const PS& ps, int p0, int np, int8_t* q_lds, floa
                     else hi |= byte << (8 * (e - 4));
                 }
             }
-            *reinterpret_cast<uint32_t*>(qrow + perm_pos(8 * vi)) = lo;
-            *reinterpret_cast<uint32_t*>(qrow + perm_pos(8 * vi + 4)) = hi;
+            lds_write_i32(qrow + perm_pos(8 * vi), static_cast<int32_t>(lo));
+            lds_write_i32(qrow + perm_pos(8 * vi + 4), static_cast<int32_t>(hi));
             if (store && vi < P.Kp / 8) gstore<u32x2>(P.q_out + 8 * vi, u32x2{lo, hi});
         }
         off += ldq;
     }
 #pragma unroll
     for (int j = 0; j < kQuantBatch; ++j) {
+        if (j >= np) break;
         const int total = wave_sum(sums[j]);
-        if (lane == 0) red_i[wave * kQuantBatch + j] = total;
+        if (lane == 0) lds_write_i32(red_i + wave * kQuantBatch + j, total);
     }
-    __syncthreads();
-    if (tid < np) {
-        const GemvProblem P = ps.get(p0 + tid);
-        const float amax = fmaxf(fmaxf(red_f[tid], red_f[kQuantBatch + tid]),
-                                 fmaxf(red_f[2 * kQuantBatch + tid], red_f[3 * kQuantBatch + tid]));
-        const int total = red_i[tid] + red_i[kQuantBatch + tid] + red_i[2 * kQuantBatch + tid] +
-                          red_i[3 * kQuantBatch + tid];
-        const float as = amax == 0.0f ? 0.0f : amax / 127.0f;
-        as_lds[16 * tid] = as;
-        rs_lds[16 * tid] = total;
-        if (P.q_out != nullptr && t_begin <= P.tile0) {
-            gstore<float>(P.a_scale_out, as);
-            gstore<int32_t>(P.rowsum_out, total);
+    barrier_lds();
+    // thread j finishes problem j; the problem's fields are read with a
+    // workgroup-uniform index (a per-thread index would be a vector load,
+    // queued behind every weight DMA already in flight)
+#pragma unroll
+    for (int j = 0; j < kQuantBatch; ++j) {
+        if (j >= np) break;
+        const GemvProblem P = ps.get(p0 + j);
+        if (tid == j) {
+            const u32x4 wm = lds_read_4x16(red_f + j), ws = lds_read_4x16(red_i + j);
+            const float amax = fmaxf(fmaxf(__uint_as_float(wm.x), __uint_as_float(wm.y)),
+                                     fmaxf(__uint_as_float(wm.z), __uint_as_float(wm.w)));
+            const int total = static_cast<int>(ws.x) + static_cast<int>(ws.y) + static_cast<int>(ws.z) +
+                              static_cast<int>(ws.w);
+            const float as = amax == 0.0f ? 0.0f : amax / 127.0f;
+            lds_write_i32(as_lds + 16 * j, __float_as_int(as));
+            lds_write_i32(rs_lds + 16 * j, total);
+            if (P.q_out != nullptr && t_begin <= P.tile0) {
+                gstore<float>(P.a_scale_out, as);
+                gstore<int32_t>(P.rowsum_out, total);
+            }
         }
     }
-    __syncthreads();                    // red_f / red_i are reused by the next batch
+    barrier_lds();                    // red_f / red_i are reused by the next batch
 }
 
 // ---------------------------------------------------------------- streaming kernel
@@ -742,12 +812,11 @@ __device__ void quantise_batch(const PS& ps, int p0, int np, int8_t* q_lds, floa
 // Share of a CU's first workgroup relative to its second, in percent (see
 // share_start).
 #ifndef BITNET_STREAM_FIRST_WEIGHT
-#define BITNET_STREAM_FIRST_WEIGHT 120
+#define BITNET_STREAM_FIRST_WEIGHT 122
 #endif
 constexpr int kDepth = BITNET_STREAM_DEPTH;
 constexpr int kStreamMaxProblems = 16;          // problems one workgroup may touch
 constexpr uint32_t kStreamOutOfRange = 0x80000000u;
-constexpr int kRsrcWord3 = 0x00020000;          // raw 32-bit buffer access on gfx9-family parts
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __shared__ __attribute__((aligned(1024))) int8_t g_stream_ring[kDepth * kThreads * 16];
@@ -778,22 +847,6 @@ __device__ __forceinline__ void wait_vm() {     // s_waitcnt vmcnt(kVm), other c
 // asm block.  The compiler does not see these reads, so it adds no wait for
 // the ring's DMA loads in flight (it would otherwise order every LDS read
 // after all of them); the loop's own vmcnt waits order the ring.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
-}
-__device__ __forceinline__ u32x4 lds_read16(const void* p) {
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p)) : "memory");
-    return v;
-}
-__device__ __forceinline__ float lds_read_f32(const void* p) {
-    float v;
-    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p)) : "memory");
-    return v;
-}
-__device__ __forceinline__ void lds_write_i32(void* p, int32_t v) {
-    asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
-}
 // Two consecutive ring slots of the lane (slot stride kThreads * 16 bytes).
 __device__ __forceinline__ void lds_read_ring2(const void* p, u32x4& w0, u32x4& w1) {
     asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:4096\n\ts_waitcnt lgkmcnt(0)"
@@ -838,19 +891,29 @@ __host__ __device__ __forceinline__ int64_t share_start(int64_t total_steps, int
 // the token rows are zero padded that far, see padded_q_row).
 __device__ __forceinline__ int stream_steps(int Kp) { return ((Kp / 64 + 3) / 4 + 1) / 2 * 2; }
 
-// Tiles [t_begin, t_end) of this workgroup: for a grouped launch the host's
-// balanced share bounds (stored after the problem table), for a single
-// problem its k-step share snapped to the nearest tile start.
+// Tiles [t_begin, t_end) of this workgroup, the first and last problem they
+// touch, and whether all of those take the batched quantiser: for a grouped
+// launch from the host's records stored after the problem table (the G + 1
+// share bounds, then per workgroup {p_first, p_last, batch, 0}), all loaded
+// at once; for a single problem its k-step share snapped to the nearest tile
+// start.
 template <bool kGrouped>
 __device__ __forceinline__ void stream_share(const Problems<kGrouped>& ps, const int32_t* bounds, int total_tiles,
-                                             int64_t total_steps, int n_first, int& t_begin, int& t_end) {
+                                             int64_t total_steps, int n_first, int& t_begin, int& t_end,
+                                             int& p_first, int& p_last, bool& batch) {
     const int G = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
     if constexpr (kGrouped) {
         t_begin = bounds[b];
         t_end = bounds[b + 1];
+        const int32_t* span = bounds + G + 1 + 4 * b;
+        p_first = span[0];
+        p_last = span[1];
+        batch = span[2] != 0;
     } else {
         t_begin = first_tile_from_step(ps, share_start(total_steps, b, G, n_first), total_tiles);
         t_end = first_tile_from_step(ps, share_start(total_steps, b + 1, G, n_first), total_tiles);
+        p_first = p_last = 0;
+        batch = quantise_batch_fits(ps.single);
     }
 }
 
@@ -888,11 +951,11 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     __shared__ __attribute__((aligned(16))) int rs_lds[kStreamMaxProblems * 16];
 
     const Problems<kGrouped> ps{table, single, count};
-    int t_begin, t_end;
-    stream_share(ps, bounds, total_tiles, total_steps, n_first, t_begin, t_end);
+    int t_begin, t_end, p_first, p_last;                // the host keeps the span within kStreamMaxProblems
+    bool batch;
+    stream_share(ps, bounds, total_tiles, total_steps, n_first, t_begin, t_end, p_first, p_last, batch);
     if (t_begin >= t_end) return;                       // workgroup-uniform
-    const int p_first = find_problem(ps, t_begin);
-    const int p_last = find_problem(ps, t_end - 1);     // the host keeps the span within kStreamMaxProblems
+    batch = batch && kFused && kXBf16;
 
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -910,20 +973,23 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     int row_p = (tp - PP.tile0) * 64 + wave * 16 + col, nb_p = (PP.K + 255) / 256;
     __amdgpu_buffer_rsrc_t bs_rsrc = kBlocked ? block_scale_rsrc(PP) : rsrc;
     float* const bs_ring = g_stream_bs_ring + wave * kWave;   // slot j of this wave: bs_ring + j * kThreads
-    auto produce = [&]() {
+    // the DMA(s) of k step `step` of the current tile into ring slot `slot`
+    auto issue = [&](int slot, int step) {
         // chunks past the row (padding steps) read nothing
-        const uint32_t off = tp < t_end && 4 * sp + grp < chunks_p ? rowoff + 64u * static_cast<uint32_t>(sp)
-                                                                   : kStreamOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(ring + slot_p * kThreads * 16), 16, off, 0, 0, 0);
+        const uint32_t off = tp < t_end && 4 * step + grp < chunks_p ? rowoff + 64u * static_cast<uint32_t>(step)
+                                                                     : kStreamOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(ring + slot * kThreads * 16), 16, off, 0, 0, 0);
         if constexpr (kBlocked) {
-            // block sp of the lane's row (zero past the last block and past N)
-            const uint32_t soff = tp < t_end && sp < nb_p && row_p < PP.N
-                                      ? static_cast<uint32_t>((sp * PP.N + row_p) * 4)
+            // block `step` of the lane's row (zero past the last block and past N)
+            const uint32_t soff = tp < t_end && step < nb_p && row_p < PP.N
+                                      ? static_cast<uint32_t>((step * PP.N + row_p) * 4)
                                       : kStreamOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lds_ptr_t)(bs_ring + slot_p * kThreads), 4, soff, 0,
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lds_ptr_t)(bs_ring + slot * kThreads), 4, soff, 0, 0,
+                                                     0);
         }
-        slot_p = slot_p + 1 == kDepth ? 0 : slot_p + 1;
+    };
+    // move past the step just issued (to the next tile, the next problem)
+    auto advance = [&]() {
         if (tp < t_end && ++sp == steps_p) {
             sp = 0;
             ++tp;
@@ -941,45 +1007,84 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
             }
         }
     };
+    auto produce = [&]() {
+        issue(slot_p, sp);
+        slot_p = slot_p + 1 == kDepth ? 0 : slot_p + 1;
+        advance();
+    };
     constexpr int kDmaPerStep = kBlocked ? 2 : 1;
-    // The ring holds kDepth steps: before the pass over steps (k, k+1) the
-    // producer has issued up to step k + kDepth - 3, and the pass issues
-    // k + kDepth - 2 and k + kDepth - 1 into the slots of k - 2 and k - 1,
-    // which the previous pass has read.
-#pragma unroll
-    for (int i = 0; i < kDepth - 2; ++i) produce();
+    static_assert(kDepth >= 4 && kDepth % 2 == 0, "the ring takes two steps per pass");
 
-    // Stage, into LDS, the w_scale of every row of the workgroup's tiles (one
-    // 64-float DMA per tile, after the token rows) and the tokens of every
-    // problem it touches.  The DMAs go out first; the token loads queue behind
-    // them and behind the ring's first loads, so one memory latency covers all.
-    {
+    // The prologue: the ring's first kDepth - 2 steps (the ring holds kDepth
+    // steps: before the pass over steps (k, k+1) the producer has issued up
+    // to step k + kDepth - 3, and the pass issues k + kDepth - 2 and
+    // k + kDepth - 1 into the slots of k - 2 and k - 1, which the previous
+    // pass has read), then the tokens of every problem the workgroup touches
+    // and the w_scale of every row of its tiles (one 64-float DMA per tile,
+    // after the token rows) into LDS.
+    //
+    // Single tokens: the first batch's token loads go out before any weight
+    // DMA, so (loads completing in order) they wait behind none of them.  The
+    // prologue comes in two copies: where the ring's first steps all lie in
+    // the workgroup's first tile (every K >= 64 * kDepth - 128), its DMAs are
+    // straight-line code, and the compiler's waits for the tokens then leave
+    // every DMA in flight; otherwise produce() issues them.
+    u32x4 raw[kQuantBatch][kQuantVecs];
+    auto prologue = [&](auto straight) __attribute__((always_inline)) {
+        if (batch) quantise_batch_load(ps, p_first, min(kQuantBatch, p_last - p_first + 1), raw);
+        if constexpr (decltype(straight)::value) {
+#pragma unroll
+            for (int i = 0; i < kDepth - 2; ++i) issue(i, i);
+            slot_p = kDepth - 2;
+            sp = kDepth - 3;
+            advance();
+        } else {
+#pragma unroll
+            for (int i = 0; i < kDepth - 2; ++i) produce();
+        }
         int q_bytes = 0;
         for (int pi = p_first; pi <= p_last; ++pi) {
             const GemvProblem Pi = ps.get(pi);
             q_bytes += Pi.M * padded_q_row(Pi.Kp);
         }
         int8_t* ws_lds = q_lds + q_bytes;
-        for (int pi = p_first; pi <= p_last && !kBlocked; ++pi) {
-            const GemvProblem Pi = ps.get(pi);
-            const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<float*>(Pi.w_scale), 0, Pi.N * static_cast<int>(sizeof(float)), kRsrcWord3);
-            const int t0 = max(t_begin, Pi.tile0), t1 = min(t_end, Pi.tile0 + Pi.ntiles);
-            for (int t = t0 + wave; t < t1; t += kWaves)   // rows past N read as zero
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    ws_rsrc, (lds_ptr_t)(ws_lds + (t - t_begin) * 64 * sizeof(float)), 4,
-                    static_cast<uint32_t>(((t - Pi.tile0) * 64 + lane) * sizeof(float)), 0, 0, 0);
-        }
-        int off = 0;
-        if (kFused && kXBf16 && quantise_batch_ok(ps, p_first, p_last)) {
-            // single tokens without a norm: up to kQuantBatch problems per pass
-            for (int pi = p_first; pi <= p_last; pi += kQuantBatch) {
+        auto stage_w_scale = [&]() {
+            for (int pi = p_first; pi <= p_last && !kBlocked; ++pi) {
+                const GemvProblem Pi = ps.get(pi);
+                const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float*>(Pi.w_scale), 0, Pi.N * static_cast<int>(sizeof(float)), kRsrcWord3);
+                const int t0 = max(t_begin, Pi.tile0), t1 = min(t_end, Pi.tile0 + Pi.ntiles);
+                for (int t = t0 + wave; t < t1; t += kWaves)   // rows past N read as zero
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        ws_rsrc, (lds_ptr_t)(ws_lds + (t - t_begin) * 64 * sizeof(float)), 4,
+                        static_cast<uint32_t>(((t - Pi.tile0) * 64 + lane) * sizeof(float)), 0, 0, 0);
+            }
+        };
+        if (batch) {
+            // single tokens, up to kQuantBatch problems per pass; the batch
+            // ends with a barrier that publishes q, a_scale and the row sums.
+            // The ring needs no barrier (each wave reads only what its own
+            // DMAs wrote, after its own vmcnt wait), and w_scale is read only
+            // after the loop's final wait and barrier, so its DMAs go out last.
+            // The first batch is kept out of the loop so that its waits count
+            // only the token loads ahead of the ring's DMAs.
+            const int np0 = min(kQuantBatch, p_last - p_first + 1);
+            quantise_batch(ps, p_first, np0, raw, q_lds, as_lds, rs_lds, red_fb, red_ib, t_begin);
+            int off = 0;
+            for (int j = 0; j < np0; ++j) off += padded_q_row(ps.get(p_first + j).Kp);
+            for (int pi = p_first + kQuantBatch; pi <= p_last; pi += kQuantBatch) {
                 const int np = min(kQuantBatch, p_last - pi + 1);
-                quantise_batch(ps, pi, np, q_lds + off, as_lds + 16 * (pi - p_first), rs_lds + 16 * (pi - p_first),
-                               red_fb, red_ib, t_begin);
+                quantise_batch_load(ps, pi, np, raw);
+                quantise_batch(ps, pi, np, raw, q_lds + off, as_lds + 16 * (pi - p_first),
+                               rs_lds + 16 * (pi - p_first), red_fb, red_ib, t_begin);
                 for (int j = 0; j < np; ++j) off += padded_q_row(ps.get(pi + j).Kp);
             }
+            stage_w_scale();
         } else {
+            // the DMAs go out first; the token loads queue behind them and
+            // behind the ring's first loads, so one memory latency covers all
+            stage_w_scale();
+            int off = 0;
             for (int pi = p_first; pi <= p_last; ++pi) {
                 const GemvProblem Pi = ps.get(pi);
                 const int j = pi - p_first;
@@ -990,13 +1095,15 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
                     stage_tokens(Pi, q_lds + off, as_lds + 16 * j, rs_lds + 16 * j, !kBlocked);
                 off += Pi.M * padded_q_row(Pi.Kp);
             }
+            // Every wave's DMAs so far (ring, w_scale, staged tokens) have
+            // landed once its own vmcnt drains; then the barrier makes them
+            // visible to all waves.
+            wait_vm<0>();
+            __syncthreads();
         }
-        // Every wave's DMAs so far (ring and w_scale) have landed once its own
-        // vmcnt drains (long done where the wave had token loads, since loads
-        // complete in order); then the barrier makes them visible to all waves.
-        wait_vm<0>();
-        __syncthreads();
-    }
+    };
+    if (steps_p >= kDepth - 2) prologue(std::true_type{});
+    else prologue(std::false_type{});
 
     // consumer
     int q_total = 0;
@@ -1165,11 +1272,10 @@ void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ 
     uint16_t* const x_lds = reinterpret_cast<uint16_t*>(g_stream_q);   // bf16 token rows of the problems
 
     const Problems<kGrouped> ps{table, single, count};
-    int t_begin, t_end;
-    stream_share(ps, bounds, total_tiles, total_steps, n_first, t_begin, t_end);
+    int t_begin, t_end, p_first, p_last;                // the host keeps the span within kStreamMaxProblems
+    bool batch;                                         // (no quantiser here)
+    stream_share(ps, bounds, total_tiles, total_steps, n_first, t_begin, t_end, p_first, p_last, batch);
     if (t_begin >= t_end) return;                       // workgroup-uniform
-    const int p_first = find_problem(ps, t_begin);
-    const int p_last = find_problem(ps, t_end - 1);     // the host keeps the span within kStreamMaxProblems
 
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -1419,23 +1525,29 @@ const int32_t* stream_bounds_of(const GemvProblem* table, int count) {
     return reinterpret_cast<const int32_t*>(table + count);
 }
 
-// Extra cost of each problem a workgroup touches beyond its first, in k-step
-// batches of a CU's second workgroup per token row: the problem's token rows
-// are quantised (or staged) into LDS before the loop, measured at ~2.5 us per
-// problem and token while such a workgroup streams ~1.3 batches per us.
+// Extra cost of each problem a workgroup touches beyond its first, in k steps
+// of a CU's second workgroup per token row: the problem's token rows are
+// quantised (or staged) into LDS before the loop and its outputs written
+// after it, measured on MI355X (c2-sized groups) at ~2.4 us per problem and
+// token while such a workgroup streams ~2.7 steps per us.
 #ifndef BITNET_STREAM_PROBLEM_COST
-#define BITNET_STREAM_PROBLEM_COST 3
+#define BITNET_STREAM_PROBLEM_COST 6
+#endif
+// Start cost of a CU's second workgroup, in the same k steps: its prologue
+// ends ~1.9 us after that of the CU's first workgroup (measured as above).
+#ifndef BITNET_STREAM_SECOND_START
+#define BITNET_STREAM_SECOND_START 5
 #endif
 
-// Greedy share of one workgroup: the tiles from `i` on whose cost (k-step
-// batches over the slot's relative rate, plus the cost of every further
-// problem) stays within `cap` and whose token rows, w_scale and exact sums
+// Greedy share of one workgroup: the tiles from `i` on whose cost (the slot's
+// start cost, k steps over the slot's relative rate, plus the cost of every
+// further problem) stays within `cap` and whose token rows, w_scale and exact sums
 // fit the LDS array.  Returns the end tile.
 int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_tiles, double cap, double rate,
-                   int token_bytes, int64_t q_limit) {
+                   double start, int token_bytes, int64_t q_limit) {
     if (i >= total_tiles) return i;
     int p = host_find_problem(t, count, i);
-    double cost = 0.0;
+    double cost = start;
     int64_t bytes = 0;
     for (int np = 0; i < total_tiles && np < kStreamMaxProblems && p < count; ++np, ++p) {
         const GemvProblem& P = t[p];
@@ -1461,8 +1573,9 @@ int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_til
 // workgroup b's tiles, whole tiles in table order) that minimise the largest
 // workgroup cost: a binary search on that cost, each candidate filled
 // greedily.  The first n_first workgroups (the first on their CU) stream
-// BITNET_STREAM_FIRST_WEIGHT percent as fast as the rest.  False if no cost
-// covers every tile within the LDS limits.
+// BITNET_STREAM_FIRST_WEIGHT percent as fast as the rest, which start
+// BITNET_STREAM_SECOND_START steps later.  False if no cost covers every tile
+// within the LDS limits.
 bool stream_bounds(const GemvProblem* t, int count, int64_t total_tiles, int grid, int n_first, int token_bytes,
                    int64_t q_limit, std::vector<int32_t>& bounds) {
     auto cover = [&](double cap, bool keep) {
@@ -1470,7 +1583,8 @@ bool stream_bounds(const GemvProblem* t, int count, int64_t total_tiles, int gri
         for (int b = 0; b < grid; ++b) {
             if (keep) bounds[b] = static_cast<int32_t>(i);
             const double rate = b < n_first ? BITNET_STREAM_FIRST_WEIGHT / 100.0 : 1.0;
-            i = fill_share(t, count, i, total_tiles, cap, rate, token_bytes, q_limit);
+            const double start = b < n_first ? 0.0 : static_cast<double>(BITNET_STREAM_SECOND_START);
+            i = fill_share(t, count, i, total_tiles, cap, rate, start, token_bytes, q_limit);
         }
         if (keep) bounds[grid] = static_cast<int32_t>(i);
         return i >= total_tiles;
@@ -1562,6 +1676,7 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
     // each workgroup's problems must fit the static array
     size_t need = 0;
     int64_t covered = 0;
+    std::vector<int32_t> spans(bounds ? 4 * static_cast<size_t>(grid) : 0, 0);
     for (int b = 0; b < grid; ++b) {
         int64_t t0, t1;
         if (bounds) {
@@ -1576,6 +1691,13 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
         if (t0 >= t1) continue;
         const int p0 = host_find_problem(host_table, count, t0), p1 = host_find_problem(host_table, count, t1 - 1);
         if (p1 - p0 + 1 > kStreamMaxProblems) return false;
+        if (bounds) {
+            bool fits = true;
+            for (int i = p0; i <= p1; ++i) fits = fits && quantise_batch_fits(host_table[i]);
+            spans[4 * static_cast<size_t>(b)] = p0;
+            spans[4 * static_cast<size_t>(b) + 1] = p1;
+            spans[4 * static_cast<size_t>(b) + 2] = fits ? 1 : 0;
+        }
         // w_scale and the M exact sums of each row
         size_t bytes = static_cast<size_t>(t1 - t0) * 64 * sizeof(float) * (1 + host_table[p0].M);
         for (int i = p0; i <= p1; ++i)
@@ -1583,6 +1705,9 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
         need = std::max(need, bytes);
     }
     if (need > static_cast<size_t>(q_limit) || covered != total_tiles) return false;
+    // the kernel's records: the grid + 1 share bounds, then {p_first, p_last,
+    // batch, 0} per workgroup (a workgroup with no tiles keeps zeros)
+    if (bounds) bounds->insert(bounds->end(), spans.begin(), spans.end());
     *grid_out = grid;
     *lds_out = 0;                                       // all of the kernel's LDS is static
     return true;
