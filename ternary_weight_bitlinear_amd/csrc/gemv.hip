@@ -847,6 +847,13 @@ __device__ __forceinline__ void wait_vm() {     // s_waitcnt vmcnt(kVm), other c
 // asm block.  The compiler does not see these reads, so it adds no wait for
 // the ring's DMA loads in flight (it would otherwise order every LDS read
 // after all of them); the loop's own vmcnt waits order the ring.
+// Two 16-byte words 64 bytes apart.
+__device__ __forceinline__ void lds_read_2x16_64(const void* p, u32x4& w0, u32x4& w1) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:64\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(w0), "=&v"(w1)
+                 : "v"(lds_addr(p))
+                 : "memory");
+}
 // Two consecutive ring slots of the lane (slot stride kThreads * 16 bytes).
 __device__ __forceinline__ void lds_read_ring2(const void* p, u32x4& w0, u32x4& w1) {
     asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:4096\n\ts_waitcnt lgkmcnt(0)"
@@ -889,7 +896,7 @@ __host__ __device__ __forceinline__ int64_t share_start(int64_t total_steps, int
 
 // k steps of a tile, rounded up to whole pairs (the loop takes two per pass;
 // the token rows are zero padded that far, see padded_q_row).
-__device__ __forceinline__ int stream_steps(int Kp) { return ((Kp / 64 + 3) / 4 + 1) / 2 * 2; }
+__host__ __device__ __forceinline__ int stream_steps(int Kp) { return ((Kp / 64 + 3) / 4 + 1) / 2 * 2; }
 
 // Tiles [t_begin, t_end) of this workgroup, the first and last problem they
 // touch, and whether all of those take the batched quantiser: for a grouped
@@ -1105,7 +1112,8 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     if (steps_p >= kDepth - 2) prologue(std::true_type{});
     else prologue(std::false_type{});
 
-    // consumer
+    // LDS after the token rows: w_scale of the workgroup's rows, the exact
+    // sums [M][rows], and (kBlocked) the block sums [step][16] per problem
     int q_total = 0;
     for (int pi = p_first; pi <= p_last; ++pi) {
         const GemvProblem Pi = ps.get(pi);
@@ -1114,7 +1122,45 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     const int wg_rows = (t_end - t_begin) * 64;
     const float* ws_lds = reinterpret_cast<const float*>(q_lds + q_total);
     int32_t* out_lds = reinterpret_cast<int32_t*>(q_lds + q_total) + wg_rows;   // [M][wg_rows] exact sums
+    int32_t* const bsum_lds = out_lds + ps.get(p_first).M * wg_rows;
+
+    // kBlocked: the exact sum of q over each 256-k block (one k step) per
+    // problem, block and token -- the term sum q that turns sum q*u into
+    // sum q*t, the same for every row of a problem, so taken once here rather
+    // than by a second matrix product per step.  Tokens past M hold zero.
+    // One (block, token) pair per thread; q rows are permuted only within
+    // 64-byte groups, so a block is 256 consecutive bytes of its row.
+    if constexpr (kBlocked) {
+        int qo = 0, bo = 0;
+        for (int pi = p_first; pi <= p_last; ++pi) {
+            const GemvProblem Pi = ps.get(pi);
+            const int nsteps = stream_steps(Pi.Kp), ldq = padded_q_row(Pi.Kp);
+            for (int e = threadIdx.x; e < nsteps * 16; e += kThreads) {
+                const int b = e / 16, m = e % 16;
+                int v = 0;
+                if (m < Pi.M) {
+                    const int8_t* src = q_lds + qo + m * ldq + 256 * b;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        v4i x[4];
+                        lds_read64(src + 64 * c, x);
+#pragma unroll
+                        for (int f = 0; f < 4; ++f)
+#pragma unroll
+                            for (int d = 0; d < 4; ++d) v = __builtin_amdgcn_sdot4(x[f][d], 0x01010101, v, false);
+                    }
+                }
+                lds_write_i32(bsum_lds + bo + e, v);
+            }
+            qo += Pi.M * ldq;
+            bo += nsteps * 16;
+        }
+        barrier_lds();
+    }
+
+    // consumer
     int pc = p_first, pj = 0, tc = t_begin, sc = 0, slot_c = 0;
+    const int32_t* bsum_c = bsum_lds;                   // kBlocked: the current problem's block sums
     GemvProblem P = ps.get(pc);
     int steps_c = stream_steps(P.Kp);
     int qoff = 0;
@@ -1126,7 +1172,6 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[f] = v4i{0, 0, 0, 0};
     float total[4] = {0.0f, 0.0f, 0.0f, 0.0f};           // kBlocked: fp32 sums of scaled block sums
-    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
     v4i a[2][4];                                        // zero where the lane has no token
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1147,20 +1192,22 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
         }
         slot_c = slot_c + 2 == kDepth ? 0 : slot_c + 2;
         if (m_ok) lds_read_a2(abase + 256 * sc, a);
+        u32x4 sq[2];                                    // kBlocked: sum q over the two blocks, tokens 4*grp + r
+        if constexpr (kBlocked) lds_read_2x16_64(bsum_c + 16 * sc + 4 * grp, sq[0], sq[1]);
 #pragma unroll
         for (int i = 0; i < 2 && kBlocked; ++i) {
             const u32x4 v = w[i];
-            v4i su = {0, 0, 0, 0}, sq = {0, 0, 0, 0};
+            v4i su = {0, 0, 0, 0};
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
                 const v4i bf = {int((v.x >> (2 * f)) & 0x03030303u), int((v.y >> (2 * f)) & 0x03030303u),
                                 int((v.z >> (2 * f)) & 0x03030303u), int((v.w >> (2 * f)) & 0x03030303u)};
                 su = mfma16(a[i][f], bf, su);          // sum q * u over the block
-                sq = mfma16(a[i][f], ones, sq);        // sum q over the block
             }
             // block order, fp32: total = total + (float)(exact block sum) * scale
 #pragma unroll
-            for (int r = 0; r < 4; ++r) total[r] = total[r] + static_cast<float>(su[r] - sq[r]) * bsc[i];
+            for (int r = 0; r < 4; ++r)
+                total[r] = total[r] + static_cast<float>(su[r] - static_cast<int32_t>(sq[i][r])) * bsc[i];
         }
 #pragma unroll
         for (int i = 0; i < 2 && !kBlocked; ++i) {
@@ -1206,6 +1253,7 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
         if (++tc == t_end) break;
         if (tc == P.tile0 + P.ntiles) {
             qoff += P.M * padded_q_row(P.Kp);
+            bsum_c += 16 * steps_c;
             P = ps.get(++pc);
             ++pj;
             steps_c = stream_steps(P.Kp);
@@ -1539,12 +1587,28 @@ const int32_t* stream_bounds_of(const GemvProblem* table, int count) {
 #define BITNET_STREAM_SECOND_START 5
 #endif
 
+// Relative speed of a CU's two workgroups, by kernel: the first workgroup on
+// a CU (older waves) wins the arbitration for memory and for the SIMDs.  The
+// int8 kernel is bound by memory (first 1.22x the second); the W1.58A16
+// kernel by its VALU code expansion, where the older waves' issue priority
+// gives the first 1.5x to 1.8x the second's rate while both run (the c2
+// group ends soonest at 1.70 to 1.85; both measured on MI355X).
+// first_weight in percent of the second's rate; second_start in k steps of
+// the second workgroup.
+struct StreamSlotCosts {
+    int first_weight;
+    int second_start;
+};
+constexpr StreamSlotCosts kSlotCostsA8{BITNET_STREAM_FIRST_WEIGHT, BITNET_STREAM_SECOND_START};
+constexpr StreamSlotCosts kSlotCostsA16{175, 0};
+constexpr StreamSlotCosts kSlotCostsBlocked{BITNET_STREAM_FIRST_WEIGHT, BITNET_STREAM_SECOND_START};
+
 // Greedy share of one workgroup: the tiles from `i` on whose cost (the slot's
 // start cost, k steps over the slot's relative rate, plus the cost of every
 // further problem) stays within `cap` and whose token rows, w_scale and exact sums
 // fit the LDS array.  Returns the end tile.
 int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_tiles, double cap, double rate,
-                   double start, int token_bytes, int64_t q_limit) {
+                   double start, int token_bytes, int64_t step_bytes, int64_t q_limit) {
     if (i >= total_tiles) return i;
     int p = host_find_problem(t, count, i);
     double cost = start;
@@ -1552,7 +1616,8 @@ int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_til
     for (int np = 0; i < total_tiles && np < kStreamMaxProblems && p < count; ++np, ++p) {
         const GemvProblem& P = t[p];
         const double enter = np > 0 ? static_cast<double>(BITNET_STREAM_PROBLEM_COST) * P.M : 0.0;
-        const int64_t enter_bytes = static_cast<int64_t>(P.M) * padded_q_row(P.Kp) * token_bytes;
+        const int64_t enter_bytes =
+            static_cast<int64_t>(P.M) * padded_q_row(P.Kp) * token_bytes + step_bytes * stream_steps(P.Kp);
         const double tile_cost = P.steps / rate;
         const int64_t tile_bytes = 64 * static_cast<int64_t>(sizeof(float)) * (1 + P.M);
         const int64_t left = P.tile0 + P.ntiles - i;
@@ -1573,18 +1638,18 @@ int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_til
 // workgroup b's tiles, whole tiles in table order) that minimise the largest
 // workgroup cost: a binary search on that cost, each candidate filled
 // greedily.  The first n_first workgroups (the first on their CU) stream
-// BITNET_STREAM_FIRST_WEIGHT percent as fast as the rest, which start
-// BITNET_STREAM_SECOND_START steps later.  False if no cost covers every tile
-// within the LDS limits.
+// slots.first_weight percent as fast as the rest, which start
+// slots.second_start steps later.  False if no cost covers every tile within
+// the LDS limits.
 bool stream_bounds(const GemvProblem* t, int count, int64_t total_tiles, int grid, int n_first, int token_bytes,
-                   int64_t q_limit, std::vector<int32_t>& bounds) {
+                   int64_t step_bytes, int64_t q_limit, const StreamSlotCosts& slots, std::vector<int32_t>& bounds) {
     auto cover = [&](double cap, bool keep) {
         int64_t i = 0;
         for (int b = 0; b < grid; ++b) {
             if (keep) bounds[b] = static_cast<int32_t>(i);
-            const double rate = b < n_first ? BITNET_STREAM_FIRST_WEIGHT / 100.0 : 1.0;
-            const double start = b < n_first ? 0.0 : static_cast<double>(BITNET_STREAM_SECOND_START);
-            i = fill_share(t, count, i, total_tiles, cap, rate, start, token_bytes, q_limit);
+            const double rate = b < n_first ? slots.first_weight / 100.0 : 1.0;
+            const double start = b < n_first ? 0.0 : static_cast<double>(slots.second_start);
+            i = fill_share(t, count, i, total_tiles, cap, rate, start, token_bytes, step_bytes, q_limit);
         }
         if (keep) bounds[grid] = static_cast<int32_t>(i);
         return i >= total_tiles;
@@ -1670,7 +1735,11 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
             return false;
     const int n_first = stream_first(grid);
     // grouped: balanced shares (built to fit; the loop below checks them)
-    if (bounds && !stream_bounds(host_table, count, total_tiles, grid, n_first, token_bytes, q_limit, *bounds))
+    const StreamSlotCosts& slots = token_bytes == 2 ? kSlotCostsA16 : blocked ? kSlotCostsBlocked : kSlotCostsA8;
+    // LDS per k step of each problem beyond its token rows: the block sums
+    const int64_t step_bytes = blocked ? 16 * static_cast<int64_t>(sizeof(int32_t)) : 0;
+    if (bounds && !stream_bounds(host_table, count, total_tiles, grid, n_first, token_bytes, step_bytes, q_limit,
+                                 slots, *bounds))
         return false;
     // the shares must tile [0, total_tiles) in order, and the token rows of
     // each workgroup's problems must fit the static array
@@ -1701,7 +1770,8 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
         // w_scale and the M exact sums of each row
         size_t bytes = static_cast<size_t>(t1 - t0) * 64 * sizeof(float) * (1 + host_table[p0].M);
         for (int i = p0; i <= p1; ++i)
-            bytes += static_cast<size_t>(host_table[i].M) * padded_q_row(host_table[i].Kp) * token_bytes;
+            bytes += static_cast<size_t>(host_table[i].M) * padded_q_row(host_table[i].Kp) * token_bytes +
+                     static_cast<size_t>(step_bytes) * stream_steps(host_table[i].Kp);
         need = std::max(need, bytes);
     }
     if (need > static_cast<size_t>(q_limit) || covered != total_tiles) return false;
