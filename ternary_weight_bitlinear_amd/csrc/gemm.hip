@@ -415,6 +415,34 @@ __device__ __forceinline__ void lds_issue_head(v4i (&na)[2], u32x4 (&nw)[2], uin
 __device__ __forceinline__ void lds_wait_head(v4i (&na)[2], u32x4 (&nw)[2]) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(na[0]), "+v"(na[1]), "+v"(nw[0]), "+v"(nw[1]) : : "memory");
 }
+// Four activation fragments (a wave tile of 128 rows: 32-row fragments 4 KB
+// apart in the stage).
+__device__ __forceinline__ void lds_issue_a(v4i (&na)[4], uint32_t ad) {
+    asm volatile("ds_read_b128 %[n0], %[ad]\n\tds_read_b128 %[n1], %[ad] offset:4096\n\t"
+                 "ds_read_b128 %[n2], %[ad] offset:8192\n\tds_read_b128 %[n3], %[ad] offset:12288"
+                 : [n0] "=&v"(na[0]), [n1] "=&v"(na[1]), [n2] "=&v"(na[2]), [n3] "=&v"(na[3])
+                 : [ad] "v"(ad)
+                 : "memory");
+}
+__device__ __forceinline__ void lds_wait_a(v4i (&na)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(na[0]), "+v"(na[1]), "+v"(na[2]), "+v"(na[3]) : : "memory");
+}
+__device__ __forceinline__ void lds_issue_head(v4i (&na)[4], u32x4 (&nw)[2], uint32_t ad, uint32_t bd) {
+    asm volatile(
+        "ds_read_b128 %[w0], %[bd]\n\tds_read_b128 %[w1], %[bd] offset:1024\n\t"
+        "ds_read_b128 %[n0], %[ad]\n\tds_read_b128 %[n1], %[ad] offset:4096\n\t"
+        "ds_read_b128 %[n2], %[ad] offset:8192\n\tds_read_b128 %[n3], %[ad] offset:12288"
+        : [n0] "=&v"(na[0]), [n1] "=&v"(na[1]), [n2] "=&v"(na[2]), [n3] "=&v"(na[3]), [w0] "=&v"(nw[0]),
+          [w1] "=&v"(nw[1])
+        : [ad] "v"(ad), [bd] "v"(bd)
+        : "memory");
+}
+__device__ __forceinline__ void lds_wait_head(v4i (&na)[4], u32x4 (&nw)[2]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(na[0]), "+v"(na[1]), "+v"(na[2]), "+v"(na[3]), "+v"(nw[0]), "+v"(nw[1])
+                 :
+                 : "memory");
+}
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -587,7 +615,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int SA = BM * BK, SB = BN * (BK / 4), STAGE = SA + SB;
     constexpr int A_DMA = SA / 1024 / kNW, B_DMA = SB / 1024 / kNW, D = A_DMA + B_DMA;
-    static_assert(TM == 2 && (TN == 2 || TN == 4), "wave tile 64 x 64 or 64 x 128");
+    static_assert((TM == 2 && (TN == 2 || TN == 4)) || (TM == 4 && TN == 2),
+                  "wave tile 64 x 64, 64 x 128 or 128 x 64");
     static_assert(SA % (1024 * kNW) == 0 && SB % (1024 * kNW) == 0 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
     static_assert(NS >= 2 && (NS - 1) * D < 64, "stage ring");
 
@@ -686,7 +715,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) facc[j][i][r] = 0.0f;
-    v4i a[2], na[2];
+    v4i a[TM], na[TM];
     u32x4 bw[TN];
     lds_issue_head(a, bw, a_rd[0], b_rd);
     lds_wait_head(a, bw);
@@ -732,8 +761,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
                 for (int j = 0; j < TN; ++j) b[j] = bx[j];
             }
-            a[0] = na[0];
-            a[1] = na[1];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) a[i] = na[i];
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) bw[j] = nbw[j];
@@ -919,6 +948,12 @@ bool use_regs_kernel() {
 #ifndef BITNET_GEMM_NS_WIDE
 #define BITNET_GEMM_NS_WIDE 3
 #endif
+// Wave grid of the wide LDS-DMA tile: 1 x 4 waves of 128x64 (each expanded
+// code word feeds four 32-row activation fragments) or 2 x 2 of 64x128 (two).
+#ifndef BITNET_GEMM_WIDE_WGM
+#define BITNET_GEMM_WIDE_WGM 1
+#endif
+constexpr int kWideWGM = BITNET_GEMM_WIDE_WGM, kWideWGN = 4 / BITNET_GEMM_WIDE_WGM;
 #ifndef BITNET_GEMM_NS_SMALL
 #define BITNET_GEMM_NS_SMALL 2
 #endif
@@ -931,7 +966,7 @@ hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_r
                        int64_t N, void* y, bool y_bf16, int64_t ldy, int32_t* acc_debug,
                        hipStream_t stream) {
     // Two tiles: 128x128 with 2x2 waves of 64x64 (3 workgroups per CU), and
-    // 128x256 with 2x2 waves of 64x128 (2 per CU), which has 40% fewer global
+    // 128x256 with 1x4 waves of 128x64 (2 per CU), which has 40% fewer global
     // bytes per MFMA and runs each tile faster.
     // The grid runs in rounds of resident workgroups, so the choice weighs
     // that gain against the share of the last round left empty (e.g. N=3840:
@@ -945,7 +980,7 @@ hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_r
     const int slots_wide =
         regs ? resident_slots(gemm_kernel<128, 256, 2, 2, BITNET_GEMM_PF, 2, true>, 256, lds_bytes<128, 256>(),
                               g_slots_wide)
-             : resident_slots(gemm_dma_kernel<128, 256, 2, 2, BITNET_GEMM_NS_WIDE, 2, true>, 256,
+             : resident_slots(gemm_dma_kernel<128, 256, kWideWGM, kWideWGN, BITNET_GEMM_NS_WIDE, 2, true>, 256,
                               BITNET_GEMM_NS_WIDE * dma_stage_bytes<128, 256>(), g_dslots_wide);
     const int64_t tiles_m = (M + 127) / 128;
     const double small = round_fill(tiles_m * ((N + 127) / 128), slots_small);
@@ -962,9 +997,9 @@ hipError_t launch_gemm(const int8_t* q, const float* a_scale, const int32_t* q_r
     if (forced == 1 || (forced < 0 && use_wide))
         return regs ? launch_tile<128, 256, 2, 2, BITNET_GEMM_PF, 2>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N,
                                                                      y, y_bf16, ldy, acc_debug, BITNET_GEMM_GM, stream)
-                    : launch_tile_dma<128, 256, 2, 2, BITNET_GEMM_NS_WIDE, 2>(q, a_scale, q_rowsum, M, Kp, packed,
-                                                                            w_scale, N, y, y_bf16, ldy, acc_debug,
-                                                                            BITNET_GEMM_GM, stream);
+                    : launch_tile_dma<128, 256, kWideWGM, kWideWGN, BITNET_GEMM_NS_WIDE, 2>(
+                          q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y, y_bf16, ldy, acc_debug, BITNET_GEMM_GM,
+                          stream);
     return regs ? launch_tile<128, 128, 2, 2, BITNET_GEMM_PF, 3>(q, a_scale, q_rowsum, M, Kp, packed, w_scale, N, y,
                                                                  y_bf16, ldy, acc_debug, BITNET_GEMM_GM, stream)
                 : launch_tile_dma<128, 128, 2, 2, BITNET_GEMM_NS_SMALL, 3>(q, a_scale, q_rowsum, M, Kp, packed,
