@@ -44,9 +44,10 @@ def kernel_source_hash(*names: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(name: str, src_hash: str):
+def traffic_from_profile(name: str, src_hash: str, key: str = "hbm_bytes_per_launch"):
     """HBM bytes per launch from a committed counter summary (profiles/<name>_traffic.md,
-    lines "- key: value"), or None when it was taken on a different kernel source."""
+    lines "- key: value"; `key` names the figure when the summary covers several
+    shapes), or None when it was taken on a different kernel source."""
     f = PROFILES / f"{name}_traffic.md"
     if not f.exists():
         return None
@@ -58,9 +59,14 @@ def traffic_from_profile(name: str, src_hash: str):
     if fields.get("kernel_source_hash") != src_hash:
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields[key])
     except (KeyError, ValueError):
         return None
+
+
+def progress(msg: str) -> None:
+    """A line on stderr per finished leg (the JSON result goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 # ------------------------------------------------------------------- decode
@@ -216,9 +222,12 @@ def bench_norm(tw, wl, torch, steps, warmup):
         ms_k = time_region(torch, run, steps * 5, warmup)
         nb = (2 if gated else 1) * 2 * M * K + 2 * K + M * tw.padded_k(K) + 8 * M
         gbps = nb / (ms_k * 1e-3) / 1e9
+        src = kernel_source_hash("act_quant.hip", "device_common.h")
         res[name] = dict(M=M, K=K, gated=gated, us_per_launch=ms_k * 1e3, value=gbps, unit="GB/s",
                          roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s",
-                                       frac=gbps / HBM_PEAK_GBPS, traffic=None))
+                                       frac=gbps / HBM_PEAK_GBPS, algorithmic_bytes=nb,
+                                       traffic=traffic_from_profile("rmsnorm_act_quant_m4096", src,
+                                                                    f"hbm_bytes_per_launch_{name}")))
         del x, up, g, q, a, r
     out["rmsnorm_act_quant"] = res
     torch.cuda.empty_cache()
@@ -265,9 +274,12 @@ def bench_a16(tw, wl, torch, steps, warmup):
     ms1 = time_region(torch, lambda: tw.linear_a16(x, pw, out=y), steps * 5, warmup)
     nb = 13824 * 2560 // 4
     gbps = nb / (ms1 * 1e-3) / 1e9
+    src1 = kernel_source_hash("gemv_a16.hip", "gemv.h", "device_common.h", "codes_bf16.h")
     out["gate_up_13824x2560"] = dict(value=gbps, unit="GB/s", us_per_launch=ms1 * 1e3,
                                      roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s",
-                                                   frac=gbps / HBM_PEAK_GBPS, traffic=None))
+                                                   frac=gbps / HBM_PEAK_GBPS,
+                                                   traffic=traffic_from_profile("decode_a16_single_13824x2560",
+                                                                                src1)))
     return out
 
 
@@ -491,7 +503,12 @@ def bench_configs(tw, wl, torch, steps, warmup):
         ms_a = time_region(torch, run, steps * 5, warmup)
         nb_a = 2 * M * K + M * tw.padded_k(K) + 8 * M
         gbps = nb_a / (ms_a * 1e-3) / 1e9
-        aq[f"M{M}_K{K}"] = dict(us=ms_a * 1e3, value=gbps, unit="GB/s", frac_of_hbm_peak=gbps / HBM_PEAK_GBPS)
+        src = kernel_source_hash("act_quant.hip", "device_common.h")
+        aq[f"M{M}_K{K}"] = dict(us=ms_a * 1e3, value=gbps, unit="GB/s", frac_of_hbm_peak=gbps / HBM_PEAK_GBPS,
+                                roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s",
+                                              frac=gbps / HBM_PEAK_GBPS, algorithmic_bytes=nb_a,
+                                              traffic=traffic_from_profile("act_quant_m4096", src,
+                                                                           f"hbm_bytes_per_launch_k{K}")))
         del x, q, a, r
     out["act_quant"] = aq
     # per-256-block weight scales: the c5 GEMMs with block-scaled weights (bf16 out),
@@ -537,8 +554,11 @@ def bench_configs(tw, wl, torch, steps, warmup):
     group = tw.GroupedBitLinear(items)
     ms_g = time_region(torch, group, steps, warmup)
     gbps = nb_codes / (ms_g * 1e-3) / 1e9
+    srcb = kernel_source_hash("gemv.hip", "gemv.h", "device_common.h", "codes_bf16.h")
     out["block_scaled"]["c2_grouped_m1"] = dict(
         value=gbps, unit="GB/s", ms_per_step=ms_g, kernel=group.kernel, packed_bytes=nb_codes, scale_bytes=nb_scales,
+        roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s", frac=gbps / HBM_PEAK_GBPS,
+                      traffic=traffic_from_profile("decode_blocked_bitnet2b_30_layers_m1", srcb)),
         with_scales_gbps=(nb_codes + nb_scales) / (ms_g * 1e-3) / 1e9, frac_of_hbm_peak=gbps / HBM_PEAK_GBPS,
         per_dispatch=dispatch_stats(time_each(torch, group, 20)),
         note="packed-code GB/s (N*K/4 per projection); with_scales counts the fp32 block scales too")
@@ -636,20 +656,26 @@ def main() -> int:
                             activations="bf16 N(0, 1), one token per projection", out_dtype="float32"))
     if args.only in (None, "decode"):
         d = bench_decode(tw, wl, torch, args.steps, args.warmup, not args.no_per_call)
+        progress("decode done")
         line.update(value=d["value"], ms_per_step=d["ms_per_step"], roofline=d["roofline"])
         line["config"]["packed_bytes"] = d["bytes"]
         if "per_call" in d:
             line["per_call"] = d["per_call"]
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_decode(wl, torch, args.cpu_seconds)
+            progress("decode cpu baseline done")
         if not args.no_norm:
             line["input_norm"] = bench_norm(tw, wl, torch, args.steps, args.warmup)
+            progress("input norm done")
         if not args.no_a16:
             line["w158a16"] = bench_a16(tw, wl, torch, args.steps, args.warmup)
+            progress("w158a16 done")
     if args.only in (None, "prefill"):
         g = bench_prefill(tw, wl, torch, args.steps, args.warmup, torch.bfloat16)
+        progress("prefill done")
         if not args.no_cpu_baseline:
             g["cpu_baseline"] = cpu_baseline_prefill(wl, torch, args.cpu_seconds)
+            progress("prefill cpu baseline done")
         line["gemm"] = g
         if args.only == "prefill":
             line.update(value=g["value"], unit="TOPS", ms_per_step=g["ms_per_step"], roofline=g["roofline"],
@@ -657,6 +683,7 @@ def main() -> int:
             line["config"]["workload"] = wl.WORKLOADS["c5"].name
     if args.only is None and not args.no_configs:
         line["configs"] = bench_configs(tw, wl, torch, args.steps, args.warmup)
+        progress("configs done")
     print(json.dumps(line), flush=True)
     return 0
 

@@ -812,7 +812,7 @@ __device__ __forceinline__ void quantise_batch(const PS& ps, int p0, int np,
 // Share of a CU's first workgroup relative to its second, in percent (see
 // share_start).
 #ifndef BITNET_STREAM_FIRST_WEIGHT
-#define BITNET_STREAM_FIRST_WEIGHT 122
+#define BITNET_STREAM_FIRST_WEIGHT 126
 #endif
 constexpr int kDepth = BITNET_STREAM_DEPTH;
 constexpr int kStreamMaxProblems = 16;          // problems one workgroup may touch
@@ -1589,7 +1589,8 @@ const int32_t* stream_bounds_of(const GemvProblem* table, int count) {
 
 // Relative speed of a CU's two workgroups, by kernel: the first workgroup on
 // a CU (older waves) wins the arbitration for memory and for the SIMDs.  The
-// int8 kernel is bound by memory (first 1.22x the second); the W1.58A16
+// int8 kernel is bound by memory (first ~1.22x the second; the c2 group ends
+// soonest with shares weighted 1.26-1.30, start cost 5-8); the W1.58A16
 // kernel by its VALU code expansion, where the older waves' issue priority
 // gives the first 1.5x to 1.8x the second's rate while both run (the c2
 // group ends soonest at 1.70 to 1.85; both measured on MI355X).
