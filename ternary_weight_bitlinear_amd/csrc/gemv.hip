@@ -650,25 +650,33 @@ __global__ __launch_bounds__(kThreads) void gemv_persistent_kernel(GemvProblem s
     }
 }
 
-// ActQuant of up to kQuantBatch single-token problems at once (M = 1, bf16
-// x, no input norm, K <= 8192): every problem's token is loaded into registers
-// before any reduction (quantise_batch_load, which the streaming kernel issues
-// ahead of its first weight DMAs so that the tokens return first), and the
-// absmax and row-sum reductions of all of them share one barrier each, so a
-// workgroup that touches several problems pays one memory latency and two
-// barriers instead of that per problem.  Results are bit-identical to
-// quantise_tokens (same fp32 operations per element).
+// ActQuant of the token rows of a workgroup's problems, kQuantBatch rows at a
+// time (bf16 x, no input norm, K <= 8192, M <= 4 shared by the group; row r
+// is token r % M of problem p_first + r / M): every row of a batch is loaded
+// into registers before any reduction (quantise_batch_load, which the
+// streaming kernel issues ahead of its first weight DMAs so that the first
+// batch returns first), and the absmax and row-sum reductions of the batch
+// share one barrier each, so a batch pays one memory latency and two barriers
+// instead of that per token.  Results are bit-identical to quantise_tokens
+// (same fp32 operations per element).
 constexpr int kQuantBatch = 4;
-constexpr int kQuantVecs = 4;                   // 8-element vectors per thread and problem
+constexpr int kQuantVecs = 4;                   // 8-element vectors per thread and row
 constexpr int kQuantBatchMaxK = 8 * kThreads * kQuantVecs;
+constexpr int kQuantBatchMaxM = 4;
 
 // Host and device test of one problem for the batched quantiser.
 __host__ __device__ inline bool quantise_batch_fits(const GemvProblem& P) {
-    return P.M == 1 && P.norm_w == nullptr && P.K <= kQuantBatchMaxK;
+    return P.M <= kQuantBatchMaxM && P.norm_w == nullptr && P.K <= kQuantBatchMaxK;
 }
 
+// Position of row r of a batch series: its problem, token and the offset of
+// its q row from the first problem's rows (q rows of a problem are [M][ldq]).
+struct BatchRow {
+    int p, m, qoff;
+};
+
 template <typename PS>
-__device__ __forceinline__ void quantise_batch_load(const PS& ps, int p0, int np,
+__device__ __forceinline__ void quantise_batch_load(const PS& ps, int p_first, int M, int r0, int nrows,
                                                     u32x4 (&raw)[kQuantBatch][kQuantVecs]) {
     // Buffer loads over the row's K bf16 (an empty range past the batch) read
     // zeros beyond it.  The loads are unconditional: straight-line code lets
@@ -677,27 +685,39 @@ __device__ __forceinline__ void quantise_batch_load(const PS& ps, int p0, int np
     const int tid = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < kQuantBatch; ++j) {
-        const GemvProblem P = ps.get(p0 + (j < np ? j : 0));
-        const __amdgpu_buffer_rsrc_t r =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(P.x), 0, j < np ? 2 * P.K : 0, kRsrcWord3);
+        const int r = r0 + (j < nrows ? j : 0);
+        const GemvProblem P = ps.get(p_first + r / M);
+        const char* xrow = static_cast<const char*>(P.x) + static_cast<int64_t>(r % M) * P.ldx * 2;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(xrow), 0, j < nrows ? 2 * P.K : 0, kRsrcWord3);
 #pragma unroll
         for (int i = 0; i < kQuantVecs; ++i)
-            raw[j][i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (tid + i * kThreads), 0, 0);
+            raw[j][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (tid + i * kThreads), 0, 0);
     }
 }
 
-// The rest of the batch from the loaded tokens; ends with a barrier, after
+// The rest of a batch of rows from the loaded tokens; `at` is the position of
+// its first row and is advanced past the batch.  Ends with a barrier, after
 // which q, a_scale and the row sums are visible to the workgroup.
 template <typename PS>
-__device__ __forceinline__ void quantise_batch(const PS& ps, int p0, int np,
+__device__ __forceinline__ void quantise_batch(const PS& ps, int p_first, int M, int nrows, BatchRow& at,
                                                const u32x4 (&raw)[kQuantBatch][kQuantVecs], int8_t* q_lds,
                                                float* as_lds, int* rs_lds, float* red_f, int* red_i, int t_begin) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     static_assert(kQuantBatch == 4 && kWaves == 4, "lds_read_4x16 reads one word per wave, 16 bytes apart");
+    // problem and token of each row without branches (the loads' waits come
+    // before the first barrier); the q offsets after it
+    BatchRow rows[kQuantBatch];
 #pragma unroll
     for (int j = 0; j < kQuantBatch; ++j) {
-        if (j >= np) break;
-        const int nvec = ps.get(p0 + j).K / 8;
+        rows[j].p = at.p + (at.m + j) / M;
+        rows[j].m = (at.m + j) % M;
+        rows[j].qoff = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kQuantBatch; ++j) {
+        if (j >= nrows) break;
+        const int nvec = ps.get(rows[j].p).K / 8;
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < kQuantVecs; ++i) {
@@ -719,20 +739,34 @@ __device__ __forceinline__ void quantise_batch(const PS& ps, int p0, int np,
 #pragma unroll
         for (int i = 0; i < kQuantVecs; ++i) asm volatile("" : : "v"(raw[j][i]));
     barrier_lds();
-    int off = 0;
+    {
+        BatchRow c = at;
+#pragma unroll
+        for (int j = 0; j < kQuantBatch; ++j) {
+            if (j >= nrows) break;                      // c stays on problems of the batch
+            rows[j].qoff = c.qoff;
+            if (++c.m == M) {
+                c.qoff += M * padded_q_row(ps.get(c.p).Kp);
+                c.m = 0;
+                ++c.p;
+            }
+            if (j + 1 == nrows) at = c;
+        }
+    }
     int sums[kQuantBatch];
 #pragma unroll
     for (int j = 0; j < kQuantBatch; ++j) {
         sums[j] = 0;
-        if (j >= np) continue;
-        const GemvProblem P = ps.get(p0 + j);
+        if (j >= nrows) continue;
+        const GemvProblem P = ps.get(rows[j].p);
         const u32x4 wm = lds_read_4x16(red_f + j);            // the waves' maxima
         const float amax = fmaxf(fmaxf(__uint_as_float(wm.x), __uint_as_float(wm.y)),
                                  fmaxf(__uint_as_float(wm.z), __uint_as_float(wm.w)));
         const float sa = (amax == 0.0f) ? 0.0f : 127.0f / amax;
         const int ldq = padded_q_row(P.Kp), nvec = P.K / 8;
-        int8_t* qrow = q_lds + off;
-        const bool store = P.q_out != nullptr && t_begin <= P.tile0;
+        int8_t* qrow = q_lds + rows[j].qoff + rows[j].m * ldq;
+        int8_t* qout = P.q_out != nullptr && t_begin <= P.tile0 ? P.q_out + static_cast<int64_t>(rows[j].m) * P.Kp
+                                                                : nullptr;
 #pragma unroll
         for (int i = 0; i < kQuantVecs; ++i) {
             const int vi = tid + i * kThreads;
@@ -753,24 +787,23 @@ __device__ __forceinline__ void quantise_batch(const PS& ps, int p0, int np,
             }
             lds_write_i32(qrow + perm_pos(8 * vi), static_cast<int32_t>(lo));
             lds_write_i32(qrow + perm_pos(8 * vi + 4), static_cast<int32_t>(hi));
-            if (store && vi < P.Kp / 8) gstore<u32x2>(P.q_out + 8 * vi, u32x2{lo, hi});
+            if (qout && vi < P.Kp / 8) gstore<u32x2>(qout + 8 * vi, u32x2{lo, hi});
         }
-        off += ldq;
     }
 #pragma unroll
     for (int j = 0; j < kQuantBatch; ++j) {
-        if (j >= np) break;
+        if (j >= nrows) break;
         const int total = wave_sum(sums[j]);
         if (lane == 0) lds_write_i32(red_i + wave * kQuantBatch + j, total);
     }
     barrier_lds();
-    // thread j finishes problem j; the problem's fields are read with a
+    // thread j finishes row j; the problem's fields are read with a
     // workgroup-uniform index (a per-thread index would be a vector load,
     // queued behind every weight DMA already in flight)
 #pragma unroll
     for (int j = 0; j < kQuantBatch; ++j) {
-        if (j >= np) break;
-        const GemvProblem P = ps.get(p0 + j);
+        if (j >= nrows) break;
+        const GemvProblem P = ps.get(rows[j].p);
         if (tid == j) {
             const u32x4 wm = lds_read_4x16(red_f + j), ws = lds_read_4x16(red_i + j);
             const float amax = fmaxf(fmaxf(__uint_as_float(wm.x), __uint_as_float(wm.y)),
@@ -778,11 +811,12 @@ __device__ __forceinline__ void quantise_batch(const PS& ps, int p0, int np,
             const int total = static_cast<int>(ws.x) + static_cast<int>(ws.y) + static_cast<int>(ws.z) +
                               static_cast<int>(ws.w);
             const float as = amax == 0.0f ? 0.0f : amax / 127.0f;
-            lds_write_i32(as_lds + 16 * j, __float_as_int(as));
-            lds_write_i32(rs_lds + 16 * j, total);
+            const int slot = 16 * (rows[j].p - p_first) + rows[j].m;
+            lds_write_i32(as_lds + slot, __float_as_int(as));
+            lds_write_i32(rs_lds + slot, total);
             if (P.q_out != nullptr && t_begin <= P.tile0) {
-                gstore<float>(P.a_scale_out, as);
-                gstore<int32_t>(P.rowsum_out, total);
+                gstore<float>(P.a_scale_out + rows[j].m, as);
+                gstore<int32_t>(P.rowsum_out + rows[j].m, total);
             }
         }
     }
@@ -1038,7 +1072,9 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     // every DMA in flight; otherwise produce() issues them.
     u32x4 raw[kQuantBatch][kQuantVecs];
     auto prologue = [&](auto straight) __attribute__((always_inline)) {
-        if (batch) quantise_batch_load(ps, p_first, min(kQuantBatch, p_last - p_first + 1), raw);
+        const int group_m = PP.M;                       // M is shared by the group
+        const int batch_rows = (p_last - p_first + 1) * group_m;
+        if (batch) quantise_batch_load(ps, p_first, group_m, 0, min(kQuantBatch, batch_rows), raw);
         if constexpr (decltype(straight)::value) {
 #pragma unroll
             for (int i = 0; i < kDepth - 2; ++i) issue(i, i);
@@ -1050,10 +1086,7 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
             for (int i = 0; i < kDepth - 2; ++i) produce();
         }
         int q_bytes = 0;
-        for (int pi = p_first; pi <= p_last; ++pi) {
-            const GemvProblem Pi = ps.get(pi);
-            q_bytes += Pi.M * padded_q_row(Pi.Kp);
-        }
+        for (int pi = p_first; pi <= p_last; ++pi) q_bytes += group_m * padded_q_row(ps.get(pi).Kp);
         int8_t* ws_lds = q_lds + q_bytes;
         auto stage_w_scale = [&]() {
             for (int pi = p_first; pi <= p_last && !kBlocked; ++pi) {
@@ -1075,16 +1108,13 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
             // after the loop's final wait and barrier, so its DMAs go out last.
             // The first batch is kept out of the loop so that its waits count
             // only the token loads ahead of the ring's DMAs.
-            const int np0 = min(kQuantBatch, p_last - p_first + 1);
-            quantise_batch(ps, p_first, np0, raw, q_lds, as_lds, rs_lds, red_fb, red_ib, t_begin);
-            int off = 0;
-            for (int j = 0; j < np0; ++j) off += padded_q_row(ps.get(p_first + j).Kp);
-            for (int pi = p_first + kQuantBatch; pi <= p_last; pi += kQuantBatch) {
-                const int np = min(kQuantBatch, p_last - pi + 1);
-                quantise_batch_load(ps, pi, np, raw);
-                quantise_batch(ps, pi, np, raw, q_lds + off, as_lds + 16 * (pi - p_first),
-                               rs_lds + 16 * (pi - p_first), red_fb, red_ib, t_begin);
-                for (int j = 0; j < np; ++j) off += padded_q_row(ps.get(pi + j).Kp);
+            BatchRow at{p_first, 0, 0};
+            quantise_batch(ps, p_first, group_m, min(kQuantBatch, batch_rows), at, raw, q_lds, as_lds, rs_lds,
+                           red_fb, red_ib, t_begin);
+            for (int r = kQuantBatch; r < batch_rows; r += kQuantBatch) {
+                const int nr = min(kQuantBatch, batch_rows - r);
+                quantise_batch_load(ps, p_first, group_m, r, nr, raw);
+                quantise_batch(ps, p_first, group_m, nr, at, raw, q_lds, as_lds, rs_lds, red_fb, red_ib, t_begin);
             }
             stage_w_scale();
         } else {
@@ -1269,20 +1299,22 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     for (int pi = p_first, j = 0; pi <= p_last; ++pi, ++j) {
         const GemvProblem Pi = ps.get(pi);
         const int t0 = max(t_begin, Pi.tile0), t1 = min(t_end, Pi.tile0 + Pi.ntiles);
-        const int rows = (t1 - t0) * 64;
-        for (int i = threadIdx.x; i < Pi.M * rows; i += kThreads) {
-            const int m = i / rows, rr = i % rows;
-            const int n = (t0 - Pi.tile0) * 64 + rr;
-            if (n >= Pi.N) continue;
-            const int lrow = (t0 - t_begin) * 64 + rr;
-            if constexpr (kBlocked) {
-                const float v = __int_as_float(out_lds[m * wg_rows + lrow]) * as_lds[16 * j + m];
-                if constexpr (kOutBf16)
-                    gstore<uint16_t>(static_cast<uint16_t*>(Pi.y) + m * Pi.ldy + n, f32_to_bf16(v));
-                else
-                    gstore<float>(static_cast<float*>(Pi.y) + m * Pi.ldy + n, v);
-            } else {
-                store_output<kOutBf16>(Pi, m, n, out_lds[m * wg_rows + lrow], as_lds[16 * j + m], ws_lds[lrow]);
+        const int n0 = (t0 - Pi.tile0) * 64, lrow0 = (t0 - t_begin) * 64;
+        const int rows = min((t1 - t0) * 64, Pi.N - n0);         // rows past N have no output
+        for (int m = 0; m < Pi.M; ++m) {
+            const float as = as_lds[16 * j + m];
+            const int32_t* const sums = out_lds + m * wg_rows + lrow0;
+#pragma unroll 4
+            for (int rr = threadIdx.x; rr < rows; rr += kThreads) {
+                if constexpr (kBlocked) {
+                    const float v = __int_as_float(sums[rr]) * as;
+                    if constexpr (kOutBf16)
+                        gstore<uint16_t>(static_cast<uint16_t*>(Pi.y) + m * Pi.ldy + n0 + rr, f32_to_bf16(v));
+                    else
+                        gstore<float>(static_cast<float*>(Pi.y) + m * Pi.ldy + n0 + rr, v);
+                } else {
+                    store_output<kOutBf16>(Pi, m, n0 + rr, sums[rr], as, ws_lds[lrow0 + rr]);
+                }
             }
         }
     }
