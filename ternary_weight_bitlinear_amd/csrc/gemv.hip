@@ -1493,17 +1493,18 @@ void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ 
     for (int pi = p_first; pi <= p_last; ++pi) {
         const GemvProblem Pi = ps.get(pi);
         const int t0 = max(t_begin, Pi.tile0), t1 = min(t_end, Pi.tile0 + Pi.ntiles);
-        const int rows = (t1 - t0) * 64;
-        for (int i = threadIdx.x; i < Pi.M * rows; i += kThreads) {
-            const int m = i / rows, rr = i % rows;
-            const int n = (t0 - Pi.tile0) * 64 + rr;
-            if (n >= Pi.N) continue;
-            const int lrow = (t0 - t_begin) * 64 + rr;
-            const float v = out_lds[m * wg_rows + lrow] * ws_lds[lrow];
-            if constexpr (kOutBf16)
-                gstore<uint16_t>(static_cast<uint16_t*>(Pi.y) + m * Pi.ldy + n, f32_to_bf16(v));
-            else
-                gstore<float>(static_cast<float*>(Pi.y) + m * Pi.ldy + n, v);
+        const int n0 = (t0 - Pi.tile0) * 64, lrow0 = (t0 - t_begin) * 64;
+        const int rows = min((t1 - t0) * 64, Pi.N - n0);         // rows past N have no output
+        for (int m = 0; m < Pi.M; ++m) {
+            const float* const sums = out_lds + m * wg_rows + lrow0;
+#pragma unroll 4
+            for (int rr = threadIdx.x; rr < rows; rr += kThreads) {
+                const float v = sums[rr] * ws_lds[lrow0 + rr];
+                if constexpr (kOutBf16)
+                    gstore<uint16_t>(static_cast<uint16_t*>(Pi.y) + m * Pi.ldy + n0 + rr, f32_to_bf16(v));
+                else
+                    gstore<float>(static_cast<float*>(Pi.y) + m * Pi.ldy + n0 + rr, v);
+            }
         }
     }
 }
