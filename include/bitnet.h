@@ -373,8 +373,10 @@ const char* bitnet_group_plan_kernel(const bitnet_group_plan_t* plan);
  * path kept 16-bit activations, and both 16-bit formats widen exactly); the
  * sum then runs on fp16 matrix cores.  The sum runs in fp32 on the matrix
  * cores in the hardware's order: |y - exact| <= w_scale[n] * (K/32 + 64) *
- * 2^-24 * sum_k |x[m][k] * t[n][k]| (+ the bf16 rounding for bf16 y).  A
- * decode-size kernel: every 16 tokens re-read the packed weight.  Errors:
+ * 2^-24 * sum_k |x[m][k] * t[n][k]| (+ the bf16 rounding for bf16 y), for
+ * partial sums below 2^127 in magnitude (bf16 x is summed as x * 2t and
+ * halved: exact below that, infinite above).  A decode-size kernel: every 16
+ * tokens re-read the packed weight.  Errors:
  * UNSUPPORTED for fp32 x; INVALID_ARG as bitnet_linear_forward; HIP.
  */
 bitnet_status_t bitnet_linear_a16(hipStream_t stream, const void* x, bitnet_dtype_t x_dtype,

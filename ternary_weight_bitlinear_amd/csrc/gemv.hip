@@ -1460,7 +1460,7 @@ void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ 
                                                                      acc, 0, 0, 0);
                     else
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a[2 * j + h]), __builtin_bit_cast(bf16x8, expand_bf16(words[j], h)),
+                            __builtin_bit_cast(bf16x8, a[2 * j + h]), __builtin_bit_cast(bf16x8, expand_bf16_twice(words[j], h)),
                             acc, 0, 0, 0);
                 }
         }
@@ -1470,6 +1470,7 @@ void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ 
         sc = 0;
         {
             const int row = (tc - t_begin) * 64 + wave * 16 + col;
+            if constexpr (!kF16) acc = acc * 0.5f;      // the bf16 operand held 2t (exact)
             const int32_t bits[4] = {__float_as_int(acc[0]), __float_as_int(acc[1]), __float_as_int(acc[2]),
                                      __float_as_int(acc[3])};
 #pragma unroll

@@ -12,9 +12,9 @@
 // 16 tokens; lane group g of wave w takes every 16th 64-code chunk of the row,
 // starting at 4w + g, so the 4 waves read contiguous 256-byte runs; partial
 // 16 x 16 tiles meet in LDS.  The packed codes go straight into MFMA operands:
-// two 2-bit fields of a word (8 consecutive k) become 8 bf16 values of t in 12
-// VALU ops, each pair by two byte permutes against a 3-entry table of the bf16
-// bytes of -1, 0, +1.  A operands are 8 consecutive bf16 of the token row,
+// two 2-bit fields of a word (8 consecutive k) become 8 16-bit values, each
+// pair by two byte permutes against a 3-entry table of high bytes (fp16 of t;
+// bf16 of 2t, whose fp32 sums are exactly twice and are halved).  A operands are 8 consecutive bf16 of the token row,
 // read from global memory (L1/L2-resident: every workgroup reads the same
 // rows).  Token tiles beyond the first 16 re-read the packed rows, so this is
 // a decode-size kernel.
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void gemv_a16_kernel(const uint16_t* __re
                                                                      acc, 0, 0, 0);
                     else
                         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                      __builtin_bit_cast(bf16x8, expand_bf16(bw[u][j], h)),
+                                                                      __builtin_bit_cast(bf16x8, expand_bf16_twice(bw[u][j], h)),
                                                                       acc, 0, 0, 0);
                 }
             }
@@ -91,6 +91,7 @@ __global__ __launch_bounds__(kThreads) void gemv_a16_kernel(const uint16_t* __re
         float s = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s += part[w][m][nc];
+        if constexpr (!kF16) s = s * 0.5f;             // the bf16 operand held 2t (exact)
         const float v = s * gload<float>(w_scale + n);
         if constexpr (kOutBf16)
             gstore<uint16_t>(static_cast<uint16_t*>(y) + (m0 + m) * ldy + n, f32_to_bf16(v));

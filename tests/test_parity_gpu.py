@@ -738,13 +738,15 @@ def test_grouped_kernels_agree_with_oracle(orc, M, x_dtype, y_dtype, monkeypatch
                 check_y(y, ref["y"])
 
 
-def test_grouped_many_problems_per_workgroup(orc):
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_grouped_many_problems_per_workgroup(orc, M):
     """A six-layer mix of a decoder's projections (each workgroup's share spans
-    several problems) next to a two-item group with fewer tiles than
+    several problems, so with M > 1 a batch of quantised token rows crosses
+    problem boundaries) next to a two-item group with fewer tiles than
     workgroups, launched back to back."""
     big = [(2560, 2560), (640, 2560), (640, 2560), (2560, 2560), (6912, 2560), (6912, 2560), (2560, 6912)] * 6
-    items, refs = _group_case(orc, 1, torch.bfloat16, torch.bfloat16, big, 1700)
-    small_items, small_refs = _group_case(orc, 1, torch.float32, torch.float32, [(130, 2560), (64, 6912)], 1800)
+    items, refs = _group_case(orc, M, torch.bfloat16, torch.bfloat16, big, 1700 + 7 * M)
+    small_items, small_refs = _group_case(orc, M, torch.float32, torch.float32, [(130, 2560), (64, 6912)], 1800 + M)
     g_big, g_small = tw.GroupedBitLinear(items), tw.GroupedBitLinear(small_items)
     assert g_big.kernel == "stream" and g_small.kernel == "stream"
     for rep in range(3):
