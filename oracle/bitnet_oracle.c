@@ -36,7 +36,9 @@
  *   R3  s = 1/mean is an fp32 division; the code uses the fp32 product W*s.
  *   R4  ActQuant uses one fp32 factor sa = 127/amax, then the fp32 product
  *       x*sa; a_scale = amax/127 (fp32 division).
- *   R5  A token with amax == 0 gets q = 0 and a_scale = 0.
+ *   R5  A token with amax == 0 gets q = 0 and a_scale = 0; so does a token
+ *       whose scale 127/amax is not a finite fp32 (amax < 127/FLT_MAX, about
+ *       2^-121), for which R4's factor cannot be formed.
  *   R6  A fused weight (q|k|v, gate|up) keeps one scale per source tensor
  *       ("segment"); w_scale[n] is the scale of row n's segment.
  *   R7  Where W*s is NaN (only 0 * inf, i.e. a zero weight in a tensor whose
@@ -108,6 +110,7 @@
  * Everything here is a direct loop over the definition.  No blocking, no
  * fusion, no intrinsics.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -379,12 +382,12 @@ int orc_act_quant(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
                 amax = a;
         }
         int64_t sum = 0;
-        if (amax == 0.0f) {
+        float sa = 127.0f / amax;                  /* +inf for amax == 0 */
+        if (!(sa <= FLT_MAX)) {                    /* R5 */
             for (int64_t k = 0; k < Kp; ++k)
                 q[m * Kp + k] = 0;
             a_scale[m] = 0.0f;
         } else {
-            float sa = 127.0f / amax;
             for (int64_t k = 0; k < K; ++k) {
                 float r = round_half_even(load_elem(x, dtype, m * ldx + k) * sa);
                 if (r > 127.0f)
@@ -432,10 +435,10 @@ int orc_rms_act_quant(const void* x, int x_dtype, const void* g, int g_dtype, in
         double r = 1.0 / sqrt(squares / (double)K + (double)eps);
         int64_t sum = 0;
         memset(&q[m * Kp], 0, (size_t)Kp);         /* zero token and the tail k >= K */
-        if (amax == 0.0f) {
+        float sa = 127.0f / amax;                  /* +inf for amax == 0 */
+        if (!(sa <= FLT_MAX)) {                    /* R5 */
             a_scale[m] = 0.0f;
         } else {
-            float sa = 127.0f / amax;
             for (int64_t k = 0; k < K; ++k) {
                 float z = load_elem(x, x_dtype, m * ldx + k) * load_elem(g, g_dtype, k);
                 float c = round_half_even(z * sa);

@@ -280,6 +280,20 @@ def pin_zero_token_and_zero_tensor(orc):
     assert not t.any() and not ws.any() and mean[0] == 0 and zeros[0] == 3 * K
     y = orc.epilogue(orc.int_dot(q, t), a, ws)
     assert np.array_equal(y, np.zeros((2, 3), dtype=np.float32))  # +0 and -0 both compare equal
+    # R5 at the edge of fp32: amax = 2^-122 makes 127/amax overflow, so the token
+    # is a zero token; at amax = 2^-121 the scale 127 * 2^121 is still finite and
+    # the token quantises normally (-2^-122 * 127 * 2^121 = -63.5, a tie -> -64)
+    tiny = np.zeros((2, K), dtype=np.uint16)
+    tiny[0, [3, 9]] = f32_to_bf16_bits(np.array([2.0 ** -122, -2.0 ** -123], dtype=np.float32))
+    tiny[1, [3, 9]] = f32_to_bf16_bits(np.array([2.0 ** -121, -2.0 ** -122], dtype=np.float32))
+    q, a, r = orc.act_quant(tiny)
+    assert not q[0].any() and a[0] == 0 and r[0] == 0
+    assert q[1, 3] == 127 and q[1, 9] == -64 and np.count_nonzero(q[1]) == 2 and r[1] == 63
+    assert a[1] == np.float32(2.0 ** -121) / np.float32(127)
+    g = f32_to_bf16_bits(np.ones(K, dtype=np.float32))
+    qn, an, rn = orc.rms_act_quant(tiny, g, 0.0)
+    assert not qn[0].any() and an[0] == 0 and rn[0] == 0
+    assert np.array_equal(qn[1], q[1]) and an[1] > 0
 
 
 def pin_int_dot_bruteforce(orc):

@@ -123,6 +123,12 @@ MUTANTS = [
     ("I2_S stride of 16", "return consecutive ? v / 4 : v % 32;", "return consecutive ? v / 4 : v % 16;"),
     ("I2_S scale not stored", "memcpy(out + total / 4, &s, sizeof s);", "(void)s;"),
     ("I2_S codes offset by 2", "unsigned c = (unsigned)(t[i] + 1);", "unsigned c = (unsigned)(t[i] + 2) & 3u;"),
+    ("ActQuant of a token whose 127/amax overflows fp32 (R5 only for amax == 0)",
+     "if (!(sa <= FLT_MAX)) {                    /* R5 */\n            for (int64_t k = 0; k < Kp; ++k)",
+     "if (amax == 0.0f) {\n            for (int64_t k = 0; k < Kp; ++k)"),
+    ("RMSNorm -> ActQuant of a token whose 127/amax overflows fp32",
+     "if (!(sa <= FLT_MAX)) {                    /* R5 */\n            a_scale[m] = 0.0f;",
+     "if (amax == 0.0f) {\n            a_scale[m] = 0.0f;"),
 ]
 
 
