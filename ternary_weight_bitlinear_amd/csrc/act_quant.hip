@@ -157,8 +157,10 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) squares += __shfl_xor(squares, o, kWave);
     }
-    // amax == 0: every value is +-0 and sa = 0 gives q = 0 exactly.
-    const float sa = (amax == 0.0f) ? 0.0f : 127.0f / amax;
+    // A zero token (amax == 0, or 127/amax not a finite fp32): sa = 0 gives
+    // q = 0, and a_scale is 0.
+    const bool zero_token = !(127.0f / amax <= __FLT_MAX__);
+    const float sa = zero_token ? 0.0f : 127.0f / amax;
 
     int sum = 0;
     if constexpr (VPT > 0) {
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     sum = wave_sum(sum);
     if (lane == 0) {
         q_rowsum[m] = sum;
-        if (amax == 0.0f) {
+        if (zero_token) {
             a_scale[m] = 0.0f;
         } else if constexpr (kMode == kPlain) {
             a_scale[m] = amax / 127.0f;

@@ -216,7 +216,9 @@ __device__ void quantise_tokens(const GemvProblem& p, int8_t* q_lds, float* as_l
         }
         __syncthreads();
         amax = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-        const float sa = (amax == 0.0f) ? 0.0f : 127.0f / amax;
+        // a zero token: amax == 0, or 127/amax not a finite fp32
+        const bool zero_token = !(127.0f / amax <= __FLT_MAX__);
+        const float sa = zero_token ? 0.0f : 127.0f / amax;
         int sum = 0;
         int8_t* qrow = q_lds + m * ldq;
         int8_t* qout = store ? p.q_out + static_cast<int64_t>(m) * p.Kp : nullptr;
@@ -261,7 +263,7 @@ __device__ void quantise_tokens(const GemvProblem& p, int8_t* q_lds, float* as_l
         if (tid == 0) {
             const int total = red_i[0] + red_i[1] + red_i[2] + red_i[3];
             float as = 0.0f;
-            if (amax != 0.0f) {
+            if (!zero_token) {
                 if (norm) {
                     const double ss = red_d[0] + red_d[1] + red_d[2] + red_d[3];
                     const double r = 1.0 / sqrt(ss / static_cast<double>(p.K) + static_cast<double>(p.eps));
@@ -762,7 +764,8 @@ __device__ __forceinline__ void quantise_batch(const PS& ps, int p_first, int M,
         const u32x4 wm = lds_read_4x16(red_f + j);            // the waves' maxima
         const float amax = fmaxf(fmaxf(__uint_as_float(wm.x), __uint_as_float(wm.y)),
                                  fmaxf(__uint_as_float(wm.z), __uint_as_float(wm.w)));
-        const float sa = (amax == 0.0f) ? 0.0f : 127.0f / amax;
+        // a zero token: amax == 0, or 127/amax not a finite fp32
+        const float sa = !(127.0f / amax <= __FLT_MAX__) ? 0.0f : 127.0f / amax;
         const int ldq = padded_q_row(P.Kp), nvec = P.K / 8;
         int8_t* qrow = q_lds + rows[j].qoff + rows[j].m * ldq;
         int8_t* qout = P.q_out != nullptr && t_begin <= P.tile0 ? P.q_out + static_cast<int64_t>(rows[j].m) * P.Kp
@@ -810,7 +813,7 @@ __device__ __forceinline__ void quantise_batch(const PS& ps, int p_first, int M,
                                      fmaxf(__uint_as_float(wm.z), __uint_as_float(wm.w)));
             const int total = static_cast<int>(ws.x) + static_cast<int>(ws.y) + static_cast<int>(ws.z) +
                               static_cast<int>(ws.w);
-            const float as = amax == 0.0f ? 0.0f : amax / 127.0f;
+            const float as = !(127.0f / amax <= __FLT_MAX__) ? 0.0f : amax / 127.0f;
             const int slot = 16 * (rows[j].p - p_first) + rows[j].m;
             lds_write_i32(as_lds + slot, __float_as_int(as));
             lds_write_i32(rs_lds + slot, total);

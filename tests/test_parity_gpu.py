@@ -83,6 +83,45 @@ def test_act_quant_strided_zero_and_extreme_tokens(orc):
     assert a[1].item() == 0 and not q[1].any()
 
 
+def test_tokens_at_the_fp32_scale_edge(orc):
+    """R5 at the edge of fp32: a token whose largest magnitude is 2^-122 (127/amax
+    overflows fp32) quantises as a zero token, one at 2^-121 as any other; every
+    quantiser -- ActQuant, RMSNorm -> ActQuant, the fused single-call decode
+    kernels and a grouped launch's batched quantiser -- agrees with the oracle."""
+    K = 2560
+    base = wl.draw_activation((4, K), seed=77).float()
+    x = base.clone()
+    x[1] = base[1] / base[1].abs().max() * 2.0 ** -122
+    x[2] = base[2] / base[2].abs().max() * 2.0 ** -121
+    x = x.to(torch.bfloat16)
+    xd = x.to(DEV)
+    q, a, r = tw.act_quant(xd)
+    qo, ao, ro = orc.act_quant(bits(x))
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(f32bits(a.cpu().numpy()), f32bits(ao))
+    assert np.array_equal(r.cpu().numpy(), ro)
+    assert ao[1] == 0 and not qo[1].any() and ao[2] > 0 and qo[2].any()
+    g = torch.ones(K, dtype=torch.bfloat16)
+    qn, an, rn = tw.rmsnorm_act_quant(xd, g.to(DEV), 1e-6)
+    qno, ano, rno = orc.rms_act_quant(bits(x), bits(g), 1e-6)
+    assert np.array_equal(qn.cpu().numpy(), qno) and np.array_equal(rn.cpu().numpy(), rno)
+    assert np.allclose(an.cpu().numpy(), ano, rtol=1e-5, atol=0) and ano[1] == 0
+    for N in (640, 13824):                   # split-K and streaming single calls
+        W = wl.draw_weight((N, K), seed=78)
+        ref = orc.linear(bits(x), bits(W))
+        check_y(tw.bitlinear(xd, tw.pack(W.to(DEV))), ref["y"])
+    items, refs = [], []
+    for i in range(4):                       # one token per problem: the batched quantiser
+        W = wl.draw_weight((2560, K), seed=80 + i)
+        items.append((xd[i:i + 1], tw.pack(W.to(DEV)), torch.full((1, 2560), float("nan"), device=DEV)))
+        refs.append(orc.linear(bits(x[i:i + 1]), bits(W))["y"])
+    group = tw.GroupedBitLinear(items)
+    group()
+    torch.cuda.synchronize()
+    for (_, _, y), ref in zip(items, refs):
+        check_y(y, ref)
+
+
 # -------------------------------------------------------------------- packer
 
 @pytest.mark.parametrize("N,K,segments,dist", [
