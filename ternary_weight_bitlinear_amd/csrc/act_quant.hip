@@ -69,17 +69,8 @@ __device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
 
 // Quantise 8 values with factor sa; returns their sum, writes 8 int8 codes.
 __device__ __forceinline__ int quant8(const float (&v)[8], float sa, uint2& out) {
-    int sum = 0;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float r = fminf(fmaxf(rne(v[i] * sa), -128.0f), 127.0f);
-        int c = static_cast<int>(r);
-        sum += c;
-        uint32_t byte = static_cast<uint32_t>(c) & 0xFFu;
-        if (i < 4) lo |= byte << (8 * i);
-        else hi |= byte << (8 * (i - 4));
-    }
+    uint32_t lo, hi;
+    const int sum = quant8_codes(v, sa, lo, hi);
     out = make_uint2(lo, hi);
     return sum;
 }

@@ -54,6 +54,29 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Round half to even (v_rndne_f32).
 __device__ __forceinline__ float rne(float v) { return __builtin_rintf(v); }
 
+// ActQuant codes of eight values: rne(fp32(v * sa)) as int8, packed little-
+// endian into lo (values 0-3) and hi (4-7); returns their sum.  For |p| below
+// 2^22, fp32(p + 1.5 * 2^23) equals 1.5 * 2^23 + rne(p) (its ulp is 1 and the
+// constant is even, so ties go to the even integer exactly as rne does), and
+// the low byte of its bits is rne(p) in two's complement.  Callers pass
+// |v| <= amax with sa = fp32(127 / amax) (or sa = 0), so |v * sa| rounds to at
+// most 127 and the [-128, 127] clamp of the definition never binds.  The
+// product and the sum are rounded separately (fp contraction is off).
+__device__ __forceinline__ int quant8_codes(const float (&v)[8], float sa, uint32_t& lo, uint32_t& hi) {
+    constexpr float kRound = 12582912.0f;                  // 1.5 * 2^23
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = __float_as_uint(__fadd_rn(__fmul_rn(v[i], sa), kRound));
+    // low bytes of two values, then of four: byte selectors 0 and 4 pick
+    // byte 0 of the second and the first operand, 12 gives zero
+    lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u),
+                               __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u), 0x05040100u);
+    hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0C0C0400u),
+                               __builtin_amdgcn_perm(b[5], b[4], 0x0C0C0400u), 0x05040100u);
+    return __builtin_amdgcn_sdot4(static_cast<int>(hi), 0x01010101,
+                                  __builtin_amdgcn_sdot4(static_cast<int>(lo), 0x01010101, 0, false), false);
+}
+
 // Four stored codes of one 32-bit packed word, lane p = 0..3: the bytes hold
 // elements 16j+4p+0..3 as unsigned values u in {0,1,2}.
 __device__ __forceinline__ uint32_t codes_of(uint32_t word, int p) {

@@ -223,15 +223,8 @@ __device__ void quantise_tokens(const GemvProblem& p, int8_t* q_lds, float* as_l
         int8_t* qrow = q_lds + m * ldq;
         int8_t* qout = store ? p.q_out + static_cast<int64_t>(m) * p.Kp : nullptr;
         auto quant8 = [&](const float (&v)[8]) {
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = static_cast<int>(fminf(fmaxf(rne(v[e] * sa), -128.0f), 127.0f));
-                sum += c;
-                const uint32_t byte = static_cast<uint32_t>(c) & 0xFFu;
-                if (e < 4) lo |= byte << (8 * e);
-                else hi |= byte << (8 * (e - 4));
-            }
+            uint32_t lo, hi;
+            sum += quant8_codes(v, sa, lo, hi);
             return u32x2{lo, hi};
         };
         for (int vi = tid; vi < ldq / 8; vi += kThreads) {
@@ -779,14 +772,7 @@ __device__ __forceinline__ void quantise_batch(const PS& ps, int p_first, int M,
                 const u32x4 w = raw[j][i];
                 const float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                                     bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int c = static_cast<int>(fminf(fmaxf(rne(v[e] * sa), -128.0f), 127.0f));
-                    sums[j] += c;
-                    const uint32_t byte = static_cast<uint32_t>(c) & 0xFFu;
-                    if (e < 4) lo |= byte << (8 * e);
-                    else hi |= byte << (8 * (e - 4));
-                }
+                sums[j] += quant8_codes(v, sa, lo, hi);
             }
             lds_write_i32(qrow + perm_pos(8 * vi), static_cast<int32_t>(lo));
             lds_write_i32(qrow + perm_pos(8 * vi + 4), static_cast<int32_t>(hi));
