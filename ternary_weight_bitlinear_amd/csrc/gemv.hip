@@ -1053,8 +1053,9 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     // and the w_scale of every row of its tiles (one 64-float DMA per tile,
     // after the token rows) into LDS.
     //
-    // Single tokens: the first batch's token loads go out before any weight
-    // DMA, so (loads completing in order) they wait behind none of them.  The
+    // Batched tokens (M <= 4, no norm): the first batch's token loads go out
+    // before any weight DMA, so (loads completing in order) they wait behind
+    // none of them.  The
     // prologue comes in two copies: where the ring's first steps all lie in
     // the workgroup's first tile (every K >= 64 * kDepth - 128), its DMAs are
     // straight-line code, and the compiler's waits for the tokens then leave
@@ -1090,8 +1091,8 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
             }
         };
         if (batch) {
-            // single tokens, up to kQuantBatch problems per pass; the batch
-            // ends with a barrier that publishes q, a_scale and the row sums.
+            // kQuantBatch token rows per pass; the batch ends with a barrier
+            // that publishes q, a_scale and the row sums.
             // The ring needs no barrier (each wave reads only what its own
             // DMAs wrote, after its own vmcnt wait), and w_scale is read only
             // after the loop's final wait and barrier, so its DMAs go out last.
