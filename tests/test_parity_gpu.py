@@ -424,12 +424,15 @@ def test_i2s_device_rejects_bad_fields():
 # --------------------------------------------------------------- W1.58A16
 
 @pytest.mark.parametrize("M,N,K", [(1, 640, 2560), (3, 257, 1152), (16, 100, 2048), (1, 2560, 6912),
-                                   (20, 130, 1152), (1, 1, 16), (2, 4352, 4304)])
+                                   (20, 130, 1152), (1, 1, 16), (2, 4352, 4304),
+                                   (1, 13824, 2560), (4, 6912, 6912), (16, 8192, 4096)])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float16])
 def test_linear_a16(orc, M, N, K, out, xdt):
     """bf16 or fp16 activations x ternary weights against the oracle's fp64 value,
-    within the bound the header states for an fp32 sum in the hardware's order."""
+    within the bound the header states for an fp32 sum in the hardware's order;
+    the last three shapes are the largest decode-size calls (8.4-11.9 MB of
+    packed weights, up to 16 tokens)."""
     x, W = wl.random_case(5100 + M * 3 + N, M, N, K, x_dist="normal_outliers")
     x = x.to(xdt)
     pw = tw.pack(W.to(DEV))
