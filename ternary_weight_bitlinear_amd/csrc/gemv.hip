@@ -1605,6 +1605,16 @@ const int32_t* stream_bounds_of(const GemvProblem* table, int count) {
 #ifndef BITNET_STREAM_PROBLEM_COST
 #define BITNET_STREAM_PROBLEM_COST 6
 #endif
+// The same for a problem the batched quantiser does not take (an input norm,
+// M > 4): its tokens are quantised one at a time (c2 with input norms ends
+// soonest at 12 of 6, 12, 20, 30 measured on MI355X).
+#ifndef BITNET_STREAM_PROBLEM_COST_SLOW
+#define BITNET_STREAM_PROBLEM_COST_SLOW 12
+#endif
+double problem_cost(const GemvProblem& P) {
+    return static_cast<double>(quantise_batch_fits(P) ? BITNET_STREAM_PROBLEM_COST : BITNET_STREAM_PROBLEM_COST_SLOW) *
+           P.M;
+}
 // Start cost of a CU's second workgroup, in the same k steps: its prologue
 // ends ~1.9 us after that of the CU's first workgroup (measured as above).
 #ifndef BITNET_STREAM_SECOND_START
@@ -1640,7 +1650,7 @@ int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_til
     int64_t bytes = 0;
     for (int np = 0; i < total_tiles && np < kStreamMaxProblems && p < count; ++np, ++p) {
         const GemvProblem& P = t[p];
-        const double enter = np > 0 ? static_cast<double>(BITNET_STREAM_PROBLEM_COST) * P.M : 0.0;
+        const double enter = np > 0 ? problem_cost(P) : 0.0;
         const int64_t enter_bytes =
             static_cast<int64_t>(P.M) * padded_q_row(P.Kp) * token_bytes + step_bytes * stream_steps(P.Kp);
         const double tile_cost = P.steps / rate;
@@ -1681,7 +1691,7 @@ bool stream_bounds(const GemvProblem* t, int count, int64_t total_tiles, int gri
     };
     double all = 0.0;
     for (int p = 0; p < count; ++p)
-        all += static_cast<double>(t[p].ntiles) * t[p].steps + static_cast<double>(BITNET_STREAM_PROBLEM_COST) * t[p].M;
+        all += static_cast<double>(t[p].ntiles) * t[p].steps + problem_cost(t[p]);
     double lo = 0.0, hi = all + 1.0;
     if (!cover(hi, false)) return false;
     for (int it = 0; it < 64 && hi - lo > 1e-3; ++it) {
