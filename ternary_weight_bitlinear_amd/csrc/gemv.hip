@@ -895,6 +895,33 @@ __device__ __forceinline__ void lds_read_a2(const void* p, v4i (&a)[2][4]) {
         : "v"(lds_addr(p))
         : "memory");
 }
+// The lane's ring words of two k steps and, for the lanes set in `rows` (the
+// others keep their registers), the 16-bit token-row operands of the same two
+// steps (2 x 128 bytes, 512 bytes apart), with one wait for all of them.
+__device__ __forceinline__ void lds_read_ring2_x16(const void* ring, const void* x, uint64_t rows, u32x4& w0,
+                                                   u32x4& w1, u32x4 (&a)[2][8]) {
+    uint64_t save;
+    asm volatile(
+        "s_mov_b64 %[save], exec\n\t"
+        "s_mov_b64 exec, %[rows]\n\t"
+        "ds_read_b128 %[a0], %[x]\n\tds_read_b128 %[a1], %[x] offset:16\n\t"
+        "ds_read_b128 %[a2], %[x] offset:32\n\tds_read_b128 %[a3], %[x] offset:48\n\t"
+        "ds_read_b128 %[a4], %[x] offset:64\n\tds_read_b128 %[a5], %[x] offset:80\n\t"
+        "ds_read_b128 %[a6], %[x] offset:96\n\tds_read_b128 %[a7], %[x] offset:112\n\t"
+        "ds_read_b128 %[b0], %[x] offset:512\n\tds_read_b128 %[b1], %[x] offset:528\n\t"
+        "ds_read_b128 %[b2], %[x] offset:544\n\tds_read_b128 %[b3], %[x] offset:560\n\t"
+        "ds_read_b128 %[b4], %[x] offset:576\n\tds_read_b128 %[b5], %[x] offset:592\n\t"
+        "ds_read_b128 %[b6], %[x] offset:608\n\tds_read_b128 %[b7], %[x] offset:624\n\t"
+        "s_mov_b64 exec, %[save]\n\t"
+        "ds_read_b128 %[w0], %[r]\n\tds_read_b128 %[w1], %[r] offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [save] "=&s"(save), [w0] "=&v"(w0), [w1] "=&v"(w1), [a0] "+v"(a[0][0]), [a1] "+v"(a[0][1]),
+          [a2] "+v"(a[0][2]), [a3] "+v"(a[0][3]), [a4] "+v"(a[0][4]), [a5] "+v"(a[0][5]), [a6] "+v"(a[0][6]),
+          [a7] "+v"(a[0][7]), [b0] "+v"(a[1][0]), [b1] "+v"(a[1][1]), [b2] "+v"(a[1][2]), [b3] "+v"(a[1][3]),
+          [b4] "+v"(a[1][4]), [b5] "+v"(a[1][5]), [b6] "+v"(a[1][6]), [b7] "+v"(a[1][7])
+        : [x] "v"(lds_addr(x)), [r] "v"(lds_addr(ring)), [rows] "s"(rows)
+        : "memory");
+}
 __device__ __forceinline__ void lds_read64(const void* p, v4i (&a)[4]) {
     asm volatile(
         "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\tds_read_b128 %2, %4 offset:32\n\t"
@@ -1315,24 +1342,17 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
 // The grouped W1.58A16 decode ("BitVLA -- 1.58-bit Vision-Language-Action on
 // Core AI", s5: 16-bit activations with the ternary weights): the streaming
 // kernel's work split, tiles and memory pipeline, with the bf16 (or, kF16,
-// fp16) token rows copied into LDS as given (no quantiser) and each lane's 16
-// bytes of codes (64 k of one row) expanded into the B operands of eight
-// v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x32_f16).  Lane group g of a wave takes the 16-byte chunk
-// 4s + g of k step s, as in the int8 kernel; its A operands are the 64
-// consecutive bf16 of the token row at the same k (128 bytes of LDS), so the
-// k order inside an MFMA differs from the int8 kernel's but pairs the same
-// x[m][k] with t[n][k].  The fp32 sums are scaled by w_scale alone.
-
-// 64 consecutive bf16 of a token row (8 A operands of 8 k).
-__device__ __forceinline__ void lds_read128(const void* p, u32x4 (&a)[8]) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\tds_read_b128 %2, %8 offset:32\n\t"
-        "ds_read_b128 %3, %8 offset:48\n\tds_read_b128 %4, %8 offset:64\n\tds_read_b128 %5, %8 offset:80\n\t"
-        "ds_read_b128 %6, %8 offset:96\n\tds_read_b128 %7, %8 offset:112\n\ts_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
-        : "v"(lds_addr(p))
-        : "memory");
-}
+// fp16) token rows copied into LDS unquantised and each lane's 16 bytes of
+// codes (64 k of one row) expanded into the B operands of eight
+// v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x32_f16).  Lane group g of a
+// wave takes the 16-byte chunk 4s + g of k step s, as in the int8 kernel;
+// its A operands are the 64 token-row values at the same k (128 bytes of
+// LDS).  The B operand is 2t, one packed 16-bit multiply-add per two values
+// (expand_twice_interleaved), in the k order 0 2 1 3 within each 4, and the
+// LDS copy of x is stored in that order, so each MFMA still pairs x[m][k]
+// with t[n][k]; the fp32 sums, exactly twice those of t, are halved and
+// scaled by w_scale.  Per pass (two k steps) one LDS wait covers the ring
+// words and the token rows.
 
 template <bool kGrouped, bool kOutBf16, bool kF16 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITNET_STREAM_PER_CU)))
@@ -1348,7 +1368,7 @@ void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ 
     if (t_begin >= t_end) return;                       // workgroup-uniform
 
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // scalar ring addresses
     const int col = lane % 16;
     const int grp = lane / 16;
     int8_t* const ring = g_stream_ring + wave * 1024;   // slot j of this wave: ring + j * kThreads * 16
@@ -1359,23 +1379,24 @@ void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ 
     __amdgpu_buffer_rsrc_t rsrc = packed_rsrc(PP);
     int tp = t_begin, sp = 0, steps_p = stream_steps(PP.Kp), chunks_p = PP.Kp / 64, slot_p = 0;
     uint32_t rowoff = static_cast<uint32_t>(((tp - PP.tile0) * 64 + wave * 16 + col) * (PP.Kp / 4) + 16 * grp);
+    auto next_tile = [&]() {
+        sp = 0;
+        ++tp;
+        rowoff += static_cast<uint32_t>(64 * (PP.Kp / 4));
+        if (tp < t_end && tp == PP.tile0 + PP.ntiles) {
+            PP = ps.get(++pp);
+            rsrc = packed_rsrc(PP);
+            steps_p = stream_steps(PP.Kp);
+            chunks_p = PP.Kp / 64;
+            rowoff = static_cast<uint32_t>((wave * 16 + col) * (PP.Kp / 4) + 16 * grp);
+        }
+    };
     auto produce = [&]() {
         const uint32_t off = tp < t_end && 4 * sp + grp < chunks_p ? rowoff + 64u * static_cast<uint32_t>(sp)
                                                                    : kStreamOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(ring + slot_p * kThreads * 16), 16, off, 0, 0, 0);
         slot_p = slot_p + 1 == kDepth ? 0 : slot_p + 1;
-        if (tp < t_end && ++sp == steps_p) {
-            sp = 0;
-            ++tp;
-            rowoff += static_cast<uint32_t>(64 * (PP.Kp / 4));
-            if (tp < t_end && tp == PP.tile0 + PP.ntiles) {
-                PP = ps.get(++pp);
-                rsrc = packed_rsrc(PP);
-                steps_p = stream_steps(PP.Kp);
-                chunks_p = PP.Kp / 64;
-                rowoff = static_cast<uint32_t>((wave * 16 + col) * (PP.Kp / 4) + 16 * grp);
-            }
-        }
+        if (tp < t_end && ++sp == steps_p) next_tile();
     };
 #pragma unroll
     for (int i = 0; i < kDepth - 2; ++i) produce();
@@ -1408,7 +1429,7 @@ void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ 
             for (int i = threadIdx.x; i < Pi.M * (ldq / 8); i += kThreads) {
                 const int m = i / (ldq / 8), k = 8 * (i % (ldq / 8));
                 const u32x4 v = k < Pi.K ? gload<u32x4>(xg + static_cast<int64_t>(m) * Pi.ldx + k) : u32x4{0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4*>(x_lds + off + m * ldq + k) = v;
+                *reinterpret_cast<u32x4*>(x_lds + off + m * ldq + k) = interleave_x_pairs(v);
             }
             off += Pi.M * ldq;
         }
@@ -1426,56 +1447,56 @@ void gemv_stream_a16_kernel(GemvProblem single, const GemvProblem* __restrict__ 
     const bool m_ok = col < P.M;                        // M is shared by the group
     const uint16_t* xbase = x_lds + (m_ok ? col : 0) * padded_q_row(P.Kp) + 64 * grp;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    u32x4 a[8];
+    u32x4 a2[2][8];                                     // zero where the lane has no token
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a2[i][e] = u32x4{0u, 0u, 0u, 0u};
+    const TwiceMultipliers mul;
+    const uint64_t rows_mask = __builtin_amdgcn_ballot_w64(m_ok);
     while (true) {
         produce();
         produce();
         wait_vm<kDepth - 2>();                          // both steps' ring loads have landed
         u32x4 w[2];
-        lds_read_ring2(ring + slot_c * kThreads * 16 + 16 * lane, w[0], w[1]);
+        lds_read_ring2_x16(ring + slot_c * kThreads * 16 + 16 * lane, xbase + 256 * sc, rows_mask, w[0], w[1], a2);
         slot_c = slot_c + 2 == kDepth ? 0 : slot_c + 2;
+        // MFMA t of the pass takes field pair t % 2 of word (t / 2) % 4 of step t / 8; its
+        // B operand is built while MFMA t - 1 runs
+        const uint32_t words[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+        u32x4 bn = expand_twice_interleaved(words[0], 0, mul);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (m_ok) lds_read128(xbase + 256 * (sc + i), a);
-            const uint32_t words[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    if constexpr (kF16)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[2 * j + h]),
-                                                                     __builtin_bit_cast(f16x8, expand_f16(words[j], h)),
-                                                                     acc, 0, 0, 0);
-                    else
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a[2 * j + h]), __builtin_bit_cast(bf16x8, expand_bf16_twice(words[j], h)),
-                            acc, 0, 0, 0);
-                }
+        for (int t = 0; t < 16; ++t) {
+            const u32x4 b = bn;
+            if (t + 1 < 16) bn = expand_twice_interleaved(words[(t + 1) / 2], (t + 1) % 2, mul);
+            if constexpr (kF16)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a2[t / 8][t % 8]),
+                                                             __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+            else
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a2[t / 8][t % 8]),
+                                                              __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
         }
         sc += 2;
-        if (sc < steps_c) continue;
-        // tile epilogue: lane holds C[m = 4*grp + r][row] of this wave's 16 rows
-        sc = 0;
-        {
+        if (sc >= steps_c) {
+            // tile epilogue: lane holds C[m = 4*grp + r][row] of this wave's 16 rows
+            sc = 0;
+            const f32x4 sum = acc * 0.5f;               // the operand held 2t (exact)
             const int row = (tc - t_begin) * 64 + wave * 16 + col;
-            if constexpr (!kF16) acc = acc * 0.5f;      // the bf16 operand held 2t (exact)
-            const int32_t bits[4] = {__float_as_int(acc[0]), __float_as_int(acc[1]), __float_as_int(acc[2]),
-                                     __float_as_int(acc[3])};
+            const int32_t bits[4] = {__float_as_int(sum[0]), __float_as_int(sum[1]), __float_as_int(sum[2]),
+                                     __float_as_int(sum[3])};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = 4 * grp + r;
                 if (m < P.M) lds_write_i32(out_lds + m * wg_rows + row, bits[r]);
             }
-        }
-        acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        if (++tc == t_end) break;
-        if (tc == P.tile0 + P.ntiles) {
-            xoff += P.M * padded_q_row(P.Kp);
-            P = ps.get(++pc);
-            steps_c = stream_steps(P.Kp);
-            xbase = x_lds + xoff + (m_ok ? col : 0) * padded_q_row(P.Kp) + 64 * grp;
+            acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (++tc == t_end) break;
+            if (tc == P.tile0 + P.ntiles) {
+                xoff += P.M * padded_q_row(P.Kp);
+                P = ps.get(++pc);
+                steps_c = stream_steps(P.Kp);
+                xbase = x_lds + xoff + (m_ok ? col : 0) * padded_q_row(P.Kp) + 64 * grp;
+            }
         }
     }
     wait_vm<0>();                                       // ring loads past the end land before the LDS is reused
