@@ -179,10 +179,13 @@ bitnet_status_t bitnet_act_quant(hipStream_t stream, const void* x, bitnet_dtype
  *
  * x        [M, K], row stride ldx >= K, dtype x_dtype (BF16 or F32).
  * up       NULL, or [M, K] with x's dtype and row stride: the input is then
- *          h = silu(x) * up (x being the gate) = x / (1 + e) * up in fp32,
- *          with e = exp(-x) by fixed fp32 steps (Cody-Waite reduction by
- *          ln 2, degree-7 Taylor polynomial, scaling by 2^n; +inf above 88,
- *          0 below -88), so results do not depend on a math library.
+ *          h = silu(x) * up (x being the gate) = x * sigmoid(x) * up in
+ *          fp32, with e = exp(-|x|) (t * log2(e) split into two fp32 parts,
+ *          the hardware exp2 of the fraction, a scaling by 2^n) and
+ *          sigmoid(x) = rcp(1 + e) for x >= 0, e * rcp(1 + e) below: h within
+ *          4.3 fp32 ulps of the exact silu(x) * up for |x| <= 87, so int8
+ *          codes whose unrounded value lies within 2e-4 of a .5 tie may
+ *          differ by one from those of the exact h.
  * norm_w   [K] RMSNorm weight g, dtype norm_dtype (BF16 or F32).
  * eps      finite, >= 0.
  * RMSNorm(h)_k = h_k * g_k * r with r = 1/sqrt(mean_k(h_k^2) + eps).  r is

@@ -15,8 +15,8 @@
 // RMSNorm scales a token by one positive factor r = 1/sqrt(mean(x^2) + eps),
 // which ActQuant's codes do not see: the codes are those of z = x * g (fp32
 // products) and r enters a_scale = amax(z) * r / 127, evaluated in fp64 with
-// the squares summed in fp64.  silu(a) * u is evaluated in fp32 with the
-// fixed-step exp of device_common.h.
+// the squares summed in fp64.  silu(a) * u is evaluated in fp32 with
+// silu_mul of device_common.h (within 4.3 fp32 ulps of the exact value).
 //
 // One wave per token (below).  The kernel is HBM-bound: 2 B read + 1 B
 // written per element for bf16 input.

@@ -141,8 +141,8 @@ __host__ __device__ __forceinline__ int padded_q_row(int Kp) {
 }
 
 // 8 values whose codes are taken, of vector vi of token row m: x, or with a
-// norm weight z = h * g where h = x or h = silu(x) * up (fp32, fixed-step
-// exp); `squares` gathers the fp64 sum of h^2 that RMSNorm needs.  The norm
+// norm weight z = h * g where h = x or h = silu(x) * up (fp32, exp_f32 and
+// rcp); `squares` gathers the fp64 sum of h^2 that RMSNorm needs.  The norm
 // factor r > 0 is common to the token, so the codes of RMSNorm(h) are those of
 // z and r enters a_scale only ("BitNet-Embeddings-0.6B/270M: I2_S Conversion
 // and Inference Optimization Guide", s3.1: each projection normalises its

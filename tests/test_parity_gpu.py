@@ -185,10 +185,10 @@ def check_y_tol(y_dev: torch.Tensor, y_orc: np.ndarray, rel_tol: float = 1e-5):
     assert np.all((rel <= rel_tol) | (y == y_orc)), float(rel.max())
 
 
-# The kernels evaluate silu(gate) * up with their own fp32 steps (an exp built
-# from a Cody-Waite reduction and a degree-7 polynomial: within 4 fp32 ulps of
-# the true silu(a) * u); the oracle evaluates the definition in fp64 and rounds
-# once.  Policy for the gated input:
+# The kernels evaluate silu(gate) * up with their own fp32 steps (exp from a
+# two-part split of t * log2(e), the hardware exp2 and an exact 2^n scaling,
+# then a reciprocal: within 4.3 fp32 ulps of the true silu(a) * u); the oracle
+# evaluates the definition in fp64 and rounds once.  Policy for the gated input:
 #   * a code may differ by one only where the oracle's value before rounding,
 #     v = fp32(h * g) * fp32(127 / amax) (exact product), lies within GATE_WINDOW
 #     of a .5 tie.  GATE_WINDOW: h differs by <= 4.5 * 2^-23 relative, then z,
