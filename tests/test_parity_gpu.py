@@ -52,6 +52,7 @@ def _announce(request):
 @pytest.mark.parametrize("M,K,dist", [
     (1, 16, "normal"), (1, 2560, "normal_outliers"), (3, 144, "normal"), (17, 1152, "normal"),
     (64, 4304, "student_t_channels"), (5, 6912, "normal"), (2, 20480, "normal"), (300, 1024, "normal"),
+    (4, 8192, "normal_outliers"), (3, 8208, "normal"),   # last K of the per-token workgroup kernel, first past it
 ])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_act_quant(orc, M, K, dist, dtype):
@@ -81,6 +82,27 @@ def test_act_quant_strided_zero_and_extreme_tokens(orc):
     assert np.array_equal(f32bits(a.cpu().numpy()), f32bits(ao))
     assert np.array_equal(r.cpu().numpy(), ro)
     assert a[1].item() == 0 and not q[1].any()
+
+
+def test_act_quant_long_rows_strided_zero_and_extreme_tokens(orc):
+    """Rows long enough for one workgroup per token (4096 < K <= 8192), not
+    16-byte aligned, with an all-zero token, huge and tiny values and exact ties."""
+    K = 4112
+    base = wl.draw_activation((6, K + 40), seed=98).to(DEV)
+    base[1].zero_()
+    base[2] *= 2.0 ** 100
+    base[3] *= 2.0 ** -100
+    base[4, 3] = 254.0
+    base[4, :3] = torch.tensor([1.0, 3.0, 5.0])
+    base[4, 4:] = 0
+    base[5, :] = base[5, :] / base[5, :].abs().max() * 2.0 ** -122   # zero token by the fp32 edge
+    x = base[:, :K]
+    q, a, r = tw.act_quant(x)
+    qo, ao, ro = orc.act_quant(bits(x))
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(f32bits(a.cpu().numpy()), f32bits(ao))
+    assert np.array_equal(r.cpu().numpy(), ro)
+    assert a[1].item() == 0 and not q[1].any() and a[5].item() == 0
 
 
 def test_tokens_at_the_fp32_scale_edge(orc):
@@ -256,7 +278,7 @@ def test_rmsnorm_act_quant(orc, M, K, dist, x_dtype, g_dtype):
     _check_scale(a, ao)
 
 
-@pytest.mark.parametrize("M,K", [(1, 6912), (4, 2048), (9, 16), (2, 20480)])
+@pytest.mark.parametrize("M,K", [(1, 6912), (4, 2048), (9, 16), (2, 20480), (3, 8192)])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_gated_rmsnorm_act_quant(orc, M, K, dtype):
     """The down projection's input: silu(gate) * up, then RMSNorm and ActQuant;
