@@ -93,8 +93,8 @@ __device__ __forceinline__ void load_input8(const T* xr, const T* ur, const void
     }
     if constexpr (kMode != kPlain) {
         float gv[8];
-        if (g_bf16) load8<uint16_t, false>(static_cast<const uint16_t*>(g) + vi * 8, gv);
-        else load8<float, false>(static_cast<const float*>(g) + vi * 8, gv);
+        if (g_bf16) load8<uint16_t, kAligned>(static_cast<const uint16_t*>(g) + vi * 8, gv);
+        else load8<float, kAligned>(static_cast<const float*>(g) + vi * 8, gv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             squares += static_cast<double>(z[e]) * static_cast<double>(z[e]);
@@ -305,8 +305,9 @@ hipError_t launch_mode(const void* x, const void* up, bool x_bf16, int64_t M, in
                        const void* g, bool g_bf16, float eps, int8_t* q, float* a_scale, int32_t* q_rowsum,
                        int64_t Kp, hipStream_t stream) {
     const size_t esize = x_bf16 ? 2 : 4;
+    // 16-byte vector loads of x, up and g, else element loads of all three
     const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(up) % 16 == 0) &&
-                         ((ldx * esize) % 16 == 0);
+                         ((ldx * esize) % 16 == 0) && (reinterpret_cast<uintptr_t>(g) % 16 == 0);
     if (x_bf16) {
         auto* p = static_cast<const uint16_t*>(x);
         auto* u = static_cast<const uint16_t*>(up);

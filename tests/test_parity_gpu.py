@@ -309,6 +309,22 @@ def test_rmsnorm_strided_unaligned_and_eps_zero(orc):
     _check_scale(a, ao)
 
 
+@pytest.mark.parametrize("K", [2560, 6912])
+def test_rmsnorm_unaligned_norm_weight(orc, K):
+    """Aligned token rows with a norm weight that is not 16-byte aligned (a view
+    one element into its buffer): every input then takes element loads."""
+    M = 5
+    x = wl.draw_activation((M, K), seed=K + 3, dist="normal_outliers")
+    g = _norm_weight(K, K + 11, torch.bfloat16)
+    gbuf = torch.empty(K + 1, dtype=torch.bfloat16, device=DEV)
+    gbuf[1:] = g.to(DEV)
+    q, a, r = tw.rmsnorm_act_quant(x.to(DEV), gbuf[1:], 1e-6)
+    qo, ao, ro = orc.rms_act_quant(bits(x), bits(g), 1e-6)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(r.cpu().numpy(), ro)
+    _check_scale(a, ao)
+
+
 def test_rmsnorm_then_linear(orc):
     """Normalised, quantised tokens through the decode and GEMM paths against the
     oracle's integer dot and epilogue on its own codes."""
