@@ -362,6 +362,20 @@ __global__ __launch_bounds__(kThreads) void gemv_splitk_kernel(GemvProblem p) {
         }
     };
     load_b(0);   // in flight during the fused quantisation
+    // the epilogue's scales of this thread's output (token threadIdx.x / 16,
+    // row n0 + threadIdx.x % 16), loaded now so that no memory round trip
+    // follows the reduction
+    const int em = threadIdx.x / 16, en = n0 + threadIdx.x % 16;
+    const bool e_ok = em < p.M && en < p.N;
+    const float ws_e = e_ok ? gload<float>(p.w_scale + en) : 0.0f;
+    int32_t rs_e = 0;
+    float as_e = 0.0f;
+    if constexpr (!kFused) {
+        if (e_ok) {
+            rs_e = gload<int32_t>(p.q_rowsum + em);
+            as_e = gload<float>(p.a_scale + em);
+        }
+    }
     if constexpr (kFused)
         quantise_tokens<kXBf16, 4, false>(p, q_lds, as_lds, rs_lds, red_f, red_i, red_d,
                                           p.q_out != nullptr && blockIdx.x == 0);
@@ -390,23 +404,16 @@ __global__ __launch_bounds__(kThreads) void gemv_splitk_kernel(GemvProblem p) {
     for (int r = 0; r < 4; ++r) part[wave][4 * grp + r][col] = acc[r];
     __syncthreads();
 
-    const int m = threadIdx.x / 16;
-    const int nc = threadIdx.x % 16;
-    const int n = n0 + nc;
-    if (m < p.M && n < p.N) {
+    if (e_ok) {
+        const int nc = threadIdx.x % 16;
         int s = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) s += part[w][m][nc];
-        int32_t rs;
-        float as;
+        for (int w = 0; w < kWaves; ++w) s += part[w][em][nc];
         if constexpr (kFused) {
-            rs = rs_lds[m];
-            as = as_lds[m];
-        } else {
-            rs = gload<int32_t>(p.q_rowsum + m);
-            as = gload<float>(p.a_scale + m);
+            rs_e = rs_lds[em];
+            as_e = as_lds[em];
         }
-        store_output<kOutBf16>(p, m, n, s - rs, as, gload<float>(p.w_scale + n));
+        store_output<kOutBf16>(p, em, en, s - rs_e, as_e, ws_e);
     }
 }
 

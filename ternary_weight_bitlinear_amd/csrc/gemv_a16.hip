@@ -48,6 +48,12 @@ __global__ __launch_bounds__(kThreads) void gemv_a16_kernel(const uint16_t* __re
     const uint8_t* brow = packed + static_cast<int64_t>(n_ok ? n0 + col : 0) * (Kp / 4);
     const uint16_t* xrow = x + static_cast<int64_t>(m_ok ? m0 + col : 0) * ldx;
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    // w_scale of this thread's output (token m0 + threadIdx.x / 16, row
+    // n0 + threadIdx.x % 16), loaded first so that no memory round trip
+    // follows the reduction
+    const int em = threadIdx.x / 16, en = n0 + threadIdx.x % 16;
+    const bool e_ok = m0 + em < M && en < N;
+    const float ws_e = e_ok ? gload<float>(w_scale + en) : 0.0f;
 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     // The loop and its exits are wave-uniform (an MFMA needs the whole wave);
@@ -85,18 +91,17 @@ __global__ __launch_bounds__(kThreads) void gemv_a16_kernel(const uint16_t* __re
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[wave][4 * grp + r][col] = acc[r];
     __syncthreads();
-    const int m = threadIdx.x / 16, nc = threadIdx.x % 16;
-    const int n = n0 + nc;
-    if (m0 + m < M && n < N) {
+    if (e_ok) {
+        const int nc = threadIdx.x % 16;
         float s = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) s += part[w][m][nc];
+        for (int w = 0; w < kWaves; ++w) s += part[w][em][nc];
         if constexpr (!kF16) s = s * 0.5f;             // the bf16 operand held 2t (exact)
-        const float v = s * gload<float>(w_scale + n);
+        const float v = s * ws_e;
         if constexpr (kOutBf16)
-            gstore<uint16_t>(static_cast<uint16_t*>(y) + (m0 + m) * ldy + n, f32_to_bf16(v));
+            gstore<uint16_t>(static_cast<uint16_t*>(y) + (m0 + em) * ldy + en, f32_to_bf16(v));
         else
-            gstore<float>(static_cast<float*>(y) + (m0 + m) * ldy + n, v);
+            gstore<float>(static_cast<float*>(y) + (m0 + em) * ldy + en, v);
     }
 }
 
