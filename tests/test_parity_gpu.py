@@ -818,6 +818,27 @@ def test_grouped_kernels_agree_with_oracle(orc, M, x_dtype, y_dtype, monkeypatch
                 check_y(y, ref["y"])
 
 
+@pytest.mark.parametrize("M,y_dtype", [(5, torch.float32), (8, torch.bfloat16), (13, torch.float32),
+                                       (16, torch.bfloat16)])
+def test_grouped_persistent_many_tokens(orc, M, y_dtype, monkeypatch):
+    """The persistent kernel at M = 5 to 16 with bf16 tokens (more tokens than the
+    streaming kernel's LDS share takes): every launch of the reused plan matches
+    the oracle.  Shapes whose M token rows (K rounded up to 512 bytes) exceed the
+    plan's 64 KiB of LDS are left out."""
+    shapes = [(N, K) for N, K in GROUP_SHAPES if M * (-(-K // 512) * 512) <= 65536]
+    items, refs = _group_case(orc, M, torch.bfloat16, y_dtype, shapes, 1900 + 10 * M)
+    monkeypatch.setenv("BITNET_GROUP_KERNEL", "persistent")
+    group = tw.GroupedBitLinear(items)
+    assert group.kernel == "persistent"
+    for rep in range(2):
+        for _, _, y in items:
+            y.fill_(float("nan"))
+        group()
+        torch.cuda.synchronize()
+        for (_, _, y), ref in zip(items, refs):
+            check_y(y, ref["y"])
+
+
 @pytest.mark.parametrize("M", [1, 2, 4])
 def test_grouped_many_problems_per_workgroup(orc, M):
     """A six-layer mix of a decoder's projections (each workgroup's share spans
