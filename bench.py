@@ -396,7 +396,8 @@ def bench_configs(tw, wl, torch, steps, warmup):
     M = 2, 4, 8 (grouped), the c3 (SigLIP, M = 2048), c4 (embedder, M = 8192)
     and c5 prefill GEMMs per shape with bf16 and fp32 output (each against the
     MFMA peak and its applicable roofline), with each workload's zero-code
-    fraction, and ActQuant alone at the c5 inputs."""
+    fraction, c4 again with its shared-input projections fused (q|k|v and
+    gate|up as segmented weights), and ActQuant alone at the c5 inputs."""
     steps = max(3, min(steps, 10))
     out = {}
     # c1 ring
@@ -447,21 +448,16 @@ def bench_configs(tw, wl, torch, steps, warmup):
     torch.cuda.empty_cache()
     # prefill GEMMs per shape
 
-    def gemm_shapes(name, out_dtypes):
-        """Every projection of a prefill workload with each output dtype: int8 TOPS,
-        % of the MFMA peak and % of the shape's applicable min(MFMA, HBM) roofline."""
-        w = wl.WORKLOADS[name]
-        res = dict(workload=w.name)
-        pws = []
-        for i, p in enumerate(w.projections):
-            pws.append(tw.pack(wl.weight_for(w, i, device="cuda"), p.segments or None))
-        res["zero_code_fraction"] = zero_fraction(pws)
+    def time_projections(M, projs, out_dtypes):
+        """int8 TOPS of each projection (name, N, K, packed weight, activation) with each
+        output dtype, % of the MFMA peak and % of the shape's applicable min(MFMA, HBM)
+        roofline, and the aggregate over the projections."""
+        res = dict(zero_code_fraction=zero_fraction([pw for _, _, _, pw, _ in projs]))
+        quant = [tw.act_quant(x) for *_, x in projs]
         for out_dtype in out_dtypes:
             rows, tot_ops, tot_ms, tot_bound = [], 0, 0.0, 0.0
-            for i, p in enumerate(w.projections):
-                pw = pws[i]
-                q, a, r = tw.act_quant(wl.activation_for(w, i, device="cuda"))
-                y = torch.empty((w.M, p.N), dtype=out_dtype, device="cuda")
+            for (pname, N, K, pw, _), (q, a, r) in zip(projs, quant):
+                y = torch.empty((M, N), dtype=out_dtype, device="cuda")
                 gg = torch.cuda.CUDAGraph()
                 tw.linear(q, a, r, pw, out=y)
                 torch.cuda.synchronize()
@@ -469,22 +465,53 @@ def bench_configs(tw, wl, torch, steps, warmup):
                     for _ in range(4):
                         tw.linear(q, a, r, pw, out=y)
                 ms_l = time_region(torch, gg.replay, steps, 2) / 4
-                ops = 2 * w.M * p.N * p.K
+                ops = 2 * M * N * K
                 tops = ops / (ms_l * 1e-3) / 1e12
-                roof = applicable_roofline(w.M, p.N, p.K, y.element_size(), ms_l * 1e-3)
-                rows.append(dict(shape=f"{p.name} {w.M}x{p.N}x{p.K}", us=ms_l * 1e3, tops=tops, **roof))
+                roof = applicable_roofline(M, N, K, y.element_size(), ms_l * 1e-3)
+                rows.append(dict(shape=f"{pname} {M}x{N}x{K}", us=ms_l * 1e3, tops=tops, **roof))
                 tot_ops += ops
                 tot_ms += ms_l
                 tot_bound += roof["frac_of_applicable"] * ms_l
-                del q, a, r, y, gg
+                del y, gg
             agg = tot_ops / (tot_ms * 1e-3) / 1e12
             res[str(out_dtype).replace("torch.", "")] = dict(
                 tops=agg, frac_of_mfma_peak=agg / INT8_PEAK_TOPS, frac_of_applicable=tot_bound / tot_ms, shapes=rows)
-        del pws
+        del quant
+        return res
+
+    def gemm_shapes(name, out_dtypes):
+        """Every projection of a prefill workload, one launch each."""
+        w = wl.WORKLOADS[name]
+        projs = [(p.name, p.N, p.K, tw.pack(wl.weight_for(w, i, device="cuda"), p.segments or None),
+                  wl.activation_for(w, i, device="cuda")) for i, p in enumerate(w.projections)]
+        res = dict(workload=w.name, **time_projections(w.M, projs, out_dtypes))
+        del projs
+        torch.cuda.empty_cache()
+        return res
+
+    def gemm_c4_shared_inputs(out_dtypes):
+        """c4 with the projections that read the same input packed as one segmented
+        weight, as c5 packs its gate|up and q|k|v: q|k|v (N = 4096, segments
+        2048/1024/1024) and gate|up (N = 6144, 3072/3072), each segment with its own
+        scale, so every code and output equals that of the separate projection; o and
+        down as before.  Four launches instead of seven for the same int ops."""
+        w = wl.WORKLOADS["c4"]
+        idx = {p.name: i for i, p in enumerate(w.projections)}
+        projs = []
+        for label, members in (("q|k|v", ("q_proj", "k_proj", "v_proj")), ("o", ("o_proj",)),
+                               ("gate|up", ("gate_proj", "up_proj")), ("down", ("down_proj",))):
+            ps = [w.projections[idx[m]] for m in members]
+            W = torch.cat([wl.weight_for(w, idx[m], device="cuda") for m in members], 0)
+            pw = tw.pack(W, [p.N for p in ps] if len(ps) > 1 else None)
+            projs.append((label, W.shape[0], ps[0].K, pw, wl.activation_for(w, idx[members[0]], device="cuda")))
+            del W
+        res = dict(workload=w.name + "-shared-input-projections-fused", **time_projections(w.M, projs, out_dtypes))
+        del projs
         torch.cuda.empty_cache()
         return res
     out["gemm_c3"] = gemm_shapes("c3", (torch.bfloat16, torch.float32))
     out["gemm_c4"] = gemm_shapes("c4", (torch.bfloat16, torch.float32))
+    out["gemm_c4_shared_inputs_fused"] = gemm_c4_shared_inputs((torch.bfloat16, torch.float32))
     out["gemm_c5"] = gemm_shapes("c5", (torch.bfloat16, torch.float32))
     # ActQuant alone (HBM-bound: 2 B in + 1 B out per element, 8 B per token)
     aq = {}
