@@ -86,10 +86,24 @@ def setup_decode(tw, wl, torch, layers: int):
     return items, nbytes
 
 
-def time_region(torch, fn, steps: int, warmup: int):
+# Measured on MI355X: after the GPU has been idle (setup, another leg), its
+# throughput climbs for tens of milliseconds of continuous work (the c2 decode
+# from 5.09 to a steady 5.36-5.38 TB/s over ~10 ms of launches, the c5 prefill
+# step from 1.56 to 1.82 int8 POPS over ~40 ms), so every timed region follows
+# a warm-up: the headline legs exactly `warmup` steps (default 300, 30 ms of
+# decode launches), the others at least MIN_WARM_MS of work.
+MIN_WARM_MS = 30.0
+
+
+def time_region(torch, fn, steps: int, warmup: int, min_warm_ms: float = MIN_WARM_MS):
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_warm_ms:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(steps):
@@ -151,7 +165,7 @@ def zero_fraction(pws) -> float:
 def bench_decode(tw, wl, torch, steps, warmup, per_call: bool):
     items, nbytes = setup_decode(tw, wl, torch, 30)
     group = tw.GroupedBitLinear(items)
-    ms = time_region(torch, group, steps, warmup)     # one launch per step
+    ms = time_region(torch, group, steps, warmup, min_warm_ms=0.0)     # one launch per step; exactly W warm-up
     gbps = nbytes / (ms * 1e-3) / 1e9
     per = dispatch_stats(time_each(torch, group, max(steps, 20)))
     src = kernel_source_hash("gemv.hip", "gemv.h", "device_common.h", "codes_bf16.h")
@@ -363,7 +377,7 @@ def bench_prefill(tw, wl, torch, steps, warmup, out_dtype):
     with torch.cuda.graph(g_gemm):
         for _ in range(reps):
             gemms()
-    ms = time_region(torch, g_step.replay, steps, warmup)
+    ms = time_region(torch, g_step.replay, steps, warmup, min_warm_ms=0.0)   # exactly W warm-up steps
     gemm_ms = time_region(torch, g_gemm.replay, max(steps // 2, 3), 2) / (reps * len(projs))
     per_shape = {}
     for p, pw, x, q, a, r, y in projs:
@@ -635,8 +649,10 @@ def _cpu_prefill(wl, torch, budget_s: float, nthreads):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps before each headline timed region (the GPU's throughput climbs "
+                         "for tens of ms after idle; 300 decode launches are ~30 ms)")
     ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="budget per CPU-baseline leg (half on all host threads, half on one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
