@@ -263,7 +263,7 @@ def bench_a16(tw, wl, torch, steps, warmup):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         calls()
-    ms = time_region(torch, g.replay, steps, warmup)
+    ms = time_region(torch, g.replay, steps, 2)     # a graph of many calls: 2 replays + the minimum warm-up time
     out = dict(stream=dict(value=nbytes / (ms * 1e-3) / 1e9, unit="GB/s", ms_per_step=ms, launches_per_step=210))
     group = tw.GroupedBitLinear(items, a16=True)
     msg = time_region(torch, group, steps, warmup)
@@ -434,7 +434,7 @@ def bench_configs(tw, wl, torch, steps, warmup):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         calls()
-    ms = time_region(torch, g.replay, steps, warmup)
+    ms = time_region(torch, g.replay, steps, 2)     # a graph of many calls: 2 replays + the minimum warm-up time
     out["c1_ring_single_calls"] = dict(value=nb / (ms * 1e-3) / 1e9, unit="GB/s", us_per_call=ms * 1e3 / len(ring),
                                        calls=len(ring), bytes=nb)
     group = tw.GroupedBitLinear(ring)
