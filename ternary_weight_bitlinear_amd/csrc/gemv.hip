@@ -973,6 +973,12 @@ __device__ __forceinline__ void stream_share(const Problems<kGrouped>& ps, const
         p_first = span[0];
         p_last = span[1];
         batch = span[2] != 0;
+        // The planner keeps every record within these bounds (the span indexes
+        // kStreamMaxProblems-sized LDS arrays); a record outside them makes
+        // the workgroup do nothing rather than touch memory outside its own.
+        if (p_first < 0 || p_last < p_first || p_last >= ps.count || p_last - p_first >= kStreamMaxProblems ||
+            t_begin < 0 || t_end > total_tiles)
+            t_end = t_begin;
     } else {
         t_begin = first_tile_from_step(ps, share_start(total_steps, b, G, n_first), total_tiles);
         t_end = first_tile_from_step(ps, share_start(total_steps, b + 1, G, n_first), total_tiles);
