@@ -846,6 +846,21 @@ __device__ __forceinline__ void quantise_batch(const PS& ps, int p_first, int M,
 #endif
 constexpr int kDepth = BITNET_STREAM_DEPTH;
 constexpr int kStreamMaxProblems = 16;          // problems one workgroup may touch
+// Groups of at most this many tokens keep the w_scale of their rows in LDS
+// for the output phase; larger ones read it from memory there (one load per
+// row after the loop), which leaves the LDS to the [M][rows] exact sums and
+// token rows that bound their shares.  Measured on MI355X (c2 group): from
+// memory, M = 4 streams 5% faster (4.32 -> 4.54 TB/s: larger shares fit), while
+// M = 1 and 2 lose 1.7% to the load's latency at the end of every workgroup.
+#ifndef BITNET_STREAM_WS_STAGE_MAX_M
+#define BITNET_STREAM_WS_STAGE_MAX_M 2
+#endif
+// LDS bytes per row of a workgroup's tiles besides the token rows: the M exact
+// sums and, when staged, w_scale (the block-scaled kernel keeps the w_scale
+// slot unused).
+__host__ __device__ inline bool stream_ws_staged(int M, bool blocked) {
+    return blocked || M <= BITNET_STREAM_WS_STAGE_MAX_M;
+}
 constexpr uint32_t kStreamOutOfRange = 0x80000000u;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -1101,6 +1116,7 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     // straight-line code, and the compiler's waits for the tokens then leave
     // every DMA in flight; otherwise produce() issues them.
     u32x4 raw[kQuantBatch][kQuantVecs];
+    const bool ws_staged = stream_ws_staged(PP.M, kBlocked);   // M is shared by the group
     auto prologue = [&](auto straight) __attribute__((always_inline)) {
         const int group_m = PP.M;                       // M is shared by the group
         const int batch_rows = (p_last - p_first + 1) * group_m;
@@ -1146,11 +1162,11 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
                 quantise_batch_load(ps, p_first, group_m, r, nr, raw);
                 quantise_batch(ps, p_first, group_m, nr, at, raw, q_lds, as_lds, rs_lds, red_fb, red_ib, t_begin);
             }
-            stage_w_scale();
+            if (ws_staged) stage_w_scale();
         } else {
             // the DMAs go out first; the token loads queue behind them and
             // behind the ring's first loads, so one memory latency covers all
-            stage_w_scale();
+            if (ws_staged) stage_w_scale();
             int off = 0;
             for (int pi = p_first; pi <= p_last; ++pi) {
                 const GemvProblem Pi = ps.get(pi);
@@ -1181,7 +1197,7 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
     }
     const int wg_rows = (t_end - t_begin) * 64;
     const float* ws_lds = reinterpret_cast<const float*>(q_lds + q_total);
-    int32_t* out_lds = reinterpret_cast<int32_t*>(q_lds + q_total) + wg_rows;   // [M][wg_rows] exact sums
+    int32_t* out_lds = reinterpret_cast<int32_t*>(q_lds + q_total) + (ws_staged ? wg_rows : 0);   // [M][wg_rows] exact sums
     int32_t* const bsum_lds = out_lds + ps.get(p_first).M * wg_rows;
 
     // kBlocked: the exact sum of q over each 256-k block (one k step) per
@@ -1331,6 +1347,15 @@ void gemv_stream_kernel(GemvProblem single, const GemvProblem* __restrict__ tabl
         const int t0 = max(t_begin, Pi.tile0), t1 = min(t_end, Pi.tile0 + Pi.ntiles);
         const int n0 = (t0 - Pi.tile0) * 64, lrow0 = (t0 - t_begin) * 64;
         const int rows = min((t1 - t0) * 64, Pi.N - n0);         // rows past N have no output
+        if (!kBlocked && !ws_staged) {
+            // w_scale from memory, once per row for all of its tokens
+            for (int rr = threadIdx.x; rr < rows; rr += kThreads) {
+                const float ws = gload<float>(Pi.w_scale + n0 + rr);
+                for (int m = 0; m < Pi.M; ++m)
+                    store_output<kOutBf16>(Pi, m, n0 + rr, out_lds[m * wg_rows + lrow0 + rr], as_lds[16 * j + m], ws);
+            }
+            continue;
+        }
         for (int m = 0; m < Pi.M; ++m) {
             const float as = as_lds[16 * j + m];
             const int32_t* const sums = out_lds + m * wg_rows + lrow0;
@@ -1677,7 +1702,7 @@ constexpr StreamSlotCosts kSlotCostsBlocked{BITNET_STREAM_FIRST_WEIGHT, BITNET_S
 // further problem) stays within `cap` and whose token rows, w_scale and exact sums
 // fit the LDS array.  Returns the end tile.
 int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_tiles, double cap, double rate,
-                   double start, int token_bytes, int64_t step_bytes, int64_t q_limit) {
+                   double start, int token_bytes, int64_t step_bytes, int64_t q_limit, bool blocked) {
     if (i >= total_tiles) return i;
     int p = host_find_problem(t, count, i);
     double cost = start;
@@ -1688,7 +1713,8 @@ int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_til
         const int64_t enter_bytes =
             static_cast<int64_t>(P.M) * padded_q_row(P.Kp) * token_bytes + step_bytes * stream_steps(P.Kp);
         const double tile_cost = P.steps / rate;
-        const int64_t tile_bytes = 64 * static_cast<int64_t>(sizeof(float)) * (1 + P.M);
+        const int64_t tile_bytes =
+            64 * static_cast<int64_t>(sizeof(float)) * ((token_bytes == 1 && !stream_ws_staged(P.M, blocked) ? 0 : 1) + P.M);
         const int64_t left = P.tile0 + P.ntiles - i;
         const double room = cap - cost - enter;
         const int64_t lds_room = q_limit - bytes - enter_bytes;
@@ -1711,14 +1737,15 @@ int64_t fill_share(const GemvProblem* t, int count, int64_t i, int64_t total_til
 // slots.second_start steps later.  False if no cost covers every tile within
 // the LDS limits.
 bool stream_bounds(const GemvProblem* t, int count, int64_t total_tiles, int grid, int n_first, int token_bytes,
-                   int64_t step_bytes, int64_t q_limit, const StreamSlotCosts& slots, std::vector<int32_t>& bounds) {
+                   int64_t step_bytes, int64_t q_limit, const StreamSlotCosts& slots, bool blocked,
+                   std::vector<int32_t>& bounds) {
     auto cover = [&](double cap, bool keep) {
         int64_t i = 0;
         for (int b = 0; b < grid; ++b) {
             if (keep) bounds[b] = static_cast<int32_t>(i);
             const double rate = b < n_first ? slots.first_weight / 100.0 : 1.0;
             const double start = b < n_first ? 0.0 : static_cast<double>(slots.second_start);
-            i = fill_share(t, count, i, total_tiles, cap, rate, start, token_bytes, step_bytes, q_limit);
+            i = fill_share(t, count, i, total_tiles, cap, rate, start, token_bytes, step_bytes, q_limit, blocked);
         }
         if (keep) bounds[grid] = static_cast<int32_t>(i);
         return i >= total_tiles;
@@ -1808,7 +1835,7 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
     // LDS per k step of each problem beyond its token rows: the block sums
     const int64_t step_bytes = blocked ? 16 * static_cast<int64_t>(sizeof(int32_t)) : 0;
     if (bounds && !stream_bounds(host_table, count, total_tiles, grid, n_first, token_bytes, step_bytes, q_limit,
-                                 slots, *bounds))
+                                 slots, blocked, *bounds))
         return false;
     // the shares must tile [0, total_tiles) in order, and the token rows of
     // each workgroup's problems must fit the static array
@@ -1836,8 +1863,10 @@ bool gemv_stream_plan(const GemvProblem* host_table, int count, int64_t total_ti
             spans[4 * static_cast<size_t>(b) + 1] = p1;
             spans[4 * static_cast<size_t>(b) + 2] = fits ? 1 : 0;
         }
-        // w_scale and the M exact sums of each row
-        size_t bytes = static_cast<size_t>(t1 - t0) * 64 * sizeof(float) * (1 + host_table[p0].M);
+        // w_scale (when staged) and the M exact sums of each row
+        const int M0 = host_table[p0].M;
+        size_t bytes = static_cast<size_t>(t1 - t0) * 64 * sizeof(float) *
+                       ((token_bytes == 1 && !stream_ws_staged(M0, blocked) ? 0 : 1) + M0);
         for (int i = p0; i <= p1; ++i)
             bytes += static_cast<size_t>(host_table[i].M) * padded_q_row(host_table[i].Kp) * token_bytes +
                      static_cast<size_t>(step_bytes) * stream_steps(host_table[i].Kp);
